@@ -1,0 +1,111 @@
+"""Builds seeded LoopVQ caches for tests: synthetic tokens, fixture codebooks,
+index pages encoded by the oracle (or drawn at random), bf16 pages, queries."""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import synth
+from oracle import lvq_oracle as orc
+
+
+@dataclass
+class Cache:
+    B: int
+    H: int
+    Hq: int
+    d: int
+    T: int
+    Tc: int
+    G: int
+    n_sink: int
+    n_recent: int
+    seq_len: np.ndarray
+    q_end: np.ndarray
+    pos: np.ndarray
+    page_table: np.ndarray
+    index_pages: np.ndarray
+    bf16_pages: np.ndarray
+    bf16_table: np.ndarray
+    codebooks: np.ndarray
+    q: np.ndarray                   # [T][B][Hq][d] bf16 bits
+    k_tokens: list = field(default_factory=list)
+    v_tokens: list = field(default_factory=list)
+
+    @property
+    def c(self):
+        return self.G // self.Tc
+
+    @property
+    def ng(self):
+        return self.d // self.c
+
+    @property
+    def nblk(self):
+        return self.T // self.Tc
+
+    def shape(self, rope_base=10000.0) -> orc.AttnShape:
+        return orc.AttnShape(self.B, self.H, self.Hq, self.d, self.T, self.Tc, self.G,
+                             self.n_sink, rope_base)
+
+    def oracle_attn(self, t, **kw):
+        return orc.decode_attn(self.shape(), self.q[t], self.page_table, self.index_pages,
+                               self.bf16_pages, self.bf16_table, self.codebooks, t, self.pos,
+                               self.seq_len, self.q_end, **kw)
+
+
+def build_cache(config: int, B: int, lengths, H: int, d: int, T: int, Tc: int, G: int,
+                n_sink: int, n_recent: int, Hq: int | None = None, books: str = "kmeans",
+                index: str = "oracle", shuffle: bool = True, q_end=None,
+                book_samples: int = 4096, keep_tokens: bool = True) -> Cache:
+    Hq = H if Hq is None else Hq
+    lengths = np.asarray(lengths, dtype=np.int32)
+    rk = np.random.default_rng(synth.seed_for(config, synth.STREAM_K))
+    rv = np.random.default_rng(synth.seed_for(config, synth.STREAM_V))
+    sc_k = synth.channel_scales(rk, H, d)
+    sc_v = synth.channel_scales(rv, H, d)
+    ks, vs = [], []
+    for b in range(B):
+        ks.append(synth.f32_to_bf16_bits(synth.gen_kv(rk, T, int(lengths[b]), H, d, sc_k)))
+        vs.append(synth.f32_to_bf16_bits(synth.gen_kv(rv, T, int(lengths[b]), H, d, sc_v)))
+    if q_end is None:
+        q_end = np.array([synth.prefill_q_end(int(L), n_recent) for L in lengths], dtype=np.int32)
+    q_end = np.asarray(q_end, dtype=np.int32)
+    if books == "kmeans":
+        cb = synth.kmeans_codebooks(config, T, Tc, G, H, d, sc_k, sc_v, n_samples=book_samples)
+    else:
+        cb = synth.random_codebooks(np.random.default_rng(synth.seed_for(config, synth.STREAM_BOOKS)),
+                                    T, Tc, G, H, d, scale=2.0)
+    c = G // Tc
+    ng, nblk = d // c, T // Tc
+    n_pages = [int(qe) // 8 for qe in q_end]
+    max_pages = max(1, max((int(L) + 7) // 8 for L in lengths))
+    rp = np.random.default_rng(synth.seed_for(config, synth.STREAM_PAGES))
+    if shuffle:
+        pt, pool = synth.shuffled_page_table(rp, n_pages, max_pages)
+    else:
+        pt = np.full((B, max_pages), -1, dtype=np.int32)
+        o = 0
+        for b, n in enumerate(n_pages):
+            pt[b, :n] = np.arange(o, o + n)
+            o += n
+        pool = o
+    pool = max(pool, 1)
+    if index == "oracle":
+        ip = np.zeros((pool, nblk, H, 2, 8, ng), dtype=np.uint8)
+        for b in range(B):
+            qe = int(q_end[b])
+            if qe == 0:
+                continue
+            for kv, toks in ((0, ks[b]), (1, vs[b])):
+                r = orc.encode(toks[:, :qe], cb, kv, T, Tc, G)
+                orc.scatter_index_pages(r.idx, kv, pt[b, :qe // 8], ip)
+    else:
+        ip = synth.random_index_pages(rp, pool, nblk, H, ng)
+    bp, lay = synth.pack_bf16_pages(ks, vs, q_end, T, H, d, rng=rp if shuffle else None)
+    rq = np.random.default_rng(synth.seed_for(config, synth.STREAM_Q))
+    q = synth.gen_queries(rq, T, B, Hq, d)
+    return Cache(B, H, Hq, d, T, Tc, G, n_sink, n_recent, lengths.copy(), q_end,
+                 lengths.copy(), pt, ip, bp, lay.bf16_table, cb, q,
+                 ks if keep_tokens else [], vs if keep_tokens else [])
