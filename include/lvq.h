@@ -1,0 +1,217 @@
+/*
+ * lvq.h -- C ABI of the LoopVQ hot path for AMD Instinct MI355X (gfx950).
+ *
+ * LoopVQ codes the KV cache of a looped transformer along the loop axis: the T
+ * loop steps are split into contiguous blocks of Tc steps, and one 8-bit code
+ * (K = 256 codewords) covers c = G / Tc channels of every step of a block, so
+ * the cache keeps 8 / G bits per element whatever Tc is.  Each loop step reads
+ * back only its own c-channel share of the chosen codeword.  Keys are coded
+ * before RoPE; attention applies RoPE to the reconstructed keys.  Sources:
+ * the LoopVQ summary (onedev.kr/papers/1681), sections "무엇과 다른가" (the
+ * joint code, the shared index, pre-RoPE keys) and "전제와 한계" (8-token
+ * pages, bf16 sink and recent tokens, one index row per loop block, encoding by
+ * a codebook-distance matrix product once all Tc steps exist, re-encoding the
+ * oldest recent page every 8 decode tokens, a decode kernel that reads only the
+ * loop-step-t codebook slice and merges Flash-Decoding splits with a
+ * log-sum-exp); the rit.work LoopVQ article, section "Когда LoopVQ меняет план
+ * развёртывания" (keys and values both rebuilt from the codebooks, merged with
+ * the uncompressed part of the cache).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array argument is DEVICE memory owned by the caller.  The library
+ *    never allocates, frees or keeps a pointer; scratch space comes only from
+ *    the caller's workspace argument.
+ *  - bf16 arrays are passed as uint16_t bit patterns.  All layouts are dense,
+ *    row-major, with the listed dimension order (last dimension contiguous).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    with no host synchronisation; outputs are valid once the stream has
+ *    reached that point.  Entry points are thread-safe; the only state is the
+ *    calling thread's last error string.
+ *  - The return value is a status code.  Every argument check happens on the
+ *    host before anything is enqueued, so on a non-zero status nothing ran.
+ *    LVQ_EINVAL: a null pointer, a size <= 0 where one is required, Tc not
+ *    dividing T or G, c = G/Tc not dividing d, t >= T, Hq not a multiple of H,
+ *    n_sink > 8, a table too small for the requested lengths.
+ *    LVQ_EUNSUPPORTED: a valid shape outside the compiled set (see each call).
+ *    LVQ_ENOSPC: the workspace is smaller than the size query returns.
+ *    LVQ_EDEVICE: a HIP launch error.
+ *  - Device-side indices (page ids, page-table entries) are range-checked in
+ *    the kernels: an out-of-range id is skipped (its tokens are treated as
+ *    absent / its rows are not written) instead of being dereferenced.
+ *  - Codebook values must lie in the float16 range (|x| < 65504): the decode
+ *    kernel stages the step-t slice in LDS as float16, which holds every such
+ *    bfloat16 value exactly up to float16 subnormals.
+ *  - Code indices are unsigned bytes; any value 0..255 is a valid code.
+ */
+#ifndef LVQ_H
+#define LVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LVQ_ABI_VERSION 1
+#define LVQ_PAGE 8      /* tokens per cache page */
+#define LVQ_NCODES 256  /* codewords per codebook (8-bit codes) */
+
+enum lvq_status {
+  LVQ_OK = 0,
+  LVQ_EINVAL = 1,
+  LVQ_EUNSUPPORTED = 2,
+  LVQ_ENOSPC = 3,
+  LVQ_EDEVICE = 4
+};
+
+/* ABI version (LVQ_ABI_VERSION of the built library). */
+int lvq_version(void);
+
+/* Text describing the calling thread's last non-zero status ("" if none). */
+const char* lvq_last_error(void);
+
+/*
+ * Codebook layout (all encode and decode calls):
+ *   codebooks: bf16 [nblk][2][H][ng][Tc][256][c], nblk = T/Tc, c = G/Tc,
+ *   ng = d/c.  Index [beta][kv][h][g][tau][k][i] is element tau*c + i of
+ *   codeword k of the book of loop block beta, K (kv = 0) or V (kv = 1),
+ *   KV head h and channel group g (channels g*c .. g*c+c-1).  The step-tau
+ *   share of every codeword of a book is one contiguous [256][c] slice.
+ *
+ * Joint vector of (block beta, token n, head h, group g), G elements:
+ *   x[tau*c + i] = X[beta*Tc + tau][n][h][g*c + i],  tau < Tc, i < c.
+ * Its code is the lowest index k minimising the squared L2 distance
+ * sum_e (x[e] - codeword_k[e])^2 (the summary, section "전제와 한계", computes
+ * these distances with a matrix product; the kernel uses the expansion
+ * |x|^2 - 2 x.C + |C|^2 on bf16 MFMA with float32 accumulation and recomputes
+ * in float64, by direct differences, every vector whose top two candidates
+ * are too close for float32 to separate them).
+ *
+ * Supported encoder shapes: G in {16, 32}; c = G/Tc in {8, 16, 32} for
+ * G = 32 and {4, 8, 16} for G = 16; d in {64, 128}.
+ */
+
+/*
+ * lvq_encode -- code one of K or V for N tokens (prefill).
+ *   kv:        bf16 [T][N][H][d], the keys (pre-RoPE) or values of all T steps.
+ *   codebooks: see above.  kv_sel = 0 uses the K books, 1 the V books.
+ *   idx:       out, uint8 [nblk][N][H][ng].
+ * Encoding needs all Tc steps of a block (the summary, section "전제와 한계").
+ */
+int lvq_encode(const uint16_t* kv, const uint16_t* codebooks, int kv_sel, int T, int Tc,
+               int G, int N, int H, int d, uint8_t* idx, void* stream);
+
+/*
+ * lvq_encode_pages -- as lvq_encode, but writes the rows into the paged cache.
+ *   chunk_page:  int32 [N/8], physical coded page of tokens 8j .. 8j+7.  N must
+ *                be a multiple of 8.  Ids outside [0, n_index_pages) are skipped.
+ *   index_pages: in/out, uint8 [n_index_pages][nblk][H][2][8][ng].  Token n is
+ *                written to page chunk_page[n/8], half kv_sel, slot n%8: one
+ *                index row per loop block (the summary, section "전제와 한계").
+ *                Only the rows of the selected half are written.
+ */
+int lvq_encode_pages(const uint16_t* kv, const uint16_t* codebooks, int kv_sel, int T, int Tc,
+                     int G, int N, int H, int d, const int32_t* chunk_page, int n_index_pages,
+                     uint8_t* index_pages, void* stream);
+
+/*
+ * lvq_reencode_pages -- decode-time re-encode: code whole bf16 pages (every
+ * loop step, head, K and V) into coded pages, all in one launch.  This is the
+ * step that turns the oldest recent page of a sequence into index rows every
+ * 8 generated tokens (the summary, section "전제와 한계").
+ *   bf16_pages:  bf16 [n_bf16_pages][T][H][2][8][d] (pre-RoPE keys, values).
+ *   src_pages:   int32 [n], bf16 pages to encode.
+ *   dst_pages:   int32 [n], coded pages to write (all 8 slots, K and V halves).
+ *   index_pages: in/out, uint8 [n_index_pages][nblk][H][2][8][ng].
+ * Ids out of range are skipped.  n = 0 is a no-op.
+ */
+int lvq_reencode_pages(const uint16_t* bf16_pages, const int32_t* src_pages,
+                       const int32_t* dst_pages, int n, const uint16_t* codebooks, int T, int Tc,
+                       int G, int H, int d, int n_bf16_pages, int n_index_pages,
+                       uint8_t* index_pages, void* stream);
+
+/*
+ * RoPE phase tables (rotate-half convention: channel j pairs with j + d/2 and
+ * turns by the angle p * theta_j, theta_j = base^(-2j/d)).  Phases are formed
+ * in float64 (angle and cos/sin); the table holds, in order:
+ *   float32 rows 0 .. ntile-1:       (cos, sin)(16 a * theta_j), j < d/2   (a = p / 16)
+ *   float32 rows ntile .. ntile+15:  (cos, sin)(o * theta_j),    j < d/2   (o = p % 16)
+ *   float64 theta_j, j < d/2
+ * with ntile = ceil(max_len / 16) and float32 row layout [d/2][2].  A position
+ * p < max_len is the float32 product of one row of each of the first two parts
+ * (error ~1e-7).  The table must be built with the d of the decode call.
+ */
+size_t lvq_rope_table_bytes(int max_len, int d);
+int lvq_rope_tables(int max_len, int d, double base, float* rope_tab, size_t rope_bytes,
+                    void* stream);
+
+/* Shape of one decode-attention call. */
+typedef struct lvq_attn_shape {
+  int32_t B;              /* sequences */
+  int32_t H;              /* KV heads */
+  int32_t Hq;             /* query heads, a multiple of H; query head hq reads KV head hq/(Hq/H) */
+  int32_t d;              /* head dim (64 or 128) */
+  int32_t T, Tc, G;       /* loop steps, steps per joint block, joint length */
+  int32_t n_sink;         /* bf16 sink tokens (<= 8), read from the bf16 copy of page 0 */
+  int32_t max_pages;      /* row length of page_table */
+  int32_t bf16_row;       /* row length of bf16_table */
+  int32_t n_index_pages;  /* rows of index_pages (range check of page ids) */
+  int32_t n_bf16_pages;   /* rows of bf16_pages */
+  int32_t max_seq_len;    /* upper bound of seq_len[b]; sizes the split grid */
+  int32_t rope_max_len;   /* max_len the rope table was built for; every pos and seq_len must be < it */
+  int32_t n_splits;       /* coded-token splits per (b, hq); 0 = automatic */
+  float scale;            /* softmax scale; 0 = 1/sqrt(d) */
+} lvq_attn_shape;
+
+/* Workspace bytes of lvq_decode_attn / lvq_decode_scores for this shape. */
+size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp);
+
+/*
+ * lvq_decode_attn -- decode attention at loop step t over the paged cache.
+ *   q:           bf16 [B][Hq][d], pre-RoPE query of loop step t.
+ *   page_table:  int32 [B][max_pages], logical page -> coded page id.  Entries of
+ *                logical pages 0 .. q_end[b]/8 - 1 are read.
+ *   index_pages: uint8 [n_index_pages][nblk][H][2][8][ng] (layout of lvq_encode_pages).
+ *   bf16_pages:  bf16 [n_bf16_pages][T][H][2][8][d], pre-RoPE keys and values.
+ *   bf16_table:  int32 [B][bf16_row]: entry 0 = bf16 copy of logical page 0 (the
+ *                sink tokens), entries 1.. = the pages of logical pages q_end/8,
+ *                q_end/8 + 1, ... (the recent window).
+ *   codebooks:   see above.
+ *   t:           loop step, 0 <= t < T; block t/Tc, step slice t%Tc are read.
+ *   pos:         int32 [B], RoPE position of the query.
+ *   seq_len:     int32 [B], cached tokens L_b (positions 0 .. L_b-1).
+ *   q_end:       int32 [B], multiple of 8: tokens [n_sink, q_end) are coded,
+ *                [0, n_sink) and [q_end, L_b) are bf16 (sink wins where both apply).
+ *   rope_tab:    table built by lvq_rope_tables for this d and base.
+ *   out:         float32 [B][Hq][d], softmax(q'.k'/scale) v over all L_b tokens.
+ *   lse:         float32 [B][Hq] or NULL: natural log-sum-exp of the scaled scores.
+ *   ws:          workspace of at least lvq_decode_attn_workspace_bytes(shp) bytes.
+ * Each call overwrites the workspace; concurrent calls need distinct workspaces.
+ * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.
+ */
+int lvq_decode_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
+                    const uint16_t* bf16_pages, const int32_t* bf16_table,
+                    const uint16_t* codebooks, int t, const int32_t* pos, const int32_t* seq_len,
+                    const int32_t* q_end, const float* rope_tab, const lvq_attn_shape* shp,
+                    float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * lvq_decode_scores -- test probe: same inputs and device code as
+ * lvq_decode_attn, but also writes the scaled scores q'.k' * scale (natural
+ * units) of every cached token to scores: float32 [B][Hq][max_seq_len]
+ * (entries at p >= seq_len[b] are left untouched).  out and lse are produced too.
+ */
+int lvq_decode_scores(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
+                      const uint16_t* bf16_pages, const int32_t* bf16_table,
+                      const uint16_t* codebooks, int t, const int32_t* pos,
+                      const int32_t* seq_len, const int32_t* q_end, const float* rope_tab,
+                      const lvq_attn_shape* shp, float* out, float* lse, float* scores,
+                      void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LVQ_H */

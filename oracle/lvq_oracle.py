@@ -299,12 +299,13 @@ def attend(qr: np.ndarray, Kr: np.ndarray, V: np.ndarray, scale: float):
 
 def decode_attn(shp: AttnShape, q_bits, page_table, index_pages, bf16_pages, bf16_table,
                 codebooks_bits, t: int, pos, seq_len, q_end, return_scores: bool = False,
-                heads=None):
+                heads=None, pairs=None):
     """Decode attention at loop step t over the paged LoopVQ cache.
 
     Returns ``out[B][Hq][d]`` and ``lse[B][Hq]`` (float64) and optionally the
     scaled scores per (b, hq).  Query head hq reads KV head hq // (Hq / H).
-    ``heads`` optionally restricts the query heads computed (others are NaN).
+    ``heads`` (query heads) or ``pairs`` ((b, hq) list) optionally restrict what is
+    computed; the rest is NaN.
     """
     B, Hq, d = shp.B, shp.Hq, shp.d
     grp = Hq // shp.H
@@ -314,20 +315,21 @@ def decode_attn(shp: AttnShape, q_bits, page_table, index_pages, bf16_pages, bf1
     lse = np.full((B, Hq), np.nan)
     scores = {}
     cache = {}
-    for b in range(B):
+    if pairs is None:
+        pairs = [(b, hq) for b in range(B) for hq in (range(Hq) if heads is None else heads)]
+    for b, hq in pairs:
         L = int(seq_len[b])
-        for hq in (range(Hq) if heads is None else heads):
-            h = hq // grp
-            if (b, h) not in cache:
-                K, V = reconstruct_kv(shp, b, h, t, L, int(q_end[b]), page_table, index_pages,
-                                      bf16_pages, bf16_table, cb)
-                cache[(b, h)] = (rope(K, np.arange(L), shp.rope_base), V)
-            Kr, V = cache[(b, h)]
-            qr = rope(q[b, hq], int(pos[b]), shp.rope_base)
-            o, ls, s = attend(qr, Kr, V, shp.sm_scale)
-            out[b, hq], lse[b, hq] = o, ls
-            if return_scores:
-                scores[(b, hq)] = s
+        h = hq // grp
+        if (b, h) not in cache:
+            K, V = reconstruct_kv(shp, b, h, t, L, int(q_end[b]), page_table, index_pages,
+                                  bf16_pages, bf16_table, cb)
+            cache[(b, h)] = (rope(K, np.arange(L), shp.rope_base), V)
+        Kr, V = cache[(b, h)]
+        qr = rope(q[b, hq], int(pos[b]), shp.rope_base)
+        o, ls, s = attend(qr, Kr, V, shp.sm_scale)
+        out[b, hq], lse[b, hq] = o, ls
+        if return_scores:
+            scores[(b, hq)] = s
     if return_scores:
         return out, lse, scores
     return out, lse

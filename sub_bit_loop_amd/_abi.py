@@ -1,0 +1,232 @@
+"""ctypes binding of liblvq.so (include/lvq.h).
+
+Argument marshalling only: tensors are checked for device, dtype and layout,
+and their data pointers and the current HIP stream are handed to the C ABI.
+Every step of the hot path runs in the library's kernels; there is no fallback,
+and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblvq.so")
+
+LVQ_OK, LVQ_EINVAL, LVQ_EUNSUPPORTED, LVQ_ENOSPC, LVQ_EDEVICE = range(5)
+PAGE = 8
+NCODES = 256
+
+_i32, _f32, _f64, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_size_t, ctypes.c_void_p
+
+
+class LvqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"lvq status {status}: {msg}")
+        self.status = status
+
+
+class AttnShape(ctypes.Structure):
+    """Mirror of lvq_attn_shape."""
+    _fields_ = [(n, _i32) for n in ("B", "H", "Hq", "d", "T", "Tc", "G", "n_sink", "max_pages",
+                                   "bf16_row", "n_index_pages", "n_bf16_pages", "max_seq_len",
+                                   "rope_max_len", "n_splits")] + [("scale", _f32)]
+
+
+_SIGS = {
+    "lvq_version": (_i32, []),
+    "lvq_last_error": (ctypes.c_char_p, []),
+    "lvq_encode": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "lvq_encode_pages": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
+    "lvq_reencode_pages": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "lvq_rope_table_bytes": (_sz, [_i32, _i32]),
+    "lvq_rope_tables": (_i32, [_i32, _i32, _f64, _vp, _sz, _vp]),
+    "lvq_decode_attn_workspace_bytes": (_sz, [ctypes.POINTER(AttnShape)]),
+    "lvq_decode_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
+                               ctypes.POINTER(AttnShape), _vp, _vp, _vp, _sz, _vp]),
+    "lvq_decode_scores": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
+                                 ctypes.POINTER(AttnShape), _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+EXPORTS = tuple(_SIGS)
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblvq.so (built in-tree); raises if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise LvqError(LVQ_EDEVICE, f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int) -> None:
+    if status != LVQ_OK:
+        raise LvqError(status, lib().lvq_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, ndim: int | None = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+BF16 = (torch.bfloat16, torch.int16, torch.uint16)   # bf16 bit patterns
+I32 = (torch.int32,)
+U8 = (torch.uint8,)
+F32 = (torch.float32,)
+
+
+def lvq_version() -> int:
+    return lib().lvq_version()
+
+
+def lvq_encode(kv, codebooks, kv_sel: int, T: int, Tc: int, G: int, idx=None) -> torch.Tensor:
+    """kv bf16 [T][N][H][d], codebooks bf16 [nblk][2][H][ng][Tc][256][c] -> idx uint8 [nblk][N][H][ng]."""
+    _dev(kv, "kv", BF16, 4)
+    _dev(codebooks, "codebooks", BF16, 7)
+    T_, N, H, d = kv.shape
+    if T_ != T:
+        raise ValueError("kv.shape[0] != T")
+    c = G // Tc if Tc > 0 else 0
+    ng = d // c if c > 0 else 0
+    if idx is None:
+        idx = torch.empty((max(T // max(Tc, 1), 0), N, H, ng), dtype=torch.uint8, device=kv.device)
+    _dev(idx, "idx", U8)
+    _check(lib().lvq_encode(_ptr(kv), _ptr(codebooks), kv_sel, T, Tc, G, N, H, d, _ptr(idx), _stream(kv)))
+    return idx
+
+
+def lvq_encode_pages(kv, codebooks, kv_sel: int, T: int, Tc: int, G: int, chunk_page,
+                     index_pages) -> torch.Tensor:
+    """Encode kv [T][N][H][d] into index_pages [P][nblk][H][2][8][ng] at pages chunk_page [N/8]."""
+    _dev(kv, "kv", BF16, 4)
+    _dev(codebooks, "codebooks", BF16, 7)
+    _dev(chunk_page, "chunk_page", I32, 1)
+    _dev(index_pages, "index_pages", U8, 6)
+    T_, N, H, d = kv.shape
+    if chunk_page.numel() * PAGE < N:
+        raise ValueError("chunk_page too short")
+    _check(lib().lvq_encode_pages(_ptr(kv), _ptr(codebooks), kv_sel, T, Tc, G, N, H, d,
+                                  _ptr(chunk_page), index_pages.shape[0], _ptr(index_pages),
+                                  _stream(kv)))
+    return index_pages
+
+
+def lvq_reencode_pages(bf16_pages, src_pages, dst_pages, codebooks, T: int, Tc: int, G: int,
+                       index_pages) -> torch.Tensor:
+    """Encode whole bf16 pages src_pages[i] (all steps, heads, K and V) into coded pages dst_pages[i]."""
+    _dev(bf16_pages, "bf16_pages", BF16, 6)
+    _dev(src_pages, "src_pages", I32, 1)
+    _dev(dst_pages, "dst_pages", I32, 1)
+    _dev(codebooks, "codebooks", BF16, 7)
+    _dev(index_pages, "index_pages", U8, 6)
+    if src_pages.numel() != dst_pages.numel():
+        raise ValueError("src_pages and dst_pages differ in length")
+    _, T_, H, _, _, d = bf16_pages.shape
+    _check(lib().lvq_reencode_pages(_ptr(bf16_pages), _ptr(src_pages), _ptr(dst_pages),
+                                    src_pages.numel(), _ptr(codebooks), T, Tc, G, H, d,
+                                    bf16_pages.shape[0], index_pages.shape[0], _ptr(index_pages),
+                                    _stream(bf16_pages)))
+    return index_pages
+
+
+def lvq_rope_table_bytes(max_len: int, d: int) -> int:
+    return lib().lvq_rope_table_bytes(max_len, d)
+
+
+def lvq_rope_tables(max_len: int, d: int, base: float = 10000.0, device="cuda") -> torch.Tensor:
+    n = lvq_rope_table_bytes(max_len, d)
+    if n == 0:
+        raise LvqError(LVQ_EINVAL, "invalid rope table size")
+    tab = torch.empty(n // 4, dtype=torch.float32, device=device)
+    _check(lib().lvq_rope_tables(max_len, d, float(base), _ptr(tab), n, _stream(tab)))
+    return tab
+
+
+def make_shape(B, H, Hq, d, T, Tc, G, n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages,
+               max_seq_len, rope_max_len, n_splits=0, scale=0.0) -> AttnShape:
+    return AttnShape(B, H, Hq, d, T, Tc, G, n_sink, max_pages, bf16_row, n_index_pages,
+                     n_bf16_pages, max_seq_len, rope_max_len, n_splits, scale)
+
+
+def lvq_decode_attn_workspace_bytes(shp: AttnShape) -> int:
+    return lib().lvq_decode_attn_workspace_bytes(ctypes.byref(shp))
+
+
+def _attn_call(fn, q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos, seq_len,
+               q_end, rope_tab, shp: AttnShape, out, lse, ws, scores=None):
+    _dev(q, "q", BF16, 3)
+    _dev(page_table, "page_table", I32, 2)
+    _dev(index_pages, "index_pages", U8, 6)
+    _dev(bf16_pages, "bf16_pages", BF16, 6)
+    _dev(bf16_table, "bf16_table", I32, 2)
+    _dev(codebooks, "codebooks", BF16, 7)
+    for name, x in (("pos", pos), ("seq_len", seq_len), ("q_end", q_end)):
+        _dev(x, name, I32, 1)
+    _dev(rope_tab, "rope_tab", F32, 1)
+    if tuple(page_table.shape) != (shp.B, shp.max_pages) or tuple(bf16_table.shape) != (shp.B, shp.bf16_row):
+        raise ValueError("page_table / bf16_table do not match the shape")
+    if index_pages.shape[0] != shp.n_index_pages or bf16_pages.shape[0] != shp.n_bf16_pages:
+        raise ValueError("pool sizes do not match the shape")
+    if rope_tab.numel() * 4 < lvq_rope_table_bytes(shp.rope_max_len, shp.d):
+        raise ValueError("rope table too small")
+    dev = q.device
+    if out is None:
+        out = torch.empty((shp.B, shp.Hq, shp.d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((shp.B, shp.Hq), dtype=torch.float32, device=dev)
+    need = lvq_decode_attn_workspace_bytes(shp)
+    if ws is None:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    _dev(out, "out", F32)
+    _dev(lse, "lse", F32)
+    args = [_ptr(q), _ptr(page_table), _ptr(index_pages), _ptr(bf16_pages), _ptr(bf16_table),
+            _ptr(codebooks), int(t), _ptr(pos), _ptr(seq_len), _ptr(q_end), _ptr(rope_tab),
+            ctypes.byref(shp), _ptr(out), _ptr(lse)]
+    if scores is not None:
+        _dev(scores, "scores", F32)
+        args.append(_ptr(scores))
+    args += [_ptr(ws), ws.numel() * ws.element_size(), _stream(q)]
+    _check(fn(*args))
+    return out, lse
+
+
+def lvq_decode_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos,
+                    seq_len, q_end, rope_tab, shp: AttnShape, out=None, lse=None, ws=None):
+    """Decode attention at loop step t; returns (out [B][Hq][d] f32, lse [B][Hq] f32)."""
+    return _attn_call(lib().lvq_decode_attn, q, page_table, index_pages, bf16_pages, bf16_table,
+                      codebooks, t, pos, seq_len, q_end, rope_tab, shp, out, lse, ws)
+
+
+def lvq_decode_scores(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos,
+                      seq_len, q_end, rope_tab, shp: AttnShape, out=None, lse=None, ws=None):
+    """Test probe: (out, lse, scores [B][Hq][max_seq_len] f32, NaN where not written)."""
+    scores = torch.full((shp.B, shp.Hq, shp.max_seq_len), math.nan, dtype=torch.float32, device=q.device)
+    out, lse = _attn_call(lib().lvq_decode_scores, q, page_table, index_pages, bf16_pages,
+                          bf16_table, codebooks, t, pos, seq_len, q_end, rope_tab, shp, out, lse,
+                          ws, scores=scores)
+    return out, lse, scores

@@ -1,0 +1,291 @@
+// C ABI of the LoopVQ hot path: argument validation, split planning and
+// dispatch to the HIP kernels.  Nothing here allocates device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "lvq_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return LVQ_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(LVQ_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shape rules shared by the encoder and the decoder (Tc | T, Tc | G, c | d).
+int check_code_shape(int T, int Tc, int G, int d) {
+  if (T <= 0 || Tc <= 0 || G <= 0 || d <= 0)
+    return fail(LVQ_EINVAL, "T=%d Tc=%d G=%d d=%d must be positive", T, Tc, G, d);
+  if (T % Tc || G % Tc) return fail(LVQ_EINVAL, "Tc=%d must divide T=%d and G=%d", Tc, T, G);
+  if (d % (G / Tc)) return fail(LVQ_EINVAL, "c=G/Tc=%d must divide d=%d", G / Tc, d);
+  if (d % 2) return fail(LVQ_EINVAL, "d=%d must be even", d);
+  return LVQ_OK;
+}
+
+struct SplitPlan {
+  int n_chunks;
+  int chunk_pages;
+};
+
+// Coded pages of a sequence are cut into chunks of whole 64-token tiles; one
+// wave works on one chunk.  Automatic sizing aims at about two waves per SIMD
+// of work (2048 chunks) while keeping a chunk at 16 tiles or more.
+SplitPlan plan_splits(const lvq_attn_shape& s) {
+  const int max_pages = (s.max_seq_len + lvq::kPage - 1) / lvq::kPage;
+  const int max_tiles = (max_pages + 7) / 8;
+  int n = s.n_splits;
+  if (n <= 0) {
+    const long items = (long)s.B * s.Hq;
+    n = (int)((2048 + items - 1) / items);
+    n = n < 1 ? 1 : n;
+    const int by_len = max_tiles / 16;
+    if (n > by_len) n = by_len < 1 ? 1 : by_len;
+  }
+  if (n > max_tiles) n = max_tiles < 1 ? 1 : max_tiles;
+  if (n > 1023) n = 1023;                       // merge kernel bound on splits
+  const int tiles = (max_tiles + n - 1) / n;
+  SplitPlan p;
+  p.chunk_pages = (tiles < 1 ? 1 : tiles) * 8;
+  p.n_chunks = (max_pages + p.chunk_pages - 1) / p.chunk_pages;
+  if (p.n_chunks < 1) p.n_chunks = 1;
+  return p;
+}
+
+int check_attn(const void* q, const void* page_table, const void* index_pages,
+               const void* bf16_pages, const void* bf16_table, const void* codebooks, int t,
+               const void* pos, const void* seq_len, const void* q_end, const void* rope_tab,
+               const lvq_attn_shape* shp, const void* out) {
+  if (!shp) return fail(LVQ_EINVAL, "shape is null");
+  const lvq_attn_shape& s = *shp;
+  if (!q || !page_table || !index_pages || !bf16_pages || !bf16_table || !codebooks || !pos ||
+      !seq_len || !q_end || !rope_tab || !out)
+    return fail(LVQ_EINVAL, "null pointer argument");
+  if (s.B <= 0 || s.H <= 0 || s.Hq <= 0) return fail(LVQ_EINVAL, "B, H, Hq must be positive");
+  if (s.Hq % s.H) return fail(LVQ_EINVAL, "Hq=%d must be a multiple of H=%d", s.Hq, s.H);
+  int st = check_code_shape(s.T, s.Tc, s.G, s.d);
+  if (st) return st;
+  if (t < 0 || t >= s.T) return fail(LVQ_EINVAL, "t=%d outside [0, T=%d)", t, s.T);
+  if (s.n_sink < 0 || s.n_sink > lvq::kPage) return fail(LVQ_EINVAL, "n_sink=%d outside [0, 8]", s.n_sink);
+  if (s.max_seq_len <= 0) return fail(LVQ_EINVAL, "max_seq_len must be positive");
+  if ((long)s.max_pages * lvq::kPage < s.max_seq_len)
+    return fail(LVQ_EINVAL, "max_pages=%d too small for max_seq_len=%d", s.max_pages, s.max_seq_len);
+  if (s.bf16_row < 1) return fail(LVQ_EINVAL, "bf16_row must be >= 1");
+  if (s.n_index_pages < 0 || s.n_bf16_pages <= 0) return fail(LVQ_EINVAL, "pool sizes must be positive");
+  if (s.rope_max_len <= s.max_seq_len)
+    return fail(LVQ_EINVAL, "rope_max_len=%d must exceed max_seq_len=%d", s.rope_max_len, s.max_seq_len);
+  if (!(s.scale >= 0.f) || isinf(s.scale)) return fail(LVQ_EINVAL, "scale must be finite and >= 0");
+  if (!lvq::attn_supported(s.d, s.G / s.Tc))
+    return fail(LVQ_EUNSUPPORTED, "decode shape d=%d c=%d not compiled (d=128: c in {8,16,32}; d=64: c in {8,16})",
+                s.d, s.G / s.Tc);
+  return LVQ_OK;
+}
+
+size_t workspace_bytes(const lvq_attn_shape& s) {
+  const SplitPlan p = plan_splits(s);
+  return (size_t)s.B * s.Hq * (p.n_chunks + 1) * (s.d + 2) * sizeof(float);
+}
+
+int run_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
+             const uint16_t* bf16_pages, const int32_t* bf16_table, const uint16_t* codebooks,
+             int t, const int32_t* pos, const int32_t* seq_len, const int32_t* q_end,
+             const float* rope_tab, const lvq_attn_shape* shp, float* out, float* lse,
+             float* scores, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos,
+                      seq_len, q_end, rope_tab, shp, out);
+  if (st) return st;
+  const lvq_attn_shape& s = *shp;
+  const size_t need = workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(LVQ_ENOSPC, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  const SplitPlan p = plan_splits(s);
+  lvq::AttnArgs a{};
+  a.q = q;
+  a.page_table = page_table;
+  a.index_pages = index_pages;
+  a.bf16_pages = bf16_pages;
+  a.bf16_table = bf16_table;
+  a.codebooks = codebooks;
+  a.pos = pos;
+  a.seq_len = seq_len;
+  a.q_end = q_end;
+  a.rope = rope_tab;
+  a.part = (float*)ws;
+  a.out = out;
+  a.lse = lse;
+  a.scores = scores;
+  a.t = t;
+  a.B = s.B;
+  a.H = s.H;
+  a.Hq = s.Hq;
+  a.d = s.d;
+  a.T = s.T;
+  a.Tc = s.Tc;
+  a.G = s.G;
+  a.n_sink = s.n_sink;
+  a.max_pages = s.max_pages;
+  a.bf16_row = s.bf16_row;
+  a.n_index_pages = s.n_index_pages;
+  a.n_bf16_pages = s.n_bf16_pages;
+  a.max_seq_len = s.max_seq_len;
+  a.rope_tiles = (s.rope_max_len + lvq::rope_tile() - 1) / lvq::rope_tile();
+  a.n_chunks = p.n_chunks;
+  a.chunk_pages = p.chunk_pages;
+  const float scale = s.scale > 0.f ? s.scale : 1.0f / sqrtf((float)s.d);
+  a.scale_log2e = scale * 1.4426950408889634f;
+  return device_status(lvq::launch_attn(a, (hipStream_t)stream), "lvq_decode_attn launch");
+}
+
+int check_encode_common(const void* kv, const void* codebooks, int T, int Tc, int G, int N,
+                        int H, int d) {
+  if (!kv || !codebooks) return fail(LVQ_EINVAL, "null pointer argument");
+  int st = check_code_shape(T, Tc, G, d);
+  if (st) return st;
+  if (N < 0 || H <= 0) return fail(LVQ_EINVAL, "N=%d must be >= 0 and H=%d > 0", N, H);
+  if (!lvq::encode_supported(G, G / Tc, d))
+    return fail(LVQ_EUNSUPPORTED, "encode shape G=%d c=%d d=%d not compiled", G, G / Tc, d);
+  return LVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lvq_version(void) { return LVQ_ABI_VERSION; }
+
+const char* lvq_last_error(void) { return g_err.c_str(); }
+
+int lvq_encode(const uint16_t* kv, const uint16_t* codebooks, int kv_sel, int T, int Tc, int G,
+               int N, int H, int d, uint8_t* idx, void* stream) {
+  int st = check_encode_common(kv, codebooks, T, Tc, G, N, H, d);
+  if (st) return st;
+  if (!idx) return fail(LVQ_EINVAL, "null pointer argument");
+  if (kv_sel != 0 && kv_sel != 1) return fail(LVQ_EINVAL, "kv_sel=%d must be 0 or 1", kv_sel);
+  if (N == 0) return ok();
+  lvq::EncodeArgs a{};
+  a.src = kv;
+  a.codebooks = codebooks;
+  a.out = idx;
+  a.src_mode = lvq::kSrcDense;
+  a.dst_mode = lvq::kDstDense;
+  a.kv_sel = kv_sel;
+  a.T = T; a.Tc = Tc; a.G = G; a.N = N; a.H = H; a.d = d;
+  a.tokens_per_block = 512;
+  return device_status(lvq::launch_encode(a, (hipStream_t)stream), "lvq_encode launch");
+}
+
+int lvq_encode_pages(const uint16_t* kv, const uint16_t* codebooks, int kv_sel, int T, int Tc,
+                     int G, int N, int H, int d, const int32_t* chunk_page, int n_index_pages,
+                     uint8_t* index_pages, void* stream) {
+  int st = check_encode_common(kv, codebooks, T, Tc, G, N, H, d);
+  if (st) return st;
+  if (!index_pages || (N > 0 && !chunk_page)) return fail(LVQ_EINVAL, "null pointer argument");
+  if (kv_sel != 0 && kv_sel != 1) return fail(LVQ_EINVAL, "kv_sel=%d must be 0 or 1", kv_sel);
+  if (N % lvq::kPage) return fail(LVQ_EINVAL, "N=%d must be a multiple of 8", N);
+  if (n_index_pages < 0) return fail(LVQ_EINVAL, "n_index_pages must be >= 0");
+  if (N == 0) return ok();
+  lvq::EncodeArgs a{};
+  a.src = kv;
+  a.codebooks = codebooks;
+  a.out = index_pages;
+  a.dst_pages = chunk_page;
+  a.src_mode = lvq::kSrcDense;
+  a.dst_mode = lvq::kDstPages;
+  a.kv_sel = kv_sel;
+  a.T = T; a.Tc = Tc; a.G = G; a.N = N; a.H = H; a.d = d;
+  a.n_dst_pages = n_index_pages;
+  a.tokens_per_block = 512;
+  return device_status(lvq::launch_encode(a, (hipStream_t)stream), "lvq_encode_pages launch");
+}
+
+int lvq_reencode_pages(const uint16_t* bf16_pages, const int32_t* src_pages,
+                       const int32_t* dst_pages, int n, const uint16_t* codebooks, int T, int Tc,
+                       int G, int H, int d, int n_bf16_pages, int n_index_pages,
+                       uint8_t* index_pages, void* stream) {
+  if (n < 0) return fail(LVQ_EINVAL, "n=%d must be >= 0", n);
+  int st = check_encode_common(bf16_pages, codebooks, T, Tc, G, lvq::kPage * n, H, d);
+  if (st) return st;
+  if (!index_pages || (n > 0 && (!src_pages || !dst_pages))) return fail(LVQ_EINVAL, "null pointer argument");
+  if (n_bf16_pages < 0 || n_index_pages < 0) return fail(LVQ_EINVAL, "pool sizes must be >= 0");
+  if (n == 0) return ok();
+  lvq::EncodeArgs a{};
+  a.src = bf16_pages;
+  a.src_pages = src_pages;
+  a.codebooks = codebooks;
+  a.out = index_pages;
+  a.dst_pages = dst_pages;
+  a.src_mode = lvq::kSrcPages;
+  a.dst_mode = lvq::kDstPages;
+  a.kv_sel = -1;
+  a.T = T; a.Tc = Tc; a.G = G; a.N = lvq::kPage * n; a.H = H; a.d = d;
+  a.n_src_pages = n_bf16_pages;
+  a.n_dst_pages = n_index_pages;
+  a.tokens_per_block = 512;
+  return device_status(lvq::launch_encode(a, (hipStream_t)stream), "lvq_reencode_pages launch");
+}
+
+size_t lvq_rope_table_bytes(int max_len, int d) {
+  if (max_len <= 0 || d <= 0 || d % 2) return 0;
+  const size_t tile = (size_t)lvq::rope_tile();
+  const size_t ntile = ((size_t)max_len + tile - 1) / tile;
+  return (ntile + tile) * (size_t)(d / 2) * 2 * sizeof(float) + (size_t)(d / 2) * sizeof(double);
+}
+
+int lvq_rope_tables(int max_len, int d, double base, float* rope_tab, size_t rope_bytes,
+                    void* stream) {
+  if (!rope_tab) return fail(LVQ_EINVAL, "null pointer argument");
+  if (max_len <= 0 || d <= 0 || d % 2) return fail(LVQ_EINVAL, "max_len=%d d=%d invalid", max_len, d);
+  if (!(base > 1.0) || isinf(base)) return fail(LVQ_EINVAL, "base must be finite and > 1");
+  const size_t need = lvq_rope_table_bytes(max_len, d);
+  if (rope_bytes < need) return fail(LVQ_ENOSPC, "rope table needs %zu bytes, %zu given", need, rope_bytes);
+  const int tile = lvq::rope_tile();
+  return device_status(lvq::launch_rope_tables((max_len + tile - 1) / tile, d, base, rope_tab, (hipStream_t)stream),
+                       "lvq_rope_tables launch");
+}
+
+size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp) {
+  if (!shp || shp->B <= 0 || shp->Hq <= 0 || shp->d <= 0 || shp->max_seq_len <= 0) return 0;
+  return workspace_bytes(*shp);
+}
+
+int lvq_decode_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
+                    const uint16_t* bf16_pages, const int32_t* bf16_table,
+                    const uint16_t* codebooks, int t, const int32_t* pos, const int32_t* seq_len,
+                    const int32_t* q_end, const float* rope_tab, const lvq_attn_shape* shp,
+                    float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return run_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos, seq_len,
+                  q_end, rope_tab, shp, out, lse, nullptr, ws, ws_bytes, stream);
+}
+
+int lvq_decode_scores(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
+                      const uint16_t* bf16_pages, const int32_t* bf16_table,
+                      const uint16_t* codebooks, int t, const int32_t* pos,
+                      const int32_t* seq_len, const int32_t* q_end, const float* rope_tab,
+                      const lvq_attn_shape* shp, float* out, float* lse, float* scores,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!scores) return fail(LVQ_EINVAL, "null pointer argument");
+  return run_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos, seq_len,
+                  q_end, rope_tab, shp, out, lse, scores, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

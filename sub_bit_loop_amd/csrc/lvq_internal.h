@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI (lvq_abi.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lvq.h"
+
+namespace lvq {
+
+constexpr int kPage = 8;
+constexpr int kCodes = 256;
+
+// ---------------------------------------------------------------- encoder
+enum EncodeSrc { kSrcDense = 0, kSrcPages = 1 };
+enum EncodeDst { kDstDense = 0, kDstPages = 1 };
+
+struct EncodeArgs {
+  const uint16_t* src;        // dense kv [T][N][H][d] or bf16 pages [P'][T][H][2][8][d]
+  const int32_t* src_pages;   // [N/8] bf16 page ids (kSrcPages)
+  const uint16_t* codebooks;  // [nblk][2][H][ng][Tc][256][c]
+  uint8_t* out;               // dense idx [nblk][N][H][ng] or index pages
+  const int32_t* dst_pages;   // [N/8] coded page ids (kDstPages)
+  int src_mode, dst_mode;
+  int kv_sel;                 // 0 / 1, or -1: both halves (pages source)
+  int T, Tc, G, N, H, d;
+  int n_src_pages, n_dst_pages;
+  int tokens_per_block;       // multiple of 16
+};
+bool encode_supported(int G, int c, int d);
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- RoPE tables
+hipError_t launch_rope_tables(int ntile, int d, double base, float* tab, hipStream_t s);
+
+// ---------------------------------------------------------------- decode attention
+struct AttnArgs {
+  const uint16_t* q;
+  const int32_t* page_table;
+  const uint8_t* index_pages;
+  const uint16_t* bf16_pages;
+  const int32_t* bf16_table;
+  const uint16_t* codebooks;
+  const int32_t* pos;
+  const int32_t* seq_len;
+  const int32_t* q_end;
+  const float* rope;          // tile rows [ntile][d/2][2], offset rows [16][d/2][2], theta [d/2] (double)
+  float* part;                // partials [B][Hq][S][d + 2]
+  float* out;                 // [B][Hq][d]
+  float* lse;                 // [B][Hq] or null
+  float* scores;              // [B][Hq][max_seq_len] or null (probe)
+  int t, B, H, Hq, d, T, Tc, G;
+  int n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages, max_seq_len, rope_tiles;
+  int n_chunks;               // coded chunks per (b, hq)
+  int chunk_pages;            // pages per chunk, multiple of 8
+  float scale_log2e;          // softmax scale * log2(e)
+};
+bool attn_supported(int d, int c);
+int rope_tile();   // positions per row of the first RoPE table part
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+}  // namespace lvq

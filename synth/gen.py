@@ -36,7 +36,7 @@ __all__ = [
     "bf16_bits_to_f32", "loop_rhos", "channel_scales", "gen_kv", "gen_queries",
     "kmeans_codebooks", "codebooks_from_samples", "shuffled_page_table",
     "uniform_lengths", "random_index_pages", "random_codebooks",
-    "CacheLayout", "pack_bf16_pages", "prefill_q_end",
+    "CacheLayout", "pack_bf16_pages", "pack_bf16_pages_parts", "prefill_q_end",
 ]
 
 STREAM_K, STREAM_V, STREAM_Q, STREAM_BOOKS, STREAM_PAGES, STREAM_LENGTHS, STREAM_NEEDLE = range(7)
@@ -253,10 +253,28 @@ def pack_bf16_pages(k_tokens: list, v_tokens: list, q_end: np.ndarray, T: int, H
     starting at logical page ``q_end[b] / 8``.  Unused slots of the last
     recent page are zero.  With ``rng`` the pool is shuffled.
     """
-    B = len(k_tokens)
+    first_k, first_v, rec_k, rec_v, lens = [], [], [], [], []
+    for b in range(len(k_tokens)):
+        L = k_tokens[b].shape[1]
+        lo = (int(q_end[b]) // PAGE) * PAGE
+        first_k.append(k_tokens[b][:, :PAGE])
+        first_v.append(v_tokens[b][:, :PAGE])
+        rec_k.append(k_tokens[b][:, lo:L])
+        rec_v.append(v_tokens[b][:, lo:L])
+        lens.append(L)
+    return pack_bf16_pages_parts(first_k, first_v, rec_k, rec_v, q_end, lens, T, H, d, rng,
+                                 max_recent_pages)
+
+
+def pack_bf16_pages_parts(first_k, first_v, rec_k, rec_v, q_end, seq_len, T: int, H: int, d: int,
+                          rng: np.random.Generator | None = None,
+                          max_recent_pages: int | None = None):
+    """As ``pack_bf16_pages`` from the parts that stay bf16: ``first_*[b]`` holds
+    tokens 0..7 (``[T][<=8][H][d]``) and ``rec_*[b]`` tokens ``8*(q_end/8) .. L-1``."""
+    B = len(first_k)
     rows = []
     for b in range(B):
-        L = k_tokens[b].shape[1]
+        L = int(seq_len[b])
         first = int(q_end[b]) // PAGE
         last = (L + PAGE - 1) // PAGE
         rows.append([0] + list(range(first, last)))
@@ -267,13 +285,18 @@ def pack_bf16_pages(k_tokens: list, v_tokens: list, q_end: np.ndarray, T: int, H
     tab = np.full((B, width), -1, dtype=np.int32)
     o = 0
     for b in range(B):
-        L = k_tokens[b].shape[1]
+        L = int(seq_len[b])
+        base = (int(q_end[b]) // PAGE) * PAGE
         for j, lp in enumerate(rows[b]):
             pid = int(perm[o])
             o += 1
             tab[b, j] = pid
             lo, hi = lp * PAGE, min(L, lp * PAGE + PAGE)
             n = hi - lo
-            pool[pid, :, :, 0, :n, :] = k_tokens[b][:, lo:hi].transpose(0, 2, 1, 3)
-            pool[pid, :, :, 1, :n, :] = v_tokens[b][:, lo:hi].transpose(0, 2, 1, 3)
+            if j == 0:
+                src_k, src_v, off = first_k[b], first_v[b], 0
+            else:
+                src_k, src_v, off = rec_k[b], rec_v[b], lo - base
+            pool[pid, :, :, 0, :n, :] = src_k[:, off:off + n].transpose(0, 2, 1, 3)
+            pool[pid, :, :, 1, :n, :] = src_v[:, off:off + n].transpose(0, 2, 1, 3)
     return pool, CacheLayout(bf16_table=tab, n_bf16_pages=total)

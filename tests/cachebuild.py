@@ -109,3 +109,60 @@ def build_cache(config: int, B: int, lengths, H: int, d: int, T: int, Tc: int, G
     return Cache(B, H, Hq, d, T, Tc, G, n_sink, n_recent, lengths.copy(), q_end,
                  lengths.copy(), pt, ip, bp, lay.bf16_table, cb, q,
                  ks if keep_tokens else [], vs if keep_tokens else [])
+
+
+def build_cache_light(config: int, B: int, lengths, H: int, d: int, T: int, Tc: int, G: int,
+                      n_sink: int, n_recent: int, Hq: int | None = None, books: str = "random",
+                      book_samples: int = 1024) -> Cache:
+    """Full-size cache without generating every token: coded pages hold uniform random
+    indices; only the bf16 parts (page 0 and the recent window) are drawn from the
+    generator.  For attention tests at real context lengths."""
+    import torch
+    Hq = H if Hq is None else Hq
+    lengths = np.asarray(lengths, dtype=np.int32)
+    rk = np.random.default_rng(synth.seed_for(config, synth.STREAM_K))
+    rv = np.random.default_rng(synth.seed_for(config, synth.STREAM_V))
+    sc_k = synth.channel_scales(rk, H, d)
+    sc_v = synth.channel_scales(rv, H, d)
+    q_end = np.array([synth.prefill_q_end(int(L), n_recent) for L in lengths], dtype=np.int32)
+    c = G // Tc
+    ng, nblk = d // c, T // Tc
+    if books == "kmeans":
+        torch.set_num_threads(min(16, torch.get_num_threads()))
+        rb = np.random.default_rng(synth.seed_for(config, synth.STREAM_BOOKS))
+        sk = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(synth.gen_kv(rb, T, book_samples, H, d, sc_k)))
+        sv = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(synth.gen_kv(rb, T, book_samples, H, d, sc_v)))
+        kw = dict(device="cpu", dtype=torch.float32)
+        cb = np.stack([synth.codebooks_from_samples(sk, Tc, G, config * 7 + 1, **kw),
+                       synth.codebooks_from_samples(sv, Tc, G, config * 7 + 2, **kw)], axis=1)
+    else:
+        rb = np.random.default_rng(synth.seed_for(config, synth.STREAM_BOOKS))
+        cb = np.ascontiguousarray(synth.random_codebooks(rb, T, Tc, G, H, d, scale=1.0))
+        # put the books on the data's per-channel scale
+        f = synth.bf16_bits_to_f32(cb).astype(np.float32)
+        for kv, sc in ((0, sc_k), (1, sc_v)):
+            scl = sc.reshape(H, ng, c)                    # [H][ng][c]
+            f[:, kv] *= scl[None, :, :, None, None, :]
+        cb = synth.f32_to_bf16_bits(f)
+    n_pages = [int(qe) // 8 for qe in q_end]
+    max_pages = max(1, max((int(L) + 7) // 8 for L in lengths))
+    rp = np.random.default_rng(synth.seed_for(config, synth.STREAM_PAGES))
+    pt, pool = synth.shuffled_page_table(rp, n_pages, max_pages)
+    ip = synth.random_index_pages(rp, max(pool, 1), nblk, H, ng)
+    fk, fv, rk_, rv_ = [], [], [], []
+    for b in range(B):
+        L = int(lengths[b])
+        base = (int(q_end[b]) // 8) * 8
+        fk.append(synth.f32_to_bf16_bits(synth.gen_kv(rk, T, min(8, L), H, d, sc_k)))
+        fv.append(synth.f32_to_bf16_bits(synth.gen_kv(rv, T, min(8, L), H, d, sc_v)))
+        rk_.append(synth.f32_to_bf16_bits(synth.gen_kv(rk, T, L - base, H, d, sc_k)))
+        rv_.append(synth.f32_to_bf16_bits(synth.gen_kv(rv, T, L - base, H, d, sc_v)))
+        if base == 0:   # page 0 is also a recent page: keep both copies identical
+            n = min(8, L)
+            rk_[-1][:, :n] = fk[-1][:, :n]
+            rv_[-1][:, :n] = fv[-1][:, :n]
+    bp, lay = synth.pack_bf16_pages_parts(fk, fv, rk_, rv_, q_end, lengths, T, H, d, rng=rp)
+    rq = np.random.default_rng(synth.seed_for(config, synth.STREAM_Q))
+    q = synth.gen_queries(rq, T, B, Hq, d)
+    return Cache(B, H, Hq, d, T, Tc, G, n_sink, n_recent, lengths.copy(), q_end, lengths.copy(),
+                 pt, ip, bp, lay.bf16_table, cb, q)

@@ -1,0 +1,115 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before touching a device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lvq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sub_bit_loop_amd import _abi
+    if not os.path.exists(_abi.LIB_PATH):
+        from sub_bit_loop_amd import build
+        build.build()
+    return _abi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in lvq.h but not exported"
+    from sub_bit_loop_amd import _abi
+    assert sorted(_abi.EXPORTS) == names
+
+
+def test_version_and_error_text(L):
+    assert L.lvq_version() == 1
+    assert isinstance(L.lvq_last_error(), bytes)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+NUL = ctypes.c_void_p(0)
+
+
+def enc(L, kv=FAKE, cb=FAKE, sel=0, T=4, Tc=2, G=16, N=8, H=1, d=64, out=FAKE):
+    return L.lvq_encode(kv, cb, sel, T, Tc, G, N, H, d, out, NUL)
+
+
+def test_encode_validation(L):
+    assert enc(L, kv=NUL) == 1
+    assert enc(L, out=NUL) == 1
+    assert enc(L, Tc=3) == 1                     # Tc does not divide T
+    assert enc(L, T=6, Tc=3, G=16) == 1          # Tc does not divide G
+    assert enc(L, G=24, Tc=2, d=64, T=4) == 1    # c = 12 does not divide 64
+    assert enc(L, sel=2) == 1
+    assert enc(L, N=-1) == 1
+    assert enc(L, d=96, G=16, Tc=2) == 2         # valid but not compiled
+    assert enc(L, G=64, Tc=2) == 2
+    assert b"Tc" in L.lvq_last_error() or L.lvq_last_error()
+    assert enc(L, N=0) == 0                      # empty input is a no-op
+    # pages: N must be a multiple of 8
+    assert L.lvq_encode_pages(FAKE, FAKE, 0, 4, 2, 16, 12, 1, 64, FAKE, 4, FAKE, NUL) == 1
+    assert L.lvq_reencode_pages(FAKE, FAKE, FAKE, -1, FAKE, 4, 2, 16, 1, 64, 4, 4, FAKE, NUL) == 1
+    assert L.lvq_reencode_pages(FAKE, FAKE, FAKE, 0, FAKE, 4, 2, 16, 1, 64, 4, 4, FAKE, NUL) == 0
+
+
+def test_rope_table_sizes(L):
+    assert L.lvq_rope_table_bytes(512, 64) == (32 + 16) * 32 * 2 * 4 + 32 * 8
+    assert L.lvq_rope_table_bytes(513, 64) == (33 + 16) * 32 * 2 * 4 + 32 * 8
+    assert L.lvq_rope_table_bytes(0, 64) == 0
+    assert L.lvq_rope_tables(512, 64, ctypes.c_double(10000.0), FAKE, 10, NUL) == 3
+    assert L.lvq_rope_tables(512, 63, ctypes.c_double(10000.0), FAKE, 1 << 20, NUL) == 1
+    assert L.lvq_rope_tables(512, 64, ctypes.c_double(1.0), FAKE, 1 << 20, NUL) == 1
+
+
+def shape(**kw):
+    from sub_bit_loop_amd import _abi
+    base = dict(B=2, H=2, Hq=4, d=128, T=4, Tc=4, G=32, n_sink=4, max_pages=64, bf16_row=12,
+                n_index_pages=100, n_bf16_pages=20, max_seq_len=512, rope_max_len=513,
+                n_splits=0, scale=0.0)
+    base.update(kw)
+    return _abi.make_shape(**base)
+
+
+def attn(L, shp, t=0, ws_bytes=1 << 30, q=FAKE):
+    return L.lvq_decode_attn(q, FAKE, FAKE, FAKE, FAKE, FAKE, t, FAKE, FAKE, FAKE, FAKE,
+                             ctypes.byref(shp), FAKE, NUL, FAKE, ws_bytes, NUL)
+
+
+def test_attn_validation(L):
+    assert attn(L, shape(), q=NUL) == 1
+    assert attn(L, shape(), t=4) == 1
+    assert attn(L, shape(Hq=3)) == 1
+    assert attn(L, shape(Tc=3)) == 1
+    assert attn(L, shape(n_sink=9)) == 1
+    assert attn(L, shape(max_pages=10)) == 1
+    assert attn(L, shape(rope_max_len=512)) == 1
+    assert attn(L, shape(d=96, G=16, Tc=2)) == 2
+    assert attn(L, shape(G=16, Tc=4)) == 2       # c = 4 not compiled for decode
+    assert attn(L, shape(d=64, G=32, Tc=1)) == 2  # c = 32 at d = 64 not compiled
+    assert attn(L, shape(), ws_bytes=4) == 3
+    assert L.lvq_decode_scores(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
+                               ctypes.byref(shape()), FAKE, NUL, NUL, FAKE, 1 << 30, NUL) == 1
+
+
+def test_workspace_size_covers_every_split(L):
+    from sub_bit_loop_amd import _abi
+    for B, Hq, msl, ns in ((8, 16, 32768, 0), (1, 16, 65536, 0), (64, 16, 16384, 0), (1, 1, 512, 7),
+                           (2, 4, 100, 0)):
+        s = shape(B=B, H=Hq, Hq=Hq, max_seq_len=msl, rope_max_len=msl + 1, max_pages=(msl + 7) // 8,
+                  n_splits=ns)
+        nbytes = _abi.lvq_decode_attn_workspace_bytes(s)
+        per = B * Hq * 130 * 4
+        assert nbytes % per == 0 and nbytes // per >= 2
