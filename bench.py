@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""LoopVQ hot-path benchmark on one MI355X.
+
+Headline: decode attention over the coded KV cache of an Ouro-1.4B-shaped
+looped model (24 layers, 4 loop steps per token, 16 KV heads, d = 128, Tc = 4,
+G = 32 -> 0.25 bit per element, 8 sequences of 32768 tokens, 4 sink + 64
+recent tokens in bf16, shuffled 8-token pages).  One step = one decode token:
+the 96 (loop step, layer) attention calls in model order (loop step outer,
+layer inner), each layer with its own index pool, bf16 pool and codebooks, so
+the 3.2 GB of coded pages stream from HBM (well beyond the 256 MB
+Infinity Cache).  Metric: KV token-steps/s = 96 * sum_b L_b / step time.
+
+Inputs are synthetic (seeded AR(1) loop-correlated keys/values, k-means
+codebooks), generated on the GPU and prefill-encoded by the library's own
+encoder before timing.  The JSON line also carries the roofline of the
+attention kernel, the CPU oracle timed on a bounded sample, and the prefill
+encoder's throughput (vectors/s, MFMA utilisation) on the 32768-token shape.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "VQ decode attn: KV token-steps/s & % HBM peak at 32K; encode vectors/s"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+# Ouro-1.4B-shaped decode configuration
+B, L, H, D, T, TC, G = 8, 32768, 16, 128, 4, 4, 32
+N_SINK, N_RECENT = 4, 64
+CONFIG_ID = 2
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=24)
+    ap.add_argument("--splits", type=int, default=0, help="coded splits per (b, head); 0 = automatic")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-encode", action="store_true", help="skip the encoder measurement")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_inputs(args, torch, lvq, synth):
+    import numpy as np
+    dev = torch.device("cuda:0")
+    c = G // TC
+    nblk, ng = T // TC, D // c
+    q_end = synth.prefill_q_end(L, N_RECENT)
+    n_coded_pages = q_end // 8
+    max_pages = L // 8
+    # shuffled page table over the pool (the same placement for every layer; each layer owns a pool)
+    rng = np.random.default_rng(synth.seed_for(CONFIG_ID, synth.STREAM_PAGES))
+    pt_np, pool = synth.shuffled_page_table(rng, [n_coded_pages] * B, max_pages)
+    pt = torch.from_numpy(pt_np).to(dev)
+    # codebooks: k-means on seeded samples for one layer, copied into every layer's buffer
+    rk = np.random.default_rng(synth.seed_for(CONFIG_ID, synth.STREAM_K))
+    rv = np.random.default_rng(synth.seed_for(CONFIG_ID, synth.STREAM_V))
+    sc_k, sc_v = synth.channel_scales(rk, H, D), synth.channel_scales(rv, H, D)
+    t0 = time.time()
+    cb_np = synth.kmeans_codebooks(CONFIG_ID, T, TC, G, H, D, sc_k, sc_v, n_samples=4096, device="cuda")
+    log(f"k-means codebooks in {time.time() - t0:.1f}s")
+    cb0 = torch.from_numpy(cb_np.view(np.int16)).to(dev)
+    # bf16 pool: per sequence the copy of page 0 and the recent pages
+    n_recent_pages = (L - q_end + 7) // 8
+    bf16_row = 1 + n_recent_pages
+    n_bf16 = B * bf16_row
+    bt = torch.arange(n_bf16, dtype=torch.int32, device=dev).view(B, bf16_row)
+    gen = torch.Generator(device=dev)
+    layers = []
+    t0 = time.time()
+    for layer in range(args.layers):
+        ip = torch.zeros((pool, nblk, H, 2, 8, ng), dtype=torch.uint8, device=dev)
+        bp = torch.zeros((n_bf16, T, H, 2, 8, D), dtype=torch.bfloat16, device=dev)
+        for b in range(B):
+            for kv in (0, 1):
+                gen.manual_seed(synth.seed_for(CONFIG_ID, kv) * 1009 + 97 * layer + b)
+                x = synth.gen_kv_torch(gen, T, L, H, D, sc_k if kv == 0 else sc_v, device=dev)
+                chunk_page = pt[b, :n_coded_pages].contiguous()
+                lvq.lvq_encode_pages(x[:, :q_end].contiguous(), cb0, kv, T, TC, G, chunk_page, ip)
+                # page 0 copy (sink tokens) and recent pages [q_end, L)
+                bp[b * bf16_row, :, :, kv] = x[:, 0:8].permute(0, 2, 1, 3)
+                rec = x[:, q_end:L].reshape(T, n_recent_pages, 8, H, D).permute(1, 0, 3, 2, 4)
+                bp[b * bf16_row + 1:(b + 1) * bf16_row, :, :, kv] = rec
+                del x
+        cb = cb0.clone()
+        qs = []
+        for t in range(T):
+            gen.manual_seed(synth.seed_for(CONFIG_ID, synth.STREAM_Q) * 1009 + 97 * layer + t)
+            qs.append(synth.gen_queries_torch(gen, B, H, D, device=dev))
+        layers.append(dict(ip=ip, bp=bp.view(torch.int16), cb=cb, q=qs))
+    torch.cuda.synchronize()
+    log(f"{args.layers} layers generated and prefill-encoded in {time.time() - t0:.1f}s")
+    pos = torch.full((B,), L, dtype=torch.int32, device=dev)
+    seq_len = torch.full((B,), L, dtype=torch.int32, device=dev)
+    qe = torch.full((B,), q_end, dtype=torch.int32, device=dev)
+    rope = lvq.lvq_rope_tables(L + 1, D, 10000.0, device=dev)
+    shp = lvq.make_shape(B, H, H, D, T, TC, G, N_SINK, max_pages, bf16_row, pool, n_bf16, L, L + 1,
+                         args.splits)
+    ws = torch.empty(lvq.lvq_decode_attn_workspace_bytes(shp), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    return dict(pt=pt, pt_np=pt_np, layers=layers, pos=pos, seq_len=seq_len, qe=qe, rope=rope,
+                shp=shp, ws=ws, out=out, lse=lse, bt=bt, pool=pool, q_end=q_end, bf16_row=bf16_row,
+                cb_np=cb_np)
+
+
+def algorithmic_bytes_per_call(q_end):
+    """Bytes the method must move per (layer, step) call: index rows of coded tokens,
+    bf16 sink/recent tokens, the step-t codebook slices once, query, output, page ids."""
+    coded = q_end - N_SINK
+    idx = B * coded * H * (2 * (D // (G // TC)))
+    bf = B * (N_SINK + (L - q_end)) * H * 2 * D * 2
+    books = H * 2 * 256 * D * 2
+    small = B * H * D * 2 + B * H * D * 4 + B * H * 4 + B * (q_end // 8) * 4
+    return idx + bf + books + small
+
+
+def run_decode(args, torch, lvq, inp):
+    layers = inp["layers"]
+    common = dict(pos=inp["pos"], seq_len=inp["seq_len"], q_end=inp["qe"], rope_tab=inp["rope"],
+                  shp=inp["shp"], out=inp["out"], lse=inp["lse"], ws=inp["ws"])
+
+    def call(layer, t):
+        Ly = layers[layer]
+        lvq.lvq_decode_attn(Ly["q"][t], inp["pt"], Ly["ip"], Ly["bp"], inp["bt"], Ly["cb"], t,
+                            common["pos"], common["seq_len"], common["q_end"], common["rope_tab"],
+                            common["shp"], common["out"], common["lse"], common["ws"])
+
+    def step(events=None):
+        k = 0
+        for t in range(T):
+            for layer in range(len(layers)):
+                if events is not None:
+                    events[k][0].record()
+                call(layer, t)
+                if events is not None:
+                    events[k][1].record()
+                k += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ncall = T * len(layers)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(ncall)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = [evs[s][k][0].elapsed_time(evs[s][k][1]) * 1e-3 for s in range(args.steps) for k in range(ncall)]
+    return wall, per_call
+
+
+def cpu_baseline(args, torch, inp):
+    """The float64 oracle on a bounded sample of the same workload: (b, head) pairs of one
+    (layer 0, loop step 1) call at full context, single thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import lvq_oracle as orc
+    Ly = inp["layers"][0]
+    t = 1
+    host = dict(
+        ip=Ly["ip"].cpu().numpy(), bp=Ly["bp"].cpu().numpy().view(np.uint16),
+        cb=Ly["cb"].cpu().numpy().view(np.uint16), q=Ly["q"][t].cpu().view(torch.int16).numpy().view(np.uint16),
+    )
+    shp = orc.AttnShape(B, H, H, D, T, TC, G, N_SINK)
+    pt = inp["pt_np"]
+    bt = inp["bt"].cpu().numpy()
+    pos = np.full(B, L)
+    qe = np.full(B, inp["q_end"])
+    pairs = [(b, h) for h in range(H) for b in range(B)]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < len(pairs) and time.perf_counter() - t0 < args.cpu_seconds:
+            orc.decode_attn(shp, host["q"], pt, host["ip"], host["bp"], bt, host["cb"], t, pos, pos, qe,
+                            pairs=[pairs[done]])
+            done += 1
+    el = time.perf_counter() - t0
+    # one (b, head) pair over L tokens is L/H token-steps of the all-head metric
+    value = done * L / H / el
+    return {"value": value, "unit": "KV token-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (sequence, head) pairs of one (layer, loop step) call at L={L}, "
+                      f"float64 numpy, 1 thread, {el:.1f}s"}
+
+
+def encode_bench(torch, lvq, synth, inp):
+    """Prefill encode of 32768 tokens x 16 heads x d=128 x 4 loop steps, K and V, for
+    (Tc, G) = (4, 32) and (2, 16)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    N = 32768
+    res = {}
+    gen = torch.Generator(device=dev)
+    rk = np.random.default_rng(synth.seed_for(4, synth.STREAM_K))
+    sc = synth.channel_scales(rk, H, D)
+    for (tc, g) in ((4, 32), (2, 16)):
+        if (tc, g) == (TC, G):
+            cb = torch.from_numpy(inp["cb_np"].view(np.int16)).to(dev)
+        else:
+            cb = torch.from_numpy(synth.kmeans_codebooks(4, T, tc, g, H, D, sc, sc, n_samples=4096,
+                                                         device="cuda").view(np.int16)).to(dev)
+        kvs = []
+        for kv in (0, 1):
+            gen.manual_seed(4000 + kv)
+            kvs.append(synth.gen_kv_torch(gen, T, N, H, D, sc, device=dev))
+        c = g // tc
+        idx = [torch.empty((T // tc, N, H, D // c), dtype=torch.uint8, device=dev) for _ in range(2)]
+        for _ in range(2):
+            for kv in (0, 1):
+                lvq.lvq_encode(kvs[kv], cb, kv, T, tc, g, idx[kv])
+        torch.cuda.synchronize()
+        reps = 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for kv in (0, 1):
+                lvq.lvq_encode(kvs[kv], cb, kv, T, tc, g, idx[kv])
+        e1.record()
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) * 1e-3 / reps        # K and V
+        nvec = 2 * (T // tc) * N * H * (D // c)
+        flops = nvec * 2 * g * 256
+        hbm = 2 * (T * N * H * D * 2) + 2 * (T // tc) * N * H * (D // c) + cb.numel() * 2
+        res[f"Tc{tc}_G{g}"] = {
+            "vectors_per_s": nvec / dt, "us_per_KV_pair": dt * 1e6,
+            "mfma_util": flops / dt / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+            "hbm_frac": hbm / dt / (HBM_PEAK_GBS * 1e9),
+        }
+        del kvs, idx
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import sub_bit_loop_amd as lvq
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    inp = build_inputs(args, torch, lvq, synth)
+    wall, per_call = run_decode(args, torch, lvq, inp)
+    ncall = T * args.layers
+    step_s = wall / args.steps
+    token_steps = ncall * B * L
+    value = token_steps / step_s
+    call_avg = sum(per_call) / len(per_call)
+    algo = algorithmic_bytes_per_call(inp["q_end"])
+    achieved_gbs = algo / call_avg / 1e9
+    log(f"step {step_s * 1e3:.3f} ms, call {call_avg * 1e6:.1f} us, {achieved_gbs:.0f} GB/s algorithmic")
+    roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "attn_kernel<128,8> + merge per (layer, step) call",
+            "algorithmic_bytes_per_call": algo, "avg_call_us": round(call_avg * 1e6, 2)}
+    res = {
+        "metric": METRIC, "value": value, "unit": "KV token-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"ouro-1.4b-shaped decode attention: {args.layers} layers x {T} loop steps "
+                               f"per token, B={B}, L={L}, H={H}, d={D}, Tc={TC}, G={G} (0.25 bit), "
+                               f"{N_SINK} sink + {N_RECENT} recent bf16, shuffled pages",
+                   "global_batch": B, "seq_len": L, "parallelism": "single-gpu"},
+        "roofline": roof,
+    }
+    if not args.no_encode:
+        try:
+            res["encode"] = encode_bench(torch, lvq, synth, inp)
+        except Exception as e:  # report, never hide the headline
+            res["encode"] = {"error": repr(e)}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(args, torch, inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

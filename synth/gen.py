@@ -37,6 +37,7 @@ __all__ = [
     "kmeans_codebooks", "codebooks_from_samples", "shuffled_page_table",
     "uniform_lengths", "random_index_pages", "random_codebooks",
     "CacheLayout", "pack_bf16_pages", "pack_bf16_pages_parts", "prefill_q_end",
+    "gen_kv_torch", "gen_queries_torch",
 ]
 
 STREAM_K, STREAM_V, STREAM_Q, STREAM_BOOKS, STREAM_PAGES, STREAM_LENGTHS, STREAM_NEEDLE = range(7)
@@ -300,3 +301,32 @@ def pack_bf16_pages_parts(first_k, first_v, rec_k, rec_v, q_end, seq_len, T: int
             pool[pid, :, :, 0, :n, :] = src_k[:, off:off + n].transpose(0, 2, 1, 3)
             pool[pid, :, :, 1, :n, :] = src_v[:, off:off + n].transpose(0, 2, 1, 3)
     return pool, CacheLayout(bf16_table=tab, n_bf16_pages=total)
+
+
+# ----------------------------------------------------------------------------
+# device-side variants of the same recipe (benchmark-scale inputs)
+# ----------------------------------------------------------------------------
+def gen_kv_torch(gen, T: int, N: int, H: int, d: int, scales, device="cuda"):
+    """``gen_kv`` on a torch device: bf16 tensor ``[T][N][H][d]`` (same recipe, torch RNG)."""
+    import torch
+    rhos = loop_rhos(T)
+    sc = torch.as_tensor(scales, dtype=torch.float32, device=device)
+    out = torch.empty((T, N, H, d), dtype=torch.bfloat16, device=device)
+    z = None
+    for t in range(T):
+        s = torch.randn((N, H, 1), generator=gen, device=device)
+        e = torch.randn((N, H, d), generator=gen, device=device)
+        eps = 0.4 * s + math.sqrt(0.84) * e
+        if t == 0:
+            z = eps
+        else:
+            r = float(rhos[t - 1])
+            z = r * z + math.sqrt(1.0 - r * r) * eps
+        out[t] = (z * sc[None]).to(torch.bfloat16)
+    return out
+
+
+def gen_queries_torch(gen, B: int, Hq: int, d: int, device="cuda"):
+    """One bf16 query tensor ``[B][Hq][d]``, N(0,1) per channel, on a torch device."""
+    import torch
+    return torch.randn((B, Hq, d), generator=gen, device=device).to(torch.bfloat16)

@@ -123,35 +123,34 @@ def test_ouro_shape_full_context_sampled():
 
 
 def plant_needle(cache, lo, span, rng):
-    """Plant a 16-token needle in sequence 0: the span's tokens share the codes of one
-    encoded key, and every loop step's query is reset so that, after RoPE, it has
-    cosine 0.9 with that reconstructed key at the middle of the span (the rest of
-    its direction is a seeded vector orthogonal to it).  Codes come from the oracle."""
+    """Plant a 16-token needle in sequence 0: the span's tokens share one code row per
+    block, the codeword of largest norm (summed over the block's steps) in every group,
+    and every loop step's query is reset so that, after RoPE, it has cosine 0.97 with
+    that reconstructed key at the middle of the span (the rest of its direction is a
+    seeded vector orthogonal to it) and scores 24 there."""
     T, Tc, G, H, d = cache.T, cache.Tc, cache.G, cache.H, cache.d
     c = G // Tc
     ng = d // c
-    cb = orc.bf16_to_f64(cache.codebooks)
-    key = synth.f32_to_bf16_bits((2.0 * rng.standard_normal((T, 1, H, d))).astype(np.float32))
-    idx = orc.encode(key, cache.codebooks, 0, T, Tc, G).idx            # [nblk][1][H][ng]
+    cb = orc.bf16_to_f64(cache.codebooks)                       # [nblk][2][H][ng][Tc][256][c]
+    idx = np.argmax((cb[:, 0] ** 2).sum(axis=(3, 5)), axis=-1)  # [nblk][H][ng]
     for i in range(span):
         p = lo + i
         P = cache.page_table[0, p // 8]
-        cache.index_pages[P, :, :, 0, p % 8, :] = idx[:, 0]
+        cache.index_pages[P, :, :, 0, p % 8, :] = idx
     pos = int(cache.pos[0])
     mid = lo + span // 2
-    q = orc.bf16_to_f64(cache.q)
+    cos = 0.97
     for t in range(T):
         beta, tau = t // Tc, t % Tc
         for h in range(H):
-            kh = np.concatenate([cb[beta, 0, h, g, tau, idx[beta, 0, h, g]] for g in range(ng)])
+            kh = np.concatenate([cb[beta, 0, h, g, tau, idx[beta, h, g]] for g in range(ng)])
             kr = orc.rope(kh, mid)
             kr /= np.linalg.norm(kr)
             u = rng.standard_normal(d)
             u -= (u @ kr) * kr
             u /= np.linalg.norm(u)
-            # query length chosen so the span's middle token scores 24 (natural units)
-            qn = 24.0 * np.sqrt(d) / (0.9 * np.linalg.norm(kh))
-            qr = qn * (0.9 * kr + np.sqrt(0.19) * u)
+            qn = 24.0 * np.sqrt(d) / (cos * np.linalg.norm(kh))
+            qr = qn * (cos * kr + np.sqrt(1.0 - cos * cos) * u)
             cache.q[t, 0, h] = synth.f32_to_bf16_bits(orc.rope(qr, -pos).astype(np.float32))
 
 
