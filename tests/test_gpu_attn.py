@@ -125,7 +125,7 @@ def test_ouro_shape_full_context_sampled():
 def plant_needle(cache, lo, span, rng):
     """Plant a 16-token needle in sequence 0: the span's tokens share one code row per
     block, the codeword of largest norm (summed over the block's steps) in every group,
-    and every loop step's query is reset so that, after RoPE, it has cosine 0.97 with
+    and every loop step's query is reset so that, after RoPE, it has cosine 0.9 with
     that reconstructed key at the middle of the span (the rest of its direction is a
     seeded vector orthogonal to it) and scores 24 there."""
     T, Tc, G, H, d = cache.T, cache.Tc, cache.G, cache.H, cache.d
@@ -139,7 +139,7 @@ def plant_needle(cache, lo, span, rng):
         cache.index_pages[P, :, :, 0, p % 8, :] = idx
     pos = int(cache.pos[0])
     mid = lo + span // 2
-    cos = 0.97
+    cos = 0.9
     for t in range(T):
         beta, tau = t // Tc, t % Tc
         for h in range(H):
