@@ -17,32 +17,62 @@
 //    accumulator input is |C_k|^2, so each MFMA returns D'_k = |C_k|^2 - 2 x.C_k
 //    = |x - C_k|^2 - |x|^2 for 16 codes x 16 vectors, float32.
 //  * Argmin: each lane holds 64 candidates of one vector (16 MFMAs x 4 rows).
-//    It folds them in four chains of 16 with v_min3 on keys whose low four
-//    mantissa bits carry the chain position (ordering ties toward the lowest
-//    code for negative D'), then merges the chain winners and the four lanes
-//    of the vector, tracking the runner-up among chain winners.
+//    Each becomes a key, D' with its six low mantissa bits replaced by the
+//    candidate's position; keys are folded three at a time (v_min3, v_med3)
+//    into the lane's smallest and second smallest key, then the four lanes of
+//    the vector merge.
 //  * Exactness: a vector is recomputed in float64 by direct differences over
-//    all 256 codewords (the definition itself) when the minimum is not safely
-//    negative or when its runner-up is within the float32 error bound of the
-//    winner.  That keeps the chosen index equal to the float64 nearest
-//    codeword except for candidates inside the float32 error band.
-//  * A workgroup holds the waves of up to 8 consecutive groups of one
-//    (block, head): together they read whole 128-byte rows of the cache, so
-//    the K/V bytes are fetched from HBM once.
+//    all 256 codewords (the definition itself) when its second smallest key is
+//    within the float32 error bound of the smallest.  So the chosen index is the
+//    float64 nearest codeword with lowest-index ties: float32 decides only where
+//    no other candidate can be within rounding of the winner.
+//  * Input tiles (16 tokens) are loaded three tiles ahead of their use.
+//  * A workgroup holds the waves of up to 4 consecutive groups of one
+//    (block, head); the workgroups that read the other halves of the same
+//    128-byte cache rows run on the same XCD at the same time, so the K/V
+//    bytes are fetched from HBM once.
 #include "lvq_internal.h"
+
+#include <atomic>
+#include <cstdint>
 
 namespace lvq {
 namespace {
 
-constexpr int kMaxTokensPerBlock = 512;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// v_min_f32 / v_max_f32 / v_min3_f32 / v_med3_f32 on argmin keys.  The keys are finite floats built by bit
+// operations; written through fminf the compiler would first quiet each one (an
+// extra v_max per candidate) because it cannot prove the operand is not a
+// signalling NaN.
+__device__ __forceinline__ float key_min(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float key_max(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float key_min3(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float key_med3(float a, float b, float c) {
+  float r;
+  asm("v_med3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 template <int EPL>
 using raw_t = typename std::conditional<EPL == 8, u16x8, u16x4>::type;
@@ -79,33 +109,44 @@ __device__ __forceinline__ uint8_t* dst_byte(const EncodeArgs& a, int beta, int 
   return a.out + (((((size_t)P * nblk + beta) * a.H + h) * 2 + kv) * kPage + (n & 7)) * ng + g;
 }
 
-// Float64 direct-difference nearest codeword of one vector, whole wave cooperating.
-// Lane l scores codes l, l+64, l+128, l+192; ties resolve to the lowest code.
-template <int G, int C>
-__device__ __forceinline__ int exact_nearest(const EncodeArgs& a, const uint16_t* cb, int beta, int n,
-                                          int h, int g, int kv, int lane) {
-  constexpr int TC = G / C;
+// Float64 direct-difference nearest codeword of vector column cv of the current tile,
+// computed from registers: the wave holds the codebook as MFMA operand (A[m] = -2 C,
+// exact) and the tile as operand B (lane (q4, col) holds elements e0..e0+EPL-1 of
+// vector col).  Lane (q4, col) sums its EPL elements for codes 16m + col, the four
+// lanes of a column add their parts (the same sum in every lane), and the 16 columns
+// compare.  Ties resolve to the lowest code.
+template <int EPL, typename R>
+__device__ __forceinline__ int exact_in_registers(const R (&A)[16], const R& B, int cv, int lane) {
+  const int q4 = lane >> 4, col = lane & 15;
+  const int src = (q4 << 4) | cv;
+  double x[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; e += 2) {
+    const uint32_t w = (uint32_t)__shfl((int)((uint32_t)B[e] | ((uint32_t)B[e + 1] << 16)), src);
+    x[e] = (double)bf2f((uint16_t)(w & 0xffffu));
+    x[e + 1] = (double)bf2f((uint16_t)(w >> 16));
+  }
   double best = __builtin_inf();
-  int bidx = 0x7fffffff;
-#pragma unroll 1
-  for (int j = 0; j < 4; ++j) {
-    const int k = lane + 64 * j;
-    double dsum = 0.0;
-#pragma unroll 1
-    for (int tau = 0; tau < TC; ++tau) {
-      const uint16_t* row = src_row(a, beta * TC + tau, n, h, kv);
-      const uint16_t* cw = cb + ((size_t)tau * kCodes + k) * C;
-#pragma unroll 4
-      for (int i = 0; i < C; ++i) {
-        const double xv = row ? (double)bf2f(row[g * C + i]) : 0.0;
-        const double df = xv - (double)bf2f(cw[i]);
-        dsum = fma(df, df, dsum);
-      }
+  int bidx = 0;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    double part = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 2) {
+      // opaque copy: keeps the conversions here instead of hoisted out of the token loop
+      uint32_t w = (uint32_t)A[m][e] | ((uint32_t)A[m][e + 1] << 16);
+      asm volatile("" : "+v"(w));
+      const double d0 = fma(0.5, (double)bf2f((uint16_t)(w & 0xffffu)), x[e]);   // x - C, A = -2 C
+      const double d1 = fma(0.5, (double)bf2f((uint16_t)(w >> 16)), x[e + 1]);
+      part = fma(d0, d0, part);
+      part = fma(d1, d1, part);
     }
-    if (dsum < best) { best = dsum; bidx = k; }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (part < best) { best = part; bidx = 16 * m + col; }   // m ascending: lowest code kept
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
+  for (int off = 1; off < 16; off <<= 1) {
     const double ob = __shfl_xor(best, off);
     const int oi = __shfl_xor(bidx, off);
     if (ob < best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
@@ -113,172 +154,278 @@ __device__ __forceinline__ int exact_nearest(const EncodeArgs& a, const uint16_t
   return bidx;
 }
 
-template <int G, int C, int D>
-__global__ __launch_bounds__(512) void encode_kernel(EncodeArgs a) {
+// Waves per workgroup: one per channel group, up to 4.
+template <int D, int C>
+constexpr int waves_per_group_block() { return D / C < 4 ? D / C : 4; }
+
+// Work items are (token range, channel-group block, head, loop block, K/V).  The
+// items of one (token range, head, loop block, K/V) that read the same 128-byte
+// rows differ only in the group block and are numbered 8 apart, so with a grid that
+// is a multiple of 8 x (group blocks) they run on the same XCD (round-robin
+// dispatch) at the same time and each row is fetched from HBM once.
+constexpr int kXcds = 8;
+
+// MODE: 0 dense source and destination, 1 dense source into coded pages,
+// 2 bf16 pages into coded pages.  Occupancy: 3 waves per SIMD at G = 32 (the
+// codebook takes 64 VGPRs), 4 at G = 16.  The grid is persistent: each workgroup
+// loads a codebook once per item and streams the item's whole token range.
+template <int G, int C, int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 32 ? 3 : 4, 8)))
+void encode_kernel(EncodeArgs a, int n_items) {
+  constexpr bool kDenseSrc = MODE != 2;
+  constexpr bool kDenseDst = MODE == 0;
   constexpr int NG = D / C;
-  constexpr int WPG = NG < 8 ? NG : 8;   // waves (groups) per workgroup
+  constexpr int WPG = waves_per_group_block<D, C>();   // waves (groups) per workgroup
   constexpr int NGB = NG / WPG;
   constexpr int EPL = (G == 32) ? 8 : 4; // elements per lane per MFMA operand
   constexpr int TC = G / C;
+  constexpr int kPart = 4;               // MFMAs issued before their results are folded
+  constexpr int kRing = 4;               // tiles in flight
   using R = raw_t<EPL>;
   __shared__ __attribute__((aligned(16))) float s_bias[WPG][kCodes];
-  __shared__ int s_flag[WPG][kMaxTokensPerBlock];   // vectors left for the float64 pass
-  __shared__ int s_nflag[WPG];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int H = a.H, N = a.N;
   const int nblk = a.T / TC;
-  const int nchunk = (N + a.tokens_per_block - 1) / a.tokens_per_block;
-  int bid = blockIdx.x;
-  const int chunk = bid % nchunk; bid /= nchunk;
-  const int gb = bid % NGB;       bid /= NGB;
-  const int h = bid % H;          bid /= H;
-  const int beta = bid % nblk;    bid /= nblk;
-  const int kv = (a.kv_sel >= 0) ? a.kv_sel : bid;
-  const int g = gb * WPG + wave;
-
+  const int tpi = a.tokens_per_block;
+  const int nparts = (N + tpi - 1) / tpi;
+  const int nrest = nparts * H * nblk * (a.kv_sel >= 0 ? 1 : 2);
   const int q4 = lane >> 4, col = lane & 15;
   const int e0 = EPL * q4;
   const int tau0 = e0 / C, i0 = e0 % C;
 
-  // ---- the codebook as MFMA A operand, scaled by -2; |C_k|^2 for the bias
-  const uint16_t* cb = a.codebooks + ((((size_t)beta * 2 + kv) * H + h) * NG + g) * ((size_t)TC * kCodes * C);
-  R A[16];
-  float cmax2 = 0.f;
-#pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const R v = *(const R*)(cb + ((size_t)tau0 * kCodes + 16 * m + col) * C + i0);
-    R w;
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float f = bf2f(v[e]);
-      s = fmaf(f, f, s);
-      w[e] = (uint16_t)(__float_as_uint(-2.f * f) >> 16);
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int xcd = item % kXcds;
+    const int r8 = item / kXcds;
+    const int gb = r8 % NGB;
+    int rest = (r8 / NGB) * kXcds + xcd;
+    if (rest >= nrest) continue;   // padding to whole XCD rounds (uniform per workgroup)
+    const int part = rest % nparts; rest /= nparts;
+    const int h = rest % H;         rest /= H;
+    const int beta = rest % nblk;   rest /= nblk;
+    const int kv = (a.kv_sel >= 0) ? a.kv_sel : rest;
+    const int g = gb * WPG + wave;
+    const int nb0 = part * tpi;
+    const int nb1 = min(N, nb0 + tpi);
+
+    // ---- the codebook as MFMA A operand, scaled by -2 (exact); |C_k|^2 in float64, rounded once
+    const uint16_t* cb = a.codebooks + ((((size_t)beta * 2 + kv) * H + h) * NG + g) * ((size_t)TC * kCodes * C);
+    R A[16];
+    float cmax2 = 0.f;
+  #pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const R v = *(const R*)(cb + ((size_t)tau0 * kCodes + 16 * m + col) * C + i0);
+      R w;
+      double s = 0.0;
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float f = bf2f(v[e]);
+        s = fma((double)f, (double)f, s);
+        w[e] = (uint16_t)(__float_as_uint(-2.f * f) >> 16);
+      }
+      A[m] = w;
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      const float sf = (float)s;
+      cmax2 = fmaxf(cmax2, sf);
+      if (q4 == 0) s_bias[wave][16 * m + col] = sf;
     }
-    A[m] = w;
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    cmax2 = fmaxf(cmax2, s);
-    if (q4 == 0) s_bias[wave][16 * m + col] = s;
-  }
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) cmax2 = fmaxf(cmax2, __shfl_xor(cmax2, off));
-  if (lane == 0) s_nflag[wave] = 0;
-  __syncthreads();
-  const float* bias = &s_bias[wave][4 * q4];
+  #pragma unroll
+    for (int off = 1; off < 16; off <<= 1) cmax2 = fmaxf(cmax2, __shfl_xor(cmax2, off));
+    const float* bias = &s_bias[wave][4 * q4];
+    // Dense rows of the lane's (loop step, channel slice) start at src_base + n * H * d;
+    // the lane's source and destination pointers advance by one tile (16 tokens) per step.
+    const size_t src_stride = (size_t)H * a.d;
+    const size_t dst_stride = (size_t)H * NG;
+    const uint16_t* src_base = a.src + ((size_t)(beta * TC + tau0) * N * H + h) * a.d + g * C + i0;
+    const uint16_t* src_any = src_base + (size_t)nb0 * src_stride;   // a readable row of this block
+    const uint16_t* src_lane = src_base + (size_t)(nb0 + col) * src_stride;
+    uint8_t* dst_lane = a.out + ((size_t)beta * N * H + h) * NG + g + (size_t)(nb0 + col) * dst_stride;
 
-  const int nb0 = chunk * a.tokens_per_block;
-  const int nb1 = min(N, nb0 + a.tokens_per_block);
-  for (int n0 = nb0; n0 < nb1; n0 += 16) {
-    const int n = n0 + col;
-    const bool in_range = n < nb1;
-    const uint16_t* row = in_range ? src_row(a, beta * TC + tau0, n, h, kv) : nullptr;
-    R B;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) B[e] = 0;
-    if (row) B = *(const R*)(row + g * C + i0);
-    float xx = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) { const float f = bf2f(B[e]); xx = fmaf(f, f, xx); }
-    xx += __shfl_xor(xx, 16);
-    xx += __shfl_xor(xx, 32);
+    // Load the lane's channel slice of tile n0 (and its destination page id).  Every load
+    // is unconditional, a slot past the range reading a row of this block and a missing
+    // bf16 page reading the codebook, so the compiler can count the loads in flight; ok
+    // says whether the slot is a real token.
+    auto fetch = [&](int n0, R& v, bool& ok, int& pg) {
+      const int n = n0 + col;
+      ok = n < nb1;
+      const uint16_t* ptr;
+      if constexpr (kDenseSrc) {
+        ptr = ok ? src_lane + (size_t)(n0 - nb0) * src_stride : src_any;
+      } else {
+        const uint16_t* r = src_row(a, beta * TC + tau0, ok ? n : nb0, h, kv);
+        ok = ok && r != nullptr;
+        ptr = r ? r + g * C + i0 : cb;
+      }
+      v = *(const R*)ptr;
+      if constexpr (kDenseDst) {
+        pg = 0;
+      } else {
+        pg = a.dst_pages[(ok ? n : nb0) >> 3];
+      }
+    };
 
-    // Argmin over the 256 expanded distances D'_k of this lane's vector.  Four
-    // chains (one per accumulator row) of 16 candidates each are folded with
-    // float min on keys whose low four mantissa bits hold the code block m;
-    // the fill makes a tie at key precision go to the lowest code: 15 - m for
-    // negative D' (a larger pattern is more negative), m for positive D'.  The
-    // MFMAs are issued in two halves of 8 to bound the live accumulators.
-    auto fold = [&](const bool positive, float& bv, float& sv, int& code) {
-      float best[4] = {__builtin_inff(), __builtin_inff(), __builtin_inff(), __builtin_inff()};
+    // One 16-token tile: distances, argmin, certification, index write or deferral.
+    auto tile = [&](int n0, bool ok, const R& B, int pg) {
+      // keep the |C_k|^2 reads from LDS inside the tile (hoisted, they would take 64 VGPRs)
+      asm volatile("" ::: "memory");
+      const int n = n0 + col;
+      // |x|^2 of the vector, only for the error bound
+      float xx = 0.f;
+  #pragma unroll
+      for (int e = 0; e < EPL; e += 2) {
+        const bf16x2 two = __builtin_bit_cast(bf16x2, (uint32_t)B[e] | ((uint32_t)B[e + 1] << 16));
+        xx = __builtin_amdgcn_fdot2_f32_bf16(two, two, xx, false);
+      }
+      xx += __shfl_xor(xx, 16);
+      xx += __shfl_xor(xx, 32);
+
+      // The lane's 64 candidates (codes 16m + 4 q4 + r) become keys: D'_k with its six
+      // low mantissa bits replaced by 63 - (4m + r).  A smaller key is a smaller D' at
+      // key precision, and every key of the lane is distinct.  Keys are folded three
+      // at a time into the smallest b1 and second smallest b2 of two alternating
+      // chains: t1 = min3, t2 = med3 of the triple, b2 = min3(max(b1, t1), b2, t2),
+      // b1 = min(b1, t1); the chains merge afterwards.
+      float c1[2] = {__builtin_inff(), __builtin_inff()};
+      float c2[2] = {__builtin_inff(), __builtin_inff()};
+      float kq[3];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        f32x4 acc[8];
+      for (int part = 0; part < 16 / kPart; ++part) {
+        f32x4 acc[kPart];
 #pragma unroll
-        for (int mm = 0; mm < 8; ++mm) {
-          const int m = 8 * half + mm;
+        for (int mm = 0; mm < kPart; ++mm) {
+          const int m = kPart * part + mm;
           acc[mm] = mfma_bf16<EPL>(A[m], B, *(const f32x4*)(bias + 16 * m));
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int mm = 0; mm < kPart; ++mm) {
 #pragma unroll
-          for (int mm = 0; mm < 8; ++mm) {
-            const int m = 8 * half + mm;
-            const uint32_t fill = positive ? (uint32_t)m : (uint32_t)(15 - m);
-            const uint32_t u = (__float_as_uint(acc[mm][r]) & 0xFFFFFFF0u) | fill;
-            best[r] = fminf(best[r], __uint_as_float(u));
+          for (int r = 0; r < 4; ++r) {
+            const int idx = 4 * (kPart * part + mm) + r;   // 0..63, compile time
+            kq[idx % 3] = __uint_as_float((__float_as_uint(acc[mm][r]) & ~63u) | (63u - (uint32_t)idx));
+            if (idx % 3 == 2) {
+              const int ch = (idx / 3) & 1;
+              const float t1 = key_min3(kq[0], kq[1], kq[2]);
+              const float t2 = key_med3(kq[0], kq[1], kq[2]);
+              c2[ch] = key_min3(key_max(c1[ch], t1), c2[ch], t2);
+              c1[ch] = key_min(c1[ch], t1);
+            } else if (idx == 63) {
+              c2[0] = key_med3(c1[0], c2[0], kq[0]);
+              c1[0] = key_min(c1[0], kq[0]);
+            }
           }
         }
       }
-      bv = best[0];
-      sv = __builtin_inff();
-      int rr = 0;
-#pragma unroll
-      for (int r = 1; r < 4; ++r) {
-        if (best[r] < bv) { sv = bv; bv = best[r]; rr = r; }
-        else sv = fminf(sv, best[r]);
-      }
-      const uint32_t low = __float_as_uint(bv) & 15u;
-      const int m = positive ? (int)low : 15 - (int)low;
-      code = 16 * m + 4 * q4 + rr;
-#pragma unroll
+      float b1 = key_min(c1[0], c1[1]);
+      float b2 = key_min(key_max(c1[0], c1[1]), key_min(c2[0], c2[1]));
+      // Merge the four lanes of the vector: smallest and second smallest key overall.
+      // The lane whose own smallest key survives holds the winning code; equal keys in
+      // two lanes make b2 == b1, which sends the vector to the float64 pass.
+      const float own = b1;
+  #pragma unroll
       for (int off = 16; off <= 32; off <<= 1) {
-        const float ob = __shfl_xor(bv, off);
-        const float os = __shfl_xor(sv, off);
-        const int oc = __shfl_xor(code, off);
-        if (ob < bv || (ob == bv && oc < code)) { sv = fminf(bv, os); bv = ob; code = oc; }
-        else sv = fminf(sv, fminf(ob, os));
+        const float o1 = __shfl_xor(b1, off);
+        const float o2 = __shfl_xor(b2, off);
+        b2 = key_min(key_max(b1, o1), key_min(b2, o2));
+        b1 = key_min(b1, o1);
+      }
+      const bool owner = own == b1;
+      // Float32 error bound for two expanded distances (33 or 17 rounded terms, each
+      // sum bounded by S = (|x| + max|C|)^2, plus the rounded |C|^2) and the six
+      // truncated key bits; the approximate square root only enters the bound.
+      const float S = xx + cmax2 + 2.f * __builtin_amdgcn_sqrtf(xx * cmax2);
+      const float tol = 80.f * 5.9604645e-8f * S + 3.0517578e-5f * fabsf(b1);
+      const bool need_exact = ok && !(b2 - b1 > tol);
+      uint8_t* o = nullptr;   // this lane's destination byte (vector col)
+      if constexpr (kDenseDst) {
+        o = dst_lane + (size_t)(n0 - nb0) * dst_stride;
+      } else if (pg >= 0 && pg < a.n_dst_pages) {
+        o = a.out + (((((size_t)pg * nblk + beta) * H + h) * 2 + kv) * kPage + (n & 7)) * NG + g;
+      }
+      if (ok && owner && !need_exact && o) {
+        const uint32_t p = 63u - (__float_as_uint(b1) & 63u);
+        *o = (uint8_t)(16 * (int)(p >> 2) + 4 * q4 + (int)(p & 3u));
+      }
+      // Vectors whose float32 decision is not certain: float64 from registers, one at a time.
+      uint64_t todo = __ballot(need_exact && q4 == 0);   // bits = vector columns
+      while (todo) {
+        const int cv = (int)__builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int ex = exact_in_registers<EPL>(A, B, cv, lane);
+        if (lane == cv && o) *o = (uint8_t)ex;
       }
     };
-    float bv, sv;
-    int code;
-    fold(false, bv, sv, code);
-    if (__any(row != nullptr && !(bv < 0.f))) {
-      float bv2, sv2;
-      int code2;
-      fold(true, bv2, sv2, code2);
-      if (!(bv < 0.f)) { bv = bv2; sv = sv2; code = code2; }
-    }
-    // float32 error bound of two expanded distances plus the key truncation
-    const float S = xx + cmax2 + 2.f * sqrtf(xx * cmax2);
-    const float tol = 80.f * 5.9604645e-8f * S + 4.0f * 1.9073486e-6f * fabsf(bv);
-    const bool need_exact = row && !(sv - bv > tol);
-    const uint64_t todo = __ballot(need_exact && q4 == 0);
-    if (todo) {
-      const int base = s_nflag[wave];
-      if (need_exact && q4 == 0) s_flag[wave][base + __popcll(todo & ((1ull << lane) - 1))] = n;
-      if (lane == 0) s_nflag[wave] = base + __popcll(todo);
-    }
-    if (row && q4 == 0 && !need_exact) {
-      uint8_t* o = dst_byte(a, beta, n, h, g, kv, NG);
-      if (o) *o = (uint8_t)code;
-    }
-  }
-  // float64 pass over the vectors whose float32 decision was not certain
-  const int nflag = s_nflag[wave];
-#pragma unroll 1
-  for (int f = 0; f < nflag; ++f) {
-    const int n = s_flag[wave][f];
-    const int ex = exact_nearest<G, C>(a, cb, beta, n, h, g, kv, lane);
-    if (lane == 0) {
-      uint8_t* o = dst_byte(a, beta, n, h, g, kv, NG);
-      if (o) *o = (uint8_t)ex;
+
+    // Buffer j is refilled right after its tile is consumed and used again kRing - 1
+    // tiles later, so each load overlaps that much work.
+    R Bq[kRing];
+    bool okq[kRing];
+    int pgq[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) fetch(nb0 + 16 * j, Bq[j], okq[j], pgq[j]);
+    for (int n0 = nb0; n0 < nb1; n0 += 16 * kRing) {
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) {
+        if (n0 + 16 * j < nb1) tile(n0 + 16 * j, okq[j], Bq[j], pgq[j]);
+        fetch(n0 + 16 * (j + kRing), Bq[j], okq[j], pgq[j]);
+      }
     }
   }
 }
 
+// Workgroups per CU the kernel reaches and the device's CU count, cached per device.
+template <typename K>
+int resident_workgroups(K kernel, int threads) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int v = per_cu * cus;
+  if (v > 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int G, int C, int D, int MODE>
+hipError_t launch_mode(const EncodeArgs& args, hipStream_t s) {
+  constexpr int NG = D / C;
+  constexpr int WPG = waves_per_group_block<D, C>();
+  constexpr int NGB = NG / WPG;
+  if (args.N <= 0) return hipSuccess;
+  auto kernel = encode_kernel<G, C, D, MODE>;
+  int slots = resident_workgroups(kernel, WPG * 64);
+  if (slots <= 0) slots = 256;
+  const int round = kXcds * NGB;
+  slots = slots / round * round;
+  if (slots < round) slots = round;
+  // split every (head, block, K/V) codebook set into enough token ranges to fill the slots
+  const long sets = (long)args.H * (args.T / args.Tc) * (args.kv_sel < 0 ? 2 : 1);
+  long parts = slots / (sets * NGB);
+  if (parts < 1) parts = 1;
+  long tpi = (args.N + parts - 1) / parts;
+  tpi = (tpi + 15) / 16 * 16;
+  parts = (args.N + tpi - 1) / tpi;
+  const long nrest = parts * sets;
+  const long items = (nrest + kXcds - 1) / kXcds * kXcds * NGB;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
+  const long grid = items < slots ? items : slots;
+  EncodeArgs a = args;
+  a.tokens_per_block = (int)tpi;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(WPG * 64), 0, s, a, (int)items);
+  return hipGetLastError();
+}
+
 template <int G, int C, int D>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t s) {
-  constexpr int NG = D / C;
-  constexpr int WPG = NG < 8 ? NG : 8;
-  const int nblk = a.T / a.Tc;
-  const int nchunk = (a.N + a.tokens_per_block - 1) / a.tokens_per_block;
-  const long grid = (long)nchunk * (NG / WPG) * a.H * nblk * (a.kv_sel < 0 ? 2 : 1);
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((encode_kernel<G, C, D>), dim3((unsigned)grid), dim3(WPG * 64), 0, s, a);
-  return hipGetLastError();
+  if (a.src_mode == kSrcPages) return launch_mode<G, C, D, 2>(a, s);
+  if (a.dst_mode == kDstPages) return launch_mode<G, C, D, 1>(a, s);
+  return launch_mode<G, C, D, 0>(a, s);
 }
 
 template <int G, int C>
