@@ -61,9 +61,12 @@ SplitPlan plan_splits(const lvq_attn_shape& s) {
     n = n < 1 ? 1 : n;
     const int by_len = max_tiles / 16;
     if (n > by_len) n = by_len < 1 ? 1 : by_len;
+    // whole workgroups of chunks
+    const int w = lvq::attn_waves_per_group();
+    if (n > w) n = (n + w - 1) / w * w;
   }
   if (n > max_tiles) n = max_tiles < 1 ? 1 : max_tiles;
-  if (n > 1023) n = 1023;                       // merge kernel bound on splits
+  if (n > 1023) n = 1023;                       // bound on splits per (b, query head)
   const int tiles = (max_tiles + n - 1) / n;
   SplitPlan p;
   p.chunk_pages = (tiles < 1 ? 1 : tiles) * 8;
@@ -103,7 +106,7 @@ int check_attn(const void* q, const void* page_table, const void* index_pages,
 
 size_t workspace_bytes(const lvq_attn_shape& s) {
   const SplitPlan p = plan_splits(s);
-  return (size_t)s.B * s.Hq * (p.n_chunks + 1) * (s.d + 2) * sizeof(float);
+  return (size_t)s.B * s.Hq * p.n_chunks * (s.d + 2) * sizeof(float);
 }
 
 int run_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,

@@ -31,8 +31,11 @@
 //  * Scores are kept in log2 units (scale * log2 e folded into the query); a
 //    running maximum is kept lazily (rescale only when a score passes it by
 //    more than 8 in log2 units).
-//  * The bf16 sink + recent tokens of every (b, query head) run as extra
-//    workgroups placed first in the grid; their partial is the last split.
+//  * The bf16 sink and recent tokens of a (b, query head) form a few virtual
+//    tiles (16 positions each) handed round-robin to the same chunk waves, read
+//    from the bf16 pages in float32: no separate workgroups, no extra partial.
+//  * LDS layout [code][16-byte chunk] and a per-lane chunk order keep the lanes
+//    of an LDS access phase on distinct banks.
 #include "lvq_internal.h"
 
 namespace lvq {
@@ -45,20 +48,20 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescale = 8.0f;   // lazy-max slack, log2 units
-constexpr int kNW = 8;             // waves per workgroup
+constexpr int kNW = 12;            // waves per workgroup
+constexpr int kWavesPerSimd = 3;   // occupancy the register budget is sized for
+constexpr int kBatch = 2;          // tiles per prefetch batch
 constexpr int kTile = 16;          // positions per tile (RoPE table granularity)
 constexpr int kPtBatch = 128;      // page ids staged in LDS per wave at a time
-constexpr int kBfTok = 32;         // bf16 tokens per batch
 
-// LDS bytes per wave of the bf16 part: K and V rows of a batch, weights, query, row addresses
+// Tile-phase buffer (floats): the d/2 pairs in 4 quarter blocks of d/8 pairs, each
+// block followed by 16 bytes of padding so the four quarters read distinct LDS banks.
 template <int D>
-constexpr size_t kBf16Scratch = 2 * kBfTok * (2 * D + 16) + kBfTok * 4 + D * 4 + kBfTok * 8;
+constexpr int phase_buf_floats() { return 4 * (2 * (D / 8) + 4); }
 
 template <int D>
 constexpr size_t lds_bytes() {
-  const size_t coded = (size_t)2 * kCodes * D * 2 + (size_t)kNW * (D * 4 + 2 * D * 4 + kPtBatch * 4);
-  const size_t bf = (size_t)kNW * kBf16Scratch<D>;
-  return coded > bf ? coded : bf;
+  return (size_t)2 * kCodes * D * 2 + (size_t)D * 4 + (size_t)kNW * (2 * phase_buf_floats<D>() * 4 + kPtBatch * 4);
 }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -82,158 +85,51 @@ __device__ __forceinline__ float2 phase(const float* __restrict__ rope, int tile
   return make_float2(c0 * c1 - s0 * s1, s0 * c1 + c0 * s1);
 }
 
-// Stage the step-tau [256][c] slices of all groups of book (beta, kv, h) into LDS as float16.
+// Stage the step-tau [256][c] slices of all groups of book (beta, kv, h) into LDS as
+// float16, laid out [code][chunk][8]: chunk k of code x holds channels 8k..8k+7 of
+// code x's share.  A gather's LDS bank then depends on the chunk, not on the code.
 template <int D, int C>
 __device__ __forceinline__ void stage_slice(const AttnArgs& a, int beta, int kv, int h, int tau,
                                             _Float16* dst) {
   constexpr int NG = D / C;
+  constexpr int NCH = D / 8;
   const uint16_t* src = a.codebooks + ((((size_t)beta * 2 + kv) * a.H + h) * NG) * ((size_t)a.Tc * kCodes * C);
   for (int e = threadIdx.x * 8; e < kCodes * D; e += kNW * 64 * 8) {
-    const int g = e / (kCodes * C), rem = e % (kCodes * C);
-    const u16x8 v = *(const u16x8*)(src + ((size_t)g * a.Tc + tau) * kCodes * C + rem);
+    const int x = e / D, k = (e % D) / 8;                // destination code and chunk
+    const int g = (8 * k) / C, i = (8 * k) % C;
+    const u16x8 v = *(const u16x8*)(src + (((size_t)g * a.Tc + tau) * kCodes + x) * C + i);
     f16x8 o;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (_Float16)bf2f(v[i]);
-    *(f16x8*)(dst + e) = o;
+    for (int q = 0; q < 8; ++q) o[q] = (_Float16)bf2f(v[q]);
+    *(f16x8*)(dst + ((size_t)x * NCH + k) * 8) = o;
   }
 }
 
-// ------------------------------------------------------------------ bf16 part
-// One wave per (b, hq): the sink tokens [0, n_sink) and the recent tokens
-// [max(q_end, n_sink), L), 32 at a time.  The K and V rows of a batch are
-// copied into LDS with all loads in flight at once; lane i < 32 scores token i
-// (RoPE on the key from the two-part phase table), then each lane accumulates
-// one channel pair of the output over the batch.
-template <int D>
-__device__ void bf16_part(const AttnArgs& a, const float* __restrict__ rope, int item, int lane,
-                          unsigned char* scratch) {
-  constexpr int HALF = D / 2;
-  constexpr int ROWB = 2 * D + 16;        // padded LDS row (bytes): spreads lanes over banks
-  const int b = item / a.Hq, hq = item % a.Hq;
-  if (b >= a.B) return;
-  const int h = hq / (a.Hq / a.H);
-  const int L = min(a.seq_len[b], a.max_seq_len);
-  const int qe = min(a.q_end[b] & ~7, L);
-  const int ns = min(a.n_sink, L);
-  const int r0 = max(qe, a.n_sink);
-  const int n_tok = ns + max(0, L - r0);
-  unsigned char* krow = scratch;                         // [kBfTok][ROWB]
-  unsigned char* vrow = scratch + kBfTok * ROWB;         // [kBfTok][ROWB]
-  float* wl = (float*)(scratch + 2 * kBfTok * ROWB);     // [kBfTok] weights
-  float* qp = wl + kBfTok;                               // [D] rotated query (pairs)
-  const uint16_t** src = (const uint16_t**)(qp + D);     // [kBfTok] K row address per token
-
-  // rotated query, pairs (j, j + d/2) interleaved, log2 units
-  if (lane < HALF) {
-    const int pq = min(max(a.pos[b], 0), a.rope_tiles * kTile - 1);
-    const uint16_t* qv = a.q + ((size_t)b * a.Hq + hq) * D;
-    const float2 cs = phase(rope, a.rope_tiles, D, pq, lane);
-    const float x = bf2f(qv[lane]), y = bf2f(qv[lane + HALF]);
-    qp[2 * lane] = (x * cs.x - y * cs.y) * a.scale_log2e;
-    qp[2 * lane + 1] = (y * cs.x + x * cs.y) * a.scale_log2e;
-  }
-  float m = -__builtin_inff(), l = 0.f, oa = 0.f, ob = 0.f;   // oa, ob: channels j, j + d/2 (j = lane)
-  for (int i0 = 0; i0 < n_tok; i0 += kBfTok) {
-    // token of this lane, its position and its K row in the page pool
-    const int i = i0 + lane;
-    const bool ok = lane < kBfTok && i < n_tok;
-    const int p = ok ? (i < ns ? i : r0 + (i - ns)) : 0;
-    const uint16_t* kr = nullptr;
-    if (ok) {
-      const int slot = (p < ns) ? 0 : 1 + (p >> 3) - (qe >> 3);
-      const int pg = slot < a.bf16_row ? a.bf16_table[(size_t)b * a.bf16_row + slot] : -1;
-      if (pg >= 0 && pg < a.n_bf16_pages)
-        kr = a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2 + 0) * kPage + (p & 7)) * D;
-    }
-    if (lane < kBfTok) src[lane] = kr;
-    // copy the batch's K and V rows into LDS: 16 bytes per lane per step, all loads issued first
-    constexpr int CPR = 2 * D / 16;                    // 16-byte chunks per row
-    constexpr int NCH = kBfTok * CPR / 64;             // chunks per lane per half
-    u32x4 kbuf[NCH], vbuf[NCH];
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const int cidx = k * 64 + lane, row = cidx / CPR, part = cidx % CPR;
-      const uint16_t* rp = src[row];
-      kbuf[k] = rp ? *(const u32x4*)(rp + part * 8) : u32x4{0, 0, 0, 0};
-      vbuf[k] = rp ? *(const u32x4*)(rp + (size_t)kPage * D + part * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const int cidx = k * 64 + lane, row = cidx / CPR, part = cidx % CPR;
-      *(u32x4*)(krow + row * ROWB + part * 16) = kbuf[k];
-      *(u32x4*)(vrow + row * ROWB + part * 16) = vbuf[k];
-    }
-    // score of this lane's token
-    float s = -__builtin_inff();
-    if (kr) {
-      const uint16_t* kk = (const uint16_t*)(krow + lane * ROWB);
-      float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < HALF; ++j) {
-        const float2 cs = phase(rope, a.rope_tiles, D, p, j);
-        const float x = bf2f(kk[j]), y = bf2f(kk[j + HALF]);
-        acc0 = fmaf(qp[2 * j], x * cs.x - y * cs.y, acc0);
-        acc1 = fmaf(qp[2 * j + 1], y * cs.x + x * cs.y, acc1);
-      }
-      s = acc0 + acc1;
-      if (a.scores) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
-    }
-    // online softmax over the batch
-    const float mb = wave_max(s);
-    const float mn = fmaxf(m, mb);
-    if (mn > -__builtin_inff()) {
-      const float f = __builtin_amdgcn_exp2f(m - mn);
-      const float w = kr ? __builtin_amdgcn_exp2f(s - mn) : 0.f;
-      if (lane < kBfTok) wl[lane] = w;
-      l = l * f + wave_sum(w);
-      oa *= f;
-      ob *= f;
-      m = mn;
-      // output channels j and j + d/2 (j = lane) over the batch's tokens
-      if (lane < HALF) {
-        const int nb = min(kBfTok, n_tok - i0);
-        for (int r = 0; r < nb; ++r) {
-          const float w_r = wl[r];
-          const uint16_t* vv = (const uint16_t*)(vrow + r * ROWB);
-          oa = fmaf(w_r, bf2f(vv[lane]), oa);
-          ob = fmaf(w_r, bf2f(vv[lane + HALF]), ob);
-        }
-      }
-    }
-  }
-  float* rec = a.part + (((size_t)b * a.Hq + hq) * (a.n_chunks + 1) + a.n_chunks) * (D + 2);
-  if (lane == 0) { rec[0] = m; rec[1] = l; }
-  if (lane < HALF) {
-    rec[2 + lane] = oa;
-    rec[2 + lane + HALF] = ob;
-  }
-}
-
-// ------------------------------------------------------------------ coded part
+// ------------------------------------------------------------------ decode attention
 template <int D, int C, bool SCORES>
-__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_bf16_wg, int n_cg) {
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
+void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
   constexpr int NG = D / C;       // groups per head
   constexpr int HALF = D / 2;
   constexpr int QP = HALF / 4;    // channel pairs per lane (score)
   constexpr int QV = D / 4;       // output channels per lane (value sum)
-  constexpr int NT = 4;           // tiles per prefetch batch
+  constexpr int NT = kBatch;      // tiles per prefetch batch
+  constexpr int NCH = D / 8;      // 16-byte chunks per codeword row in LDS
+  constexpr int KPC = QP / 8;     // key chunks per lane in each half
+  constexpr int NV = QV / 8;      // value chunks per lane
   static_assert(NG >= 4 && QP % 8 == 0 && QV % 8 == 0, "shape outside the compiled set");
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* kl = (_Float16*)smem;                          // [NG][256][C]
   _Float16* vl = kl + (size_t)kCodes * D;                  // [NG][256][C]
-  float* qs = (float*)(vl + (size_t)kCodes * D);           // [kNW][D]
-  float* e0buf = qs + kNW * D;                             // [kNW][2][D]
-  int* ptbuf = (int*)(e0buf + kNW * 2 * D);                // [kNW][kPtBatch]
+  float* qs = (float*)(vl + (size_t)kCodes * D);           // [D] rotated query
+  constexpr int ER = phase_buf_floats<D>();
+  float* e0buf = qs + D;                                   // [kNW][2][ER]
+  int* ptbuf = (int*)(e0buf + kNW * 2 * ER);               // [kNW][kPtBatch]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  if ((int)blockIdx.x < n_bf16_wg) {
-    bf16_part<D>(a, rope, blockIdx.x * kNW + wave, lane, smem + (size_t)wave * kBf16Scratch<D>);
-    return;
-  }
-  int bid = blockIdx.x - n_bf16_wg;
+  int bid = blockIdx.x;
   const int cg = bid % n_cg; bid /= n_cg;
   const int hq = bid % a.Hq; bid /= a.Hq;
   const int b = bid;
@@ -241,16 +137,23 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_bf16_wg, int 
   const int beta = a.t / a.Tc, tau = a.t % a.Tc;
   const int nblk = a.T / a.Tc;
   const int chunk = cg * kNW + wave;
-  const int qe = min(a.q_end[b] & ~7, min(a.seq_len[b], a.max_seq_len));
+  const int L = min(a.seq_len[b], a.max_seq_len);
+  const int qe = min(a.q_end[b] & ~7, L);
   const int P_lo = chunk * a.chunk_pages;
   const int P_hi = min(qe >> 3, P_lo + a.chunk_pages);
   const bool active = chunk < a.n_chunks;
+  // bf16 tokens as virtual tiles: the sink tile [0, ns) and the tiles over [r0, L)
+  const int ns = min(a.n_sink, L);
+  const int r0 = max(qe, a.n_sink);
+  const int vt_lo = r0 / kTile;
+  const int vt_hi = L > r0 ? (L - 1) / kTile + 1 : vt_lo;
+  const int n_vt = (ns > 0 ? 1 : 0) + (vt_hi - vt_lo);
 
   stage_slice<D, C>(a, beta, 0, h, tau, kl);
   stage_slice<D, C>(a, beta, 1, h, tau, vl);
-  // rotated query of this (b, hq), log2 units, pairs interleaved
-  float* qw = qs + wave * D;
-  if (lane < HALF) {
+  // rotated query of this (b, hq), log2 units, pairs interleaved (one copy per workgroup)
+  float* qw = qs;
+  if (wave == 0 && lane < HALF) {
     const int pq = min(max(a.pos[b], 0), a.rope_tiles * kTile - 1);
     const uint16_t* qv = a.q + ((size_t)b * a.Hq + hq) * D;
     const float2 cs = phase(rope, a.rope_tiles, D, pq, lane);
@@ -262,19 +165,25 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_bf16_wg, int 
   if (!active) return;
 
   const int qt = lane & 3, t = lane >> 2;       // lane quarter, token in tile
+  // Chunk order per lane, so the lanes of one LDS access phase hit distinct banks:
+  // register block v of the keys holds the lane's chunk kperm(v) (pairs swap with the
+  // token's parity), value block v holds chunk (v + vrot) mod NV.
+  const int kswap = (KPC == 2) ? (t & 1) : 0;
+  const int vrot = (NV == 4) ? ((t + 2 * (qt >> 1)) & 3) : (t & (NV - 1));
   float m = -__builtin_inff(), l = 0.f;
   float o[QV];
 #pragma unroll
   for (int i = 0; i < QV; ++i) o[i] = 0.f;
 
-  if (P_lo < P_hi && a.n_index_pages > 0) {
+  const bool has_coded = P_lo < P_hi && a.n_index_pages > 0;
+  if (has_coded || chunk < n_vt) {
     // F, G: the query turned back by the token's in-tile offset t, for this lane's pairs
     float F[QP], Gc[QP];
     {
       const float* e1 = rope + (size_t)(a.rope_tiles + t) * D;
 #pragma unroll
       for (int jj = 0; jj < QP; ++jj) {
-        const int j = qt * QP + jj;
+        const int j = qt * QP + 8 * ((jj / 8) ^ kswap) + (jj % 8);
         const float A = qw[2 * j], Bq = qw[2 * j + 1];
         const float c1 = e1[2 * j], s1 = e1[2 * j + 1];
         F[jj] = A * c1 + Bq * s1;
@@ -286,7 +195,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_bf16_wg, int 
     const int wlo = glo & ~3, whi = ghi & ~3, wv = gv & ~3;
     const int r = t & 7;
     const size_t row_stride = (size_t)kPage * NG;
-    float* e0s = e0buf + wave * 2 * D;
+    float* e0s = e0buf + wave * 2 * ER;
     int* ptl = ptbuf + wave * kPtBatch;
     const int* pt = a.page_table + (size_t)b * a.max_pages;
     int pt_base = -kPtBatch;
@@ -321,28 +230,29 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_bf16_wg, int 
       return in;
     };
     auto tile = [&](int P0, const TileIn& in, int buf) {
-      float* er = e0s + buf * D;
-      if (lane < HALF) *(float2*)(er + 2 * lane) = in.e0;
+      float* er = e0s + buf * ER;
+      if (lane < HALF) *(float2*)(er + (lane / QP) * (2 * QP + 4) + 2 * (lane % QP)) = in.e0;
       const int p = 8 * P0 + t;
       const bool valid = in.phys >= 0 && p >= a.n_sink;
       // keys: low channels [qt*QP, qt*QP + QP) and the partners + d/2
       f16x8 xl[QP / 8], xh[QP / 8];
 #pragma unroll
       for (int v = 0; v < QP / 8; ++v) {
-        const int cl = qt * QP + 8 * v, ch = cl + HALF;
+        const int cl = qt * QP + 8 * (v ^ kswap), ch = cl + HALF;
         const int gl = cl / C, gh = ch / C;
         const int codl = (in.kwl >> (8 * (gl - wlo))) & 0xff;
         const int codh = (in.kwh >> (8 * (gh - whi))) & 0xff;
-        xl[v] = *(const f16x8*)(kl + ((size_t)gl * kCodes + codl) * C + cl % C);
-        xh[v] = *(const f16x8*)(kl + ((size_t)gh * kCodes + codh) * C + ch % C);
+        xl[v] = *(const f16x8*)(kl + ((size_t)codl * NCH + cl / 8) * 8);
+        xh[v] = *(const f16x8*)(kl + ((size_t)codh * NCH + ch / 8) * 8);
       }
       float s0acc = 0.f, s1acc = 0.f;
 #pragma unroll
       for (int v = 0; v < QP / 8; ++v) {
 #pragma unroll
         for (int i4 = 0; i4 < 2; ++i4) {
-          const f32x4 e_a = *(const f32x4*)(er + 2 * (qt * QP + 8 * v + 4 * i4));
-          const f32x4 e_b = *(const f32x4*)(er + 2 * (qt * QP + 8 * v + 4 * i4) + 4);
+          const float* ep = er + qt * (2 * QP + 4) + 2 * (8 * (v ^ kswap) + 4 * i4);
+          const f32x4 e_a = *(const f32x4*)ep;
+          const f32x4 e_b = *(const f32x4*)(ep + 4);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int i = 4 * i4 + k, jj = 8 * v + i;
@@ -372,11 +282,11 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_bf16_wg, int 
       l += (qt == 0) ? w : 0.f;
       // values: output channels [qt*QV, qt*QV + QV)
 #pragma unroll
-      for (int v = 0; v < QV / 8; ++v) {
-        const int cv = qt * QV + 8 * v;
+      for (int v = 0; v < NV; ++v) {
+        const int cv = qt * QV + 8 * ((v + vrot) & (NV - 1));
         const int g = cv / C;
         const int cod = (in.vw >> (8 * (g - wv))) & 0xff;
-        const f16x8 x = *(const f16x8*)(vl + ((size_t)g * kCodes + cod) * C + cv % C);
+        const f16x8 x = *(const f16x8*)(vl + ((size_t)cod * NCH + cv / 8) * 8);
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, (float)x[i], o[8 * v + i]);
       }
@@ -384,19 +294,109 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_bf16_wg, int 
     // Software pipeline in batches of NT tiles: each iteration loads the inputs of
     // the next batch, computes the current batch, then moves next to current, so no
     // load is in flight across the loop back-edge.
-    TileIn cur[NT], nxt[NT];
+    if (has_coded) {
+      TileIn cur[NT], nxt[NT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) cur[i] = fetch(P_lo + 2 * i);
-    for (int P0 = P_lo; P0 < P_hi; P0 += 2 * NT) {
+      for (int i = 0; i < NT; ++i) cur[i] = fetch(P_lo + 2 * i);
+      for (int P0 = P_lo; P0 < P_hi; P0 += 2 * NT) {
 #pragma unroll
-      for (int i = 0; i < NT; ++i) nxt[i] = fetch(P0 + 2 * NT + 2 * i);
+        for (int i = 0; i < NT; ++i) nxt[i] = fetch(P0 + 2 * NT + 2 * i);
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        if (P0 + 2 * i < P_hi) tile(P0 + 2 * i, cur[i], i & 1);
+        for (int i = 0; i < NT; ++i) {
+          if (P0 + 2 * i < P_hi) tile(P0 + 2 * i, cur[i], i & 1);
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i) cur[i] = nxt[i];
       }
-#pragma unroll
-      for (int i = 0; i < NT; ++i) cur[i] = nxt[i];
     }
+    // bf16 sink and recent tokens: virtual tile vt of (b, hq) runs on chunk vt mod n_chunks,
+    // with the same lane layout and RoPE factorisation; keys and values are read from the
+    // bf16 pages and used in float32 (a bf16 value need not fit float16).
+    for (int vt = chunk; vt < n_vt; vt += a.n_chunks) {
+      const bool sink_tile = ns > 0 && vt == 0;
+      const int a_tile = sink_tile ? 0 : vt_lo + vt - (ns > 0 ? 1 : 0);
+      const int lo = sink_tile ? 0 : r0, hi = sink_tile ? ns : L;
+      const int p = kTile * a_tile + t;
+      const uint16_t* krow = nullptr;
+      if (p >= lo && p < hi) {
+        const int slot = sink_tile ? 0 : 1 + (p >> 3) - (qe >> 3);
+        const int pg = slot < a.bf16_row ? a.bf16_table[(size_t)b * a.bf16_row + slot] : -1;
+        if (pg >= 0 && pg < a.n_bf16_pages)
+          krow = a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2) * kPage + (p & 7)) * D;
+      }
+      const bool valid = krow != nullptr;
+      float* er = e0s;   // the coded tiles are done with both buffers
+      if (lane < HALF) {
+        const int tile_idx = min(a_tile, a.rope_tiles - 1);
+        *(float2*)(er + (lane / QP) * (2 * QP + 4) + 2 * (lane % QP)) =
+            *(const float2*)(rope + (size_t)tile_idx * D + 2 * lane);
+      }
+      float s0acc = 0.f, s1acc = 0.f;
+      if (valid) {
+#pragma unroll
+        for (int v = 0; v < KPC; ++v) {
+          const int cl = qt * QP + 8 * (v ^ kswap), ch = cl + HALF;
+          const u16x8 xlr = *(const u16x8*)(krow + cl);
+          const u16x8 xhr = *(const u16x8*)(krow + ch);
+#pragma unroll
+          for (int i4 = 0; i4 < 2; ++i4) {
+            const float* ep = er + qt * (2 * QP + 4) + 2 * (8 * (v ^ kswap) + 4 * i4);
+            const f32x4 e_a = *(const f32x4*)ep;
+            const f32x4 e_b = *(const f32x4*)(ep + 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int i = 4 * i4 + k, jj = 8 * v + i;
+              const float c0 = k < 2 ? e_a[2 * k] : e_b[2 * (k - 2)];
+              const float sn = k < 2 ? e_a[2 * k + 1] : e_b[2 * (k - 2) + 1];
+              const float u = c0 * F[jj] + sn * Gc[jj];
+              const float w_ = c0 * Gc[jj] - sn * F[jj];
+              s0acc = fmaf(u, bf2f(xlr[i]), s0acc);
+              s1acc = fmaf(w_, bf2f(xhr[i]), s1acc);
+            }
+          }
+        }
+      }
+      float s = s0acc + s1acc;
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s = valid ? s : -__builtin_inff();
+      if (SCORES && valid && qt == 0) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
+      if (__any(s > m + kRescale)) {
+        const float mn = fmaxf(m, wave_max(s));
+        const float f = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+        for (int i = 0; i < QV; ++i) o[i] *= f;
+        l *= f;
+        m = mn;
+      }
+      const float w = valid ? __builtin_amdgcn_exp2f(s - m) : 0.f;
+      l += (qt == 0) ? w : 0.f;
+      if (valid) {
+        const uint16_t* vrow = krow + (size_t)kPage * D;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const u16x8 x = *(const u16x8*)(vrow + qt * QV + 8 * ((v + vrot) & (NV - 1)));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, bf2f(x[i]), o[8 * v + i]);
+        }
+      }
+    }
+  }
+  // value block v holds chunk (v + vrot) mod NV: put chunk c back in block c
+  {
+    float ot[QV];
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float val = o[8 * c + i];
+#pragma unroll
+        for (int k = 1; k < NV; ++k) val = (vrot == k) ? o[8 * ((c - k) & (NV - 1)) + i] : val;
+        ot[8 * c + i] = val;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < QV; ++i) o[i] = ot[i];
   }
   // fold the 16 token lanes of each quarter and write the partial (m, l, o)
 #pragma unroll
@@ -405,7 +405,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_bf16_wg, int 
     for (int i = 0; i < QV; ++i) o[i] += __shfl_xor(o[i], off);
   }
   l = wave_sum(l);
-  float* rec = a.part + (((size_t)b * a.Hq + hq) * (a.n_chunks + 1) + chunk) * (D + 2);
+  float* rec = a.part + (((size_t)b * a.Hq + hq) * a.n_chunks + chunk) * (D + 2);
   if (lane == 0) { rec[0] = m; rec[1] = l; }
   if (t == 0) {
 #pragma unroll
@@ -414,48 +414,51 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_bf16_wg, int 
 }
 
 // ------------------------------------------------------------------ merge
-// One workgroup per (b, hq): m = max m_i, l = sum l_i 2^(m_i - m),
-// out = sum o_i 2^(m_i - m) / l, lse = (m + log2 l) ln 2.
-constexpr int kMergeMax = 1024;
+// One workgroup per (b, hq), one thread per output channel.  The split partials
+// (m_i, l_i, o_i) are in log2 units: m = max m_i, l = sum l_i 2^(m_i - m),
+// out = sum o_i 2^(m_i - m) / l, lse = (m + log2 l) ln 2.  The (m_i, l_i) pairs are
+// read in one round into LDS, the weights computed there, then each channel's S
+// partial values are loaded together.
+constexpr int kMergeMax = 1024;   // splits per (b, hq) at most (the planner caps them lower)
 __global__ __launch_bounds__(128) void merge_kernel(AttnArgs a) {
-  __shared__ float sw[kMergeMax];
-  __shared__ float red[2];
+  __shared__ float2 sml[kMergeMax];
+  __shared__ float s_w[kMergeMax];
+  __shared__ float s_ml[2];
   const int item = blockIdx.x;           // b * Hq + hq
-  const int S = a.n_chunks + 1;
-  const float* rec = a.part + (size_t)item * S * (a.d + 2);
+  const int S = a.n_chunks;
+  const int D2 = a.d + 2;
+  const float* rec = a.part + (size_t)item * S * D2;
   const int tid = threadIdx.x;
-  float mloc = -__builtin_inff();
-  for (int i = tid; i < S; i += blockDim.x) {
-    const float mi = rec[(size_t)i * (a.d + 2)];
-    sw[i] = mi;
-    mloc = fmaxf(mloc, mi);
-  }
-  mloc = wave_max(mloc);
-  if ((tid & 63) == 0) red[tid >> 6] = mloc;
+  for (int i = tid; i < S; i += blockDim.x) sml[i] = *(const float2*)(rec + (size_t)i * D2);
   __syncthreads();
-  const float M = fmaxf(red[0], red[1]);
-  __syncthreads();
-  float lloc = 0.f;
-  for (int i = tid; i < S; i += blockDim.x) {
-    const float li = rec[(size_t)i * (a.d + 2) + 1];
-    const float f = (M > -__builtin_inff() && li > 0.f) ? exp2f(sw[i] - M) : 0.f;
-    sw[i] = f;
-    lloc += li * f;
-  }
-  lloc = wave_sum(lloc);
-  if ((tid & 63) == 0) red[tid >> 6] = lloc;
-  __syncthreads();
-  const float Ls = red[0] + red[1];
-  for (int ch = tid; ch < a.d; ch += blockDim.x) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < S; ++i) {
-      const float f = sw[i];
-      if (f > 0.f) acc += rec[(size_t)i * (a.d + 2) + 2 + ch] * f;
+  if (tid < 64) {
+    float mloc = -__builtin_inff();
+    for (int i = tid; i < S; i += 64) mloc = sml[i].y > 0.f ? fmaxf(mloc, sml[i].x) : mloc;
+    const float M = wave_max(mloc);
+    float lloc = 0.f;
+    for (int i = tid; i < S; i += 64) {
+      const float w = sml[i].y > 0.f ? __builtin_amdgcn_exp2f(sml[i].x - M) : 0.f;
+      s_w[i] = w;
+      lloc = fmaf(sml[i].y, w, lloc);
     }
-    a.out[(size_t)item * a.d + ch] = Ls > 0.f ? acc / Ls : 0.f;
+    const float Ls = wave_sum(lloc);
+    if (tid == 0) { s_ml[0] = M; s_ml[1] = Ls; }
   }
-  if (a.lse && tid == 0) a.lse[item] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -__builtin_inff();
+  __syncthreads();
+  const float M = s_ml[0], Ls = s_ml[1];
+  const int ch = tid;
+  if (ch < a.d) {
+    float acc0 = 0.f, acc1 = 0.f;
+    int i = 0;
+    for (; i + 1 < S; i += 2) {
+      const float o0 = rec[(size_t)i * D2 + 2 + ch], o1 = rec[(size_t)(i + 1) * D2 + 2 + ch];
+      acc0 = fmaf(o0, s_w[i], acc0);
+      acc1 = fmaf(o1, s_w[i + 1], acc1);
+    }
+    if (i < S) acc0 = fmaf(rec[(size_t)i * D2 + 2 + ch], s_w[i], acc0);
+    a.out[(size_t)item * a.d + ch] = Ls > 0.f ? (acc0 + acc1) / Ls : 0.f;
+  }
+  if (a.lse && tid == 0) a.lse[item] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
 }
 
 // ------------------------------------------------------------------ RoPE tables
@@ -486,11 +489,10 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
     attr_set = true;
   }
   const int n_items = a.B * a.Hq;
-  const int n_bf16_wg = (n_items + kNW - 1) / kNW;
   const int n_cg = (a.n_chunks + kNW - 1) / kNW;
-  const long grid = (long)n_bf16_wg + (long)n_cg * n_items;
+  const long grid = (long)n_cg * n_items;
   hipLaunchKernelGGL((attn_kernel<D, C, SCORES>), dim3((unsigned)grid), dim3(kNW * 64), lds, s, a,
-                     a.rope, n_bf16_wg, n_cg);
+                     a.rope, n_cg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_kernel, dim3(n_items), dim3(128), 0, s, a);
@@ -505,6 +507,8 @@ hipError_t launch_attn_s(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 int rope_tile() { return kTile; }
+
+int attn_waves_per_group() { return kNW; }
 
 bool attn_supported(int d, int c) {
   if (d == 128) return c == 8 || c == 16 || c == 32;

@@ -45,7 +45,7 @@ struct AttnArgs {
   const int32_t* seq_len;
   const int32_t* q_end;
   const float* rope;          // tile rows [ntile][d/2][2], offset rows [16][d/2][2], theta [d/2] (double)
-  float* part;                // partials [B][Hq][S][d + 2]
+  float* part;                // partials [B][Hq][n_chunks][d + 2]
   float* out;                 // [B][Hq][d]
   float* lse;                 // [B][Hq] or null
   float* scores;              // [B][Hq][max_seq_len] or null (probe)
@@ -57,6 +57,7 @@ struct AttnArgs {
 };
 bool attn_supported(int d, int c);
 int rope_tile();   // positions per row of the first RoPE table part
+int attn_waves_per_group();   // coded chunks (waves) per attention workgroup
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 }  // namespace lvq
