@@ -71,6 +71,12 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
 }
+// sum over the 4 lanes of a quad (lanes 4i..4i+3), by DPP quad permutes
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // [2,3,0,1]
+  return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -195,6 +201,37 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
     const int wlo = glo & ~3, whi = ghi & ~3, wv = gv & ~3;
     const int r = t & 7;
     const size_t row_stride = (size_t)kPage * NG;
+    const size_t page_bytes = (size_t)nblk * a.H * 2 * row_stride;
+    // the lane's three index words within a page, and the page base
+    const uint8_t* lane_row = a.index_pages + (((size_t)beta * a.H + h) * 2) * row_stride + r * NG;
+    // Per-lane gather constants: bit offset of the code in its index word, and the LDS
+    // byte offset of the chunk (code x of chunk k sits at byte (x * NCH + k) * 16).
+    constexpr int kRowShift = (NCH == 16) ? 8 : 7;   // log2(NCH * 16)
+    // A partner chunk (channels + d/2) sits HALF / 8 chunks further on (an immediate
+    // offset of the LDS read) and its code is KSH bits further along in its index word
+    // than the low chunk's code in its own word (the same for every lane).
+    constexpr uint32_t kHighOff = (HALF / 8) * 16;
+    // HALF / C groups separate the two codes; with a multiple of 4 they sit at the same
+    // byte of their words, with 2 (the low code in byte 0 or 1) two bytes further on.
+    static_assert((HALF / C) % 4 == 0 || HALF / C == 2, "shape outside the compiled set");
+    constexpr uint32_t kHighShift = ((HALF / C) % 4 == 0) ? 0 : 8 * (HALF / C);
+    uint32_t shl[KPC], offl[KPC], shv[NV], offv[NV];
+#pragma unroll
+    for (int v = 0; v < KPC; ++v) {
+      const int cl = qt * QP + 8 * (v ^ kswap);
+      shl[v] = 8 * (cl / C - wlo);
+      offl[v] = (uint32_t)(cl / 8) * 16;
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int cv = qt * QV + 8 * ((v + vrot) & (NV - 1));
+      shv[v] = 8 * (cv / C - wv);
+      offv[v] = (uint32_t)(kCodes * D * 2) + (uint32_t)(cv / 8) * 16;   // value slices follow the keys
+    }
+    auto gather = [&](uint32_t word, uint32_t sh, uint32_t off) -> f16x8 {
+      const uint32_t code = __builtin_amdgcn_ubfe(word, sh, 8);
+      return *(const f16x8*)(smem + ((code << kRowShift) | off));
+    };
     float* e0s = e0buf + wave * 2 * ER;
     int* ptl = ptbuf + wave * kPtBatch;
     const int* pt = a.page_table + (size_t)b * a.max_pages;
@@ -221,7 +258,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
       TileIn in;
       if (P0 + 1 >= pt_base + kPtBatch) stage_pt(P0);
       in.phys = P0 < P_hi ? ptl[P0 - pt_base + (t >> 3)] : -1;
-      const uint8_t* base = a.index_pages + ((((size_t)max(in.phys, 0) * nblk + beta) * a.H + h) * 2) * row_stride + r * NG;
+      const uint8_t* base = lane_row + (size_t)(uint32_t)max(in.phys, 0) * page_bytes;
       in.kwl = *(const uint32_t*)(base + wlo);
       in.kwh = *(const uint32_t*)(base + whi);
       in.vw = *(const uint32_t*)(base + row_stride + wv);
@@ -237,13 +274,9 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
       // keys: low channels [qt*QP, qt*QP + QP) and the partners + d/2
       f16x8 xl[QP / 8], xh[QP / 8];
 #pragma unroll
-      for (int v = 0; v < QP / 8; ++v) {
-        const int cl = qt * QP + 8 * (v ^ kswap), ch = cl + HALF;
-        const int gl = cl / C, gh = ch / C;
-        const int codl = (in.kwl >> (8 * (gl - wlo))) & 0xff;
-        const int codh = (in.kwh >> (8 * (gh - whi))) & 0xff;
-        xl[v] = *(const f16x8*)(kl + ((size_t)codl * NCH + cl / 8) * 8);
-        xh[v] = *(const f16x8*)(kl + ((size_t)codh * NCH + ch / 8) * 8);
+      for (int v = 0; v < KPC; ++v) {
+        xl[v] = gather(in.kwl, shl[v], offl[v]);
+        xh[v] = gather(in.kwh, shl[v] + kHighShift, offl[v] + kHighOff);
       }
       float s0acc = 0.f, s1acc = 0.f;
 #pragma unroll
@@ -265,10 +298,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
           }
         }
       }
-      float s = s0acc + s1acc;
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s = valid ? s : -__builtin_inff();
+      const float s = valid ? quad_sum(s0acc + s1acc) : -__builtin_inff();
       if (SCORES && valid && qt == 0) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
       if (__any(s > m + kRescale)) {
         const float mn = fmaxf(m, wave_max(s));
@@ -283,10 +313,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
       // values: output channels [qt*QV, qt*QV + QV)
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const int cv = qt * QV + 8 * ((v + vrot) & (NV - 1));
-        const int g = cv / C;
-        const int cod = (in.vw >> (8 * (g - wv))) & 0xff;
-        const f16x8 x = *(const f16x8*)(vl + ((size_t)cod * NCH + cv / 8) * 8);
+        const f16x8 x = gather(in.vw, shv[v], offv[v]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, (float)x[i], o[8 * v + i]);
       }
@@ -356,10 +383,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
           }
         }
       }
-      float s = s0acc + s1acc;
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s = valid ? s : -__builtin_inff();
+      const float s = valid ? quad_sum(s0acc + s1acc) : -__builtin_inff();
       if (SCORES && valid && qt == 0) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
       if (__any(s > m + kRescale)) {
         const float mn = fmaxf(m, wave_max(s));
