@@ -36,6 +36,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 B, L, H, D, T, TC, G = 8, 32768, 16, 128, 4, 4, 32
 N_SINK, N_RECENT = 4, 64
 CONFIG_ID = 2
+CALIB_BYTES = 1 << 30          # calibration copy for the HBM byte counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_ouro_b8_l32k_traffic.txt")
+ATTN_SOURCES = [os.path.join(ROOT, "sub_bit_loop_amd", "csrc", f) for f in ("lvq_attn.hip", "lvq_internal.h")]
 
 
 def parse():
@@ -48,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-encode", action="store_true", help="skip the encoder measurement")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench "
+                         "into the HBM-traffic record the bench line reports")
     return ap.parse_args()
 
 
@@ -67,6 +73,10 @@ def build_inputs(args, torch, lvq, synth):
     rng = np.random.default_rng(synth.seed_for(CONFIG_ID, synth.STREAM_PAGES))
     pt_np, pool = synth.shuffled_page_table(rng, [n_coded_pages] * B, max_pages)
     pt = torch.from_numpy(pt_np).to(dev)
+    # one spare coded page per sequence receives the decode-time re-encode of its oldest
+    # recent page (the attention inputs stay those of the 32768-token state)
+    spare = torch.arange(pool, pool + B, dtype=torch.int32, device=dev)
+    pool += B
     # codebooks: k-means on seeded samples for one layer, copied into every layer's buffer
     rk = np.random.default_rng(synth.seed_for(CONFIG_ID, synth.STREAM_K))
     rv = np.random.default_rng(synth.seed_for(CONFIG_ID, synth.STREAM_V))
@@ -114,9 +124,100 @@ def build_inputs(args, torch, lvq, synth):
     ws = torch.empty(lvq.lvq_decode_attn_workspace_bytes(shp), dtype=torch.uint8, device=dev)
     out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    # a plain device copy of known size: the scale of the rocprofv3 byte counters
+    calib = torch.empty(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
+    torch.empty_like(calib).copy_(calib)
+    torch.cuda.synchronize()
+    del calib
     return dict(pt=pt, pt_np=pt_np, layers=layers, pos=pos, seq_len=seq_len, qe=qe, rope=rope,
                 shp=shp, ws=ws, out=out, lse=lse, bt=bt, pool=pool, q_end=q_end, bf16_row=bf16_row,
-                cb_np=cb_np)
+                cb_np=cb_np, spare=spare)
+
+
+def attn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _pmc_per_dispatch(directory, counter):
+    """{kernel name: [value per dispatch]} for one counter of a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in vals.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """HBM bytes per decode-attention call from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the counter reads for the bench's calibration copy of CALIB_BYTES."""
+    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+
+    def calib(d):
+        cands = [max(v) for k, v in d.items() if "copy" in k.lower()]
+        return max(cands) * 1024.0 if cands else float("nan")
+
+    def per_launch(d, key):
+        v = [x for k, xs in d.items() if key in k for x in xs]
+        return (sum(v) / len(v) * 1024.0, len(v)) if v else (float("nan"), 0)
+
+    cf, cw = calib(fetch), calib(write)
+    sf, sw = CALIB_BYTES / cf, CALIB_BYTES / cw
+    af, na = per_launch(fetch, "attn_kernel<128, 8, false>")
+    aw, _ = per_launch(write, "attn_kernel<128, 8, false>")
+    mf, nm = per_launch(fetch, "merge_kernel")
+    mw, _ = per_launch(write, "merge_kernel")
+    traffic = (af + mf) * sf + (aw + mw) * sw
+    algo = algorithmic_bytes_per_call(synth_q_end())
+    print("# HBM traffic of one decode-attention call (attn_kernel<128, 8, false> + merge_kernel),")
+    print("# Ouro-1.4B-shaped 32K decode bench\n")
+    print("Commands (repository root $REPO on the GPU host):\n")
+    for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        print(f"    cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv "
+              f"-d {d} -o bench -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-encode")
+    print(f"    python3 $REPO/bench.py --pmc-summary {fetch_dir} {write_dir}\n")
+    print(f"source_sha256: {attn_source_hash()}")
+    print(f"calibration_copy_bytes: {CALIB_BYTES}")
+    print(f"calibration_fetch_counter_bytes: {cf:.0f}  (scale {sf:.4f})")
+    print(f"calibration_write_counter_bytes: {cw:.0f}  (scale {sw:.4f})")
+    print(f"attn_kernel dispatches {na}: FETCH_SIZE {af / 1024:.1f} KiB, WRITE_SIZE {aw / 1024:.1f} KiB per dispatch")
+    print(f"merge_kernel dispatches {nm}: FETCH_SIZE {mf / 1024:.1f} KiB, WRITE_SIZE {mw / 1024:.1f} KiB per dispatch")
+    print(f"algorithmic_bytes_per_call: {algo}")
+    print(f"traffic_bytes_per_call: {traffic:.0f}")
+    print(f"traffic_over_algorithmic: {traffic / algo:.3f}")
+
+
+def recorded_traffic():
+    """Traffic per call from the committed counter record, or None if the kernel changed since."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and not line.startswith(" "))
+    if fields.get("source_sha256", "").strip() != attn_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_call"].split()[0])
+    except (KeyError, ValueError):
+        return None
+
+
+def synth_q_end():
+    return 8 * ((L - N_RECENT) // 8)
 
 
 def algorithmic_bytes_per_call(q_end):
@@ -141,7 +242,17 @@ def run_decode(args, torch, lvq, inp):
                             common["pos"], common["seq_len"], common["q_end"], common["rope_tab"],
                             common["shp"], common["out"], common["lse"], common["ws"])
 
-    def step(events=None):
+    # After a token's forward pass, every 8 tokens each sequence encodes its oldest recent
+    # page (all loop steps, heads, K and V) in every layer; with 8 sequences that is one
+    # sequence's page per step on average: step s re-encodes sequence s mod B.
+    def reencode(s_idx):
+        b = s_idx % B
+        src = inp["bt"][b, 1:2].contiguous()
+        dst = inp["spare"][b:b + 1].contiguous()
+        for Ly in layers:
+            lvq.lvq_reencode_pages(Ly["bp"], src, dst, Ly["cb"], T, TC, G, Ly["ip"])
+
+    def step(s_idx, events=None):
         k = 0
         for t in range(T):
             for layer in range(len(layers)):
@@ -151,9 +262,10 @@ def run_decode(args, torch, lvq, inp):
                 if events is not None:
                     events[k][1].record()
                 k += 1
+        reencode(s_idx)
 
-    for _ in range(args.warmup):
-        step()
+    for w in range(args.warmup):
+        step(w)
     torch.cuda.synchronize()
     ncall = T * len(layers)
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -161,7 +273,7 @@ def run_decode(args, torch, lvq, inp):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(evs[s])
+        step(s, evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call = [evs[s][k][0].elapsed_time(evs[s][k][1]) * 1e-3 for s in range(args.steps) for k in range(ncall)]
@@ -250,6 +362,9 @@ def encode_bench(torch, lvq, synth, inp):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -270,9 +385,11 @@ def main():
     algo = algorithmic_bytes_per_call(inp["q_end"])
     achieved_gbs = algo / call_avg / 1e9
     log(f"step {step_s * 1e3:.3f} ms, call {call_avg * 1e6:.1f} us, {achieved_gbs:.0f} GB/s algorithmic")
+    traffic = recorded_traffic()
     roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "attn_kernel<128,8> + merge per (layer, step) call",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": "lvq_decode_attn call: attn_kernel<128,8> + merge_kernel, one (layer, loop step)",
             "algorithmic_bytes_per_call": algo, "avg_call_us": round(call_avg * 1e6, 2)}
     res = {
         "metric": METRIC, "value": value, "unit": "KV token-steps/s", "n_gpus": 1,
