@@ -318,24 +318,6 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
         for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, (float)x[i], o[8 * v + i]);
       }
     };
-    // Software pipeline in batches of NT tiles: each iteration loads the inputs of
-    // the next batch, computes the current batch, then moves next to current, so no
-    // load is in flight across the loop back-edge.
-    if (has_coded) {
-      TileIn cur[NT], nxt[NT];
-#pragma unroll
-      for (int i = 0; i < NT; ++i) cur[i] = fetch(P_lo + 2 * i);
-      for (int P0 = P_lo; P0 < P_hi; P0 += 2 * NT) {
-#pragma unroll
-        for (int i = 0; i < NT; ++i) nxt[i] = fetch(P0 + 2 * NT + 2 * i);
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          if (P0 + 2 * i < P_hi) tile(P0 + 2 * i, cur[i], i & 1);
-        }
-#pragma unroll
-        for (int i = 0; i < NT; ++i) cur[i] = nxt[i];
-      }
-    }
     // bf16 sink and recent tokens: virtual tile vt of (b, hq) runs on chunk vt mod n_chunks,
     // with the same lane layout and RoPE factorisation; keys and values are read from the
     // bf16 pages and used in float32 (a bf16 value need not fit float16).
@@ -352,7 +334,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
           krow = a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2) * kPage + (p & 7)) * D;
       }
       const bool valid = krow != nullptr;
-      float* er = e0s;   // the coded tiles are done with both buffers
+      float* er = e0s;   // buffer 0, before the coded tiles use both
       if (lane < HALF) {
         const int tile_idx = min(a_tile, a.rope_tiles - 1);
         *(float2*)(er + (lane / QP) * (2 * QP + 4) + 2 * (lane % QP)) =
@@ -403,6 +385,24 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, bf2f(x[i]), o[8 * v + i]);
         }
+      }
+    }
+    // Software pipeline in batches of NT tiles: each iteration loads the inputs of
+    // the next batch, computes the current batch, then moves next to current, so no
+    // load is in flight across the loop back-edge.
+    if (has_coded) {
+      TileIn cur[NT], nxt[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) cur[i] = fetch(P_lo + 2 * i);
+      for (int P0 = P_lo; P0 < P_hi; P0 += 2 * NT) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) nxt[i] = fetch(P0 + 2 * NT + 2 * i);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          if (P0 + 2 * i < P_hi) tile(P0 + 2 * i, cur[i], i & 1);
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i) cur[i] = nxt[i];
       }
     }
   }
