@@ -26,7 +26,8 @@
 //    within the float32 error bound of the smallest.  So the chosen index is the
 //    float64 nearest codeword with lowest-index ties: float32 decides only where
 //    no other candidate can be within rounding of the winner.
-//  * Input tiles (16 tokens) are loaded three tiles ahead of their use.
+//  * Input tiles (16 tokens) are loaded two tiles ahead of their use; the |C_k|^2
+//    of the next group of MFMAs is read from LDS while the current group folds.
 //  * A workgroup holds the waves of up to 4 consecutive groups of one
 //    (block, head); the workgroups that read the other halves of the same
 //    128-byte cache rows run on the same XCD at the same time, so the K/V
@@ -180,7 +181,8 @@ void encode_kernel(EncodeArgs a, int n_items) {
   constexpr int EPL = (G == 32) ? 8 : 4; // elements per lane per MFMA operand
   constexpr int TC = G / C;
   constexpr int kPart = 4;               // MFMAs issued before their results are folded
-  constexpr int kRing = 4;               // tiles in flight
+  constexpr bool kBiasAhead = true;      // read the next group's |C_k|^2 during the fold
+  constexpr int kRing = 3;               // tiles in flight
   using R = raw_t<EPL>;
   __shared__ __attribute__((aligned(16))) float s_bias[WPG][kCodes];
 
@@ -290,13 +292,22 @@ void encode_kernel(EncodeArgs a, int n_items) {
       float c1[2] = {__builtin_inff(), __builtin_inff()};
       float c2[2] = {__builtin_inff(), __builtin_inff()};
       float kq[3];
+      // |C_k|^2 of the next group of MFMAs is read from LDS while the current group folds
+      f32x4 bq[kPart];
+#pragma unroll
+      for (int mm = 0; mm < kPart; ++mm) bq[mm] = *(const f32x4*)(bias + 16 * mm);
 #pragma unroll
       for (int part = 0; part < 16 / kPart; ++part) {
         f32x4 acc[kPart];
 #pragma unroll
         for (int mm = 0; mm < kPart; ++mm) {
           const int m = kPart * part + mm;
-          acc[mm] = mfma_bf16<EPL>(A[m], B, *(const f32x4*)(bias + 16 * m));
+          if (!kBiasAhead && part > 0) bq[mm] = *(const f32x4*)(bias + 16 * m);
+          acc[mm] = mfma_bf16<EPL>(A[m], B, bq[mm]);
+        }
+        if (kBiasAhead && part + 1 < 16 / kPart) {
+#pragma unroll
+          for (int mm = 0; mm < kPart; ++mm) bq[mm] = *(const f32x4*)(bias + 16 * (kPart * (part + 1) + mm));
         }
 #pragma unroll
         for (int mm = 0; mm < kPart; ++mm) {
