@@ -389,3 +389,110 @@ def decode_attn_split(shp: AttnShape, q_bits, page_table, index_pages, bf16_page
 def needle_mass(scores: np.ndarray, lse: float, lo: int, hi: int) -> float:
     """Attention mass on positions [lo, hi): sum of exp(s_p - lse)."""
     return float(np.exp(scores[lo:hi] - lse).sum())
+
+
+# ----------------------------------------------------------------------------
+# codebook builder: k-means++ seeding and Lloyd iterations
+# ----------------------------------------------------------------------------
+# The summary (section "어떻게 쓰나") learns the codebooks by k-means on
+# calibration K/V; the pages fix neither the seeding nor the precision.  Readings:
+# k-means++ seeding (D^2 sampling) driven by draws passed in, Lloyd iterations whose
+# assignment uses the centers rounded to bf16 (the stored codebook precision, so the
+# assignment is exactly the encoder's nearest codeword) and whose update is the
+# float64 mean of the members taken in sample order, an empty cluster keeping its
+# center, and the final centers rounded to bf16 (via float32, round to nearest even).
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> float32 (round to nearest even) -> bf16 (round to nearest even), as float64."""
+    bits = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32)).view(np.uint32)
+    bits = bits.astype(np.uint64)
+    rounded = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16).astype(np.uint16)
+    return bf16_to_f64(rounded)
+
+
+def bf16_bits_of(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of float64 values that are exactly bf16."""
+    return (np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def sq_dist_sequential(X: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """sum_e (X[s][e] - c[e])^2 for every s, adding the squares in order e = 0, 1, ..."""
+    d = np.zeros(X.shape[0])
+    for e in range(X.shape[1]):
+        df = X[:, e] - c[e]
+        d = d + df * df
+    return d
+
+
+def kmeanspp_seed(X: np.ndarray, draws: np.ndarray, K: int = NCODES) -> np.ndarray:
+    """k-means++ seeding: indices of the K samples chosen as initial centers.
+
+    Draw 0 picks sample floor(u_0 * S).  Draw k >= 1 picks, with D^2_s the squared
+    distance of sample s to its nearest chosen center and c_s = D^2_0 + ... + D^2_s
+    summed in sample order, the first s with c_s > u_k * c_{S-1}; if rounding leaves
+    none, the last s with D^2_s > 0; if every D^2_s is 0, sample floor(u_k * S).
+    """
+    S = X.shape[0]
+    picks = np.empty(K, dtype=np.int64)
+    picks[0] = min(int(draws[0] * S), S - 1)
+    D2 = sq_dist_sequential(X, X[picks[0]])
+    for k in range(1, K):
+        cum = np.cumsum(D2)
+        total = cum[-1]
+        if total > 0:
+            target = draws[k] * total
+            above = np.flatnonzero(cum > target)
+            i = int(above[0]) if len(above) else int(np.flatnonzero(D2 > 0)[-1])
+        else:
+            i = min(int(draws[k] * S), S - 1)
+        picks[k] = i
+        D2 = np.minimum(D2, sq_dist_sequential(X, X[i]))
+    return picks
+
+
+def lloyd(X: np.ndarray, centers: np.ndarray, n_iter: int, bf16_assign: bool = True) -> np.ndarray:
+    """n_iter Lloyd iterations from ``centers`` (float64 [K][G]).
+
+    Assignment: nearest center by squared L2, lowest index on ties, against the
+    centers rounded to bf16 (``bf16_assign``) or as they are.  Update: the mean of
+    each cluster's members summed in sample order; an empty cluster keeps its center.
+    """
+    C = np.array(centers, dtype=np.float64)
+    K, G = C.shape
+    for _ in range(n_iter):
+        A = round_bf16(C) if bf16_assign else C
+        assign = nearest_codeword(X, A).idx
+        new = C.copy()
+        for k in range(K):
+            members = np.flatnonzero(assign == k)
+            if len(members):
+                acc = np.zeros(G)
+                for s in members:
+                    acc = acc + X[s]
+                new[k] = acc / len(members)
+        C = new
+    return C
+
+
+def build_codebooks(samples_bits: np.ndarray, draws: np.ndarray, Tc: int, G: int, n_iter: int,
+                    books=None) -> np.ndarray:
+    """Codebooks of one of K / V: ``samples[T][S][H][d]`` (bf16) -> bf16 bits ``[nblk][H][ng][Tc][256][c]``.
+
+    draws: ``[nblk][H][ng][256]`` uniform numbers in [0, 1).  Book (beta, h, g) is
+    trained on the joint vectors of its (block, head, group) over the S samples.
+    ``books`` optionally restricts the work to a list of (beta, h, g); the rest stays 0.
+    """
+    X = bf16_to_f64(samples_bits)
+    T, S, H, d = X.shape
+    J = joint_vectors(X, Tc, G)                 # [nblk][S][H][ng][G]
+    nblk, ng, c = T // Tc, d // (G // Tc), G // Tc
+    out = np.zeros((nblk, H, ng, Tc, NCODES, c), dtype=np.uint16)
+    todo = books if books is not None else [(b, h, g) for b in range(nblk) for h in range(H) for g in range(ng)]
+    for beta, h, g in todo:
+        x = J[beta, :, h, g]
+        picks = kmeanspp_seed(x, draws[beta, h, g])
+        C = lloyd(x, x[picks], n_iter)
+        Cb = bf16_bits_of(round_bf16(C))            # [256][G]
+        for tau in range(Tc):
+            out[beta, h, g, tau] = Cb[:, tau * c:(tau + 1) * c]
+    return out
