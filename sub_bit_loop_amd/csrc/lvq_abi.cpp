@@ -247,6 +247,43 @@ int lvq_reencode_pages(const uint16_t* bf16_pages, const int32_t* src_pages,
   return device_status(lvq::launch_encode(a, (hipStream_t)stream), "lvq_reencode_pages launch");
 }
 
+size_t lvq_build_codebooks_workspace_bytes(int T, int Tc, int G, int S, int H, int d) {
+  if (T <= 0 || Tc <= 0 || G <= 0 || S <= 0 || H <= 0 || d <= 0) return 0;
+  if (T % Tc || G % Tc || d % (G / Tc)) return 0;
+  const size_t nblk = (size_t)(T / Tc), ng = (size_t)(d / (G / Tc));
+  const size_t centers = nblk * H * ng * lvq::kCodes * (size_t)G * sizeof(double);
+  const size_t assign = nblk * (size_t)S * H * ng;
+  return (centers + 255) / 256 * 256 + assign;
+}
+
+int lvq_build_codebooks(const uint16_t* samples, const double* draws, int kv_sel, int T, int Tc,
+                        int G, int S, int H, int d, int n_iter, uint16_t* codebooks, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int st = check_encode_common(samples, codebooks, T, Tc, G, S, H, d);
+  if (st) return st;
+  if (!draws) return fail(LVQ_EINVAL, "null pointer argument");
+  if (kv_sel != 0 && kv_sel != 1) return fail(LVQ_EINVAL, "kv_sel=%d must be 0 or 1", kv_sel);
+  if (S < 1) return fail(LVQ_EINVAL, "S=%d samples: at least one is needed", S);
+  if (S > lvq::kMaxKmeansSamples)
+    return fail(LVQ_EUNSUPPORTED, "S=%d samples per book above the supported %d", S, lvq::kMaxKmeansSamples);
+  if (n_iter < 0 || n_iter > 1000) return fail(LVQ_EINVAL, "n_iter=%d outside [0, 1000]", n_iter);
+  const size_t need = lvq_build_codebooks_workspace_bytes(T, Tc, G, S, H, d);
+  if (!ws || ws_bytes < need)
+    return fail(LVQ_ENOSPC, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  lvq::KmeansArgs a{};
+  a.samples = samples;
+  a.draws = draws;
+  a.codebooks = codebooks;
+  a.kv_sel = kv_sel;
+  a.T = T; a.Tc = Tc; a.G = G; a.S = S; a.H = H; a.d = d;
+  a.n_iter = n_iter;
+  a.n_books = (T / Tc) * H * (d / (G / Tc));
+  const size_t centers = (size_t)a.n_books * lvq::kCodes * G * sizeof(double);
+  a.centers = (double*)ws;
+  a.assign = (uint8_t*)ws + (centers + 255) / 256 * 256;
+  return device_status(lvq::launch_build_codebooks(a, (hipStream_t)stream), "lvq_build_codebooks launch");
+}
+
 size_t lvq_rope_table_bytes(int max_len, int d) {
   if (max_len <= 0 || d <= 0 || d % 2) return 0;
   const size_t tile = (size_t)lvq::rope_tile();

@@ -30,6 +30,18 @@ struct EncodeArgs {
 bool encode_supported(int G, int c, int d);
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- codebook builder
+constexpr int kMaxKmeansSamples = 8192;   // samples per book (float64 D^2 and running sums in LDS)
+struct KmeansArgs {
+  const uint16_t* samples;    // bf16 [T][S][H][d]
+  const double* draws;        // [n_books][256] uniform in [0, 1), book = (beta * H + h) * ng + g
+  uint16_t* codebooks;        // bf16 [nblk][2][H][ng][Tc][256][c]; half kv_sel is written
+  double* centers;            // workspace [n_books][256][G]
+  uint8_t* assign;            // workspace [nblk][S][H][ng]
+  int kv_sel, T, Tc, G, S, H, d, n_iter, n_books;
+};
+hipError_t launch_build_codebooks(const KmeansArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- RoPE tables
 hipError_t launch_rope_tables(int ntile, int d, double base, float* tab, hipStream_t s);
 

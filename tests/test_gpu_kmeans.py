@@ -1,0 +1,93 @@
+"""GPU codebook builder (k-means++ seeding + Lloyd iterations) against the oracle:
+bf16 codebooks bit-exact."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import lvq_oracle as orc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _samples(seed, T, S, H, d):
+    rng = np.random.default_rng(seed)
+    sc = synth.channel_scales(rng, H, d)
+    return synth.f32_to_bf16_bits(synth.gen_kv(rng, T, S, H, d, sc)), rng
+
+
+def _gpu_build(bits, draws, kv_sel, T, Tc, G, n_iter, codebooks=None):
+    import sub_bit_loop_amd as lvq
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(bits.view(np.int16)).to(dev)
+    u = torch.from_numpy(draws).to(dev)
+    cb = None if codebooks is None else torch.from_numpy(codebooks.view(np.int16)).to(dev)
+    out = lvq.lvq_build_codebooks(x, u, kv_sel, T, Tc, G, n_iter, codebooks=cb)
+    torch.cuda.synchronize()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _compare(gpu_half, ref, books):
+    for (beta, h, g) in books:
+        got, want = gpu_half[beta, h, g], ref[beta, h, g]
+        bad = np.argwhere(got != want)
+        assert len(bad) == 0, f"book {(beta, h, g)}: {len(bad)} codeword elements differ, first {bad[:4]}"
+
+
+@pytest.mark.parametrize("T,Tc,G,S,H,d,n_iter", [
+    (4, 2, 16, 600, 2, 64, 4),      # 0.5 bit, two blocks
+    (4, 4, 32, 500, 1, 128, 3),     # 0.25 bit
+    (1, 1, 32, 300, 1, 64, 2),      # prelude layer coded per step (c = 32)
+    (4, 4, 16, 280, 1, 64, 2),      # c = 4
+])
+def test_builder_matches_oracle(T, Tc, G, S, H, d, n_iter):
+    print(f"\ncase build T={T} Tc={Tc} G={G} S={S} H={H} d={d} iters={n_iter}", flush=True)
+    bits, rng = _samples(61, T, S, H, d)
+    nblk, ng = T // Tc, d // (G // Tc)
+    draws = rng.random((nblk, H, ng, 256))
+    out = _gpu_build(bits, draws, 0, T, Tc, G, n_iter)
+    ref = orc.build_codebooks(bits, draws, Tc, G, n_iter)
+    _compare(out[:, 0], ref, [(b, h, g) for b in range(nblk) for h in range(H) for g in range(ng)])
+
+
+def test_builder_few_samples_and_v_half():
+    """S < 256: the seeding runs out of distinct samples (every D^2 reaches 0 and the uniform
+    fallback repeats samples); only the selected half (V) is written."""
+    T, Tc, G, S, H, d = 4, 2, 16, 100, 1, 64
+    print("\ncase build few samples", flush=True)
+    bits, rng = _samples(62, T, S, H, d)
+    draws = rng.random((2, H, 8, 256))
+    pre = np.full((2, 2, H, 8, Tc, 256, 8), 0x1234, dtype=np.uint16)
+    out = _gpu_build(bits, draws, 1, T, Tc, G, 3, codebooks=pre)
+    assert (out[:, 0] == 0x1234).all()
+    ref = orc.build_codebooks(bits, draws, Tc, G, 3)
+    _compare(out[:, 1], ref, [(b, 0, g) for b in range(2) for g in range(8)])
+
+
+def test_builder_ouro_shape_sampled_books():
+    """Ouro-shaped layer: 16 heads, d = 128, T = Tc = 4, G = 32, 4096 samples, 10 Lloyd
+    iterations; every book is built on the GPU, three are checked against the oracle."""
+    T, Tc, G, S, H, d = 4, 4, 32, 4096, 16, 128
+    print("\ncase build Ouro shape", flush=True)
+    bits, rng = _samples(63, T, S, H, d)
+    draws = rng.random((1, H, 16, 256))
+    out = _gpu_build(bits, draws, 0, T, Tc, G, 10)
+    books = [(0, 0, 0), (0, 7, 11), (0, 15, 3)]
+    ref = orc.build_codebooks(bits, draws, Tc, G, 10, books=books)
+    _compare(out[:, 0], ref, books)
+    # every book has 256 codewords drawn from a non-degenerate training set
+    assert np.all(out[:, 0] != 0x7FC0)
+
+
+def test_builder_rejects_bad_arguments():
+    import sub_bit_loop_amd as lvq
+    dev = torch.device("cuda:0")
+    x = torch.zeros((4, 16, 1, 64), dtype=torch.bfloat16, device=dev)
+    u = torch.zeros((2, 1, 8, 256), dtype=torch.float64, device=dev)
+    with pytest.raises(lvq.LvqError):
+        lvq.lvq_build_codebooks(x, u, 2, 4, 2, 16, 1)            # kv_sel
+    with pytest.raises(lvq.LvqError):
+        lvq.lvq_build_codebooks(x, u, 0, 4, 2, 16, -1)           # n_iter
+    big = torch.zeros((4, 8193, 1, 64), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(lvq.LvqError):
+        lvq.lvq_build_codebooks(big, u, 0, 4, 2, 16, 1)          # S above 8192
