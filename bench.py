@@ -77,14 +77,13 @@ def build_inputs(args, torch, lvq, synth):
     # recent page (the attention inputs stay those of the 32768-token state)
     spare = torch.arange(pool, pool + B, dtype=torch.int32, device=dev)
     pool += B
-    # codebooks: k-means on seeded samples for one layer, copied into every layer's buffer
+    # codebooks: built on the device (k-means++ and 10 Lloyd iterations on 4096 seeded
+    # samples per book) for one layer, copied into every layer's buffer
     rk = np.random.default_rng(synth.seed_for(CONFIG_ID, synth.STREAM_K))
     rv = np.random.default_rng(synth.seed_for(CONFIG_ID, synth.STREAM_V))
     sc_k, sc_v = synth.channel_scales(rk, H, D), synth.channel_scales(rv, H, D)
-    t0 = time.time()
-    cb_np = synth.kmeans_codebooks(CONFIG_ID, T, TC, G, H, D, sc_k, sc_v, n_samples=4096, device="cuda")
-    log(f"k-means codebooks in {time.time() - t0:.1f}s")
-    cb0 = torch.from_numpy(cb_np.view(np.int16)).to(dev)
+    cb0, build_s = build_books(torch, lvq, synth, TC, G, sc_k, sc_v, synth.seed_for(CONFIG_ID, synth.STREAM_BOOKS))
+    log(f"codebooks (2 x {H * (D // (G // TC)) * (T // TC)} books) built on the device in {build_s * 1e3:.1f} ms")
     # bf16 pool: per sequence the copy of page 0 and the recent pages
     n_recent_pages = (L - q_end + 7) // 8
     bf16_row = 1 + n_recent_pages
@@ -131,7 +130,7 @@ def build_inputs(args, torch, lvq, synth):
     del calib
     return dict(pt=pt, pt_np=pt_np, layers=layers, pos=pos, seq_len=seq_len, qe=qe, rope=rope,
                 shp=shp, ws=ws, out=out, lse=lse, bt=bt, pool=pool, q_end=q_end, bf16_row=bf16_row,
-                cb_np=cb_np, spare=spare)
+                cb0=cb0, build_s=build_s, spare=spare)
 
 
 def attn_source_hash():
@@ -231,6 +230,33 @@ def algorithmic_bytes_per_call(q_end):
     return idx + bf + books + small
 
 
+N_BOOK_SAMPLES, N_LLOYD = 4096, 10
+
+
+def build_books(torch, lvq, synth, tc, g, sc_k, sc_v, seed):
+    """K and V codebooks of one layer with lvq_build_codebooks: 4096 seeded sample tokens of
+    the AR(1) generator, k-means++ draws from a seeded device generator, 10 Lloyd iterations.
+    Returns (codebook bits as int16 [nblk][2][H][ng][Tc][256][c], seconds of the two builds)."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    c = g // tc
+    nblk, ng = T // tc, D // c
+    cb = torch.zeros((nblk, 2, H, ng, tc, 256, c), dtype=torch.bfloat16, device=dev)
+    samples, draws = [], []
+    for kv, sc in ((0, sc_k), (1, sc_v)):
+        gen.manual_seed(seed * 7 + kv)
+        samples.append(synth.gen_kv_torch(gen, T, N_BOOK_SAMPLES, H, D, sc, device=dev))
+        draws.append(torch.rand((nblk, H, ng, 256), generator=gen, dtype=torch.float64, device=dev))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for kv in (0, 1):
+        lvq.lvq_build_codebooks(samples[kv], draws[kv], kv, T, tc, g, N_LLOYD, codebooks=cb)
+    e1.record()
+    torch.cuda.synchronize()
+    return cb.view(torch.int16), e0.elapsed_time(e1) * 1e-3
+
+
 def run_decode(args, torch, lvq, inp):
     layers = inp["layers"]
     common = dict(pos=inp["pos"], seq_len=inp["seq_len"], q_end=inp["qe"], rope_tab=inp["rope"],
@@ -325,10 +351,9 @@ def encode_bench(torch, lvq, synth, inp):
     sc = synth.channel_scales(rk, H, D)
     for (tc, g) in ((4, 32), (2, 16)):
         if (tc, g) == (TC, G):
-            cb = torch.from_numpy(inp["cb_np"].view(np.int16)).to(dev)
+            cb = inp["cb0"]
         else:
-            cb = torch.from_numpy(synth.kmeans_codebooks(4, T, tc, g, H, D, sc, sc, n_samples=4096,
-                                                         device="cuda").view(np.int16)).to(dev)
+            cb, _ = build_books(torch, lvq, synth, tc, g, sc, sc, synth.seed_for(4, synth.STREAM_BOOKS))
         kvs = []
         for kv in (0, 1):
             gen.manual_seed(4000 + kv)
@@ -402,6 +427,11 @@ def main():
                    "global_batch": B, "seq_len": L, "parallelism": "single-gpu"},
         "roofline": roof,
     }
+    n_books = 2 * H * (D // (G // TC)) * (T // TC)
+    res["codebook_build"] = {
+        "workload": f"one layer, K and V: {n_books} books of 256 codewords, {N_BOOK_SAMPLES} samples "
+                    f"each, k-means++ + {N_LLOYD} Lloyd iterations (Tc={TC}, G={G})",
+        "ms": round(inp["build_s"] * 1e3, 2), "books_per_s": round(n_books / inp["build_s"], 1)}
     if not args.no_encode:
         try:
             res["encode"] = encode_bench(torch, lvq, synth, inp)
