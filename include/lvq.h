@@ -135,26 +135,36 @@ int lvq_reencode_pages(const uint16_t* bf16_pages, const int32_t* src_pages,
 /*
  * lvq_build_codebooks -- learn the 256-word codebooks of one of K / V from sample
  * tokens on the device: k-means on calibration keys and values (the summary,
- * section "어떻게 쓰나"), every book (loop block, head, group) at once.
+ * section "어떻게 쓰나"), Fisher-weighted when weights are given (section "무엇과
+ * 다른가": the codebooks start from Fisher-weighted k-means; the Fisher information
+ * needs model gradients, so the weights are an input).  Every book (loop block,
+ * head, group) is built at once.
  *   samples:   bf16 [T][S][H][d], S sample tokens (pre-RoPE keys or values), the
  *              encoder's input layout.  1 <= S <= 8192.
  *   draws:     float64 [nblk][H][ng][256], uniform numbers in [0, 1) that drive the
- *              k-means++ seeding of each book (draw 0 picks sample floor(u0 S); draw
- *              k picks by D^2 sampling: the first s whose running sum of D^2 in sample
- *              order exceeds u_k times the total).
+ *              k-means++ seeding of each book.  Draw k picks the first sample s whose
+ *              running sum of terms (sample order, float64) exceeds u_k times the
+ *              total: the terms are w_s for draw 0 (so sample floor(u0 S) without
+ *              weights) and w_s D^2_s for k >= 1, D^2 the squared distance to the
+ *              nearest chosen center; the last s with a positive term if rounding
+ *              leaves none; sample floor(u_k S) if the total is not positive.
+ *   weights:   float64 [nblk][S][H][ng], one finite weight >= 0 per joint vector (the
+ *              assignment layout), or NULL for all 1.  Negative or non-finite
+ *              weights give unspecified books (the kernels stay in bounds).
  *   n_iter:    Lloyd iterations, 0 .. 1000.  Each assigns every sample to its nearest
  *              center rounded to bf16 (exact, lowest index on ties) and moves each
- *              center to the float64 mean of its members (an empty cluster keeps its
- *              center).
+ *              center to sum(w_s x_s) / sum(w_s) over its members, both float64 sums
+ *              in sample order (a cluster of zero total weight keeps its center).
  *   codebooks: out, bf16 [nblk][2][H][ng][Tc][256][c]; only half kv_sel is written,
  *              the final centers rounded to bf16 through float32.
  *   ws:        device workspace of lvq_build_codebooks_workspace_bytes() bytes.
- * Same shapes as lvq_encode (status 2 outside them, or for S > 8192).
+ * Same shapes as lvq_encode (status 2 outside them, or for S > 8192).  The result
+ * is bit-reproducible: every float64 step has a fixed order.
  */
 size_t lvq_build_codebooks_workspace_bytes(int T, int Tc, int G, int S, int H, int d);
-int lvq_build_codebooks(const uint16_t* samples, const double* draws, int kv_sel, int T, int Tc,
-                        int G, int S, int H, int d, int n_iter, uint16_t* codebooks, void* ws,
-                        size_t ws_bytes, void* stream);
+int lvq_build_codebooks(const uint16_t* samples, const double* draws, const double* weights,
+                        int kv_sel, int T, int Tc, int G, int S, int H, int d, int n_iter,
+                        uint16_t* codebooks, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * RoPE phase tables (rotate-half convention: channel j pairs with j + d/2 and

@@ -395,12 +395,15 @@ def needle_mass(scores: np.ndarray, lse: float, lo: int, hi: int) -> float:
 # codebook builder: k-means++ seeding and Lloyd iterations
 # ----------------------------------------------------------------------------
 # The summary (section "어떻게 쓰나") learns the codebooks by k-means on
-# calibration K/V; the pages fix neither the seeding nor the precision.  Readings:
-# k-means++ seeding (D^2 sampling) driven by draws passed in, Lloyd iterations whose
-# assignment uses the centers rounded to bf16 (the stored codebook precision, so the
-# assignment is exactly the encoder's nearest codeword) and whose update is the
-# float64 mean of the members taken in sample order, an empty cluster keeping its
-# center, and the final centers rounded to bf16 (via float32, round to nearest even).
+# calibration K/V, and (section "무엇과 다른가") initialises them by Fisher-weighted
+# k-means; the pages fix neither the seeding, the weights nor the precision.
+# Readings: one non-negative weight per joint vector, given as an input (the Fisher
+# information itself needs model gradients); k-means++ seeding (weighted D^2
+# sampling) driven by draws passed in; Lloyd iterations whose assignment uses the
+# centers rounded to bf16 (the stored codebook precision, so the assignment is
+# exactly the encoder's nearest codeword) and whose update is the float64 weighted
+# mean of the members taken in sample order, a cluster of zero total weight keeping
+# its center; the final centers rounded to bf16 (via float32, round to nearest even).
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """float64 -> float32 (round to nearest even) -> bf16 (round to nearest even), as float64."""
@@ -424,62 +427,80 @@ def sq_dist_sequential(X: np.ndarray, c: np.ndarray) -> np.ndarray:
     return d
 
 
-def kmeanspp_seed(X: np.ndarray, draws: np.ndarray, K: int = NCODES) -> np.ndarray:
+def _running_sum_pick(terms: np.ndarray, u: float) -> int:
+    """The first s whose running sum terms_0 + ... + terms_s (sample order) exceeds
+    u times the total; the last s with a positive term if rounding leaves none; sample
+    floor(u * S) if the total is not positive."""
+    S = terms.shape[0]
+    cum = np.cumsum(terms)
+    total = cum[-1]
+    if total > 0:
+        above = np.flatnonzero(cum > u * total)
+        return int(above[0]) if len(above) else int(np.flatnonzero(terms > 0)[-1])
+    return min(max(int(u * S), 0), S - 1)
+
+
+def kmeanspp_seed(X: np.ndarray, draws: np.ndarray, K: int = NCODES, w=None) -> np.ndarray:
     """k-means++ seeding: indices of the K samples chosen as initial centers.
 
-    Draw 0 picks sample floor(u_0 * S).  Draw k >= 1 picks, with D^2_s the squared
-    distance of sample s to its nearest chosen center and c_s = D^2_0 + ... + D^2_s
-    summed in sample order, the first s with c_s > u_k * c_{S-1}; if rounding leaves
-    none, the last s with D^2_s > 0; if every D^2_s is 0, sample floor(u_k * S).
+    Sample s carries weight w_s (1 when ``w`` is None).  Draw 0 picks by weight alone
+    (every distance taken as 1), which is sample floor(u_0 * S) without weights.  Draw
+    k >= 1 picks by the terms w_s * D^2_s, D^2_s being the squared distance of sample
+    s to its nearest chosen center.  Each pick is ``_running_sum_pick``: running sums
+    in sample order compared with u_k times the total.
     """
     S = X.shape[0]
+    wv = np.ones(S) if w is None else np.asarray(w, dtype=np.float64)
     picks = np.empty(K, dtype=np.int64)
-    picks[0] = min(int(draws[0] * S), S - 1)
+    picks[0] = _running_sum_pick(wv, draws[0])
     D2 = sq_dist_sequential(X, X[picks[0]])
     for k in range(1, K):
-        cum = np.cumsum(D2)
-        total = cum[-1]
-        if total > 0:
-            target = draws[k] * total
-            above = np.flatnonzero(cum > target)
-            i = int(above[0]) if len(above) else int(np.flatnonzero(D2 > 0)[-1])
-        else:
-            i = min(int(draws[k] * S), S - 1)
+        i = _running_sum_pick(wv * D2, draws[k])
         picks[k] = i
         D2 = np.minimum(D2, sq_dist_sequential(X, X[i]))
     return picks
 
 
-def lloyd(X: np.ndarray, centers: np.ndarray, n_iter: int, bf16_assign: bool = True) -> np.ndarray:
+def lloyd(X: np.ndarray, centers: np.ndarray, n_iter: int, bf16_assign: bool = True, w=None) -> np.ndarray:
     """n_iter Lloyd iterations from ``centers`` (float64 [K][G]).
 
     Assignment: nearest center by squared L2, lowest index on ties, against the
-    centers rounded to bf16 (``bf16_assign``) or as they are.  Update: the mean of
-    each cluster's members summed in sample order; an empty cluster keeps its center.
+    centers rounded to bf16 (``bf16_assign``) or as they are.  Update: the weighted
+    mean sum(w_s x_s) / sum(w_s) of each cluster's members (w_s = 1 when ``w`` is
+    None), both sums in sample order; a cluster whose weights sum to 0 (an empty one
+    in particular) keeps its center.
     """
     C = np.array(centers, dtype=np.float64)
     K, G = C.shape
+    wv = None if w is None else np.asarray(w, dtype=np.float64)
     for _ in range(n_iter):
         A = round_bf16(C) if bf16_assign else C
         assign = nearest_codeword(X, A).idx
         new = C.copy()
         for k in range(K):
-            members = np.flatnonzero(assign == k)
-            if len(members):
-                acc = np.zeros(G)
-                for s in members:
+            acc = np.zeros(G)
+            wsum = 0.0
+            for s in np.flatnonzero(assign == k):
+                if wv is None:
                     acc = acc + X[s]
-                new[k] = acc / len(members)
+                    wsum = wsum + 1.0
+                else:
+                    acc = acc + wv[s] * X[s]
+                    wsum = wsum + wv[s]
+            if wsum != 0.0:
+                new[k] = acc / wsum
         C = new
     return C
 
 
 def build_codebooks(samples_bits: np.ndarray, draws: np.ndarray, Tc: int, G: int, n_iter: int,
-                    books=None) -> np.ndarray:
+                    books=None, weights=None) -> np.ndarray:
     """Codebooks of one of K / V: ``samples[T][S][H][d]`` (bf16) -> bf16 bits ``[nblk][H][ng][Tc][256][c]``.
 
     draws: ``[nblk][H][ng][256]`` uniform numbers in [0, 1).  Book (beta, h, g) is
-    trained on the joint vectors of its (block, head, group) over the S samples.
+    trained on the joint vectors of its (block, head, group) over the S samples, with
+    the per-vector weights ``weights[beta][s][h][g]`` (float64 [nblk][S][H][ng]; None =
+    all 1), k-means++ seeding and ``n_iter`` Lloyd iterations, then rounded to bf16.
     ``books`` optionally restricts the work to a list of (beta, h, g); the rest stays 0.
     """
     X = bf16_to_f64(samples_bits)
@@ -490,8 +511,9 @@ def build_codebooks(samples_bits: np.ndarray, draws: np.ndarray, Tc: int, G: int
     todo = books if books is not None else [(b, h, g) for b in range(nblk) for h in range(H) for g in range(ng)]
     for beta, h, g in todo:
         x = J[beta, :, h, g]
-        picks = kmeanspp_seed(x, draws[beta, h, g])
-        C = lloyd(x, x[picks], n_iter)
+        w = None if weights is None else weights[beta, :, h, g]
+        picks = kmeanspp_seed(x, draws[beta, h, g], w=w)
+        C = lloyd(x, x[picks], n_iter, w=w)
         Cb = bf16_bits_of(round_bf16(C))            # [256][G]
         for tau in range(Tc):
             out[beta, h, g, tau] = Cb[:, tau * c:(tau + 1) * c]

@@ -42,7 +42,8 @@ _SIGS = {
     "lvq_encode_pages": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
     "lvq_reencode_pages": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "lvq_build_codebooks_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "lvq_build_codebooks": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "lvq_build_codebooks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                   _sz, _vp]),
     "lvq_rope_table_bytes": (_sz, [_i32, _i32]),
     "lvq_rope_tables": (_i32, [_i32, _i32, _f64, _vp, _sz, _vp]),
     "lvq_decode_attn_workspace_bytes": (_sz, [ctypes.POINTER(AttnShape)]),
@@ -157,9 +158,10 @@ def lvq_reencode_pages(bf16_pages, src_pages, dst_pages, codebooks, T: int, Tc: 
 
 
 def lvq_build_codebooks(samples, draws, kv_sel: int, T: int, Tc: int, G: int, n_iter: int,
-                        codebooks=None, ws=None) -> torch.Tensor:
-    """k-means codebooks of one of K / V from samples bf16 [T][S][H][d] and float64 draws
-    [nblk][H][ng][256]; writes half kv_sel of codebooks bf16 [nblk][2][H][ng][Tc][256][c]."""
+                        codebooks=None, ws=None, weights=None) -> torch.Tensor:
+    """k-means codebooks of one of K / V from samples bf16 [T][S][H][d], float64 draws
+    [nblk][H][ng][256] and optional float64 weights [nblk][S][H][ng]; writes half kv_sel of
+    codebooks bf16 [nblk][2][H][ng][Tc][256][c]."""
     _dev(samples, "samples", BF16, 4)
     _dev(draws, "draws", (torch.float64,), 4)
     T_, S, H, d = samples.shape
@@ -170,13 +172,18 @@ def lvq_build_codebooks(samples, draws, kv_sel: int, T: int, Tc: int, G: int, n_
     ng = d // c if c > 0 else 0
     if tuple(draws.shape) != (nblk, H, ng, NCODES):
         raise ValueError(f"draws must have shape {(nblk, H, ng, NCODES)}")
+    if weights is not None:
+        _dev(weights, "weights", (torch.float64,), 4)
+        if tuple(weights.shape) != (nblk, S, H, ng):
+            raise ValueError(f"weights must have shape {(nblk, S, H, ng)}")
     if codebooks is None:
         codebooks = torch.zeros((nblk, 2, H, ng, Tc, NCODES, c), dtype=torch.bfloat16, device=samples.device)
     _dev(codebooks, "codebooks", BF16, 7)
     need = lib().lvq_build_codebooks_workspace_bytes(T, Tc, G, S, H, d)
     if ws is None:
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=samples.device)
-    _check(lib().lvq_build_codebooks(_ptr(samples), _ptr(draws), kv_sel, T, Tc, G, S, H, d, n_iter,
+    _check(lib().lvq_build_codebooks(_ptr(samples), _ptr(draws), None if weights is None else _ptr(weights),
+                                     kv_sel, T, Tc, G, S, H, d, n_iter,
                                      _ptr(codebooks), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream(samples)))
     return codebooks

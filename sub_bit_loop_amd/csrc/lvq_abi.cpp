@@ -256,9 +256,9 @@ size_t lvq_build_codebooks_workspace_bytes(int T, int Tc, int G, int S, int H, i
   return (centers + 255) / 256 * 256 + assign;
 }
 
-int lvq_build_codebooks(const uint16_t* samples, const double* draws, int kv_sel, int T, int Tc,
-                        int G, int S, int H, int d, int n_iter, uint16_t* codebooks, void* ws,
-                        size_t ws_bytes, void* stream) {
+int lvq_build_codebooks(const uint16_t* samples, const double* draws, const double* weights,
+                        int kv_sel, int T, int Tc, int G, int S, int H, int d, int n_iter,
+                        uint16_t* codebooks, void* ws, size_t ws_bytes, void* stream) {
   int st = check_encode_common(samples, codebooks, T, Tc, G, S, H, d);
   if (st) return st;
   if (!draws) return fail(LVQ_EINVAL, "null pointer argument");
@@ -273,6 +273,7 @@ int lvq_build_codebooks(const uint16_t* samples, const double* draws, int kv_sel
   lvq::KmeansArgs a{};
   a.samples = samples;
   a.draws = draws;
+  a.weights = weights;
   a.codebooks = codebooks;
   a.kv_sel = kv_sel;
   a.T = T; a.Tc = Tc; a.G = G; a.S = S; a.H = H; a.d = d;

@@ -35,6 +35,7 @@ constexpr int kMaxKmeansSamples = 8192;   // samples per book (float64 D^2 and r
 struct KmeansArgs {
   const uint16_t* samples;    // bf16 [T][S][H][d]
   const double* draws;        // [n_books][256] uniform in [0, 1), book = (beta * H + h) * ng + g
+  const double* weights;      // [nblk][S][H][ng] per joint vector, or null (all 1)
   uint16_t* codebooks;        // bf16 [nblk][2][H][ng][Tc][256][c]; half kv_sel is written
   double* centers;            // workspace [n_books][256][G]
   uint8_t* assign;            // workspace [nblk][S][H][ng]

@@ -16,13 +16,14 @@ def _samples(seed, T, S, H, d):
     return synth.f32_to_bf16_bits(synth.gen_kv(rng, T, S, H, d, sc)), rng
 
 
-def _gpu_build(bits, draws, kv_sel, T, Tc, G, n_iter, codebooks=None):
+def _gpu_build(bits, draws, kv_sel, T, Tc, G, n_iter, codebooks=None, weights=None):
     import sub_bit_loop_amd as lvq
     dev = torch.device("cuda:0")
     x = torch.from_numpy(bits.view(np.int16)).to(dev)
     u = torch.from_numpy(draws).to(dev)
     cb = None if codebooks is None else torch.from_numpy(codebooks.view(np.int16)).to(dev)
-    out = lvq.lvq_build_codebooks(x, u, kv_sel, T, Tc, G, n_iter, codebooks=cb)
+    w = None if weights is None else torch.from_numpy(weights).to(dev)
+    out = lvq.lvq_build_codebooks(x, u, kv_sel, T, Tc, G, n_iter, codebooks=cb, weights=w)
     torch.cuda.synchronize()
     return out.view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -79,6 +80,44 @@ def test_builder_ouro_shape_sampled_books():
     assert np.all(out[:, 0] != 0x7FC0)
 
 
+@pytest.mark.parametrize("T,Tc,G,S,H,d,n_iter", [
+    (4, 2, 16, 600, 2, 64, 3),
+    (4, 4, 32, 700, 1, 128, 2),
+])
+def test_weighted_builder_matches_oracle(T, Tc, G, S, H, d, n_iter):
+    """Per-vector weights (a quarter of them 0, the rest spread over two decades)."""
+    print(f"\ncase weighted build T={T} Tc={Tc} G={G} S={S} H={H} d={d}", flush=True)
+    bits, rng = _samples(64, T, S, H, d)
+    nblk, ng = T // Tc, d // (G // Tc)
+    draws = rng.random((nblk, H, ng, 256))
+    w = 10.0 ** rng.uniform(-1, 1, (nblk, S, H, ng))
+    w[rng.random(w.shape) < 0.25] = 0.0
+    out = _gpu_build(bits, draws, 1, T, Tc, G, n_iter, weights=w)
+    ref = orc.build_codebooks(bits, draws, Tc, G, n_iter, weights=w)
+    _compare(out[:, 1], ref, [(b, h, g) for b in range(nblk) for h in range(H) for g in range(ng)])
+
+
+def test_builder_at_the_sample_limit():
+    """S = 8192 (the largest supported: the seeding keeps 2 x 8192 float64 in LDS)."""
+    T, Tc, G, S, H, d = 4, 4, 32, 8192, 1, 64
+    print("\ncase build S=8192", flush=True)
+    bits, rng = _samples(66, T, S, H, d)
+    draws = rng.random((1, H, 8, 256))
+    out = _gpu_build(bits, draws, 0, T, Tc, G, 2)
+    books = [(0, 0, 0), (0, 0, 5)]
+    _compare(out[:, 0], orc.build_codebooks(bits, draws, Tc, G, 2, books=books), books)
+
+
+def test_weighted_builder_unit_weights_is_unweighted():
+    T, Tc, G, S, H, d = 4, 4, 32, 4096, 16, 128
+    print("\ncase unit weights Ouro shape", flush=True)
+    bits, rng = _samples(65, T, S, H, d)
+    draws = rng.random((1, H, 16, 256))
+    a = _gpu_build(bits, draws, 0, T, Tc, G, 4)
+    b = _gpu_build(bits, draws, 0, T, Tc, G, 4, weights=np.ones((1, S, H, 16)))
+    assert (a == b).all()
+
+
 def test_builder_rejects_bad_arguments():
     import sub_bit_loop_amd as lvq
     dev = torch.device("cuda:0")
@@ -88,6 +127,9 @@ def test_builder_rejects_bad_arguments():
         lvq.lvq_build_codebooks(x, u, 2, 4, 2, 16, 1)            # kv_sel
     with pytest.raises(lvq.LvqError):
         lvq.lvq_build_codebooks(x, u, 0, 4, 2, 16, -1)           # n_iter
+    with pytest.raises(ValueError):
+        lvq.lvq_build_codebooks(x, u, 0, 4, 2, 16, 1,
+                                weights=torch.ones((2, 15, 1, 8), dtype=torch.float64, device=dev))
     big = torch.zeros((4, 8193, 1, 64), dtype=torch.bfloat16, device=dev)
     with pytest.raises(lvq.LvqError):
         lvq.lvq_build_codebooks(big, u, 0, 4, 2, 16, 1)          # S above 8192

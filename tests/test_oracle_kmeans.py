@@ -179,3 +179,113 @@ def test_lowest_index_tie_in_lloyd():
     # duplicate centers: the member goes to the lower index, the duplicate keeps its place
     C = orc.lloyd(np.array([[1.0]]), np.array([[0.0], [0.0]]), 1)
     np.testing.assert_array_equal(C, [[1.0], [0.0]])
+
+
+# ---------------------------------------------------------------- weighted k-means
+def test_weighted_lloyd_matches_scikit_learn():
+    # weighted Lloyd from the same initial centers = scikit-learn's with sample_weight
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(8)
+    K, G, per = 12, 4, 25
+    means = rng.standard_normal((K, G)) * 10
+    X = np.concatenate([m + rng.standard_normal((per, G)) for m in means])
+    w = rng.uniform(0.1, 3.0, len(X))
+    init = X[np.arange(K) * per + 5]
+    ours = orc.lloyd(X, init, 6, bf16_assign=False, w=w)
+    km = KMeans(n_clusters=K, init=init, n_init=1, max_iter=6, tol=0.0, algorithm="lloyd").fit(X, sample_weight=w)
+    np.testing.assert_allclose(ours, km.cluster_centers_, rtol=0, atol=1e-12)
+    # the weights matter: the unweighted means differ
+    plain = orc.lloyd(X, init, 6, bf16_assign=False)
+    assert np.abs(plain - ours).max() > 1e-3
+
+
+def _integer_cloud(seed, S, G, lo=-20, hi=20):
+    rng = np.random.default_rng(seed)
+    X = rng.integers(lo, hi, (S, G)).astype(np.float64)
+    return X, rng
+
+
+def test_integer_weights_equal_duplicated_samples():
+    # weight m on a sample = m copies of it: with integer coordinates every distance, running
+    # sum, member sum and weight sum is exact, so seeding picks the same points (mapped back to
+    # the original samples) and Lloyd yields the same centers to the bit
+    K = 16
+    X, rng = _integer_cloud(9, 120, 6)
+    w = rng.integers(0, 4, len(X)).astype(np.float64)
+    w[:3] = [0, 2, 3]
+    rep = np.repeat(np.arange(len(X)), w.astype(int))
+    Xd = X[rep]
+    draws = rng.random(K)
+    pw = orc.kmeanspp_seed(X, draws, K=K, w=w)
+    pd = orc.kmeanspp_seed(Xd, draws, K=K)
+    np.testing.assert_array_equal(pw, rep[pd])
+    assert np.all(w[pw] > 0)
+    Cw = orc.lloyd(X, X[pw], 4, w=w)
+    Cd = orc.lloyd(Xd, Xd[pd], 4)
+    np.testing.assert_array_equal(Cw, Cd)
+
+
+def test_zero_weight_outliers_change_nothing():
+    # samples of weight 0 are never seeds and add nothing to a mean, wherever they sit
+    T, S, H, d, Tc, G = 2, 300, 1, 16, 2, 16
+    rng = np.random.default_rng(10)
+    x = orc.round_bf16(rng.standard_normal((T, S, H, d)))
+    draws = rng.random((1, H, 2, 256))
+    base = orc.build_codebooks(orc.bf16_bits_of(x), draws, Tc, G, 3)
+    ins = np.sort(rng.choice(S + 40, 40, replace=False))
+    keep = np.setdiff1d(np.arange(S + 40), ins)
+    y = np.zeros((T, S + 40, H, d))
+    y[:, keep] = x
+    y[:, ins] = orc.round_bf16(50.0 + 10 * rng.standard_normal((T, 40, H, d)))
+    w = np.ones((1, S + 40, H, 2))
+    w[:, ins] = 0.0
+    out = orc.build_codebooks(orc.bf16_bits_of(y), draws, Tc, G, 3, weights=w)
+    np.testing.assert_array_equal(out, base)
+    # unit weights are the unweighted build
+    np.testing.assert_array_equal(orc.build_codebooks(orc.bf16_bits_of(x), draws, Tc, G, 3,
+                                                      weights=np.ones((1, S, H, 2))), base)
+
+
+@pytest.mark.parametrize("mutant", ["seed_ignores_weight", "first_pick_uniform", "mean_over_count"])
+def test_weighted_mutants_are_caught(mutant, monkeypatch):
+    """Plausible mistakes in the weighted builder, planted in the oracle on the CPU, fail a pin."""
+    real_pick, real_lloyd = orc._running_sum_pick, orc.lloyd
+
+    def seed_mut(X, draws, K=orc.NCODES, w=None):
+        S = X.shape[0]
+        wv = np.ones(S) if w is None else np.asarray(w, dtype=np.float64)
+        picks = np.empty(K, dtype=np.int64)
+        picks[0] = real_pick(np.ones(S) if mutant == "first_pick_uniform" else wv, draws[0])
+        D2 = orc.sq_dist_sequential(X, X[picks[0]])
+        for k in range(1, K):
+            picks[k] = real_pick(D2 if mutant == "seed_ignores_weight" else wv * D2, draws[k])
+            D2 = np.minimum(D2, orc.sq_dist_sequential(X, X[picks[k]]))
+        return picks
+
+    def lloyd_mut(X, centers, n_iter, bf16_assign=True, w=None):
+        if w is None:
+            return real_lloyd(X, centers, n_iter, bf16_assign)
+        C = np.array(centers, dtype=np.float64)
+        for _ in range(n_iter):
+            A = orc.round_bf16(C) if bf16_assign else C
+            assign = orc.nearest_codeword(X, A).idx
+            new = C.copy()
+            for k in range(C.shape[0]):
+                m = np.flatnonzero(assign == k)
+                if len(m):
+                    new[k] = (w[m, None] * X[m]).sum(0) / len(m)
+            C = new
+        return C
+
+    if mutant == "mean_over_count":
+        monkeypatch.setattr(orc, "lloyd", lloyd_mut)
+    else:
+        monkeypatch.setattr(orc, "kmeanspp_seed", seed_mut)
+    failed = 0
+    for chk in (test_weighted_lloyd_matches_scikit_learn, test_integer_weights_equal_duplicated_samples,
+                test_zero_weight_outliers_change_nothing):
+        try:
+            chk()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"mutant {mutant} not caught"
