@@ -244,6 +244,110 @@ int lvq_decode_scores(const uint16_t* q, const int32_t* page_table, const uint8_
                       const lvq_attn_shape* shp, float* out, float* lse, float* scores,
                       void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Paged cache manager -- the page bookkeeping of the decode loop, on the device,
+ * with no host synchronisation.  It keeps the rules of the summary, section
+ * "전제와 한계": the cache is paged in 8 tokens; the sink tokens and the recent
+ * window stay bf16; once a token's forward pass (all loop steps and layers) is
+ * done and the window holds n_recent + 8 tokens, its oldest page is quantised
+ * across every layer and loop step and leaves the window.  Between calls, for every
+ * live sequence b:
+ *   q_end[b] = 8 * floor((seq_len[b] - n_recent) / 8), or 0 when that is negative;
+ *   page_table[b][0 .. q_end/8) = its coded pages;
+ *   bf16_table[b][0] = the bf16 page of logical page 0 (the sink copy), and
+ *   bf16_table[b][1 ..] = the bf16 pages of logical pages q_end/8, q_end/8 + 1, ...
+ * which are exactly the arrays lvq_decode_attn reads.  A page id names the same
+ * page in every layer's pools (index_pages and bf16_pages of each layer), so one
+ * state serves the whole model.
+ *
+ * Every array is int32 device memory owned by the caller:
+ *   page_table [B][max_pages], bf16_table [B][bf16_row], seq_len [B], q_end [B];
+ *   index_free [n_index_pages], bf16_free [n_bf16_pages]: stacks of free page ids;
+ *   counters [4]: free coded pages, free bf16 pages, error bits, 0;
+ *   re_src [B], re_dst [B]: the pending re-encode of each sequence (bf16 page ->
+ *   coded page) between lvq_cache_end_token and lvq_cache_commit, else -1.
+ * Page ids are handed out lowest first, sequences in index order, so the state is
+ * a deterministic function of the calls.  Error bits (counters[2], sticky, read by
+ * the caller when convenient): 1 coded pool empty, 2 bf16 pool empty, 4 a sequence
+ * longer than max_pages pages, 8 a window longer than bf16_row allows.  The
+ * allocation that fails is skipped (its entry stays -1, which attention and
+ * encoding skip as out of range); the contents are then unspecified, but every
+ * kernel stays within the arrays above.
+ *
+ * One decode token, in order: lvq_cache_begin_token; for each loop step t and
+ * layer: lvq_cache_append (that layer's K/V at step t), then lvq_decode_attn;
+ * lvq_cache_end_token; for each layer lvq_reencode_pages(bf16 pool, re_src,
+ * re_dst, B, ...); lvq_cache_commit.  All calls on one stream.
+ */
+typedef struct lvq_cache {
+  int32_t B;              /* sequence slots */
+  int32_t max_pages;      /* page_table row length: at most 8 * max_pages tokens */
+  int32_t bf16_row;       /* bf16_table row length, >= lvq_cache_min_bf16_row(n_recent) */
+  int32_t n_sink;         /* bf16 sink tokens, 0 .. 8 (kept in logical page 0) */
+  int32_t n_recent;       /* recent bf16 tokens kept, >= 0 */
+  int32_t n_index_pages;  /* coded pages per layer pool */
+  int32_t n_bf16_pages;   /* bf16 pages per layer pool */
+  int32_t* page_table;
+  int32_t* bf16_table;
+  int32_t* seq_len;
+  int32_t* q_end;
+  int32_t* index_free;
+  int32_t* bf16_free;
+  int32_t* counters;
+  int32_t* re_src;
+  int32_t* re_dst;
+} lvq_cache;
+
+/* Smallest bf16_row for n_recent: entry 0 plus ceil((n_recent + 8) / 8) pages. */
+int lvq_cache_min_bf16_row(int n_recent);
+
+/* Empty cache: every page free, tables -1, lengths 0, no error. */
+int lvq_cache_init(const lvq_cache* c, void* stream);
+
+/*
+ * Prefill bookkeeping: each slot b with seq_len[b] == 0 and lengths[b] > 0 (int32
+ * [B], device) gets L = lengths[b] tokens: q_end by the rule above, coded pages for
+ * logical pages [0, q_end/8), bf16 pages for logical page 0 and [q_end/8, ceil(L/8)).
+ * The caller then fills them per layer: lvq_encode_pages of tokens [0, q_end) with
+ * chunk_page = page_table + b * max_pages, and lvq_cache_store_tokens.
+ */
+int lvq_cache_prefill(const lvq_cache* c, const int32_t* lengths, void* stream);
+
+/*
+ * Copies tokens first .. first+n-1 of sequence b into one layer's bf16 pages, the
+ * tokens that live there (logical page 0 and positions >= q_end[b]); tokens at or
+ * beyond seq_len[b] are ignored.  k, v: bf16 [T][n][H][d] (pre-RoPE); bf16_pages:
+ * [n_bf16_pages][T][H][2][8][d].  d must be a multiple of 8.
+ */
+int lvq_cache_store_tokens(const lvq_cache* c, int b, int first, int n, const uint16_t* k,
+                           const uint16_t* v, int T, int H, int d, uint16_t* bf16_pages,
+                           void* stream);
+
+/* A new token for every live sequence (seq_len > 0): a bf16 page when the token
+ * starts a page, then seq_len += 1. */
+int lvq_cache_begin_token(const lvq_cache* c, void* stream);
+
+/*
+ * Writes the new token (position seq_len[b] - 1) of every live sequence into one
+ * layer's bf16 pages, loop steps t0 .. t0+n_steps-1.  k, v: bf16 [n_steps][B][H][d];
+ * T is the pages' loop-step count (t0 + n_steps <= T).
+ */
+int lvq_cache_append(const lvq_cache* c, int t0, int n_steps, const uint16_t* k,
+                     const uint16_t* v, int T, int H, int d, uint16_t* bf16_pages, void* stream);
+
+/* After the token's forward pass: re_src/re_dst name the pages to re-encode (a coded
+ * page is taken for every sequence whose window reached n_recent + 8), -1 elsewhere. */
+int lvq_cache_end_token(const lvq_cache* c, void* stream);
+
+/* After the re-encode of every layer: the coded pages join the page tables, q_end
+ * advances by 8, and the re-encoded bf16 pages leave the windows (back to the pool,
+ * except logical page 0, which stays as the sink copy). */
+int lvq_cache_commit(const lvq_cache* c, void* stream);
+
+/* Frees every page of the slots with mask[b] != 0 (int32 [B], device) and empties
+ * them (seq_len 0), ready for lvq_cache_prefill. */
+int lvq_cache_release(const lvq_cache* c, const int32_t* mask, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -518,3 +518,23 @@ def build_codebooks(samples_bits: np.ndarray, draws: np.ndarray, Tc: int, G: int
         for tau in range(Tc):
             out[beta, h, g, tau] = Cb[:, tau * c:(tau + 1) * c]
     return out
+
+
+# ----------------------------------------------------------------------------
+# paged cache bookkeeping
+# ----------------------------------------------------------------------------
+# The summary (section "전제와 한계") keeps the sink and the recent window in bf16,
+# pages the cache in 8 tokens, and once a token's forward pass is over quantises the
+# oldest recent page (all layers and loop steps) every 8 tokens.  Readings: after
+# prefill the coded run ends at q_end = 8 floor((L - n_recent) / 8) (0 when negative);
+# after each decode token, with L tokens cached, the oldest recent page is coded when
+# L - q_end >= n_recent + 8.
+
+def prefill_boundary(L: int, n_recent: int) -> int:
+    """q_end right after a prefill of L tokens."""
+    return max(0, PAGE * ((L - n_recent) // PAGE))
+
+
+def decode_boundary(q_end: int, L: int, n_recent: int) -> int:
+    """q_end after the forward pass of the token that brought the cache to L tokens."""
+    return q_end + PAGE if L - q_end >= n_recent + PAGE else q_end

@@ -35,6 +35,16 @@ class AttnShape(ctypes.Structure):
                                    "rope_max_len", "n_splits")] + [("scale", _f32)]
 
 
+class CacheDesc(ctypes.Structure):
+    """Mirror of lvq_cache."""
+    _fields_ = [(n, _i32) for n in ("B", "max_pages", "bf16_row", "n_sink", "n_recent", "n_index_pages",
+                                   "n_bf16_pages")] + \
+               [(n, _vp) for n in ("page_table", "bf16_table", "seq_len", "q_end", "index_free", "bf16_free",
+                                   "counters", "re_src", "re_dst")]
+
+
+_CP = ctypes.POINTER(CacheDesc)
+
 _SIGS = {
     "lvq_version": (_i32, []),
     "lvq_last_error": (ctypes.c_char_p, []),
@@ -51,6 +61,15 @@ _SIGS = {
                                ctypes.POINTER(AttnShape), _vp, _vp, _vp, _sz, _vp]),
     "lvq_decode_scores": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                  ctypes.POINTER(AttnShape), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lvq_cache_min_bf16_row": (_i32, [_i32]),
+    "lvq_cache_init": (_i32, [_CP, _vp]),
+    "lvq_cache_prefill": (_i32, [_CP, _vp, _vp]),
+    "lvq_cache_store_tokens": (_i32, [_CP, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "lvq_cache_begin_token": (_i32, [_CP, _vp]),
+    "lvq_cache_append": (_i32, [_CP, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "lvq_cache_end_token": (_i32, [_CP, _vp]),
+    "lvq_cache_commit": (_i32, [_CP, _vp]),
+    "lvq_cache_release": (_i32, [_CP, _vp, _vp]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -265,3 +284,100 @@ def lvq_decode_scores(q, page_table, index_pages, bf16_pages, bf16_table, codebo
                           bf16_table, codebooks, t, pos, seq_len, q_end, rope_tab, shp, out, lse,
                           ws, scores=scores)
     return out, lse, scores
+
+
+# ---------------------------------------------------------------- paged cache manager
+CACHE_ERRORS = {1: "coded pool empty", 2: "bf16 pool empty", 4: "sequence beyond max_pages",
+                8: "window beyond bf16_row"}
+
+
+class PagedCache:
+    """Device state of the paged cache manager (lvq_cache) in torch int32 tensors.
+
+    The tensors page_table, bf16_table, seq_len and q_end are the ones lvq_decode_attn
+    takes; re_src / re_dst feed lvq_reencode_pages between end_token and commit.  Every
+    method only marshals arguments; the bookkeeping runs in the library's kernels.
+    """
+
+    def __init__(self, B: int, max_pages: int, n_sink: int, n_recent: int, n_index_pages: int,
+                 n_bf16_pages: int, bf16_row: int | None = None, device="cuda"):
+        if bf16_row is None:
+            bf16_row = lib().lvq_cache_min_bf16_row(n_recent)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.page_table = torch.empty((B, max_pages), **i32)
+        self.bf16_table = torch.empty((B, bf16_row), **i32)
+        self.seq_len = torch.empty(B, **i32)
+        self.q_end = torch.empty(B, **i32)
+        self.index_free = torch.empty(max(n_index_pages, 1), **i32)
+        self.bf16_free = torch.empty(max(n_bf16_pages, 1), **i32)
+        self.counters = torch.empty(4, **i32)
+        self.re_src = torch.empty(B, **i32)
+        self.re_dst = torch.empty(B, **i32)
+        self.desc = CacheDesc(B, max_pages, bf16_row, n_sink, n_recent, n_index_pages, n_bf16_pages,
+                              *[_ptr(t) for t in (self.page_table, self.bf16_table, self.seq_len, self.q_end,
+                                                  self.index_free, self.bf16_free, self.counters,
+                                                  self.re_src, self.re_dst)])
+        self.B, self.max_pages, self.bf16_row = B, max_pages, bf16_row
+        self.n_sink, self.n_recent = n_sink, n_recent
+        self.n_index_pages, self.n_bf16_pages = n_index_pages, n_bf16_pages
+        self.init()
+
+    def _s(self):
+        return _stream(self.seq_len)
+
+    def init(self):
+        _check(lib().lvq_cache_init(ctypes.byref(self.desc), self._s()))
+
+    def prefill(self, lengths):
+        _dev(lengths, "lengths", I32, 1)
+        if lengths.numel() != self.B:
+            raise ValueError("lengths must have B entries")
+        _check(lib().lvq_cache_prefill(ctypes.byref(self.desc), _ptr(lengths), self._s()))
+
+    def store_tokens(self, b: int, first: int, k, v, bf16_pages):
+        """k, v bf16 [T][n][H][d]: tokens first .. first+n-1 of sequence b."""
+        _dev(k, "k", BF16, 4)
+        _dev(v, "v", BF16, 4)
+        _dev(bf16_pages, "bf16_pages", BF16, 6)
+        if k.shape != v.shape:
+            raise ValueError("k and v differ in shape")
+        T, n, H, d = k.shape
+        self._check_pool(bf16_pages, T, H, d)
+        _check(lib().lvq_cache_store_tokens(ctypes.byref(self.desc), b, first, n, _ptr(k), _ptr(v), T, H, d,
+                                            _ptr(bf16_pages), self._s()))
+
+    def begin_token(self):
+        _check(lib().lvq_cache_begin_token(ctypes.byref(self.desc), self._s()))
+
+    def append(self, t0: int, k, v, bf16_pages):
+        """k, v bf16 [n_steps][B][H][d]: the new token at loop steps t0 .. t0+n_steps-1."""
+        _dev(k, "k", BF16, 4)
+        _dev(v, "v", BF16, 4)
+        _dev(bf16_pages, "bf16_pages", BF16, 6)
+        if k.shape != v.shape or k.shape[1] != self.B:
+            raise ValueError("k and v must both be [n_steps][B][H][d]")
+        n_steps, _, H, d = k.shape
+        T = bf16_pages.shape[1]
+        self._check_pool(bf16_pages, T, H, d)
+        _check(lib().lvq_cache_append(ctypes.byref(self.desc), t0, n_steps, _ptr(k), _ptr(v), T, H, d,
+                                      _ptr(bf16_pages), self._s()))
+
+    def end_token(self):
+        _check(lib().lvq_cache_end_token(ctypes.byref(self.desc), self._s()))
+
+    def commit(self):
+        _check(lib().lvq_cache_commit(ctypes.byref(self.desc), self._s()))
+
+    def release(self, mask):
+        _dev(mask, "mask", I32, 1)
+        if mask.numel() != self.B:
+            raise ValueError("mask must have B entries")
+        _check(lib().lvq_cache_release(ctypes.byref(self.desc), _ptr(mask), self._s()))
+
+    def errors(self) -> int:
+        """Sticky error bits (synchronises with the device)."""
+        return int(self.counters[2].item())
+
+    def _check_pool(self, pool, T, H, d):
+        if tuple(pool.shape[1:]) != (T, H, 2, PAGE, d) or pool.shape[0] != self.n_bf16_pages:
+            raise ValueError(f"bf16_pages must be [{self.n_bf16_pages}][{T}][{H}][2][8][{d}]")

@@ -170,6 +170,51 @@ int check_encode_common(const void* kv, const void* codebooks, int T, int Tc, in
   return LVQ_OK;
 }
 
+int cache_args(const lvq_cache* c, lvq::CacheArgs& a) {
+  if (!c) return fail(LVQ_EINVAL, "null pointer argument");
+  if (c->B <= 0 || c->max_pages <= 0 || c->n_index_pages <= 0 || c->n_bf16_pages <= 0)
+    return fail(LVQ_EINVAL, "B, max_pages and pool sizes must be positive");
+  if (c->n_sink < 0 || c->n_sink > lvq::kPage) return fail(LVQ_EINVAL, "n_sink=%d outside [0, 8]", c->n_sink);
+  if (c->n_recent < 0) return fail(LVQ_EINVAL, "n_recent=%d must be >= 0", c->n_recent);
+  const int need_row = 1 + (c->n_recent + 2 * lvq::kPage - 1) / lvq::kPage;
+  if (c->bf16_row < need_row)
+    return fail(LVQ_EINVAL, "bf16_row=%d below %d for n_recent=%d", c->bf16_row, need_row, c->n_recent);
+  if (!c->page_table || !c->bf16_table || !c->seq_len || !c->q_end || !c->index_free || !c->bf16_free ||
+      !c->counters || !c->re_src || !c->re_dst)
+    return fail(LVQ_EINVAL, "null pointer in lvq_cache");
+  a.B = c->B;
+  a.max_pages = c->max_pages;
+  a.bf16_row = c->bf16_row;
+  a.n_sink = c->n_sink;
+  a.n_recent = c->n_recent;
+  a.n_index_pages = c->n_index_pages;
+  a.n_bf16_pages = c->n_bf16_pages;
+  a.page_table = c->page_table;
+  a.bf16_table = c->bf16_table;
+  a.seq_len = c->seq_len;
+  a.q_end = c->q_end;
+  a.index_free = c->index_free;
+  a.bf16_free = c->bf16_free;
+  a.counters = c->counters;
+  a.re_src = c->re_src;
+  a.re_dst = c->re_dst;
+  return LVQ_OK;
+}
+
+int token_copy(const uint16_t* k, const uint16_t* v, int T, int H, int d, uint16_t* pool,
+               lvq::TokenCopy& tc) {
+  if (!k || !v || !pool) return fail(LVQ_EINVAL, "null pointer argument");
+  if (T <= 0 || H <= 0 || d <= 0 || d % 8)
+    return fail(LVQ_EINVAL, "T=%d H=%d d=%d: positive, d a multiple of 8", T, H, d);
+  tc.k = k;
+  tc.v = v;
+  tc.pool = pool;
+  tc.T = T;
+  tc.H = H;
+  tc.d = d;
+  return LVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -302,6 +347,85 @@ int lvq_rope_tables(int max_len, int d, double base, float* rope_tab, size_t rop
   const int tile = lvq::rope_tile();
   return device_status(lvq::launch_rope_tables((max_len + tile - 1) / tile, d, base, rope_tab, (hipStream_t)stream),
                        "lvq_rope_tables launch");
+}
+
+int lvq_cache_min_bf16_row(int n_recent) {
+  if (n_recent < 0) return 0;
+  return 1 + (n_recent + 2 * lvq::kPage - 1) / lvq::kPage;
+}
+
+int lvq_cache_init(const lvq_cache* c, void* stream) {
+  lvq::CacheArgs a;
+  int st = cache_args(c, a);
+  if (st) return st;
+  return device_status(lvq::launch_cache_init(a, (hipStream_t)stream), "lvq_cache_init launch");
+}
+
+int lvq_cache_prefill(const lvq_cache* c, const int32_t* lengths, void* stream) {
+  lvq::CacheArgs a;
+  int st = cache_args(c, a);
+  if (st) return st;
+  if (!lengths) return fail(LVQ_EINVAL, "null pointer argument");
+  return device_status(lvq::launch_cache_prefill(a, lengths, (hipStream_t)stream), "lvq_cache_prefill launch");
+}
+
+int lvq_cache_store_tokens(const lvq_cache* c, int b, int first, int n, const uint16_t* k,
+                           const uint16_t* v, int T, int H, int d, uint16_t* bf16_pages,
+                           void* stream) {
+  lvq::CacheArgs a;
+  int st = cache_args(c, a);
+  if (st) return st;
+  if (b < 0 || b >= c->B) return fail(LVQ_EINVAL, "sequence %d outside [0, %d)", b, c->B);
+  if (first < 0 || n < 0) return fail(LVQ_EINVAL, "first=%d n=%d must be >= 0", first, n);
+  if (n == 0) return ok();
+  lvq::TokenCopy tc;
+  st = token_copy(k, v, T, H, d, bf16_pages, tc);
+  if (st) return st;
+  return device_status(lvq::launch_cache_store(a, tc, b, first, n, (hipStream_t)stream),
+                       "lvq_cache_store_tokens launch");
+}
+
+int lvq_cache_begin_token(const lvq_cache* c, void* stream) {
+  lvq::CacheArgs a;
+  int st = cache_args(c, a);
+  if (st) return st;
+  return device_status(lvq::launch_cache_step(a, 0, (hipStream_t)stream), "lvq_cache_begin_token launch");
+}
+
+int lvq_cache_append(const lvq_cache* c, int t0, int n_steps, const uint16_t* k,
+                     const uint16_t* v, int T, int H, int d, uint16_t* bf16_pages, void* stream) {
+  lvq::CacheArgs a;
+  int st = cache_args(c, a);
+  if (st) return st;
+  if (n_steps < 1 || t0 < 0 || t0 + n_steps > T)
+    return fail(LVQ_EINVAL, "steps [%d, %d) outside [0, T=%d)", t0, t0 + n_steps, T);
+  lvq::TokenCopy tc;
+  st = token_copy(k, v, T, H, d, bf16_pages, tc);
+  if (st) return st;
+  return device_status(lvq::launch_cache_append(a, tc, t0, n_steps, (hipStream_t)stream),
+                       "lvq_cache_append launch");
+}
+
+int lvq_cache_end_token(const lvq_cache* c, void* stream) {
+  lvq::CacheArgs a;
+  int st = cache_args(c, a);
+  if (st) return st;
+  return device_status(lvq::launch_cache_step(a, 1, (hipStream_t)stream), "lvq_cache_end_token launch");
+}
+
+int lvq_cache_commit(const lvq_cache* c, void* stream) {
+  lvq::CacheArgs a;
+  int st = cache_args(c, a);
+  if (st) return st;
+  return device_status(lvq::launch_cache_step(a, 2, (hipStream_t)stream), "lvq_cache_commit launch");
+}
+
+int lvq_cache_release(const lvq_cache* c, const int32_t* mask, void* stream) {
+  lvq::CacheArgs a;
+  int st = cache_args(c, a);
+  if (st) return st;
+  if (!mask) return fail(LVQ_EINVAL, "null pointer argument");
+  return device_status(lvq::launch_cache_release(a, mask, (hipStream_t)stream), "lvq_cache_release launch");
 }
 
 size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp) {

@@ -43,6 +43,32 @@ struct KmeansArgs {
 };
 hipError_t launch_build_codebooks(const KmeansArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- paged cache manager
+struct CacheArgs {
+  int B, max_pages, bf16_row, n_sink, n_recent, n_index_pages, n_bf16_pages;
+  int32_t* page_table;        // [B][max_pages]
+  int32_t* bf16_table;        // [B][bf16_row]
+  int32_t* seq_len;           // [B]
+  int32_t* q_end;             // [B]
+  int32_t* index_free;        // [n_index_pages] stack of free coded page ids
+  int32_t* bf16_free;         // [n_bf16_pages] stack of free bf16 page ids
+  int32_t* counters;          // [4] free coded, free bf16, error bits, 0
+  int32_t* re_src;            // [B]
+  int32_t* re_dst;            // [B]
+};
+struct TokenCopy {
+  const uint16_t* k;          // bf16 keys of the tokens to copy
+  const uint16_t* v;          // bf16 values
+  uint16_t* pool;             // bf16 pages [n_bf16_pages][T][H][2][8][d] of one layer
+  int T, H, d;
+};
+hipError_t launch_cache_init(const CacheArgs& c, hipStream_t s);
+hipError_t launch_cache_prefill(const CacheArgs& c, const int32_t* lengths, hipStream_t s);
+hipError_t launch_cache_step(const CacheArgs& c, int which, hipStream_t s);   // 0 begin, 1 end, 2 commit
+hipError_t launch_cache_release(const CacheArgs& c, const int32_t* mask, hipStream_t s);
+hipError_t launch_cache_store(const CacheArgs& c, const TokenCopy& tc, int b, int first, int n, hipStream_t s);
+hipError_t launch_cache_append(const CacheArgs& c, const TokenCopy& tc, int t0, int n_steps, hipStream_t s);
+
 // ---------------------------------------------------------------- RoPE tables
 hipError_t launch_rope_tables(int ntile, int d, double base, float* tab, hipStream_t s);
 

@@ -1,0 +1,289 @@
+"""On-device paged cache manager against the oracle's bookkeeping rules.
+
+A logical model of the cache (every token of every layer and sequence, kept on the
+host) is advanced token by token beside the device manager.  After prefill and after
+decode tokens the device state must match: q_end by the oracle's rules, coded pages
+equal to the oracle's encoding of the logical tokens (bit-exact), bf16 pages equal to
+the logical tokens, every page owned once, and attention through the managed tables
+within tolerance of the oracle's attention over the logical cache.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import lvq_oracle as orc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def _host16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+class Model:
+    """Logical cache: K/V bf16 bits [T][L][H][d] per (layer, sequence)."""
+
+    def __init__(self, seed, n_layers, B, lengths, T, H, d, Tc, G, n_sink, n_recent):
+        self.rng = np.random.default_rng(seed)
+        self.T, self.H, self.d, self.Tc, self.G = T, H, d, Tc, G
+        self.n_sink, self.n_recent, self.B = n_sink, n_recent, B
+        self.sc = [synth.channel_scales(self.rng, H, d) for _ in range(n_layers)]
+        self.K = [[self._tok(layer, int(L)) for L in lengths] for layer in range(n_layers)]
+        self.V = [[self._tok(layer, int(L)) for L in lengths] for layer in range(n_layers)]
+        self.L = [int(L) for L in lengths]
+        self.qe = [orc.prefill_boundary(L, n_recent) if L > 0 else 0 for L in self.L]
+        self.books = [synth.random_codebooks(self.rng, T, Tc, G, H, d, scale=2.0) for _ in range(n_layers)]
+
+    def _tok(self, layer, n):
+        return synth.f32_to_bf16_bits(synth.gen_kv(self.rng, self.T, n, self.H, self.d, self.sc[layer]))
+
+    def new_token(self):
+        """Per layer: K, V [T][B][H][d] of the next token of every live sequence."""
+        return [(self._tok(layer, self.B), self._tok(layer, self.B)) for layer in range(len(self.K))]
+
+    def append(self, new):
+        for layer, (k, v) in enumerate(new):
+            for b in range(self.B):
+                if self.L[b] > 0:
+                    self.K[layer][b] = np.concatenate([self.K[layer][b], k[:, b:b + 1]], axis=1)
+                    self.V[layer][b] = np.concatenate([self.V[layer][b], v[:, b:b + 1]], axis=1)
+        for b in range(self.B):
+            if self.L[b] > 0:
+                self.L[b] += 1
+
+    def end_token(self):
+        """The token's forward pass is over: the re-encode rule moves q_end."""
+        for b in range(self.B):
+            if self.L[b] > 0:
+                self.qe[b] = orc.decode_boundary(self.qe[b], self.L[b], self.n_recent)
+
+    def oracle_attn(self, layer, q, t, pos):
+        """Oracle attention over the logical cache, paged in the oracle's own layout."""
+        T, H, d, Tc, G = self.T, self.H, self.d, self.Tc, self.G
+        c = G // Tc
+        nblk, ng = T // Tc, d // c
+        n_pages = [qe // 8 for qe in self.qe]
+        max_pages = max(1, max((L + 7) // 8 for L in self.L))
+        pt = np.full((self.B, max_pages), -1, np.int32)
+        ip = np.zeros((max(1, sum(n_pages)), nblk, H, 2, 8, ng), np.uint8)
+        o = 0
+        for b in range(self.B):
+            pt[b, :n_pages[b]] = np.arange(o, o + n_pages[b])
+            o += n_pages[b]
+            if self.qe[b]:
+                for kv, toks in ((0, self.K[layer][b]), (1, self.V[layer][b])):
+                    r = orc.encode(toks[:, :self.qe[b]], self.books[layer], kv, T, Tc, G)
+                    orc.scatter_index_pages(r.idx, kv, pt[b, :n_pages[b]], ip)
+        bp, lay = synth.pack_bf16_pages(self.K[layer], self.V[layer], np.array(self.qe), T, H, d)
+        shp = orc.AttnShape(self.B, H, H, d, T, Tc, G, self.n_sink, 10000.0)
+        return orc.decode_attn(shp, q, pt, ip, bp, lay.bf16_table, self.books[layer], t, pos,
+                               np.array(self.L), np.array(self.qe))
+
+
+def check_state(m, cache, ips, bps):
+    """Device tables and pools against the logical model (bit-exact)."""
+    pt = cache.page_table.cpu().numpy()
+    bt = cache.bf16_table.cpu().numpy()
+    cnt = cache.counters.cpu().numpy()
+    assert cnt[2] == 0, f"error bits {cnt[2]}"
+    assert list(cache.seq_len.cpu().numpy()) == m.L
+    assert list(cache.q_end.cpu().numpy()) == m.qe
+    # every page owned once; owned + free = the pool
+    coded = [int(pt[b, j]) for b in range(m.B) for j in range(m.qe[b] // 8)]
+    bf16 = []
+    for b in range(m.B):
+        if m.L[b] == 0:
+            continue
+        rows = {int(bt[b, 0])}
+        for r in range(m.qe[b] // 8, (m.L[b] + 7) // 8):
+            rows.add(int(bt[b, 1 + r - m.qe[b] // 8]))
+        bf16 += sorted(rows)
+    free_i = set(cache.index_free[:cnt[0]].cpu().numpy().tolist())
+    free_b = set(cache.bf16_free[:cnt[1]].cpu().numpy().tolist())
+    assert len(set(coded)) == len(coded) and min(coded, default=0) >= 0
+    assert len(set(bf16)) == len(bf16) and min(bf16, default=0) >= 0
+    assert not (set(coded) & free_i) and len(coded) + len(free_i) == cache.n_index_pages
+    assert not (set(bf16) & free_b) and len(bf16) + len(free_b) == cache.n_bf16_pages
+    T, Tc, G = m.T, m.Tc, m.G
+    for layer in range(len(ips)):
+        ip = ips[layer].cpu().numpy()
+        bp = _host16(bps[layer])
+        for b in range(m.B):
+            L, qe = m.L[b], m.qe[b]
+            for kv, toks in ((0, m.K[layer][b]), (1, m.V[layer][b])):
+                if qe:
+                    idx = orc.encode(toks[:, :qe], m.books[layer], kv, T, Tc, G).idx   # [nblk][qe][H][ng]
+                    for j in range(qe // 8):
+                        got = ip[pt[b, j]][:, :, kv]                                    # [nblk][H][8][ng]
+                        want = idx[:, 8 * j:8 * j + 8].transpose(0, 2, 1, 3)
+                        assert (got == want).all(), f"layer {layer} seq {b} page {j} kv {kv}"
+                if L:
+                    for s in range(min(8, L)):
+                        assert (bp[bt[b, 0]][:, :, kv, s] == toks[:, s]).all(), f"sink seq {b} slot {s}"
+                for p in range(qe, L):
+                    page = bt[b, 1 + p // 8 - qe // 8]
+                    assert (bp[page][:, :, kv, p % 8] == toks[:, p]).all(), f"recent seq {b} pos {p}"
+
+
+def _setup(m, lengths, n_layers, max_pages, n_index, n_bf16):
+    import sub_bit_loop_amd as lvq
+    T, H, d, Tc, G = m.T, m.H, m.d, m.Tc, m.G
+    c = G // Tc
+    cache = lvq.PagedCache(m.B, max_pages, m.n_sink, m.n_recent, n_index, n_bf16)
+    cache.prefill(_dev(np.array(lengths, np.int32)))
+    ips = [torch.zeros((n_index, T // Tc, H, 2, 8, d // c), dtype=torch.uint8, device="cuda")
+           for _ in range(n_layers)]
+    bps = [torch.zeros((n_bf16, T, H, 2, 8, d), dtype=torch.int16, device="cuda") for _ in range(n_layers)]
+    cbs = [_dev(bk) for bk in m.books]
+    for layer in range(n_layers):
+        for b in range(m.B):
+            if m.L[b] == 0:
+                continue
+            k, v = _dev(m.K[layer][b]), _dev(m.V[layer][b])
+            if m.qe[b]:
+                row = cache.page_table[b, :m.qe[b] // 8].contiguous()
+                lvq.lvq_encode_pages(k[:, :m.qe[b]].contiguous(), cbs[layer], 0, T, Tc, G, row, ips[layer])
+                lvq.lvq_encode_pages(v[:, :m.qe[b]].contiguous(), cbs[layer], 1, T, Tc, G, row, ips[layer])
+            cache.store_tokens(b, 0, k, v, bps[layer])
+    torch.cuda.synchronize()
+    return cache, ips, bps, cbs
+
+
+def _decode_token(m, cache, ips, bps, cbs, attn_at=None):
+    """One decode token through the manager; attention at (t, layer) pairs in attn_at is
+    compared with the oracle.  Returns the worst (max_abs, max_rel)."""
+    import sub_bit_loop_amd as lvq
+    from gpu_helpers import attn_close
+    T, H, d, Tc, G = m.T, m.H, m.d, m.Tc, m.G
+    new = m.new_token()
+    live_before = [L > 0 for L in m.L]
+    cache.begin_token()
+    m.append(new)                                  # the logical cache now holds the token
+    worst = (0.0, 0.0)
+    for t in range(T):
+        for layer in range(len(ips)):
+            k, v = new[layer]
+            cache.append(t, _dev(k[t:t + 1]), _dev(v[t:t + 1]), bps[layer])
+            if attn_at and (t, layer) in attn_at:
+                q = synth.gen_queries(m.rng, 1, m.B, H, d)[0]
+                pos = np.array([max(L - 1, 0) for L in m.L], np.int32)
+                rml = max(m.L) + 8
+                shp = lvq.make_shape(m.B, H, H, d, T, Tc, G, m.n_sink, cache.max_pages, cache.bf16_row,
+                                     cache.n_index_pages, cache.n_bf16_pages, max(m.L), rml, 0)
+                out, lse = lvq.lvq_decode_attn(_dev(q), cache.page_table, ips[layer], bps[layer],
+                                               cache.bf16_table, cbs[layer], t, _dev(pos), cache.seq_len,
+                                               cache.q_end, lvq.lvq_rope_tables(rml, d), shp)
+                torch.cuda.synchronize()
+                ro, rl = m.oracle_attn(layer, q, t, pos)
+                live = np.array([L > 0 for L in m.L])
+                ok, mabs, mrel = attn_close(out.cpu().numpy()[live], ro[live])
+                assert ok, f"attention t={t} layer={layer}: max_abs {mabs:.3e} max_rel {mrel:.3e}"
+                assert np.abs(lse.cpu().numpy()[live] - rl[live]).max() < 2e-3
+                worst = (max(worst[0], mabs), max(worst[1], mrel))
+    cache.end_token()
+    for layer in range(len(ips)):
+        lvq.lvq_reencode_pages(bps[layer], cache.re_src, cache.re_dst, cbs[layer], T, Tc, G, ips[layer])
+    cache.commit()
+    m.end_token()
+    torch.cuda.synchronize()
+    assert live_before == [L > 0 for L in m.L]
+    return worst
+
+
+def test_manager_prefill_and_decode_loop():
+    """Three sequences (one shorter than a page, one shorter than the window, one coded),
+    two layers, 30 decode tokens: every sequence crosses at least two re-encodes."""
+    B, lengths, n_layers = 3, [5, 37, 100], 2
+    T, H, d, Tc, G, n_sink, n_recent = 4, 2, 64, 2, 16, 4, 16
+    print(f"\ncase cache manager B={B} L={lengths} layers={n_layers}", flush=True)
+    m = Model(71, n_layers, B, lengths, T, H, d, Tc, G, n_sink, n_recent)
+    cache, ips, bps, cbs = _setup(m, lengths, n_layers, max_pages=32, n_index=64, n_bf16=40)
+    check_state(m, cache, ips, bps)
+    for step in range(30):
+        attn_at = {(0, 0), (T - 1, 1)} if step % 7 in (0, 3) else None
+        _decode_token(m, cache, ips, bps, cbs, attn_at)
+        if step % 5 == 4 or step == 29:
+            check_state(m, cache, ips, bps)
+    assert m.qe[0] >= 16 and m.qe[1] >= 48
+
+
+def test_manager_release_and_refill():
+    """A finished sequence returns its pages; a new one of another length takes the slot."""
+    import sub_bit_loop_amd as lvq
+    B, lengths, n_layers = 3, [40, 90, 17], 1
+    T, H, d, Tc, G, n_sink, n_recent = 4, 1, 64, 4, 32, 4, 16
+    print("\ncase cache manager release/refill", flush=True)
+    m = Model(72, n_layers, B, lengths, T, H, d, Tc, G, n_sink, n_recent)
+    cache, ips, bps, cbs = _setup(m, lengths, n_layers, max_pages=24, n_index=40, n_bf16=20)
+    for _ in range(9):
+        _decode_token(m, cache, ips, bps, cbs)
+    check_state(m, cache, ips, bps)
+    free_before = cache.counters[:2].cpu().numpy().copy()
+    held = (m.qe[1] // 8, 1 + (m.L[1] + 7) // 8 - m.qe[1] // 8)
+    cache.release(_dev(np.array([0, 1, 0], np.int32)))
+    torch.cuda.synchronize()
+    assert list(cache.counters[:2].cpu().numpy()) == [free_before[0] + held[0], free_before[1] + held[1]]
+    # the logical model: slot 1 restarts with 61 new tokens
+    m.L[1], m.qe[1] = 61, orc.prefill_boundary(61, n_recent)
+    m.K[0][1], m.V[0][1] = m._tok(0, 61), m._tok(0, 61)
+    cache.prefill(_dev(np.array([99, 61, 99], np.int32)))   # live slots ignore their entry
+    k, v = _dev(m.K[0][1]), _dev(m.V[0][1])
+    row = cache.page_table[1, :m.qe[1] // 8].contiguous()
+    lvq.lvq_encode_pages(k[:, :m.qe[1]].contiguous(), cbs[0], 0, T, Tc, G, row, ips[0])
+    lvq.lvq_encode_pages(v[:, :m.qe[1]].contiguous(), cbs[0], 1, T, Tc, G, row, ips[0])
+    cache.store_tokens(1, 0, k, v, bps[0])
+    torch.cuda.synchronize()
+    check_state(m, cache, ips, bps)
+    for _ in range(12):
+        _decode_token(m, cache, ips, bps, cbs, {(T - 1, 0)} if _ % 6 == 5 else None)
+    check_state(m, cache, ips, bps)
+
+
+def test_manager_reports_exhausted_pools():
+    """Pools too small: the failing allocations are skipped and flagged, nothing else breaks."""
+    import sub_bit_loop_amd as lvq
+    print("\ncase cache manager exhaustion", flush=True)
+    cache = lvq.PagedCache(2, 16, 4, 16, n_index_pages=3, n_bf16_pages=3)
+    # the first sequence needs 5 coded pages (3 exist): skipped; the second takes 1 coded
+    # page (q_end = 8) and all 3 bf16 pages (the sink copy and logical pages 1, 2)
+    cache.prefill(_dev(np.array([60, 24], np.int32)))
+    torch.cuda.synchronize()
+    assert cache.errors() == 1
+    assert list(cache.seq_len.cpu().numpy()) == [0, 24]
+    assert list(cache.q_end.cpu().numpy()) == [0, 8]
+    assert list(cache.counters[:2].cpu().numpy()) == [2, 0]
+    # the next token starts logical page 3 and finds the bf16 pool empty
+    cache.begin_token()
+    torch.cuda.synchronize()
+    assert cache.errors() == 1 | 2
+    assert int(cache.bf16_table[1, 3].item()) == -1
+    # carry on until the coded pool and the window run out too: flagged, no fault
+    for _ in range(40):
+        cache.end_token()
+        cache.commit()
+        cache.begin_token()
+    torch.cuda.synchronize()
+    assert cache.errors() == 1 | 2 | 8
+    cnt = cache.counters.cpu().numpy()
+    assert 0 <= cnt[0] <= 3 and 0 <= cnt[1] <= 3
+
+
+def test_manager_rejects_bad_descriptors():
+    import sub_bit_loop_amd as lvq
+    with pytest.raises(lvq.LvqError):
+        lvq.PagedCache(2, 16, 9, 16, 8, 8)                    # n_sink above 8
+    with pytest.raises(lvq.LvqError):
+        lvq.PagedCache(2, 16, 4, 16, 8, 8, bf16_row=3)        # window needs 4 entries
+    cache = lvq.PagedCache(2, 16, 4, 16, 8, 8)
+    k = torch.zeros((1, 2, 1, 64), dtype=torch.int16, device="cuda")
+    pool = torch.zeros((8, 4, 1, 2, 8, 64), dtype=torch.int16, device="cuda")
+    with pytest.raises(lvq.LvqError):
+        cache.append(4, k, k, pool)                           # step 4 of T = 4
