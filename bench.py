@@ -339,6 +339,75 @@ def cpu_baseline(args, torch, inp):
                       f"float64 numpy, 1 thread, {el:.1f}s"}
 
 
+def manager_bench(torch, lvq, inp, n_tokens=64):
+    """The paged cache manager through the decode loop of the same model shape: per token,
+    begin_token, one append per (loop step, layer) of the new token's K/V, end_token, the
+    re-encode of every due page in every layer, commit.  The sequences start at 32768
+    tokens (pages allocated by the manager's prefill); attention is timed by the main loop
+    and left out here.  Returns microseconds per token, whole and bookkeeping only."""
+    dev = torch.device("cuda:0")
+    c = G // TC
+    nblk, ng = T // TC, D // c
+    max_pages = (L + 4 * n_tokens) // 8 + 4          # three timed runs and their warm-up tokens
+    n_index = B * max_pages
+    cache = lvq.PagedCache(B, max_pages, N_SINK, N_RECENT, n_index, B * 12)
+    cache.prefill(torch.full((B,), L, dtype=torch.int32, device=dev))
+    nl = len(inp["layers"])
+    ip = torch.zeros((n_index, nblk, H, 2, 8, ng), dtype=torch.uint8, device=dev)   # one pool, all layers
+    bps = [torch.zeros((B * 12, T, H, 2, 8, D), dtype=torch.bfloat16, device=dev) for _ in range(nl)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    kv = [torch.randn((2, 1, B, H, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(4)]
+
+    def token(i, reencode=True):
+        cache.begin_token()
+        for t in range(T):
+            for layer in range(nl):
+                k = kv[(t + layer) % 4]
+                cache.append(t, k[0], k[1], bps[layer])
+        cache.end_token()
+        if reencode:
+            for layer in range(nl):
+                lvq.lvq_reencode_pages(bps[layer], cache.re_src, cache.re_dst, inp["layers"][layer]["cb"],
+                                       T, TC, G, ip)
+        cache.commit()
+
+    res = {}
+    for name, reenc in (("us_per_token", True), ("us_per_token_bookkeeping", False)):
+        token(0, reenc)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_tokens):
+            token(i, reenc)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1e3 / n_tokens, 2)
+    # the whole token holds no host decision, so it replays as one captured graph
+    token(0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        token(0)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_tokens):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    res["us_per_token_graph"] = round(e0.elapsed_time(e1) * 1e3 / n_tokens, 2)
+    if cache.errors():
+        raise RuntimeError(f"cache manager error bits {cache.errors()}")
+    res["workload"] = (f"B={B} sequences from L={L}, {n_tokens} decode tokens, {nl} layers x {T} loop steps: "
+                       f"begin, {nl * T} appends, end, re-encode of due pages in every layer, commit "
+                       f"(8 pages x {nl} layers every 8 tokens)")
+    return res
+
+
 def encode_bench(torch, lvq, synth, inp):
     """Prefill encode of 32768 tokens x 16 heads x d=128 x 4 loop steps, K and V, for
     (Tc, G) = (4, 32) and (2, 16)."""
@@ -385,6 +454,27 @@ def encode_bench(torch, lvq, synth, inp):
     return res
 
 
+def hbm_probe(torch):
+    """Attainable HBM rates on this GPU: a 2 GiB float32 reduction (streaming read) and a
+    2 GiB copy (read + write), five timed repetitions each after a warm-up."""
+    n = (2 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, nbytes in (("read_gbs", lambda: x.sum(), 4 * n), ("copy_gbs", lambda: y.copy_(x), 8 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del x, y
+    return out
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -411,11 +501,16 @@ def main():
     achieved_gbs = algo / call_avg / 1e9
     log(f"step {step_s * 1e3:.3f} ms, call {call_avg * 1e6:.1f} us, {achieved_gbs:.0f} GB/s algorithmic")
     traffic = recorded_traffic()
+    probe = hbm_probe(torch)
+    pc = sorted(per_call)
+    pct = {f"p{q}": round(pc[min(len(pc) - 1, int(q / 100 * len(pc)))] * 1e6, 2) for q in (10, 50, 90)}
     roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
             "kernel": "lvq_decode_attn call: attn_kernel<128,8> + merge_kernel, one (layer, loop step)",
-            "algorithmic_bytes_per_call": algo, "avg_call_us": round(call_avg * 1e6, 2)}
+            "algorithmic_bytes_per_call": algo, "avg_call_us": round(call_avg * 1e6, 2),
+            "call_us_percentiles": pct,
+            "attainable": probe, "frac_of_attainable_read": round(achieved_gbs / probe["read_gbs"], 4)}
     res = {
         "metric": METRIC, "value": value, "unit": "KV token-steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
@@ -432,6 +527,10 @@ def main():
         "workload": f"one layer, K and V: {n_books} books of 256 codewords, {N_BOOK_SAMPLES} samples "
                     f"each, k-means++ + {N_LLOYD} Lloyd iterations (Tc={TC}, G={G})",
         "ms": round(inp["build_s"] * 1e3, 2), "books_per_s": round(n_books / inp["build_s"], 1)}
+    try:
+        res["cache_manager"] = manager_bench(torch, lvq, inp)
+    except Exception as e:  # report, never hide the headline
+        res["cache_manager"] = {"error": repr(e)}
     if not args.no_encode:
         try:
             res["encode"] = encode_bench(torch, lvq, synth, inp)

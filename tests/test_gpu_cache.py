@@ -287,3 +287,91 @@ def test_manager_rejects_bad_descriptors():
     pool = torch.zeros((8, 4, 1, 2, 8, 64), dtype=torch.int16, device="cuda")
     with pytest.raises(lvq.LvqError):
         cache.append(4, k, k, pool)                           # step 4 of T = 4
+
+
+def test_manager_decode_token_replays_in_a_hip_graph():
+    """A whole decode token (manager bookkeeping, appends, attention, re-encodes) needs no
+    host decision, so it can be captured once and replayed: every replay must leave the
+    same state and attention output as the same token run eagerly on a twin cache."""
+    import sub_bit_loop_amd as lvq
+    B, lengths, n_layers = 3, [6, 30, 77], 2
+    T, H, d, Tc, G, n_sink, n_recent = 4, 2, 64, 2, 16, 4, 16
+    print("\ncase cache manager graph replay", flush=True)
+    ma = Model(73, n_layers, B, lengths, T, H, d, Tc, G, n_sink, n_recent)
+    mb = Model(73, n_layers, B, lengths, T, H, d, Tc, G, n_sink, n_recent)
+    ca, ipa, bpa, cba = _setup(ma, lengths, n_layers, max_pages=24, n_index=48, n_bf16=30)
+    cg, ipg, bpg, cbg = _setup(mb, lengths, n_layers, max_pages=24, n_index=48, n_bf16=30)
+    rml = 256
+    rope = lvq.lvq_rope_tables(rml, d)
+    shp = lvq.make_shape(B, H, H, d, T, Tc, G, n_sink, 24, ca.bf16_row, 48, 30, 150, rml, 0)
+    wsz = lvq.lvq_decode_attn_workspace_bytes(shp)
+    kin = [[torch.zeros((1, B, H, d), dtype=torch.int16, device="cuda") for _ in range(n_layers)] for _ in range(T)]
+    vin = [[torch.zeros_like(kin[0][0]) for _ in range(n_layers)] for _ in range(T)]
+    q = torch.zeros((B, H, d), dtype=torch.int16, device="cuda")
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def token(cache, ips, bps, cbs, ws, out, lse):
+        cache.begin_token()
+        for t in range(T):
+            for layer in range(n_layers):
+                cache.append(t, kin[t][layer], vin[t][layer], bps[layer])
+                if t == T - 1 and layer == 0:
+                    lvq.lvq_decode_attn(q, cache.page_table, ips[0], bps[0], cache.bf16_table, cbs[0], t, pos,
+                                        cache.seq_len, cache.q_end, rope, shp, out=out, lse=lse, ws=ws)
+        cache.end_token()
+        for layer in range(n_layers):
+            lvq.lvq_reencode_pages(bps[layer], cache.re_src, cache.re_dst, cbs[layer], T, Tc, G, ips[layer])
+        cache.commit()
+
+    def outs():
+        return (torch.empty((B, H, d), dtype=torch.float32, device="cuda"),
+                torch.empty((B, H), dtype=torch.float32, device="cuda"),
+                torch.empty(wsz, dtype=torch.uint8, device="cuda"))
+
+    oa, la, wa = outs()
+    og, lg, wg = outs()
+    rng = np.random.default_rng(5)
+
+    def load_inputs(i):
+        new = ma.new_token()
+        mb.new_token()
+        for t in range(T):
+            for layer in range(n_layers):
+                kin[t][layer].copy_(_dev(new[layer][0][t:t + 1]))
+                vin[t][layer].copy_(_dev(new[layer][1][t:t + 1]))
+        q.copy_(_dev(synth.gen_queries(rng, 1, B, H, d)[0]))
+        pos.copy_(_dev(np.array([L for L in ma.L], np.int32)))
+        return new
+
+    # warm-up token, eager on both (first launches set kernel attributes)
+    new = load_inputs(0)
+    token(ca, ipa, bpa, cba, wa, oa, la)
+    token(cg, ipg, bpg, cbg, wg, og, lg)
+    for m in (ma, mb):
+        m.append(new)
+        m.end_token()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    new = load_inputs(1)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        token(cg, ipg, bpg, cbg, wg, og, lg)
+    # capture does not run the work: replay it for token 1, then 14 more tokens
+    for i in range(1, 16):
+        if i > 1:
+            new = load_inputs(i)
+        graph.replay()
+        token(ca, ipa, bpa, cba, wa, oa, la)
+        torch.cuda.synchronize()
+        for m in (ma, mb):
+            m.append(new)
+            m.end_token()
+        for x, y in ((ca.page_table, cg.page_table), (ca.bf16_table, cg.bf16_table), (ca.seq_len, cg.seq_len),
+                     (ca.q_end, cg.q_end), (ca.counters, cg.counters), (ca.index_free, cg.index_free),
+                     (ca.bf16_free, cg.bf16_free), (oa, og), (la, lg)):
+            assert torch.equal(x, y), f"token {i}: graph replay differs from the eager run"
+        for layer in range(n_layers):
+            assert torch.equal(ipa[layer], ipg[layer]) and torch.equal(bpa[layer], bpg[layer])
+    check_state(mb, cg, ipg, bpg)
