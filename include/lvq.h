@@ -245,6 +245,46 @@ int lvq_decode_scores(const uint16_t* q, const int32_t* page_table, const uint8_
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Multi-row attention: many query rows per KV head in one call, each key rebuilt
+ * and rotated once and shared by the rows.  Two uses (the summary, sections "전제와
+ * 한계" -- the same decode attention, and a prefill that the summary notes runs
+ * slightly slower than bf16 -- and "무엇과 다른가" -- RoPE after reconstruction):
+ *  - prefill chunk over an existing coded prefix: NQ new tokens per sequence, each
+ *    attending to the paged prefix and causally to the chunk's own keys;
+ *  - GQA decode (NQ = 1, no new keys): the Hq/H query heads of a KV head are the rows.
+ * Query i of sequence b, head hq, at RoPE position pos[b] + i, attends over the paged
+ * tokens [0, prefix_len[b]) exactly as lvq_decode_attn does with seq_len = prefix_len
+ * (coded [n_sink, q_end), bf16 sink and recent), plus, when k_new is given, the new
+ * keys 0 .. i at positions prefix_len[b] + i'.
+ *   q:            bf16 [B][NQ][Hq][d], pre-RoPE.
+ *   k_new, v_new: bf16 [B][NQ][H][d] pre-RoPE keys and values of the chunk at loop
+ *                 step t, or both NULL.
+ *   page_table, index_pages, bf16_pages, bf16_table, codebooks, t, q_end, rope_tab:
+ *                 as lvq_decode_attn.
+ *   prefix_len:   int32 [B], paged tokens visible to every query.
+ *   out:          float32 [B][NQ][Hq][d]; lse: float32 [B][NQ][Hq] or NULL.
+ *   ws:           lvq_rows_attn_workspace_bytes(shp) bytes.
+ * Scores and the value sum run on float32 matrix cores (products exact in float32).
+ * Supported: d = 128, c in {8, 16, 32}.
+ */
+typedef struct lvq_rows_shape {
+  int32_t B, NQ, H, Hq, d, T, Tc, G;
+  int32_t n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages;
+  int32_t max_prefix;     /* upper bound of prefix_len[b] */
+  int32_t rope_max_len;   /* >= max_prefix + NQ; every pos[b] + NQ - 1 must be below it */
+  int32_t n_splits;       /* key chunks per row; 0 = automatic */
+  float scale;            /* softmax scale; 0 = 1/sqrt(d) */
+} lvq_rows_shape;
+
+size_t lvq_rows_attn_workspace_bytes(const lvq_rows_shape* shp);
+int lvq_rows_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                  const int32_t* page_table, const uint8_t* index_pages, const uint16_t* bf16_pages,
+                  const int32_t* bf16_table, const uint16_t* codebooks, int t, const int32_t* pos,
+                  const int32_t* prefix_len, const int32_t* q_end, const float* rope_tab,
+                  const lvq_rows_shape* shp, float* out, float* lse, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/*
  * Paged cache manager -- the page bookkeeping of the decode loop, on the device,
  * with no host synchronisation.  It keeps the rules of the summary, section
  * "전제와 한계": the cache is paged in 8 tokens; the sink tokens and the recent

@@ -35,6 +35,13 @@ class AttnShape(ctypes.Structure):
                                    "rope_max_len", "n_splits")] + [("scale", _f32)]
 
 
+class RowsShape(ctypes.Structure):
+    """Mirror of lvq_rows_shape."""
+    _fields_ = [(n, _i32) for n in ("B", "NQ", "H", "Hq", "d", "T", "Tc", "G", "n_sink", "max_pages",
+                                   "bf16_row", "n_index_pages", "n_bf16_pages", "max_prefix",
+                                   "rope_max_len", "n_splits")] + [("scale", _f32)]
+
+
 class CacheDesc(ctypes.Structure):
     """Mirror of lvq_cache."""
     _fields_ = [(n, _i32) for n in ("B", "max_pages", "bf16_row", "n_sink", "n_recent", "n_index_pages",
@@ -61,6 +68,9 @@ _SIGS = {
                                ctypes.POINTER(AttnShape), _vp, _vp, _vp, _sz, _vp]),
     "lvq_decode_scores": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                  ctypes.POINTER(AttnShape), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lvq_rows_attn_workspace_bytes": (_sz, [ctypes.POINTER(RowsShape)]),
+    "lvq_rows_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
+                             ctypes.POINTER(RowsShape), _vp, _vp, _vp, _sz, _vp]),
     "lvq_cache_min_bf16_row": (_i32, [_i32]),
     "lvq_cache_init": (_i32, [_CP, _vp]),
     "lvq_cache_prefill": (_i32, [_CP, _vp, _vp]),
@@ -381,3 +391,50 @@ class PagedCache:
     def _check_pool(self, pool, T, H, d):
         if tuple(pool.shape[1:]) != (T, H, 2, PAGE, d) or pool.shape[0] != self.n_bf16_pages:
             raise ValueError(f"bf16_pages must be [{self.n_bf16_pages}][{T}][{H}][2][8][{d}]")
+
+
+# ---------------------------------------------------------------- multi-row attention
+def lvq_rows_attn_workspace_bytes(shp: RowsShape) -> int:
+    return lib().lvq_rows_attn_workspace_bytes(ctypes.byref(shp))
+
+
+def lvq_rows_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos, prefix_len,
+                  q_end, rope_tab, shp: RowsShape, k_new=None, v_new=None, out=None, lse=None, ws=None):
+    """Query rows q [B][NQ][Hq][d] over the paged prefix (and the chunk's own keys k_new/v_new
+    [B][NQ][H][d], causally); returns (out [B][NQ][Hq][d] f32, lse [B][NQ][Hq] f32)."""
+    _dev(q, "q", BF16, 4)
+    for name, x in (("page_table", page_table), ("bf16_table", bf16_table)):
+        _dev(x, name, I32, 2)
+    _dev(index_pages, "index_pages", U8, 6)
+    _dev(bf16_pages, "bf16_pages", BF16, 6)
+    _dev(codebooks, "codebooks", BF16, 7)
+    for name, x in (("pos", pos), ("prefix_len", prefix_len), ("q_end", q_end)):
+        _dev(x, name, I32, 1)
+    _dev(rope_tab, "rope_tab", F32, 1)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        _dev(k_new, "k_new", BF16, 4)
+        _dev(v_new, "v_new", BF16, 4)
+    if tuple(q.shape) != (shp.B, shp.NQ, shp.Hq, shp.d):
+        raise ValueError("q must be [B][NQ][Hq][d] of the shape")
+    dev = q.device
+    if out is None:
+        out = torch.empty((shp.B, shp.NQ, shp.Hq, shp.d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((shp.B, shp.NQ, shp.Hq), dtype=torch.float32, device=dev)
+    need = lvq_rows_attn_workspace_bytes(shp)
+    if ws is None:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    _check(lib().lvq_rows_attn(_ptr(q), None if k_new is None else _ptr(k_new),
+                               None if v_new is None else _ptr(v_new), _ptr(page_table), _ptr(index_pages),
+                               _ptr(bf16_pages), _ptr(bf16_table), _ptr(codebooks), t, _ptr(pos),
+                               _ptr(prefix_len), _ptr(q_end), _ptr(rope_tab), ctypes.byref(shp), _ptr(out),
+                               _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+    return out, lse
+
+
+def make_rows_shape(B, NQ, H, Hq, d, T, Tc, G, n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages,
+                    max_prefix, rope_max_len, n_splits=0, scale=0.0) -> RowsShape:
+    return RowsShape(B, NQ, H, Hq, d, T, Tc, G, n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages,
+                     max_prefix, rope_max_len, n_splits, scale)

@@ -170,6 +170,68 @@ int check_encode_common(const void* kv, const void* codebooks, int T, int Tc, in
   return LVQ_OK;
 }
 
+// ------------------------------------------------------------------ multi-row attention
+struct RowsPlan {
+  int n_rb, n_chunks, chunk_pages;
+};
+
+RowsPlan plan_rows(const lvq_rows_shape& s) {
+  RowsPlan p;
+  const int g = s.Hq / s.H;
+  p.n_rb = (s.NQ * g + 15) / 16;
+  const int coded_pages = (s.max_prefix + lvq::kPage - 1) / lvq::kPage;
+  const int w = lvq::rows_waves_per_group();
+  int n = s.n_splits;
+  if (n <= 0) {
+    const long items = (long)s.B * s.H * p.n_rb;
+    n = (int)((2048 + items - 1) / items);
+    const int by_len = coded_pages / 16;            // at least 8 tiles per chunk
+    if (n > by_len) n = by_len;
+  }
+  if (n < 1) n = 1;
+  n = (n + w - 1) / w * w;                         // whole workgroups
+  if (n > 1016) n = 1016;                          // bound on splits per row
+  int cp = (coded_pages + n - 1) / n;
+  cp = (cp + 1) / 2 * 2;
+  p.chunk_pages = cp < 2 ? 2 : cp;
+  p.n_chunks = n;
+  return p;
+}
+
+int check_rows(const void* q, const void* k_new, const void* v_new, const void* page_table,
+               const void* index_pages, const void* bf16_pages, const void* bf16_table,
+               const void* codebooks, int t, const void* pos, const void* prefix_len,
+               const void* q_end, const void* rope_tab, const lvq_rows_shape* shp, const void* out) {
+  if (!shp) return fail(LVQ_EINVAL, "shape is null");
+  const lvq_rows_shape& s = *shp;
+  if (!q || !page_table || !index_pages || !bf16_pages || !bf16_table || !codebooks || !pos ||
+      !prefix_len || !q_end || !rope_tab || !out)
+    return fail(LVQ_EINVAL, "null pointer argument");
+  if (!k_new != !v_new) return fail(LVQ_EINVAL, "k_new and v_new must both be given or both be null");
+  if (s.B <= 0 || s.NQ <= 0 || s.H <= 0 || s.Hq <= 0) return fail(LVQ_EINVAL, "B, NQ, H, Hq must be positive");
+  if (s.Hq % s.H) return fail(LVQ_EINVAL, "Hq=%d must be a multiple of H=%d", s.Hq, s.H);
+  int st = check_code_shape(s.T, s.Tc, s.G, s.d);
+  if (st) return st;
+  if (t < 0 || t >= s.T) return fail(LVQ_EINVAL, "t=%d outside [0, T=%d)", t, s.T);
+  if (s.n_sink < 0 || s.n_sink > lvq::kPage) return fail(LVQ_EINVAL, "n_sink=%d outside [0, 8]", s.n_sink);
+  if (s.max_prefix < 0) return fail(LVQ_EINVAL, "max_prefix must be >= 0");
+  if ((long)s.max_pages * lvq::kPage < s.max_prefix)
+    return fail(LVQ_EINVAL, "max_pages=%d too small for max_prefix=%d", s.max_pages, s.max_prefix);
+  if (s.bf16_row < 1) return fail(LVQ_EINVAL, "bf16_row must be >= 1");
+  if (s.n_index_pages < 0 || s.n_bf16_pages <= 0) return fail(LVQ_EINVAL, "pool sizes must be positive");
+  if ((long)s.rope_max_len < (long)s.max_prefix + s.NQ)
+    return fail(LVQ_EINVAL, "rope_max_len=%d below max_prefix + NQ = %ld", s.rope_max_len, (long)s.max_prefix + s.NQ);
+  if (!(s.scale >= 0.f) || isinf(s.scale)) return fail(LVQ_EINVAL, "scale must be finite and >= 0");
+  if (!lvq::rows_supported(s.d, s.G / s.Tc))
+    return fail(LVQ_EUNSUPPORTED, "multi-row shape d=%d c=%d not compiled (d=128, c in {8,16,32})", s.d, s.G / s.Tc);
+  return LVQ_OK;
+}
+
+size_t rows_workspace(const lvq_rows_shape& s) {
+  const RowsPlan p = plan_rows(s);
+  return (size_t)s.B * s.NQ * s.Hq * p.n_chunks * (s.d + 2) * sizeof(float);
+}
+
 int cache_args(const lvq_cache* c, lvq::CacheArgs& a) {
   if (!c) return fail(LVQ_EINVAL, "null pointer argument");
   if (c->B <= 0 || c->max_pages <= 0 || c->n_index_pages <= 0 || c->n_bf16_pages <= 0)
@@ -426,6 +488,75 @@ int lvq_cache_release(const lvq_cache* c, const int32_t* mask, void* stream) {
   if (st) return st;
   if (!mask) return fail(LVQ_EINVAL, "null pointer argument");
   return device_status(lvq::launch_cache_release(a, mask, (hipStream_t)stream), "lvq_cache_release launch");
+}
+
+size_t lvq_rows_attn_workspace_bytes(const lvq_rows_shape* shp) {
+  if (!shp || shp->B <= 0 || shp->NQ <= 0 || shp->H <= 0 || shp->Hq <= 0 || shp->d <= 0 || shp->Hq % shp->H ||
+      shp->max_prefix < 0)
+    return 0;
+  return rows_workspace(*shp);
+}
+
+int lvq_rows_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                  const int32_t* page_table, const uint8_t* index_pages, const uint16_t* bf16_pages,
+                  const int32_t* bf16_table, const uint16_t* codebooks, int t, const int32_t* pos,
+                  const int32_t* prefix_len, const int32_t* q_end, const float* rope_tab,
+                  const lvq_rows_shape* shp, float* out, float* lse, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int st = check_rows(q, k_new, v_new, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos,
+                      prefix_len, q_end, rope_tab, shp, out);
+  if (st) return st;
+  const lvq_rows_shape& s = *shp;
+  const size_t need = rows_workspace(s);
+  if (!ws || ws_bytes < need)
+    return fail(LVQ_ENOSPC, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  const RowsPlan p = plan_rows(s);
+  lvq::RowsArgs a{};
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.page_table = page_table;
+  a.index_pages = index_pages;
+  a.bf16_pages = bf16_pages;
+  a.bf16_table = bf16_table;
+  a.codebooks = codebooks;
+  a.pos = pos;
+  a.prefix_len = prefix_len;
+  a.q_end = q_end;
+  a.rope = rope_tab;
+  a.part = (float*)ws;
+  a.t = t;
+  a.B = s.B;
+  a.NQ = s.NQ;
+  a.H = s.H;
+  a.Hq = s.Hq;
+  a.d = s.d;
+  a.T = s.T;
+  a.Tc = s.Tc;
+  a.G = s.G;
+  a.n_sink = s.n_sink;
+  a.max_pages = s.max_pages;
+  a.bf16_row = s.bf16_row;
+  a.n_index_pages = s.n_index_pages;
+  a.n_bf16_pages = s.n_bf16_pages;
+  a.max_prefix = s.max_prefix;
+  a.rope_tiles = (s.rope_max_len + lvq::rope_tile() - 1) / lvq::rope_tile();
+  a.n_rb = p.n_rb;
+  a.n_chunks = p.n_chunks;
+  a.chunk_pages = p.chunk_pages;
+  const float scale = s.scale > 0.f ? s.scale : 1.0f / sqrtf((float)s.d);
+  a.scale_log2e = scale * 1.4426950408889634f;
+  hipError_t e = lvq::launch_rows(a, (hipStream_t)stream);
+  if (e != hipSuccess) return device_status(e, "lvq_rows_attn launch");
+  lvq::AttnArgs m{};
+  m.part = a.part;
+  m.out = out;
+  m.lse = lse;
+  m.B = s.B * s.NQ;
+  m.Hq = s.Hq;
+  m.d = s.d;
+  m.n_chunks = p.n_chunks;
+  return device_status(lvq::launch_merge(m, (hipStream_t)stream), "lvq_rows_attn merge launch");
 }
 
 size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp) {

@@ -540,6 +540,11 @@ bool attn_supported(int d, int c) {
   return false;
 }
 
+hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int c = a.G / a.Tc;
   if (a.d == 128) {

@@ -43,6 +43,33 @@ struct KmeansArgs {
 };
 hipError_t launch_build_codebooks(const KmeansArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- multi-row attention
+// Query rows (query token i of a chunk, query head hq) of one KV head share each key's
+// dequantisation and rotation; scores and the value sum run on fp32 MFMA.
+struct RowsArgs {
+  const uint16_t* q;          // [B][NQ][Hq][d]
+  const uint16_t* k_new;      // [B][NQ][H][d] or null: the chunk's own keys at step t
+  const uint16_t* v_new;      // [B][NQ][H][d] or null
+  const int32_t* page_table;
+  const uint8_t* index_pages;
+  const uint16_t* bf16_pages;
+  const int32_t* bf16_table;
+  const uint16_t* codebooks;
+  const int32_t* pos;         // [B] position of query 0
+  const int32_t* prefix_len;  // [B] paged tokens, visible to every query
+  const int32_t* q_end;       // [B]
+  const float* rope;
+  float* part;                // [B * NQ][Hq][n_chunks][d + 2]
+  int t, B, NQ, H, Hq, d, T, Tc, G;
+  int n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages, max_prefix, rope_tiles;
+  int n_rb;                   // row blocks of 16 per (b, KV head)
+  int n_chunks, chunk_pages;  // key chunks per row block; coded pages per chunk (even)
+  float scale_log2e;
+};
+bool rows_supported(int d, int c);
+int rows_waves_per_group();
+hipError_t launch_rows(const RowsArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- paged cache manager
 struct CacheArgs {
   int B, max_pages, bf16_row, n_sink, n_recent, n_index_pages, n_bf16_pages;
@@ -94,6 +121,7 @@ struct AttnArgs {
   int chunk_pages;            // pages per chunk, multiple of 8
   float scale_log2e;          // softmax scale * log2(e)
 };
+hipError_t launch_merge(const AttnArgs& a, hipStream_t s);   // merge of a.part into a.out / a.lse
 bool attn_supported(int d, int c);
 int rope_tile();   // positions per row of the first RoPE table part
 int attn_waves_per_group();   // coded chunks (waves) per attention workgroup

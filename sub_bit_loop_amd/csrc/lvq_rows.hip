@@ -1,0 +1,396 @@
+// Multi-row attention over the LoopVQ cache, gfx950: many query rows per KV head.
+//
+// What it computes (LoopVQ summary, onedev.kr/papers/1681, sections "전제와 한계" and
+// "무엇과 다른가"; the same attention as the decode kernel): at loop step t, query i of
+// sequence b and query head hq (RoPE position pos[b] + i) attends over the paged cache
+// [0, prefix_len[b]) -- coded tokens rebuilt from the step-(t % Tc) codebook slices,
+// bf16 sink and recent tokens, keys rotated after dequantisation -- and, when the call
+// carries them, over the chunk's own new keys 0 .. i (positions prefix_len[b] + i',
+// causal).  Two uses: a prefill chunk attending to an existing coded prefix (the
+// summary notes prefill runs slightly slower than bf16), and GQA decode, where the
+// query heads of one KV head are the rows.
+//
+// Design (MI355X): a workgroup owns 16 query rows of one (sequence, KV head) and 8
+// waves; each wave walks one chunk of keys, 16 keys per tile.  Each key is rebuilt and
+// rotated once per tile in float32 and shared by all 16 rows through v_mfma_f32_16x16x4f32:
+//  * lane (key j, quarter k) holds key j's channel pairs [16k, 16k+16) with their
+//    partners + d/2, rebuilt by four 16-byte LDS gathers and rotated in registers (the
+//    rotation of a pair stays inside the lane); those 32 values are its B operands of
+//    the 32 score MFMAs, whose A operands are the rotated query rows in the same order;
+//  * the 16 x 16 scores land one row quarter per lane group; the online softmax keeps
+//    (max, sum) per row, with the same lazy maximum as the decode kernel;
+//  * probabilities go through a 1 KB LDS tile to the A-operand layout of the value
+//    MFMAs; lane (column c, key quarter) gathers chunk c (channels 8c .. 8c+7) of four
+//    keys, so output channel 8c + b of value block b sits in that lane: 32 MFMAs per tile.
+// Float32 MFMA keeps the products exact in float32, as in the decode kernel.
+#include "lvq_internal.h"
+
+namespace lvq {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kRW = 8;          // waves per workgroup
+constexpr int kRows = 16;       // query rows per workgroup
+constexpr int kKeys = 16;       // keys per tile (the RoPE table's tile)
+constexpr float kRescaleR = 8.0f;
+constexpr int kD = 128;         // head dim compiled
+
+constexpr size_t rows_lds_bytes() {
+  // K and V slices (float16) + per wave a 16 x 16 probability tile
+  return (size_t)2 * kCodes * kD * 2 + (size_t)kRW * kKeys * kRows * 4;
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <int C>
+__device__ __forceinline__ void stage_slice_rows(const RowsArgs& a, int beta, int kv, int h, int tau,
+                                                 _Float16* dst) {
+  constexpr int NG = kD / C;
+  constexpr int NCH = kD / 8;
+  const uint16_t* src = a.codebooks + ((((size_t)beta * 2 + kv) * a.H + h) * NG) * ((size_t)a.Tc * kCodes * C);
+  for (int e = threadIdx.x * 8; e < kCodes * kD; e += kRW * 64 * 8) {
+    const int x = e / kD, k = (e % kD) / 8;
+    const int g = (8 * k) / C, i = (8 * k) % C;
+    const u16x8 v = *(const u16x8*)(src + (((size_t)g * a.Tc + tau) * kCodes + x) * C + i);
+    f16x8 o;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = (_Float16)bf2f(v[q]);
+    *(f16x8*)(dst + ((size_t)x * NCH + k) * 8) = o;
+  }
+}
+
+// max over the 16 lanes of a lane group (xor offsets stay inside the group)
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <int C>
+__global__ __launch_bounds__(kRW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void rows_kernel(RowsArgs a, int n_cg) {
+  constexpr int D = kD, HALF = D / 2, NG = D / C, NCH = D / 8;
+  extern __shared__ __align__(16) unsigned char smem[];
+  _Float16* kl = (_Float16*)smem;
+  _Float16* vl = kl + (size_t)kCodes * D;
+  float* ptile_all = (float*)(vl + (size_t)kCodes * D);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int bid = blockIdx.x;
+  const int cg = bid % n_cg; bid /= n_cg;
+  const int rb = bid % a.n_rb; bid /= a.n_rb;
+  const int h = bid % a.H; bid /= a.H;
+  const int b = bid;
+  const int g = a.Hq / a.H;
+  const int R = a.NQ * g;
+  const int beta = a.t / a.Tc, tau = a.t % a.Tc, nblk = a.T / a.Tc;
+  const int chunk = cg * kRW + wave;
+  const int L = min(max(a.prefix_len[b], 0), a.max_prefix);
+  const int qe = min(a.q_end[b] & ~7, L);
+  const int P_lo = chunk * a.chunk_pages;
+  const int P_hi = a.n_index_pages > 0 ? min(qe >> 3, P_lo + a.chunk_pages) : P_lo;
+  const bool active = chunk < a.n_chunks;
+  const int ns = min(a.n_sink, L);
+  const int r0 = max(qe, a.n_sink);
+  const int vt_lo = r0 / kKeys;
+  const int vt_hi = L > r0 ? (L - 1) / kKeys + 1 : vt_lo;
+  // new-key tiles: up to the largest query index among this block's rows
+  const int i_max = min(a.NQ - 1, (rb * kRows + kRows - 1) / g);
+  const int n_new = a.k_new ? i_max / kKeys + 1 : 0;
+  const int n_vt = (ns > 0 ? 1 : 0) + (vt_hi - vt_lo) + n_new;
+
+  stage_slice_rows<C>(a, beta, 0, h, tau, kl);
+  stage_slice_rows<C>(a, beta, 1, h, tau, vl);
+  __syncthreads();
+  if (!active) return;
+
+  const int j = lane & 15, kq = lane >> 4;     // key in tile / quarter (B side); row / quarter (A side)
+  // A operands: rotated query rows, pairs [16 kq, 16 kq + 16) then their partners
+  float qf[32];
+  int row_q[4];                                  // query index of the 4 rows this lane holds in D layout
+  {
+    const int r_abs = rb * kRows + j;
+    const bool row_ok = r_abs < R;
+    const int qi = row_ok ? r_abs / g : 0, hq = h * g + (row_ok ? r_abs % g : 0);
+    const int pq = min(max(a.pos[b] + qi, 0), a.rope_tiles * kKeys - 1);
+    const uint16_t* qv = a.q + (((size_t)b * a.NQ + qi) * a.Hq + hq) * D;
+    const float* e0 = a.rope + (size_t)(pq / kKeys) * D;
+    const float* e1 = a.rope + (size_t)(a.rope_tiles + pq % kKeys) * D;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int pr = 16 * kq + s;
+      const float c0 = e0[2 * pr], s0 = e0[2 * pr + 1], c1 = e1[2 * pr], s1 = e1[2 * pr + 1];
+      const float c = c0 * c1 - s0 * s1, sn = s0 * c1 + c0 * s1;
+      const float x = row_ok ? bf2f(qv[pr]) : 0.f, y = row_ok ? bf2f(qv[pr + HALF]) : 0.f;
+      qf[s] = (x * c - y * sn) * a.scale_log2e;
+      qf[16 + s] = (y * c + x * sn) * a.scale_log2e;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ra = rb * kRows + 4 * kq + r;
+      row_q[r] = ra < R ? ra / g : -1;
+    }
+  }
+  // the in-tile offset phase of key j for this lane's pairs
+  float e1c[16], e1s[16];
+  {
+    const float* e1 = a.rope + (size_t)(a.rope_tiles + j) * D;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      e1c[s] = e1[2 * (16 * kq + s)];
+      e1s[s] = e1[2 * (16 * kq + s) + 1];
+    }
+  }
+  float m[4], lp[4];
+  f32x4 O[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { m[r] = -__builtin_inff(); lp[r] = 0.f; }
+#pragma unroll
+  for (int c8 = 0; c8 < 8; ++c8) O[c8] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float* ptile = ptile_all + wave * kKeys * kRows;
+
+  const size_t row_stride = (size_t)kPage * NG;
+  const size_t page_bytes = (size_t)nblk * a.H * 2 * row_stride;
+  const uint8_t* head_rows = a.index_pages + (((size_t)beta * a.H + h) * 2) * row_stride;
+  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+  const int32_t* bt = a.bf16_table + (size_t)b * a.bf16_row;
+
+  auto gather = [&](const _Float16* slice, uint32_t code, int ch) -> f16x8 {
+    return *(const f16x8*)(slice + ((size_t)code * NCH + ch) * 8);
+  };
+  // One tile: keys at positions pbase + 0..15 (pbase a multiple of 16).
+  //  kf: this lane's 32 raw key values (pairs of quarter kq, then partners), float32;
+  //  vraw[s2][0..7]: chunk j of the value of key 4 s2 + kq;
+  //  kok: the key of this lane is valid for every row; causal_base >= 0: new-key tile
+  //  whose key i' = causal_base + j is visible to rows with query index >= i'.
+  // rotate this lane's key values by position pbase + j (pbase a multiple of 16): the
+  // tile phase E(pbase) times the lane's offset phase E(j)
+  auto rotate_aligned = [&](int pbase, float (&kf)[32]) {
+    const int a_tile = min(pbase / kKeys, a.rope_tiles - 1);
+    const f32x4* e0 = (const f32x4*)(a.rope + (size_t)a_tile * D + 2 * 16 * kq);
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const f32x4 e = e0[s2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int s = 2 * s2 + u;
+        const float c0 = e[2 * u], s0 = e[2 * u + 1];
+        const float c = c0 * e1c[s] - s0 * e1s[s], sn = s0 * e1c[s] + c0 * e1s[s];
+        const float lo = kf[s], hi = kf[16 + s];
+        kf[s] = lo * c - hi * sn;
+        kf[16 + s] = lo * sn + hi * c;
+      }
+    }
+  };
+  // One tile of 16 rotated keys against the 16 rows.
+  //  kf: this lane's 32 rotated key values (pairs of quarter kq, then partners);
+  //  vraw[s2][0..7]: chunk j of the value of key 4 s2 + kq;
+  //  kok: the key of lane column j exists; causal_base >= 0: new-key tile whose key
+  //  i' = causal_base + j is visible to rows with query index >= i'.
+  auto tile = [&](const float (&kf)[32], const float (&vraw)[4][8], bool kok, int causal_base) {
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], kf[s], S, 0, 0, 0);
+    // masks: the key of lane column j against the 4 rows this lane holds
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bool ok = kok && row_q[r] >= 0;
+      if (causal_base >= 0) ok = ok && causal_base + j <= row_q[r];
+      sv[r] = ok ? S[r] : -__builtin_inff();
+    }
+    if (__any(sv[0] > m[0] + kRescaleR || sv[1] > m[1] + kRescaleR || sv[2] > m[2] + kRescaleR ||
+              sv[3] > m[3] + kRescaleR)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mn = fmaxf(m[r], group16_max(sv[r]));
+        const float f = mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m[r] - mn);
+        lp[r] *= f;
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) O[c8][r] *= f;
+        m[r] = mn;
+      }
+    }
+    f32x4 P;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      P[r] = sv[r] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m[r]);
+      lp[r] += P[r];
+    }
+    // P[row][key] -> A layout: lane (row j, key quarter kq) takes keys 4 s2 + kq
+    *(f32x4*)(ptile + j * kRows + 4 * kq) = P;          // [key][row]
+    asm volatile("" ::: "memory");
+    float pa[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) pa[s2] = ptile[(4 * s2 + kq) * kRows + j];
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c8 = 0; c8 < 8; ++c8)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], vraw[s2][c8], O[c8], 0, 0, 0);
+  };
+
+  // ---- virtual tiles: bf16 sink, recent window, new keys
+  for (int vt = chunk; vt < n_vt; vt += a.n_chunks) {
+    const bool sink_tile = ns > 0 && vt == 0;
+    const int after_sink = vt - (ns > 0 ? 1 : 0);
+    const bool new_tile = after_sink >= vt_hi - vt_lo;
+    float kf[32], vraw[4][8];
+    bool kok = false;
+    int pbase = 0, causal = -1;
+    // this lane's key row (channels of quarter kq and their partners) as float32
+    auto load_krow = [&](const uint16_t* krow, float (&kf)[32]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ch0 = (u >> 1) * HALF + 16 * kq + 8 * (u & 1);
+        u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (krow) x = *(const u16x8*)(krow + ch0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kf[(u & 1) * 8 + (u >> 1) * 16 + i] = bf2f(x[i]);
+      }
+    };
+    if (new_tile) {
+      const int nt = after_sink - (vt_hi - vt_lo);
+      causal = nt * kKeys;
+      const int ik = causal + j;
+      kok = ik < a.NQ;
+      load_krow(kok ? a.k_new + (((size_t)b * a.NQ + ik) * a.H + h) * D : nullptr, kf);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int iv = causal + 4 * s2 + kq;
+        u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (iv < a.NQ) x = *(const u16x8*)(a.v_new + (((size_t)b * a.NQ + iv) * a.H + h) * D + 8 * j);
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) vraw[s2][c8] = bf2f(x[c8]);
+      }
+      // new key i' sits at position L + i' (not tile aligned): its own phase E0 * E1
+      const int pc = min(L + ik, a.rope_tiles * kKeys - 1);
+      const float* e0 = a.rope + (size_t)(pc / kKeys) * D;
+      const float* e1 = a.rope + (size_t)(a.rope_tiles + pc % kKeys) * D;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int pr = 16 * kq + s;
+        const float c0 = e0[2 * pr], s0 = e0[2 * pr + 1], c1 = e1[2 * pr], s1 = e1[2 * pr + 1];
+        const float c = c0 * c1 - s0 * s1, sn = s0 * c1 + c0 * s1;
+        const float lo = kf[s], hi = kf[16 + s];
+        kf[s] = lo * c - hi * sn;
+        kf[16 + s] = lo * sn + hi * c;
+      }
+    } else {
+      const int a_tile = sink_tile ? 0 : vt_lo + after_sink;
+      const int lo = sink_tile ? 0 : r0, hi = sink_tile ? ns : L;
+      pbase = kKeys * a_tile;
+      auto row_of = [&](int p) -> const uint16_t* {
+        if (p < lo || p >= hi) return nullptr;
+        const int slot = sink_tile ? 0 : 1 + (p >> 3) - (qe >> 3);
+        const int pg = slot < a.bf16_row ? bt[slot] : -1;
+        if (pg < 0 || pg >= a.n_bf16_pages) return nullptr;
+        return a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2) * kPage + (p & 7)) * D;
+      };
+      const uint16_t* krow = row_of(pbase + j);
+      kok = krow != nullptr;
+      load_krow(krow, kf);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const uint16_t* vr = row_of(pbase + 4 * s2 + kq);
+        u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (vr) x = *(const u16x8*)(vr + (size_t)kPage * D + 8 * j);
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) vraw[s2][c8] = bf2f(x[c8]);
+      }
+      rotate_aligned(pbase, kf);
+    }
+    tile(kf, vraw, kok, causal);
+  }
+
+  // ---- coded tiles: pages [P_lo, P_hi), two pages per tile
+  for (int P0 = P_lo; P0 < P_hi; P0 += 2) {
+    const int pbase = 8 * P0;
+    float kf[32], vraw[4][8];
+    // keys: lane column j
+    const int pk = P0 + (j >> 3);
+    const int physk = pk < P_hi ? pt[pk] : -1;
+    const bool kok = physk >= 0 && physk < a.n_index_pages && pbase + j >= a.n_sink;
+    {
+      const uint8_t* krow = head_rows + (size_t)(kok ? physk : 0) * page_bytes + (j & 7) * NG;
+      const int chs[4] = {2 * kq, 2 * kq + 1, NCH / 2 + 2 * kq, NCH / 2 + 2 * kq + 1};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t code = krow[(8 * chs[u]) / C];
+        const f16x8 x = gather(kl, code, chs[u]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kf[(u & 1) * 8 + (u >> 1) * 16 + i] = kok ? (float)x[i] : 0.f;
+      }
+    }
+    // values: keys 4 s2 + kq, chunk j
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int kv = 4 * s2 + kq;
+      const int pv = P0 + (kv >> 3);
+      const int physv = pv < P_hi ? pt[pv] : -1;
+      const bool vok = physv >= 0 && physv < a.n_index_pages && pbase + kv >= a.n_sink;
+      const uint8_t* vrow = head_rows + (size_t)(vok ? physv : 0) * page_bytes + row_stride + (kv & 7) * NG;
+      const uint32_t code = vrow[(8 * j) / C];
+      const f16x8 x = gather(vl, code, j);
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8) vraw[s2][c8] = vok ? (float)x[c8] : 0.f;
+    }
+    rotate_aligned(pbase, kf);
+    tile(kf, vraw, kok, -1);
+  }
+
+  // ---- partial records of the 4 rows this lane holds
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float l = group16_sum(lp[r]);
+    const int ra = rb * kRows + 4 * kq + r;
+    if (ra < R) {
+      const int qi = ra / g, hq = h * g + ra % g;
+      float* rec = a.part + ((((size_t)b * a.NQ + qi) * a.Hq + hq) * a.n_chunks + chunk) * (D + 2);
+      if (j == 0) { rec[0] = m[r]; rec[1] = l; }
+      f32x4 o0 = {O[0][r], O[1][r], O[2][r], O[3][r]};
+      f32x4 o1 = {O[4][r], O[5][r], O[6][r], O[7][r]};
+      *(f32x4*)(rec + 2 + 8 * j) = o0;
+      *(f32x4*)(rec + 2 + 8 * j + 4) = o1;
+    }
+  }
+}
+
+template <int C>
+hipError_t launch_rows_t(const RowsArgs& a, hipStream_t s) {
+  constexpr size_t lds = rows_lds_bytes();
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)rows_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int n_cg = (a.n_chunks + kRW - 1) / kRW;
+  const long grid = (long)n_cg * a.n_rb * a.H * a.B;
+  hipLaunchKernelGGL((rows_kernel<C>), dim3((unsigned)grid), dim3(kRW * 64), lds, s, a, n_cg);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool rows_supported(int d, int c) { return d == kD && (c == 8 || c == 16 || c == 32); }
+int rows_waves_per_group() { return kRW; }
+
+hipError_t launch_rows(const RowsArgs& a, hipStream_t s) {
+  const int c = a.G / a.Tc;
+  if (c == 8) return launch_rows_t<8>(a, s);
+  if (c == 16) return launch_rows_t<16>(a, s);
+  return launch_rows_t<32>(a, s);
+}
+
+}  // namespace lvq

@@ -1,0 +1,194 @@
+"""Multi-row attention (prefill chunk over a coded prefix; GQA decode) against the float64
+oracle, through the C ABI.
+
+Query i of a chunk is the oracle's decode attention over the prefix plus the chunk's
+tokens 0 .. i (appended as bf16 tokens after the prefix), at position prefix + i.
+Tolerance as for decode: |gpu - oracle| <= 2e-3 or <= 1e-2 |oracle|; lse within 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from cachebuild import build_cache, build_cache_light
+from gpu_helpers import attn_close, to_dev
+from oracle import lvq_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def _page_tokens(bp, pg, n):
+    """Tokens 0..n-1 of bf16 page pg as K, V [T][n][H][d]."""
+    return (np.ascontiguousarray(bp[pg][:, :, 0, :n].transpose(0, 2, 1, 3)),
+            np.ascontiguousarray(bp[pg][:, :, 1, :n].transpose(0, 2, 1, 3)))
+
+
+def extended_bf16(cache, ck, cv):
+    """The oracle's bf16 pages for prefix + chunk: page 0 and the recent tokens of the
+    prefix (read from the prefix's pages) followed by the chunk's tokens ck/cv [b][T][NQ][H][d]."""
+    fk, fv, rk, rv, lens = [], [], [], [], []
+    NQ = ck[0].shape[1]
+    for b in range(cache.B):
+        L, qe = int(cache.seq_len[b]), int(cache.q_end[b])
+        k0, v0 = _page_tokens(cache.bf16_pages, cache.bf16_table[b, 0], min(8, L))
+        base = (qe // 8) * 8
+        ks, vs = [], []
+        for p0 in range(base, L, 8):
+            pg = cache.bf16_table[b, 1 + (p0 - base) // 8]
+            k_, v_ = _page_tokens(cache.bf16_pages, pg, min(8, L - p0))
+            ks.append(k_)
+            vs.append(v_)
+        ks.append(ck[b])
+        vs.append(cv[b])
+        rec_k, rec_v = np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
+        if base == 0:   # the chunk can reach into page 0 only when the prefix is shorter than 8
+            n0 = min(8, L + NQ)
+            k0, v0 = rec_k[:, :n0], rec_v[:, :n0]
+        fk.append(k0)
+        fv.append(v0)
+        rk.append(rec_k)
+        rv.append(rec_v)
+        lens.append(L + NQ)
+    return synth.pack_bf16_pages_parts(fk, fv, rk, rv, cache.q_end, lens, cache.T, cache.H, cache.d)
+
+
+def oracle_rows(cache, q_rows, t, ck=None, cv=None, queries=None, pairs=None):
+    """out [B][NQ][Hq][d], lse [B][NQ][Hq] (NaN where not computed)."""
+    B, NQ = q_rows.shape[0], q_rows.shape[1]
+    shp = cache.shape()
+    L = cache.seq_len.astype(np.int64)
+    if ck is not None:
+        bp, lay = extended_bf16(cache, ck, cv)
+        bt = lay.bf16_table
+    else:
+        bp, bt = cache.bf16_pages, cache.bf16_table
+    out = np.full((B, NQ, cache.Hq, cache.d), np.nan)
+    lse = np.full((B, NQ, cache.Hq), np.nan)
+    for i in (range(NQ) if queries is None else queries):
+        extra = i + 1 if ck is not None else 0
+        o, ls = orc.decode_attn(shp, q_rows[:, i], cache.page_table, cache.index_pages, bp, bt,
+                                cache.codebooks, t, L + i if ck is not None else cache.pos,
+                                L + extra, cache.q_end, pairs=pairs)
+        out[:, i], lse[:, i] = o, ls
+    return out, lse
+
+
+def gpu_rows(dc, cache, q_rows, t, ck=None, cv=None, n_splits=0):
+    import sub_bit_loop_amd as lvq
+    B, NQ = q_rows.shape[0], q_rows.shape[1]
+    shp = lvq.make_rows_shape(B, NQ, cache.H, cache.Hq, cache.d, cache.T, cache.Tc, cache.G, cache.n_sink,
+                              dc.page_table.shape[1], dc.bf16_table.shape[1], dc.index_pages.shape[0],
+                              dc.bf16_pages.shape[0], int(cache.seq_len.max()), dc.rope_max_len, n_splits)
+    pos = cache.seq_len if ck is not None else cache.pos
+    kn = vn = None
+    if ck is not None:
+        kn = _dev(np.stack([k[t] for k in ck]))          # [B][NQ][H][d]
+        vn = _dev(np.stack([v[t] for v in cv]))
+    out, lse = lvq.lvq_rows_attn(_dev(q_rows), dc.page_table, dc.index_pages, dc.bf16_pages, dc.bf16_table,
+                                 dc.codebooks, t, _dev(pos.astype(np.int32)), dc.seq_len, dc.q_end, dc.rope, shp,
+                                 k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def compare(got, ref, label):
+    (o, l), (ro, rl) = got, ref
+    sel = ~np.isnan(rl)
+    ok, mabs, mrel = attn_close(o[sel], ro[sel])
+    lerr = float(np.abs(l[sel] - rl[sel]).max())
+    print(f"  {label}: {int(sel.sum())} rows, max-abs {mabs:.2e} max-rel {mrel:.2e} lse err {lerr:.2e}", flush=True)
+    assert ok, f"{label}: output outside tolerance (max-abs {mabs:.3e})"
+    assert lerr <= 1e-4, f"{label}: lse error {lerr:.3e}"
+
+
+def _chunk(seed, B, T, NQ, H, d, Hq):
+    rng = np.random.default_rng(seed)
+    sc = synth.channel_scales(rng, H, d)
+    ck = [synth.f32_to_bf16_bits(synth.gen_kv(rng, T, NQ, H, d, sc)) for _ in range(B)]
+    cv = [synth.f32_to_bf16_bits(synth.gen_kv(rng, T, NQ, H, d, sc)) for _ in range(B)]
+    q = synth.gen_queries(rng, NQ, B, Hq, d).transpose(1, 0, 2, 3)      # [B][NQ][Hq][d]
+    return ck, cv, np.ascontiguousarray(q)
+
+
+@pytest.mark.parametrize("cfg,lengths,NQ,H,Hq,T,Tc,G,ns,nr,steps", [
+    (41, [100, 300], 20, 2, 4, 4, 4, 32, 4, 16, (0, 3)),     # GQA x2, c = 8, ragged row blocks
+    (42, [520], 37, 2, 2, 4, 2, 32, 4, 64, (1,)),            # c = 16, three row blocks
+    (43, [5, 61], 18, 1, 1, 1, 1, 32, 4, 16, (0,)),          # c = 32; a prefix shorter than a page
+])
+def test_prefill_chunk_matches_oracle(cfg, lengths, NQ, H, Hq, T, Tc, G, ns, nr, steps):
+    print(f"\ncase prefill chunk cfg={cfg} L={lengths} NQ={NQ} H={H} Hq={Hq} T={T} Tc={Tc} G={G}", flush=True)
+    cache = build_cache(cfg, len(lengths), lengths, H, 128, T, Tc, G, ns, nr, Hq=Hq, books="random")
+    dc = to_dev(cache, max_seq_len=int(max(lengths)) + NQ)
+    ck, cv, q = _chunk(cfg, len(lengths), T, NQ, H, 128, Hq)
+    for t in steps:
+        compare(gpu_rows(dc, cache, q, t, ck, cv), oracle_rows(cache, q, t, ck, cv), f"t={t}")
+
+
+@pytest.mark.parametrize("cfg,lengths,H,Hq,T,Tc,G", [
+    (44, [64, 333, 1000], 2, 8, 4, 4, 32),                   # 4 query heads per KV head
+    (45, [17, 700], 1, 16, 1, 1, 32),                        # 16 heads on one KV head, c = 32
+])
+def test_gqa_decode_matches_oracle(cfg, lengths, H, Hq, T, Tc, G):
+    print(f"\ncase GQA decode cfg={cfg} L={lengths} H={H} Hq={Hq}", flush=True)
+    cache = build_cache(cfg, len(lengths), lengths, H, 128, T, Tc, G, 4, 64, Hq=Hq, books="random")
+    dc = to_dev(cache)
+    q = np.ascontiguousarray(cache.q[T - 1][:, None])                    # [B][1][Hq][d]
+    compare(gpu_rows(dc, cache, q, T - 1), oracle_rows(cache, q, T - 1), f"t={T - 1}")
+
+
+def test_rows_split_count_does_not_change_the_result():
+    """Explicit split counts (one workgroup of chunks, and many) agree with the oracle."""
+    cache = build_cache(46, 1, [900], 2, 128, 4, 4, 32, 4, 16, Hq=4, books="random")
+    dc = to_dev(cache, max_seq_len=900 + 9)
+    ck, cv, q = _chunk(46, 1, 4, 9, 2, 128, 4)
+    ref = oracle_rows(cache, q, 2, ck, cv)
+    for n in (8, 56):
+        compare(gpu_rows(dc, cache, q, 2, ck, cv, n_splits=n), ref, f"splits={n}")
+
+
+def test_prefill_chunk_at_32k_sampled():
+    """64 new tokens over a 32768-token coded prefix (Ouro-shaped head, 16 heads, MHA); the
+    oracle checks three query positions of two heads."""
+    print("\ncase prefill chunk 64 over 32K", flush=True)
+    NQ = 64
+    cache = build_cache_light(47, 1, [32768], 16, 128, 4, 4, 32, 4, 64)
+    dc = to_dev(cache, max_seq_len=32768 + NQ)
+    ck, cv, q = _chunk(47, 1, 4, NQ, 16, 128, 16)
+    got = gpu_rows(dc, cache, q, 1, ck, cv)
+    ref = oracle_rows(cache, q, 1, ck, cv, queries=(0, 31, 63), pairs=[(0, 3), (0, 12)])
+    compare(got, ref, "t=1")
+
+
+def test_gqa_decode_at_32k_sampled():
+    """GQA decode at 32K: 8 sequences, 4 KV heads x 4 query heads; sampled pairs."""
+    print("\ncase GQA decode B=8 L=32K H=4 Hq=16", flush=True)
+    cache = build_cache_light(48, 8, [32768] * 8, 4, 128, 4, 4, 32, 4, 64, Hq=16)
+    dc = to_dev(cache)
+    q = np.ascontiguousarray(cache.q[2][:, None])
+    got = gpu_rows(dc, cache, q, 2)
+    ref = oracle_rows(cache, q, 2, pairs=[(0, 0), (3, 7), (7, 15)])
+    compare(got, ref, "t=2")
+
+
+def test_rows_rejects_bad_arguments():
+    import sub_bit_loop_amd as lvq
+    cache = build_cache(49, 1, [40], 1, 128, 4, 4, 32, 4, 16, books="random")
+    dc = to_dev(cache)
+    q = np.zeros((1, 1, 1, 128), np.uint16)
+    shp = lvq.make_rows_shape(1, 1, 1, 1, 128, 4, 4, 32, 4, dc.page_table.shape[1], dc.bf16_table.shape[1],
+                              dc.index_pages.shape[0], dc.bf16_pages.shape[0], 40, 40)   # rope too short
+    with pytest.raises(lvq.LvqError):
+        lvq.lvq_rows_attn(_dev(q), dc.page_table, dc.index_pages, dc.bf16_pages, dc.bf16_table, dc.codebooks, 0,
+                          dc.pos, dc.seq_len, dc.q_end, dc.rope, shp)
+    shp.rope_max_len = dc.rope_max_len
+    shp.d = 64
+    with pytest.raises((lvq.LvqError, ValueError)):
+        lvq.lvq_rows_attn(_dev(q), dc.page_table, dc.index_pages, dc.bf16_pages, dc.bf16_table, dc.codebooks, 0,
+                          dc.pos, dc.seq_len, dc.q_end, dc.rope, shp)
