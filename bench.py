@@ -408,6 +408,109 @@ def manager_bench(torch, lvq, inp, n_tokens=64):
     return res
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def _event_time(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def rows_bench(torch, lvq, inp, nq=512):
+    """Multi-row attention at the model shape.
+    prefill: nq new tokens of sequence 0 over its 32768-token coded prefix (layer 0, loop
+      step 1, 16 heads), causal within the chunk; flops 4 d per (query, visible key) per
+      head on fp32 matrix cores.  Context: the same attention in bf16 with torch matmuls on
+      dense K/V (not the path).
+    gqa: decode over 8 x 32768 tokens with 4 KV heads x 4 query heads: the multi-row kernel
+      against the decode kernel on the same cache."""
+    dev = torch.device("cuda:0")
+    Ly = inp["layers"][0]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    res = {}
+    # ---- prefill chunk
+    rope = lvq.lvq_rope_tables(L + nq + 1, D, 10000.0, device=dev)
+    q = torch.randn((1, nq, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    kn = torch.randn((1, nq, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    vn = torch.randn((1, nq, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    one = lambda v: torch.full((1,), v, dtype=torch.int32, device=dev)
+    shp = lvq.make_rows_shape(1, nq, H, H, D, T, TC, G, N_SINK, inp["pt"].shape[1], inp["bf16_row"], inp["pool"],
+                              inp["bf16_row"] * B, L, L + nq + 1)
+    ws = torch.empty(lvq.lvq_rows_attn_workspace_bytes(shp), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, nq, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, nq, H), dtype=torch.float32, device=dev)
+    pt0, bt0, pl, qe0 = inp["pt"][0:1].contiguous(), inp["bt"][0:1].contiguous(), one(L), one(inp["q_end"])
+    run = lambda: lvq.lvq_rows_attn(q, pt0, Ly["ip"], Ly["bp"], bt0, Ly["cb"], 1, pl, pl, qe0, rope, shp,
+                                    k_new=kn, v_new=vn, out=out, lse=lse, ws=ws)
+    sec = _event_time(torch, run, 10)
+    pairs = nq * L + nq * (nq + 1) // 2
+    flops = 4.0 * D * pairs * H
+    # context: dense bf16 attention over the same lengths with torch matmuls (contiguous operands)
+    Kd = torch.randn((H, L + nq, D), generator=gen, device=dev).to(torch.bfloat16)
+    KdT = Kd.transpose(1, 2).contiguous()
+    Vd = torch.randn((H, L + nq, D), generator=gen, device=dev).to(torch.bfloat16)
+    Qd = q[0].transpose(0, 1).contiguous()                  # [H][nq][D]
+    mask = torch.ones((nq, L + nq), dtype=torch.bool, device=dev).tril(L)
+
+    def dense():
+        sc = torch.matmul(Qd, KdT).float() * (D ** -0.5)
+        sc.masked_fill_(~mask, float("-inf"))
+        return torch.matmul(torch.softmax(sc, dim=-1).to(torch.bfloat16), Vd)
+
+    dsec = _event_time(torch, dense, 5)
+    del Kd, KdT, Vd
+    res["prefill_chunk"] = {
+        "workload": f"{nq} new tokens over a {L}-token coded prefix, 16 heads, d={D}, Tc={TC}, G={G}, one (layer, step)",
+        "us": round(sec * 1e6, 1), "tokens_per_s": round(nq / sec, 1),
+        "tflops": round(flops / sec / 1e12, 2), "fp32_mfma_peak": FP32_MFMA_PEAK_TFLOPS,
+        "frac_fp32_mfma": round(flops / sec / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        "dense_bf16_torch_us": round(dsec * 1e6, 1)}
+    # ---- GQA decode: 16 query heads over 4, 2 or 1 KV heads
+    c = G // TC
+    ng = D // c
+    n_coded = inp["q_end"] // 8
+    pool = B * n_coded
+    nbf = B * inp["bf16_row"]
+    Hq = 16
+    full = lambda v: torch.full((B,), v, dtype=torch.int32, device=dev)
+    posg, qeg = full(L), full(inp["q_end"])
+    pt = torch.full((B, L // 8), -1, dtype=torch.int32, device=dev)
+    pt[:, :n_coded] = torch.randperm(pool, generator=gen, device=dev).to(torch.int32).view(B, n_coded)
+    qg = torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    res["gqa_decode"] = {"workload": f"B={B}, L={L}, {Hq} query heads over Hk KV heads, d={D}, Tc={TC}, G={G}, "
+                                     f"one (layer, step)"}
+    for Hk in (4, 2, 1):
+        ip = torch.randint(0, 256, (pool, T // TC, Hk, 2, 8, ng), generator=gen, device=dev, dtype=torch.uint8)
+        bp = torch.randn((nbf, T, Hk, 2, 8, D), generator=gen, device=dev).to(torch.bfloat16)
+        cb = torch.randn((T // TC, 2, Hk, ng, TC, 256, c), generator=gen, device=dev).to(torch.bfloat16)
+        dshp = lvq.make_shape(B, Hk, Hq, D, T, TC, G, N_SINK, L // 8, inp["bf16_row"], pool, nbf, L, L + 1)
+        dws = torch.empty(lvq.lvq_decode_attn_workspace_bytes(dshp), dtype=torch.uint8, device=dev)
+        o1 = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        l1 = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        dec = lambda: lvq.lvq_decode_attn(qg, pt, ip, bp, inp["bt"], cb, 2, posg, posg, qeg, inp["rope"], dshp,
+                                          out=o1, lse=l1, ws=dws)
+        rshp = lvq.make_rows_shape(B, 1, Hk, Hq, D, T, TC, G, N_SINK, L // 8, inp["bf16_row"], pool, nbf, L, L + 1)
+        rws = torch.empty(lvq.lvq_rows_attn_workspace_bytes(rshp), dtype=torch.uint8, device=dev)
+        o2 = torch.empty((B, 1, Hq, D), dtype=torch.float32, device=dev)
+        l2 = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
+        q4 = qg.view(B, 1, Hq, D)
+        rows = lambda: lvq.lvq_rows_attn(q4, pt, ip, bp, inp["bt"], cb, 2, posg, posg, qeg, inp["rope"], rshp,
+                                         out=o2, lse=l2, ws=rws)
+        ds, rs = _event_time(torch, dec, 20), _event_time(torch, rows, 20)
+        res["gqa_decode"][f"g{Hq // Hk}"] = {
+            "rows_us": round(rs * 1e6, 1), "decode_kernel_us": round(ds * 1e6, 1), "speedup": round(ds / rs, 2),
+            "max_abs_diff_between_kernels": float((o1 - o2[:, 0]).abs().max())}
+    return res
+
+
 def encode_bench(torch, lvq, synth, inp):
     """Prefill encode of 32768 tokens x 16 heads x d=128 x 4 loop steps, K and V, for
     (Tc, G) = (4, 32) and (2, 16)."""
@@ -529,6 +632,10 @@ def main():
         "workload": f"one layer, K and V: {n_books} books of 256 codewords, {N_BOOK_SAMPLES} samples "
                     f"each, k-means++ + {N_LLOYD} Lloyd iterations (Tc={TC}, G={G})",
         "ms": round(inp["build_s"] * 1e3, 2), "books_per_s": round(n_books / inp["build_s"], 1)}
+    try:
+        res.update(rows_bench(torch, lvq, inp))
+    except Exception as e:  # report, never hide the headline
+        res["prefill_chunk"] = {"error": repr(e)}
     try:
         res["cache_manager"] = manager_bench(torch, lvq, inp)
     except Exception as e:  # report, never hide the headline

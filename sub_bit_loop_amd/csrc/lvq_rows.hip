@@ -38,9 +38,13 @@ constexpr int kKeys = 16;       // keys per tile (the RoPE table's tile)
 constexpr float kRescaleR = 8.0f;
 constexpr int kD = 128;         // head dim compiled
 
+constexpr int kPtR = 256;       // page ids staged in LDS per wave at a time
+constexpr int kErow = 4 * 36;   // tile-phase row: 4 quarters of 16 pairs, padded to 36 floats
+
 constexpr size_t rows_lds_bytes() {
-  // K and V slices (float16) + per wave a 16 x 16 probability tile
-  return (size_t)2 * kCodes * kD * 2 + (size_t)kRW * kKeys * kRows * 4;
+  // K and V slices (float16) + per wave: a 16 x 16 probability tile, a tile-phase row,
+  // a batch of page ids
+  return (size_t)2 * kCodes * kD * 2 + (size_t)kRW * (kKeys * kRows + kErow + kPtR) * 4;
 }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -82,6 +86,8 @@ void rows_kernel(RowsArgs a, int n_cg) {
   _Float16* kl = (_Float16*)smem;
   _Float16* vl = kl + (size_t)kCodes * D;
   float* ptile_all = (float*)(vl + (size_t)kCodes * D);
+  float* erow_all = ptile_all + kRW * kKeys * kRows;
+  int* ptl_all = (int*)(erow_all + kRW * kErow);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -191,16 +197,11 @@ void rows_kernel(RowsArgs a, int n_cg) {
       }
     }
   };
-  // One tile of 16 rotated keys against the 16 rows.
-  //  kf: this lane's 32 rotated key values (pairs of quarter kq, then partners);
-  //  vraw[s2][0..7]: chunk j of the value of key 4 s2 + kq;
+  // Masks, online softmax and the transpose of the probabilities into the A layout of
+  // the value MFMAs: returns pa[s2] = P[row j][key 4 s2 + kq].
   //  kok: the key of lane column j exists; causal_base >= 0: new-key tile whose key
   //  i' = causal_base + j is visible to rows with query index >= i'.
-  auto tile = [&](const float (&kf)[32], const float (&vraw)[4][8], bool kok, int causal_base) {
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 32; ++s) S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], kf[s], S, 0, 0, 0);
-    // masks: the key of lane column j against the 4 rows this lane holds
+  auto softmax_step = [&](const f32x4& S, bool kok, int causal_base, float (&pa)[4]) {
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -226,17 +227,24 @@ void rows_kernel(RowsArgs a, int n_cg) {
       P[r] = sv[r] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m[r]);
       lp[r] += P[r];
     }
-    // P[row][key] -> A layout: lane (row j, key quarter kq) takes keys 4 s2 + kq
     *(f32x4*)(ptile + j * kRows + 4 * kq) = P;          // [key][row]
     asm volatile("" ::: "memory");
-    float pa[4];
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) pa[s2] = ptile[(4 * s2 + kq) * kRows + j];
     asm volatile("" ::: "memory");
+  };
+  // A tile of 16 rotated keys (kf: this lane's 32 values, pairs of quarter kq then the
+  // partners) and values (vraw[s2]: chunk j of key 4 s2 + kq) against the 16 rows.
+  auto tile = [&](const float (&kf)[32], const float (&vraw)[4][8], bool kok, int causal_base) {
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c8 = 0; c8 < 8; ++c8)
+    for (int s = 0; s < 32; ++s) S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], kf[s], S, 0, 0, 0);
+    float pa[4];
+    softmax_step(S, kok, causal_base, pa);
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], vraw[s2][c8], O[c8], 0, 0, 0);
+    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8) O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], vraw[s2][c8], O[c8], 0, 0, 0);
   };
 
   // ---- virtual tiles: bf16 sink, recent window, new keys
@@ -312,40 +320,104 @@ void rows_kernel(RowsArgs a, int n_cg) {
     tile(kf, vraw, kok, causal);
   }
 
-  // ---- coded tiles: pages [P_lo, P_hi), two pages per tile
-  for (int P0 = P_lo; P0 < P_hi; P0 += 2) {
-    const int pbase = 8 * P0;
-    float kf[32], vraw[4][8];
-    // keys: lane column j
-    const int pk = P0 + (j >> 3);
-    const int physk = pk < P_hi ? pt[pk] : -1;
-    const bool kok = physk >= 0 && physk < a.n_index_pages && pbase + j >= a.n_sink;
+  // ---- coded tiles: pages [P_lo, P_hi), two pages per tile; the index words and the
+  // tile phase of the next tile are loaded while the current one computes
+  {
+    float* erow = erow_all + wave * kErow;
+    int* ptl = ptl_all + wave * kPtR;
+    int pt_base = -kPtR;
+    auto stage_pt = [&](int P) {
+      pt_base = P;
+      int v[kPtR / 64];
+#pragma unroll
+      for (int k = 0; k < kPtR / 64; ++k) v[k] = pt[min(P + k * 64 + lane, a.max_pages - 1)];
+#pragma unroll
+      for (int k = 0; k < kPtR / 64; ++k) {
+        const int q = P + k * 64 + lane;
+        ptl[k * 64 + lane] = (q < P_hi && v[k] >= 0 && v[k] < a.n_index_pages) ? v[k] : -1;
+      }
+      asm volatile("" ::: "memory");
+    };
+    // index-word byte offsets and code shifts of this lane (key chunks 2kq, 2kq+1 share
+    // word wl, their partners word wh; value chunk j sits in word wv)
+    const int gl = (16 * kq) / C, gh = (HALF + 16 * kq) / C, gv = (8 * j) / C;
+    const int wl = gl & ~3, wh = gh & ~3, wv = gv & ~3;
+    uint32_t shk[4];
     {
-      const uint8_t* krow = head_rows + (size_t)(kok ? physk : 0) * page_bytes + (j & 7) * NG;
       const int chs[4] = {2 * kq, 2 * kq + 1, NCH / 2 + 2 * kq, NCH / 2 + 2 * kq + 1};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t code = krow[(8 * chs[u]) / C];
-        const f16x8 x = gather(kl, code, chs[u]);
+      for (int u = 0; u < 4; ++u) shk[u] = 8 * (((8 * chs[u]) / C) & 3);
+    }
+    const uint32_t shv = 8 * (gv & 3);
+    struct CIn {
+      uint32_t kwl, kwh, vw[4];
+      float2 e0;
+      int physk;
+    };
+    auto fetch = [&](int P0) -> CIn {
+      CIn in;
+      if (P0 + 2 > pt_base + kPtR) stage_pt(P0);
+      const int ph0 = P0 < P_hi ? ptl[P0 - pt_base] : -1;
+      const int ph1 = P0 + 1 < P_hi ? ptl[P0 + 1 - pt_base] : -1;
+      in.physk = (j >> 3) ? ph1 : ph0;
+      const uint8_t* kb = head_rows + (size_t)max(in.physk, 0) * page_bytes + (j & 7) * NG;
+      in.kwl = *(const uint32_t*)(kb + wl);
+      in.kwh = *(const uint32_t*)(kb + wh);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kf[(u & 1) * 8 + (u >> 1) * 16 + i] = kok ? (float)x[i] : 0.f;
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int kv = 4 * s2 + kq;
+        const int ph = (kv >> 3) ? ph1 : ph0;
+        const uint8_t* vb = head_rows + (size_t)max(ph, 0) * page_bytes + row_stride + (kv & 7) * NG;
+        in.vw[s2] = *(const uint32_t*)(vb + wv);
+      }
+      const int a_tile = min((8 * P0) / kKeys, a.rope_tiles - 1);
+      in.e0 = *(const float2*)(a.rope + (size_t)a_tile * D + 2 * lane);
+      return in;
+    };
+    auto coded_tile = [&](int P0, const CIn& in) {
+      const int pbase = 8 * P0;
+      *(float2*)(erow + 36 * (lane >> 4) + 2 * (lane & 15)) = in.e0;     // pair `lane`
+      asm volatile("" ::: "memory");
+      const bool kok = in.physk >= 0 && pbase + j >= a.n_sink;
+      f16x8 xk[4];
+      {
+        const int chs[4] = {2 * kq, 2 * kq + 1, NCH / 2 + 2 * kq, NCH / 2 + 2 * kq + 1};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          xk[u] = gather(kl, __builtin_amdgcn_ubfe(u < 2 ? in.kwl : in.kwh, shk[u], 8), chs[u]);
+      }
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const f32x4 e = *(const f32x4*)(erow + 36 * kq + 4 * s2);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int s = 2 * s2 + u;
+          const float c0 = e[2 * u], s0 = e[2 * u + 1];
+          const float c = c0 * e1c[s] - s0 * e1s[s], sn = s0 * e1c[s] + c0 * e1s[s];
+          const float lo = (float)xk[s >> 3][s & 7], hi = (float)xk[2 + (s >> 3)][s & 7];
+          S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], lo * c - hi * sn, S, 0, 0, 0);
+          S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[16 + s], lo * sn + hi * c, S, 0, 0, 0);
+        }
+      }
+      float pa[4];
+      softmax_step(S, kok, -1, pa);
+      // invalid keys have P = 0 and finite codewords, so their values need no mask
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const f16x8 x = gather(vl, __builtin_amdgcn_ubfe(in.vw[s2], shv, 8), j);
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], (float)x[c8], O[c8], 0, 0, 0);
+      }
+    };
+    if (P_lo < P_hi) {
+      CIn cur = fetch(P_lo);
+      for (int P0 = P_lo; P0 < P_hi; P0 += 2) {
+        const CIn nxt = fetch(P0 + 2);
+        coded_tile(P0, cur);
+        cur = nxt;
       }
     }
-    // values: keys 4 s2 + kq, chunk j
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const int kv = 4 * s2 + kq;
-      const int pv = P0 + (kv >> 3);
-      const int physv = pv < P_hi ? pt[pv] : -1;
-      const bool vok = physv >= 0 && physv < a.n_index_pages && pbase + kv >= a.n_sink;
-      const uint8_t* vrow = head_rows + (size_t)(vok ? physv : 0) * page_bytes + row_stride + (kv & 7) * NG;
-      const uint32_t code = vrow[(8 * j) / C];
-      const f16x8 x = gather(vl, code, j);
-#pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8) vraw[s2][c8] = vok ? (float)x[c8] : 0.f;
-    }
-    rotate_aligned(pbase, kf);
-    tile(kf, vraw, kok, -1);
   }
 
   // ---- partial records of the 4 rows this lane holds
