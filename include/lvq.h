@@ -223,7 +223,10 @@ size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp);
  *   lse:         float32 [B][Hq] or NULL: natural log-sum-exp of the scaled scores.
  *   ws:          workspace of at least lvq_decode_attn_workspace_bytes(shp) bytes.
  * Each call overwrites the workspace; concurrent calls need distinct workspaces.
- * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.
+ * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.  With 8 or more
+ * query heads per KV head at d = 128 the call runs on the multi-row kernel (see
+ * lvq_rows_attn), which shares each key's reconstruction among those heads; the
+ * workspace size accounts for it.
  */
 int lvq_decode_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
                     const uint16_t* bf16_pages, const int32_t* bf16_table,

@@ -104,72 +104,6 @@ int check_attn(const void* q, const void* page_table, const void* index_pages,
   return LVQ_OK;
 }
 
-size_t workspace_bytes(const lvq_attn_shape& s) {
-  const SplitPlan p = plan_splits(s);
-  return (size_t)s.B * s.Hq * p.n_chunks * (s.d + 2) * sizeof(float);
-}
-
-int run_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
-             const uint16_t* bf16_pages, const int32_t* bf16_table, const uint16_t* codebooks,
-             int t, const int32_t* pos, const int32_t* seq_len, const int32_t* q_end,
-             const float* rope_tab, const lvq_attn_shape* shp, float* out, float* lse,
-             float* scores, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos,
-                      seq_len, q_end, rope_tab, shp, out);
-  if (st) return st;
-  const lvq_attn_shape& s = *shp;
-  const size_t need = workspace_bytes(s);
-  if (!ws || ws_bytes < need)
-    return fail(LVQ_ENOSPC, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
-  const SplitPlan p = plan_splits(s);
-  lvq::AttnArgs a{};
-  a.q = q;
-  a.page_table = page_table;
-  a.index_pages = index_pages;
-  a.bf16_pages = bf16_pages;
-  a.bf16_table = bf16_table;
-  a.codebooks = codebooks;
-  a.pos = pos;
-  a.seq_len = seq_len;
-  a.q_end = q_end;
-  a.rope = rope_tab;
-  a.part = (float*)ws;
-  a.out = out;
-  a.lse = lse;
-  a.scores = scores;
-  a.t = t;
-  a.B = s.B;
-  a.H = s.H;
-  a.Hq = s.Hq;
-  a.d = s.d;
-  a.T = s.T;
-  a.Tc = s.Tc;
-  a.G = s.G;
-  a.n_sink = s.n_sink;
-  a.max_pages = s.max_pages;
-  a.bf16_row = s.bf16_row;
-  a.n_index_pages = s.n_index_pages;
-  a.n_bf16_pages = s.n_bf16_pages;
-  a.max_seq_len = s.max_seq_len;
-  a.rope_tiles = (s.rope_max_len + lvq::rope_tile() - 1) / lvq::rope_tile();
-  a.n_chunks = p.n_chunks;
-  a.chunk_pages = p.chunk_pages;
-  const float scale = s.scale > 0.f ? s.scale : 1.0f / sqrtf((float)s.d);
-  a.scale_log2e = scale * 1.4426950408889634f;
-  return device_status(lvq::launch_attn(a, (hipStream_t)stream), "lvq_decode_attn launch");
-}
-
-int check_encode_common(const void* kv, const void* codebooks, int T, int Tc, int G, int N,
-                        int H, int d) {
-  if (!kv || !codebooks) return fail(LVQ_EINVAL, "null pointer argument");
-  int st = check_code_shape(T, Tc, G, d);
-  if (st) return st;
-  if (N < 0 || H <= 0) return fail(LVQ_EINVAL, "N=%d must be >= 0 and H=%d > 0", N, H);
-  if (!lvq::encode_supported(G, G / Tc, d))
-    return fail(LVQ_EUNSUPPORTED, "encode shape G=%d c=%d d=%d not compiled", G, G / Tc, d);
-  return LVQ_OK;
-}
-
 // ------------------------------------------------------------------ multi-row attention
 struct RowsPlan {
   int n_rb, n_chunks, chunk_pages;
@@ -230,6 +164,98 @@ int check_rows(const void* q, const void* k_new, const void* v_new, const void* 
 size_t rows_workspace(const lvq_rows_shape& s) {
   const RowsPlan p = plan_rows(s);
   return (size_t)s.B * s.NQ * s.Hq * p.n_chunks * (s.d + 2) * sizeof(float);
+}
+
+// Decode with many query heads per KV head runs on the multi-row kernel: at 8 or more
+// heads per KV head it is the faster of the two (one key rebuild for all the heads).
+constexpr int kRowsMinGroup = 8;
+
+bool decode_on_rows(const lvq_attn_shape& s) {
+  return s.Hq / s.H >= kRowsMinGroup && lvq::rows_supported(s.d, s.G / s.Tc);
+}
+
+lvq_rows_shape rows_shape_of(const lvq_attn_shape& s) {
+  lvq_rows_shape r{};
+  r.B = s.B; r.NQ = 1; r.H = s.H; r.Hq = s.Hq; r.d = s.d; r.T = s.T; r.Tc = s.Tc; r.G = s.G;
+  r.n_sink = s.n_sink; r.max_pages = s.max_pages; r.bf16_row = s.bf16_row;
+  r.n_index_pages = s.n_index_pages; r.n_bf16_pages = s.n_bf16_pages;
+  r.max_prefix = s.max_seq_len; r.rope_max_len = s.rope_max_len; r.n_splits = s.n_splits; r.scale = s.scale;
+  return r;
+}
+
+size_t workspace_bytes(const lvq_attn_shape& s) {
+  const SplitPlan p = plan_splits(s);
+  const size_t dec = (size_t)s.B * s.Hq * p.n_chunks * (s.d + 2) * sizeof(float);
+  if (!decode_on_rows(s)) return dec;
+  const size_t rows = rows_workspace(rows_shape_of(s));
+  return rows > dec ? rows : dec;
+}
+
+int run_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
+             const uint16_t* bf16_pages, const int32_t* bf16_table, const uint16_t* codebooks,
+             int t, const int32_t* pos, const int32_t* seq_len, const int32_t* q_end,
+             const float* rope_tab, const lvq_attn_shape* shp, float* out, float* lse,
+             float* scores, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos,
+                      seq_len, q_end, rope_tab, shp, out);
+  if (st) return st;
+  const lvq_attn_shape& s = *shp;
+  const size_t need = workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(LVQ_ENOSPC, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  if (!scores && decode_on_rows(s)) {
+    // the same attention with the query heads of a KV head as the rows (NQ = 1, no chunk)
+    const lvq_rows_shape rs = rows_shape_of(s);
+    return lvq_rows_attn(q, nullptr, nullptr, page_table, index_pages, bf16_pages, bf16_table, codebooks, t,
+                         pos, seq_len, q_end, rope_tab, &rs, out, lse, ws, ws_bytes, stream);
+  }
+  const SplitPlan p = plan_splits(s);
+  lvq::AttnArgs a{};
+  a.q = q;
+  a.page_table = page_table;
+  a.index_pages = index_pages;
+  a.bf16_pages = bf16_pages;
+  a.bf16_table = bf16_table;
+  a.codebooks = codebooks;
+  a.pos = pos;
+  a.seq_len = seq_len;
+  a.q_end = q_end;
+  a.rope = rope_tab;
+  a.part = (float*)ws;
+  a.out = out;
+  a.lse = lse;
+  a.scores = scores;
+  a.t = t;
+  a.B = s.B;
+  a.H = s.H;
+  a.Hq = s.Hq;
+  a.d = s.d;
+  a.T = s.T;
+  a.Tc = s.Tc;
+  a.G = s.G;
+  a.n_sink = s.n_sink;
+  a.max_pages = s.max_pages;
+  a.bf16_row = s.bf16_row;
+  a.n_index_pages = s.n_index_pages;
+  a.n_bf16_pages = s.n_bf16_pages;
+  a.max_seq_len = s.max_seq_len;
+  a.rope_tiles = (s.rope_max_len + lvq::rope_tile() - 1) / lvq::rope_tile();
+  a.n_chunks = p.n_chunks;
+  a.chunk_pages = p.chunk_pages;
+  const float scale = s.scale > 0.f ? s.scale : 1.0f / sqrtf((float)s.d);
+  a.scale_log2e = scale * 1.4426950408889634f;
+  return device_status(lvq::launch_attn(a, (hipStream_t)stream), "lvq_decode_attn launch");
+}
+
+int check_encode_common(const void* kv, const void* codebooks, int T, int Tc, int G, int N,
+                        int H, int d) {
+  if (!kv || !codebooks) return fail(LVQ_EINVAL, "null pointer argument");
+  int st = check_code_shape(T, Tc, G, d);
+  if (st) return st;
+  if (N < 0 || H <= 0) return fail(LVQ_EINVAL, "N=%d must be >= 0 and H=%d > 0", N, H);
+  if (!lvq::encode_supported(G, G / Tc, d))
+    return fail(LVQ_EUNSUPPORTED, "encode shape G=%d c=%d d=%d not compiled", G, G / Tc, d);
+  return LVQ_OK;
 }
 
 int cache_args(const lvq_cache* c, lvq::CacheArgs& a) {

@@ -192,3 +192,17 @@ def test_rows_rejects_bad_arguments():
     with pytest.raises((lvq.LvqError, ValueError)):
         lvq.lvq_rows_attn(_dev(q), dc.page_table, dc.index_pages, dc.bf16_pages, dc.bf16_table, dc.codebooks, 0,
                           dc.pos, dc.seq_len, dc.q_end, dc.rope, shp)
+
+
+def test_decode_attn_routes_wide_groups_to_the_rows_kernel():
+    """lvq_decode_attn with 8 query heads per KV head (d = 128) runs on the multi-row kernel;
+    the result is the oracle's and the workspace query covers it."""
+    from gpu_helpers import gpu_attn
+    print("\ncase decode attn, 8 query heads per KV head", flush=True)
+    cache = build_cache(50, 2, [77, 640], 2, 128, 4, 2, 32, 4, 64, Hq=16, books="random")
+    dc = to_dev(cache)
+    out, lse = gpu_attn(dc, 3)
+    ro, rl = cache.oracle_attn(3)
+    ok, mabs, mrel = attn_close(out.cpu().numpy(), ro)
+    assert ok, f"max-abs {mabs:.3e}"
+    assert float(np.abs(lse.cpu().numpy() - rl).max()) <= 1e-4
