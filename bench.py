@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="coded splits per (b, head); 0 = automatic")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-encode", action="store_true", help="skip the encoder measurement")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the decode-attention measurement (for counter runs): no HBM probe, "
+                         "multi-row, cache-manager or encoder legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench "
@@ -187,7 +190,7 @@ def pmc_summary(fetch_dir, write_dir):
     print("Commands (repository root $REPO on the GPU host):\n")
     for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         print(f"    cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv "
-              f"-d {d} -o bench -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --no-encode")
+              f"-d {d} -o bench -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --headline-only")
     print(f"    python3 $REPO/bench.py --pmc-summary {fetch_dir} {write_dir}\n")
     print(f"source_sha256: {attn_source_hash()}")
     print(f"calibration_copy_bytes: {CALIB_BYTES}")
@@ -613,7 +616,7 @@ def main():
     achieved_gbs = algo / call_avg / 1e9
     log(f"step {step_s * 1e3:.3f} ms, call {call_avg * 1e6:.1f} us, {achieved_gbs:.0f} GB/s algorithmic")
     traffic = recorded_traffic()
-    probe = hbm_probe(torch)
+    probe = None if args.headline_only else hbm_probe(torch)
     pc = sorted(per_call)
     pct = {f"p{q}": round(pc[min(len(pc) - 1, int(q / 100 * len(pc)))] * 1e6, 2) for q in (10, 50, 90)}
     roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -622,7 +625,8 @@ def main():
             "kernel": "lvq_decode_attn call: attn_kernel<128,8> + merge_kernel, one (layer, loop step)",
             "algorithmic_bytes_per_call": algo, "avg_call_us": round(call_avg * 1e6, 2),
             "call_us_percentiles": pct,
-            "attainable": probe, "frac_of_attainable_read": round(achieved_gbs / probe["read_gbs"], 4)}
+            "attainable": probe,
+            "frac_of_attainable_read": None if probe is None else round(achieved_gbs / probe["read_gbs"], 4)}
     res = {
         "metric": METRIC, "value": value, "unit": "KV token-steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
@@ -639,15 +643,16 @@ def main():
         "workload": f"one layer, K and V: {n_books} books of 256 codewords, {N_BOOK_SAMPLES} samples "
                     f"each, k-means++ + {N_LLOYD} Lloyd iterations (Tc={TC}, G={G})",
         "ms": round(inp["build_s"] * 1e3, 2), "books_per_s": round(n_books / inp["build_s"], 1)}
-    try:
-        res.update(rows_bench(torch, lvq, inp))
-    except Exception as e:  # report, never hide the headline
-        res["prefill_chunk"] = {"error": repr(e)}
-    try:
-        res["cache_manager"] = manager_bench(torch, lvq, inp)
-    except Exception as e:  # report, never hide the headline
-        res["cache_manager"] = {"error": repr(e)}
-    if not args.no_encode:
+    if not args.headline_only:
+        try:
+            res.update(rows_bench(torch, lvq, inp))
+        except Exception as e:  # report, never hide the headline
+            res["prefill_chunk"] = {"error": repr(e)}
+        try:
+            res["cache_manager"] = manager_bench(torch, lvq, inp)
+        except Exception as e:  # report, never hide the headline
+            res["cache_manager"] = {"error": repr(e)}
+    if not args.no_encode and not args.headline_only:
         try:
             res["encode"] = encode_bench(torch, lvq, synth, inp)
         except Exception as e:  # report, never hide the headline
