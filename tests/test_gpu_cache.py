@@ -375,3 +375,25 @@ def test_manager_decode_token_replays_in_a_hip_graph():
         for layer in range(n_layers):
             assert torch.equal(ipa[layer], ipg[layer]) and torch.equal(bpa[layer], bpg[layer])
     check_state(mb, cg, ipg, bpg)
+
+
+def test_manager_more_sequences_than_a_wave():
+    """70 sequences: the bookkeeping kernels rank allocations over two 64-lane groups; page
+    ids must still be handed out in sequence order with no page owned twice."""
+    B, n_layers = 70, 1
+    T, H, d, Tc, G, n_sink, n_recent = 4, 1, 64, 4, 32, 4, 8
+    rng = np.random.default_rng(74)
+    lengths = [int(x) for x in rng.integers(1, 40, B)]
+    lengths[5] = 0                                     # an empty slot stays empty
+    print(f"\ncase cache manager B={B}", flush=True)
+    m = Model(74, n_layers, B, lengths, T, H, d, Tc, G, n_sink, n_recent)
+    cache, ips, bps, cbs = _setup(m, lengths, n_layers, max_pages=16, n_index=600, n_bf16=600)
+    check_state(m, cache, ips, bps)
+    # the prefill took coded pages in sequence order, lowest ids first
+    pt = cache.page_table.cpu().numpy()
+    first = [int(pt[b, 0]) for b in range(B) if m.qe[b] > 0]
+    assert first == sorted(first)
+    for _ in range(20):
+        _decode_token(m, cache, ips, bps, cbs)
+    check_state(m, cache, ips, bps)
+    assert m.L[5] == 0

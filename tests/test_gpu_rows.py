@@ -206,3 +206,17 @@ def test_decode_attn_routes_wide_groups_to_the_rows_kernel():
     ok, mabs, mrel = attn_close(out.cpu().numpy(), ro)
     assert ok, f"max-abs {mabs:.3e}"
     assert float(np.abs(lse.cpu().numpy() - rl).max()) <= 1e-4
+
+
+def test_prefill_chunk_with_an_empty_prefix_and_single_queries():
+    """prefix_len = 0 (the chunk attends only to itself) next to a one-token chunk."""
+    print("\ncase prefill chunk, empty prefix / one token", flush=True)
+    for cfg, lengths, NQ in ((51, [0, 45], 23), (52, [33], 1)):
+        cache = build_cache(cfg, len(lengths), [max(L, 1) for L in lengths], 2, 128, 4, 4, 32, 4, 16, Hq=2,
+                            books="random")
+        # an empty prefix: zero the sequence's length and coded run (its pages are simply unused)
+        cache.seq_len = np.array(lengths, np.int32)
+        cache.q_end = np.array([orc.prefill_boundary(L, 16) for L in lengths], np.int32)
+        dc = to_dev(cache, max_seq_len=max(lengths) + NQ)
+        ck, cv, q = _chunk(cfg, len(lengths), 4, NQ, 2, 128, 2)
+        compare(gpu_rows(dc, cache, q, 0, ck, cv), oracle_rows(cache, q, 0, ck, cv), f"cfg={cfg}")
