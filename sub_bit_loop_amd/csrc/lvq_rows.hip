@@ -49,6 +49,9 @@ constexpr size_t rows_lds_bytes() {
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Chunk k of code x sits at slot k ^ (x mod 16) of the key slice (XOR swizzle): the 16
+// lanes that gather the same key chunk of random codes then spread over the LDS banks.
+// The value slice keeps slot = k; its gathers already read distinct chunks per lane.
 template <int C>
 __device__ __forceinline__ void stage_slice_rows(const RowsArgs& a, int beta, int kv, int h, int tau,
                                                  _Float16* dst) {
@@ -62,7 +65,8 @@ __device__ __forceinline__ void stage_slice_rows(const RowsArgs& a, int beta, in
     f16x8 o;
 #pragma unroll
     for (int q = 0; q < 8; ++q) o[q] = (_Float16)bf2f(v[q]);
-    *(f16x8*)(dst + ((size_t)x * NCH + k) * 8) = o;
+    const int slot = kv == 0 ? (k ^ (x & (NCH - 1))) : k;
+    *(f16x8*)(dst + ((size_t)x * NCH + slot) * 8) = o;
   }
 }
 
@@ -172,6 +176,9 @@ void rows_kernel(RowsArgs a, int n_cg) {
 
   auto gather = [&](const _Float16* slice, uint32_t code, int ch) -> f16x8 {
     return *(const f16x8*)(slice + ((size_t)code * NCH + ch) * 8);
+  };
+  auto gather_k = [&](uint32_t code, int ch) -> f16x8 {
+    return *(const f16x8*)(kl + ((size_t)code * NCH + (ch ^ (code & (NCH - 1)))) * 8);
   };
   // One tile: keys at positions pbase + 0..15 (pbase a multiple of 16).
   //  kf: this lane's 32 raw key values (pairs of quarter kq, then partners), float32;
@@ -384,7 +391,7 @@ void rows_kernel(RowsArgs a, int n_cg) {
         const int chs[4] = {2 * kq, 2 * kq + 1, NCH / 2 + 2 * kq, NCH / 2 + 2 * kq + 1};
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          xk[u] = gather(kl, __builtin_amdgcn_ubfe(u < 2 ? in.kwl : in.kwh, shk[u], 8), chs[u]);
+          xk[u] = gather_k(__builtin_amdgcn_ubfe(u < 2 ? in.kwl : in.kwh, shk[u], 8), chs[u]);
       }
       f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
