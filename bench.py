@@ -521,6 +521,82 @@ def rows_bench(torch, lvq, inp, nq=512):
     return res
 
 
+def decode_loop_bench(torch, lvq, inp, n_tokens=24):
+    """The whole decode loop as the product runs it, one token per replay of a captured HIP
+    graph: the cache manager (begin, end, commit), the append of each (loop step, layer)'s
+    new K/V, the 96 attention calls over the managed tables, and the re-encode of the pages
+    that fall due, in all 24 layers, for B=8 sequences from 32768 tokens.  Page ids are
+    handed out from a shuffled free list; codes and bf16 tokens are random."""
+    dev = torch.device("cuda:0")
+    nl = len(inp["layers"])
+    c = G // TC
+    nblk, ng = T // TC, D // c
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9001)
+    max_pages = (L + 2 * n_tokens) // 8 + 4
+    n_index = B * max_pages
+    n_bf16 = B * 12
+    cache = lvq.PagedCache(B, max_pages, N_SINK, N_RECENT, n_index, n_bf16)
+    cache.index_free.copy_(cache.index_free[torch.randperm(n_index, generator=gen, device=dev)])
+    cache.prefill(torch.full((B,), L, dtype=torch.int32, device=dev))
+    ips = [torch.randint(0, 256, (n_index, nblk, H, 2, 8, ng), generator=gen, device=dev, dtype=torch.uint8)
+           for _ in range(nl)]
+    bps = [torch.randn((n_bf16, T, H, 2, 8, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(nl)]
+    kvs = [torch.randn((2, 1, B, H, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(4)]
+    max_len = L + 2 * n_tokens + 8
+    rope = lvq.lvq_rope_tables(max_len + 1, D, 10000.0, device=dev)
+    shp = lvq.make_shape(B, H, H, D, T, TC, G, N_SINK, max_pages, cache.bf16_row, n_index, n_bf16, max_len,
+                         max_len + 1)
+    ws = torch.empty(lvq.lvq_decode_attn_workspace_bytes(shp), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    pos = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def token():
+        cache.begin_token()
+        torch.sub(cache.seq_len, 1, out=pos)
+        for t in range(T):
+            for layer in range(nl):
+                kv = kvs[(t + layer) % 4]
+                cache.append(t, kv[0], kv[1], bps[layer])
+                Ly = inp["layers"][layer]
+                lvq.lvq_decode_attn(Ly["q"][t], cache.page_table, ips[layer], bps[layer], cache.bf16_table,
+                                    Ly["cb"], t, pos, cache.seq_len, cache.q_end, rope, shp, out=out, lse=lse,
+                                    ws=ws)
+        cache.end_token()
+        for layer in range(nl):
+            lvq.lvq_reencode_pages(bps[layer], cache.re_src, cache.re_dst, inp["layers"][layer]["cb"], T, TC, G,
+                                   ips[layer])
+        cache.commit()
+
+    token()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        token()
+    graph.replay()
+    torch.cuda.synchronize()
+    L0 = int(cache.seq_len.sum().item())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_tokens):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3
+    if cache.errors():
+        raise RuntimeError(f"cache manager error bits {cache.errors()}")
+    # KV token-steps: every call attends over each sequence's current length
+    steps = sum(nl * T * (L0 + B * (i + 1)) for i in range(n_tokens))
+    return {"workload": f"B={B} sequences from about {L} tokens, {nl} layers x {T} loop steps per token, "
+                        f"{n_tokens} tokens: manager + {nl * T} appends + {nl * T} attention calls + re-encodes, "
+                        f"one HIP graph replay per token",
+            "ms_per_token": round(sec * 1e3 / n_tokens, 3), "tokens_per_s": round(B * n_tokens / sec, 1),
+            "kv_token_steps_per_s": steps / sec}
+
+
 def encode_bench(torch, lvq, synth, inp):
     """Prefill encode of 32768 tokens x 16 heads x d=128 x 4 loop steps, K and V, for
     (Tc, G) = (4, 32) and (2, 16)."""
@@ -652,6 +728,10 @@ def main():
             res["cache_manager"] = manager_bench(torch, lvq, inp)
         except Exception as e:  # report, never hide the headline
             res["cache_manager"] = {"error": repr(e)}
+        try:
+            res["decode_loop"] = decode_loop_bench(torch, lvq, inp)
+        except Exception as e:  # report, never hide the headline
+            res["decode_loop"] = {"error": repr(e)}
     if not args.no_encode and not args.headline_only:
         try:
             res["encode"] = encode_bench(torch, lvq, synth, inp)
