@@ -113,3 +113,66 @@ def test_workspace_size_covers_every_split(L):
         nbytes = _abi.lvq_decode_attn_workspace_bytes(s)
         per = B * Hq * 130 * 4           # one (m, l, o[128]) record per split
         assert nbytes % per == 0 and nbytes // per >= 1
+
+
+def test_builder_validation(L):
+    ws = FAKE
+    # a null weights pointer is fine (unweighted); the rest must be given
+    assert L.lvq_build_codebooks(NUL, FAKE, NUL, 0, 4, 2, 16, 100, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 1
+    assert L.lvq_build_codebooks(FAKE, NUL, NUL, 0, 4, 2, 16, 100, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 1
+    assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 2, 4, 2, 16, 100, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 1
+    assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 0, 4, 2, 16, 0, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 1
+    assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 0, 4, 2, 16, 8193, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 2
+    assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 0, 4, 2, 16, 100, 1, 64, 1001, FAKE, ws, 1 << 30, NUL) == 1
+    need = L.lvq_build_codebooks_workspace_bytes(4, 2, 16, 100, 1, 64)
+    # centers (2 blocks x 8 groups x 256 x 16 float64, 256-aligned) + assignments
+    assert need == 2 * 8 * 256 * 16 * 8 + 2 * 100 * 8
+    assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 0, 4, 2, 16, 100, 1, 64, 1, FAKE, ws, need - 1, NUL) == 3
+
+
+def test_cache_descriptor_validation(L):
+    from sub_bit_loop_amd import _abi
+    assert L.lvq_cache_min_bf16_row(64) == 10
+    assert L.lvq_cache_min_bf16_row(0) == 2
+    assert L.lvq_cache_min_bf16_row(5) == 3
+    ptrs = [0x1000] * 9
+
+    def desc(**kw):
+        base = dict(B=2, max_pages=16, bf16_row=10, n_sink=4, n_recent=64, n_index_pages=8, n_bf16_pages=8)
+        base.update(kw)
+        return _abi.CacheDesc(*base.values(), *ptrs)
+
+    assert L.lvq_cache_init(None, NUL) == 1
+    for bad in (dict(n_sink=9), dict(bf16_row=9), dict(B=0), dict(n_index_pages=0), dict(n_recent=-1)):
+        assert L.lvq_cache_init(ctypes.byref(desc(**bad)), NUL) == 1, bad
+    d = desc()
+    assert L.lvq_cache_prefill(ctypes.byref(d), NUL, NUL) == 1
+    assert L.lvq_cache_release(ctypes.byref(d), NUL, NUL) == 1
+    assert L.lvq_cache_store_tokens(ctypes.byref(d), 2, 0, 1, FAKE, FAKE, 4, 1, 64, FAKE, NUL) == 1   # b = B
+    assert L.lvq_cache_store_tokens(ctypes.byref(d), 0, 0, 0, FAKE, FAKE, 4, 1, 64, FAKE, NUL) == 0   # nothing
+    assert L.lvq_cache_store_tokens(ctypes.byref(d), 0, 0, 1, FAKE, FAKE, 4, 1, 60, FAKE, NUL) == 1   # d % 8
+    assert L.lvq_cache_append(ctypes.byref(d), 3, 2, FAKE, FAKE, 4, 1, 64, FAKE, NUL) == 1           # steps 3..4
+    assert L.lvq_cache_append(ctypes.byref(d), 0, 1, NUL, FAKE, 4, 1, 64, FAKE, NUL) == 1
+
+
+def test_rows_shape_validation(L):
+    from sub_bit_loop_amd import _abi
+
+    def rs(**kw):
+        base = dict(B=1, NQ=4, H=2, Hq=4, d=128, T=4, Tc=4, G=32, n_sink=4, max_pages=64, bf16_row=12,
+                    n_index_pages=100, n_bf16_pages=20, max_prefix=500, rope_max_len=504, n_splits=0)
+        base.update(kw)
+        return _abi.RowsShape(*base.values(), 0.0)
+
+    def call(s, k=FAKE, v=FAKE, ws_bytes=1 << 30):
+        return L.lvq_rows_attn(FAKE, k, v, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
+                               ctypes.byref(s), FAKE, FAKE, FAKE, ws_bytes, NUL)
+
+    assert call(rs(), k=NUL) == 1                       # k_new without v_new
+    assert call(rs(Hq=3)) == 1
+    assert call(rs(rope_max_len=503)) == 1              # below max_prefix + NQ
+    assert call(rs(max_pages=62)) == 1                  # 62 pages hold fewer than 500 tokens
+    assert call(rs(d=64, G=16, Tc=2)) == 2              # multi-row kernel compiled for d = 128 only
+    need = L.lvq_rows_attn_workspace_bytes(ctypes.byref(rs()))
+    assert need > 0 and need % (4 * 130) == 0
+    assert call(rs(), ws_bytes=need - 1) == 3

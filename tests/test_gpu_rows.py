@@ -154,15 +154,15 @@ def test_rows_split_count_does_not_change_the_result():
 
 
 def test_prefill_chunk_at_32k_sampled():
-    """64 new tokens over a 32768-token coded prefix (Ouro-shaped head, 16 heads, MHA); the
-    oracle checks three query positions of two heads."""
-    print("\ncase prefill chunk 64 over 32K", flush=True)
-    NQ = 64
+    """512 new tokens over a 32768-token coded prefix (Ouro-shaped head, 16 heads, MHA), the
+    launch the bench times; the oracle checks three query positions of two heads."""
+    print("\ncase prefill chunk 512 over 32K", flush=True)
+    NQ = 512
     cache = build_cache_light(47, 1, [32768], 16, 128, 4, 4, 32, 4, 64)
     dc = to_dev(cache, max_seq_len=32768 + NQ)
     ck, cv, q = _chunk(47, 1, 4, NQ, 16, 128, 16)
     got = gpu_rows(dc, cache, q, 1, ck, cv)
-    ref = oracle_rows(cache, q, 1, ck, cv, queries=(0, 31, 63), pairs=[(0, 3), (0, 12)])
+    ref = oracle_rows(cache, q, 1, ck, cv, queries=(0, 255, 511), pairs=[(0, 3), (0, 12)])
     compare(got, ref, "t=1")
 
 
