@@ -54,6 +54,9 @@ def parse():
                     help="only the decode-attention measurement (for counter runs): no HBM probe, "
                          "multi-row, cache-manager or encoder legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-instructions", metavar="DIR",
+                    help="summarise a rocprofv3 --pmc run of the SQ instruction counters of this bench "
+                         "into the instruction record the bench line reports")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench "
                          "into the HBM-traffic record the bench line reports")
@@ -201,6 +204,54 @@ def pmc_summary(fetch_dir, write_dir):
     print(f"algorithmic_bytes_per_call: {algo}")
     print(f"traffic_bytes_per_call: {traffic:.0f}")
     print(f"traffic_over_algorithmic: {traffic / algo:.3f}")
+
+
+INSTR_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                          "decode_attn_ouro_b8_l32k_instructions.txt")
+INSTR_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_LDS_BANK_CONFLICT")
+SIMDS, CLOCK_GHZ, VALU_CYCLES = 256 * 4, 2.4, 4   # a wave64 VALU instruction holds a 16-lane SIMD 4 cycles
+
+
+def pmc_instructions(directory):
+    """Instruction counts per decode-attention call (attn_kernel + merge_kernel) from a
+    rocprofv3 --pmc run of SQ counters, and the VALU issue time they imply."""
+    per = {}
+    for c in INSTR_COUNTERS:
+        d = _pmc_per_dispatch(directory, c)
+        tot = 0.0
+        for key in ("attn_kernel<128, 8, false>", "merge_kernel"):
+            v = [x for k, xs in d.items() if key in k for x in xs]
+            tot += sum(v) / len(v) if v else float("nan")
+        per[c] = tot
+    valu = per["SQ_INSTS_VALU"] - per["SQ_INSTS_MFMA"]
+    bound_us = valu * VALU_CYCLES / SIMDS / (CLOCK_GHZ * 1e3)
+    print("# Instruction counts of one decode-attention call (attn_kernel<128, 8, false> + merge_kernel),")
+    print("# Ouro-1.4B-shaped 32K decode bench\n")
+    print("Command (repository root $REPO on the GPU host):\n")
+    print(f"    cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {' '.join(INSTR_COUNTERS)} --output-format csv "
+          f"-d {directory} -o bench -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu --headline-only")
+    print(f"    python3 $REPO/bench.py --pmc-instructions {directory}\n")
+    print(f"source_sha256: {attn_source_hash()}")
+    for c in INSTR_COUNTERS:
+        print(f"{c.lower()}_per_call: {per[c]:.0f}")
+    print(f"valu_instructions_per_call: {valu:.0f}")
+    print(f"valu_issue_bound_us: {bound_us:.2f}  ({SIMDS} SIMDs, {VALU_CYCLES} cycles per wave64 VALU "
+          f"instruction, {CLOCK_GHZ} GHz)")
+
+
+def recorded_instructions():
+    """VALU issue bound per call (us) from the committed record, or None if stale."""
+    try:
+        text = open(INSTR_FILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and not line.startswith(" "))
+    if fields.get("source_sha256", "").strip() != attn_source_hash():
+        return None
+    try:
+        return float(fields["valu_issue_bound_us"].split()[0])
+    except (KeyError, ValueError):
+        return None
 
 
 def recorded_traffic():
@@ -671,6 +722,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return
+    if args.pmc_instructions:
+        pmc_instructions(args.pmc_instructions)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -692,6 +746,7 @@ def main():
     achieved_gbs = algo / call_avg / 1e9
     log(f"step {step_s * 1e3:.3f} ms, call {call_avg * 1e6:.1f} us, {achieved_gbs:.0f} GB/s algorithmic")
     traffic = recorded_traffic()
+    valu_bound = recorded_instructions()
     probe = None if args.headline_only else hbm_probe(torch)
     pc = sorted(per_call)
     pct = {f"p{q}": round(pc[min(len(pc) - 1, int(q / 100 * len(pc)))] * 1e6, 2) for q in (10, 50, 90)}
@@ -701,6 +756,8 @@ def main():
             "kernel": "lvq_decode_attn call: attn_kernel<128,8> + merge_kernel, one (layer, loop step)",
             "algorithmic_bytes_per_call": algo, "avg_call_us": round(call_avg * 1e6, 2),
             "call_us_percentiles": pct,
+            "valu_issue_bound_us": valu_bound,
+            "frac_of_valu_issue_bound": None if valu_bound is None else round(valu_bound / (call_avg * 1e6), 4),
             "attainable": probe,
             "frac_of_attainable_read": None if probe is None else round(achieved_gbs / probe["read_gbs"], 4)}
     res = {
