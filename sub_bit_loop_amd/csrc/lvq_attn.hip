@@ -48,6 +48,8 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescale = 8.0f;   // lazy-max slack, log2 units
+constexpr float kNoMax = -1e30f;   // running maximum before the first valid score (finite,
+                                   // so an invalid score of -inf still gives weight 0)
 constexpr int kNW = 12;            // waves per workgroup
 constexpr int kWavesPerSimd = 3;   // occupancy the register budget is sized for
 constexpr int kBatch = 2;          // tiles per prefetch batch
@@ -65,6 +67,11 @@ constexpr size_t lds_bytes() {
 }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// 16-byte LDS read at a byte address.  The attention kernel declares no static LDS, so
+// its dynamic LDS starts at address 0 and the code-table offsets are LDS addresses.
+typedef const f16x8 __attribute__((address_space(3)))* lds_f16x8_ptr;
+__device__ __forceinline__ f16x8 lds_read16(uint32_t addr) { return *(lds_f16x8_ptr)(size_t)addr; }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -112,7 +119,7 @@ __device__ __forceinline__ void stage_slice(const AttnArgs& a, int beta, int kv,
 }
 
 // ------------------------------------------------------------------ decode attention
-template <int D, int C, bool SCORES>
+template <int D, int C, bool SCORES, bool WIDE>
 __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
   constexpr int NG = D / C;       // groups per head
@@ -176,7 +183,8 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
   // token's parity), value block v holds chunk (v + vrot) mod NV.
   const int kswap = (KPC == 2) ? (t & 1) : 0;
   const int vrot = (NV == 4) ? ((t + 2 * (qt >> 1)) & 3) : (t & (NV - 1));
-  float m = -__builtin_inff(), l = 0.f;
+  float m = kNoMax, l = 0.f;
+  float m_hi = kNoMax + kRescale;   // rescale threshold
   float o[QV];
 #pragma unroll
   for (int i = 0; i < QV; ++i) o[i] = 0.f;
@@ -202,8 +210,10 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
     const int r = t & 7;
     const size_t row_stride = (size_t)kPage * NG;
     const size_t page_bytes = (size_t)nblk * a.H * 2 * row_stride;
-    // the lane's three index words within a page, and the page base
-    const uint8_t* lane_row = a.index_pages + (((size_t)beta * a.H + h) * 2) * row_stride + r * NG;
+    // the rows of (beta, h) in page 0 (wave-uniform), and the lane's three index words
+    // as byte offsets from a page's start
+    const uint8_t* head_rows = a.index_pages + (((size_t)beta * a.H + h) * 2) * row_stride;
+    const uint32_t o_kl = r * NG + wlo, o_kh = r * NG + whi, o_v = (uint32_t)row_stride + r * NG + wv;
     // Per-lane gather constants: bit offset of the code in its index word, and the LDS
     // byte offset of the chunk (code x of chunk k sits at byte (x * NCH + k) * 16).
     constexpr int kRowShift = (NCH == 16) ? 8 : 7;   // log2(NCH * 16)
@@ -215,22 +225,31 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
     // byte of their words, with 2 (the low code in byte 0 or 1) two bytes further on.
     static_assert((HALF / C) % 4 == 0 || HALF / C == 2, "shape outside the compiled set");
     constexpr uint32_t kHighShift = ((HALF / C) % 4 == 0) ? 0 : 8 * (HALF / C);
-    uint32_t shl[KPC], offl[KPC], shv[NV], offv[NV];
+    // With 256-byte code rows (d = 128) the gather address is one byte permute: byte 0 is
+    // the chunk offset, byte 1 the code taken from its index word, byte 2 the slice base
+    // (0 for keys, 1 for values at 64 KB).  Otherwise a bit-field extract and a shift.
+    constexpr bool kPermAddr = kRowShift == 8;
+    auto code_sel = [](uint32_t sh) -> uint32_t {
+      return kPermAddr ? (0x0c020000u | ((4u + sh / 8) << 8)) : sh;
+    };
+    uint32_t sell[KPC], selh[KPC], offl[KPC], selv[NV], offv[NV];
 #pragma unroll
     for (int v = 0; v < KPC; ++v) {
       const int cl = qt * QP + 8 * (v ^ kswap);
-      shl[v] = 8 * (cl / C - wlo);
+      const uint32_t sh = 8 * (cl / C - wlo);
+      sell[v] = code_sel(sh);
+      selh[v] = code_sel(sh + kHighShift);
       offl[v] = (uint32_t)(cl / 8) * 16;
     }
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int cv = qt * QV + 8 * ((v + vrot) & (NV - 1));
-      shv[v] = 8 * (cv / C - wv);
+      selv[v] = code_sel(8 * (cv / C - wv));
       offv[v] = (uint32_t)(kCodes * D * 2) + (uint32_t)(cv / 8) * 16;   // value slices follow the keys
     }
-    auto gather = [&](uint32_t word, uint32_t sh, uint32_t off) -> f16x8 {
-      const uint32_t code = __builtin_amdgcn_ubfe(word, sh, 8);
-      return *(const f16x8*)(smem + ((code << kRowShift) | off));
+    auto gather = [&](uint32_t word, uint32_t sel, uint32_t off) -> uint32_t {
+      if constexpr (kPermAddr) return __builtin_amdgcn_perm(word, off, sel);
+      else return (__builtin_amdgcn_ubfe(word, sel, 8) << kRowShift) + off;
     };
     float* e0s = e0buf + wave * 2 * ER;
     int* ptl = ptbuf + wave * kPtBatch;
@@ -258,10 +277,18 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
       TileIn in;
       if (P0 + 1 >= pt_base + kPtBatch) stage_pt(P0);
       in.phys = P0 < P_hi ? ptl[P0 - pt_base + (t >> 3)] : -1;
-      const uint8_t* base = lane_row + (size_t)(uint32_t)max(in.phys, 0) * page_bytes;
-      in.kwl = *(const uint32_t*)(base + wlo);
-      in.kwh = *(const uint32_t*)(base + whi);
-      in.vw = *(const uint32_t*)(base + row_stride + wv);
+      if constexpr (WIDE) {
+        const uint8_t* base = head_rows + (size_t)(uint32_t)max(in.phys, 0) * page_bytes;
+        in.kwl = *(const uint32_t*)(base + o_kl);
+        in.kwh = *(const uint32_t*)(base + o_kh);
+        in.vw = *(const uint32_t*)(base + o_v);
+      } else {
+        // the pool spans under 4 GiB and 2^24 pages: 32-bit offsets from a uniform base
+        const uint32_t po = __umul24((uint32_t)max(in.phys, 0), (uint32_t)page_bytes);
+        in.kwl = *(const uint32_t*)(head_rows + (po + o_kl));
+        in.kwh = *(const uint32_t*)(head_rows + (po + o_kh));
+        in.vw = *(const uint32_t*)(head_rows + (po + o_v));
+      }
       const int tile_idx = min((8 * P0) / kTile, a.rope_tiles - 1);
       in.e0 = *(const float2*)(rope + (size_t)tile_idx * D + 2 * (lane % HALF));
       return in;
@@ -275,8 +302,8 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
       f16x8 xl[QP / 8], xh[QP / 8];
 #pragma unroll
       for (int v = 0; v < KPC; ++v) {
-        xl[v] = gather(in.kwl, shl[v], offl[v]);
-        xh[v] = gather(in.kwh, shl[v] + kHighShift, offl[v] + kHighOff);
+        xl[v] = lds_read16(gather(in.kwl, sell[v], offl[v]));
+        xh[v] = lds_read16(gather(in.kwh, selh[v], offl[v]) + kHighOff);
       }
       float s0acc = 0.f, s1acc = 0.f;
 #pragma unroll
@@ -300,20 +327,21 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
       }
       const float s = valid ? quad_sum(s0acc + s1acc) : -__builtin_inff();
       if (SCORES && valid && qt == 0) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
-      if (__any(s > m + kRescale)) {
+      if (__any(s > m_hi)) {
         const float mn = fmaxf(m, wave_max(s));
         const float f = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
         for (int i = 0; i < QV; ++i) o[i] *= f;
         l *= f;
         m = mn;
+        m_hi = mn + kRescale;
       }
-      const float w = valid ? __builtin_amdgcn_exp2f(s - m) : 0.f;
-      l += (qt == 0) ? w : 0.f;
+      const float w = __builtin_amdgcn_exp2f(s - m);   // 0 for an invalid token (s = -inf)
+      l += w;   // every lane of a token adds the same weight; folded over tokens only
       // values: output channels [qt*QV, qt*QV + QV)
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const f16x8 x = gather(in.vw, shv[v], offv[v]);
+        const f16x8 x = lds_read16(gather(in.vw, selv[v], offv[v]));
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, (float)x[i], o[8 * v + i]);
       }
@@ -367,16 +395,17 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
       }
       const float s = valid ? quad_sum(s0acc + s1acc) : -__builtin_inff();
       if (SCORES && valid && qt == 0) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
-      if (__any(s > m + kRescale)) {
+      if (__any(s > m_hi)) {
         const float mn = fmaxf(m, wave_max(s));
         const float f = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
         for (int i = 0; i < QV; ++i) o[i] *= f;
         l *= f;
         m = mn;
+        m_hi = mn + kRescale;
       }
-      const float w = valid ? __builtin_amdgcn_exp2f(s - m) : 0.f;
-      l += (qt == 0) ? w : 0.f;
+      const float w = __builtin_amdgcn_exp2f(s - m);   // 0 for an invalid token (s = -inf)
+      l += w;   // every lane of a token adds the same weight; folded over tokens only
       if (valid) {
         const uint16_t* vrow = krow + (size_t)kPage * D;
 #pragma unroll
@@ -428,7 +457,8 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
 #pragma unroll
     for (int i = 0; i < QV; ++i) o[i] += __shfl_xor(o[i], off);
   }
-  l = wave_sum(l);
+#pragma unroll
+  for (int off = 4; off < 64; off <<= 1) l += __shfl_xor(l, off);
   float* rec = a.part + (((size_t)b * a.Hq + hq) * a.n_chunks + chunk) * (D + 2);
   if (lane == 0) { rec[0] = m; rec[1] = l; }
   if (t == 0) {
@@ -502,12 +532,12 @@ __global__ void rope_kernel(int ntile, int d, double base, float* tab) {
   if (i < half) ((double*)(tab + (size_t)(ntile + kTile) * d))[i] = theta;
 }
 
-template <int D, int C, bool SCORES>
+template <int D, int C, bool SCORES, bool WIDE>
 hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   constexpr size_t lds = lds_bytes<D>();
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, C, SCORES>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, C, SCORES, WIDE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -515,7 +545,7 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   const int n_items = a.B * a.Hq;
   const int n_cg = (a.n_chunks + kNW - 1) / kNW;
   const long grid = (long)n_cg * n_items;
-  hipLaunchKernelGGL((attn_kernel<D, C, SCORES>), dim3((unsigned)grid), dim3(kNW * 64), lds, s, a,
+  hipLaunchKernelGGL((attn_kernel<D, C, SCORES, WIDE>), dim3((unsigned)grid), dim3(kNW * 64), lds, s, a,
                      a.rope, n_cg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -525,7 +555,12 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
 
 template <int D, int C>
 hipError_t launch_attn_s(const AttnArgs& a, hipStream_t s) {
-  return a.scores ? launch_attn_t<D, C, true>(a, s) : launch_attn_t<D, C, false>(a, s);
+  // 32-bit index-pool offsets when every page starts below 4 GiB and ids fit 24 bits
+  const uint64_t page_bytes = (uint64_t)(a.T / a.Tc) * a.H * 2 * kPage * (D / C);
+  const bool wide = (uint64_t)a.n_index_pages * page_bytes > 0xFFFFFFFFull || a.n_index_pages > (1 << 24) ||
+                    page_bytes >= (1u << 24);
+  if (a.scores) return wide ? launch_attn_t<D, C, true, true>(a, s) : launch_attn_t<D, C, true, false>(a, s);
+  return wide ? launch_attn_t<D, C, false, true>(a, s) : launch_attn_t<D, C, false, false>(a, s);
 }
 
 }  // namespace
