@@ -5,6 +5,8 @@ float32 output; lse within 1e-4 absolute.  Full context lengths are run on the
 GPU in the launch configuration the benchmark uses; the oracle checks sampled
 (sequence, head) pairs.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -88,6 +90,30 @@ def test_split_counts_and_page_permutation():
     # same inputs twice: identical bits
     o3, _ = gpu_attn(dc, t, n_splits=7)
     np.testing.assert_array_equal(o3.cpu().numpy(), o2.cpu().numpy())
+
+
+def test_index_pool_beyond_4gib():
+    """An index pool over 4 GiB takes the kernel's 64-bit page addressing.  The same pages
+    moved to the top of such a pool give the same bits as the compact pool (page
+    placement invariance), so the 32-bit and 64-bit address paths agree."""
+    print("\ncase index pool over 4 GiB", flush=True)
+    cache = build_cache(39, 1, [2000], 2, 128, 4, 4, 32, 4, 64, books="random", index="random")
+    dc = to_dev(cache)
+    ref, ref_lse = gpu_attn(dc, 1)
+    pool = dc.index_pages
+    page_bytes = pool[0].numel()
+    n_big = (4 << 30) // page_bytes + 4096
+    assert n_big * page_bytes > 1 << 32
+    big = torch.empty((n_big,) + tuple(pool.shape[1:]), dtype=pool.dtype, device=pool.device)
+    off = n_big - pool.shape[0]
+    big[off:] = pool
+    pt = dc.page_table.clone()
+    pt[pt >= 0] += off
+    got, got_lse = gpu_attn(dataclasses.replace(dc, index_pages=big, page_table=pt), 1)
+    del big
+    torch.cuda.empty_cache()
+    np.testing.assert_array_equal(got.cpu().numpy(), ref.cpu().numpy())
+    np.testing.assert_array_equal(got_lse.cpu().numpy(), ref_lse.cpu().numpy())
 
 
 def test_step_slice_locality_on_gpu():
