@@ -694,6 +694,180 @@ def encode_bench(torch, lvq, synth, inp):
     return res
 
 
+MIXED_B, MIXED_LO, MIXED_HI, MIXED_CONFIG = 64, 1024, 16384, 5
+MIXED_LAYERS = ((8, 4, 32), (1, 1, 32))   # looped layer (two loop blocks), prelude layer (c = 32)
+
+
+def mixed_bench(torch, lvq, synth, n_steps=64, warmup=3):
+    """Mixed serving decode: 64 sequences with seeded lengths U[1024, 16384], H = 16, d = 128,
+    4 sink + 64..71 recent bf16 tokens, shuffled pages.  One decode step = the looped
+    layer's 8 loop-step calls (T = 8, Tc = 4, G = 32), the prelude layer's call (T = 1,
+    Tc = 1, G = 32: c = 32, 4 groups) and the batched page re-encode of the 8 sequences
+    whose recent window reaches 72 tokens at that step (round robin; both layers, K and V,
+    one launch per layer).  Index pools hold uniform random codes (time does not depend on
+    their values); the looped pool alone is larger than twice the 256 MB Infinity Cache."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    Bm = MIXED_B
+    rl = np.random.default_rng(synth.seed_for(MIXED_CONFIG, synth.STREAM_LENGTHS))
+    lengths = synth.uniform_lengths(rl, Bm, MIXED_LO, MIXED_HI)
+    Lmax = int(lengths.max())
+    q_end = np.array([synth.prefill_q_end(int(x), N_RECENT) for x in lengths], dtype=np.int64)
+    n_coded = (q_end // 8).tolist()
+    max_pages = (Lmax + 7) // 8
+    rp = np.random.default_rng(synth.seed_for(MIXED_CONFIG, synth.STREAM_PAGES))
+    pool = int(sum(n_coded)) + Bm          # one spare page per sequence receives its re-encode
+    pt_np, pool = synth.shuffled_page_table(rp, n_coded, max_pages, pool=pool)
+    pt = torch.from_numpy(pt_np).to(dev)
+    spare = torch.from_numpy(np.setdiff1d(np.arange(pool), pt_np[pt_np >= 0]).astype(np.int32)).to(dev)
+    bf16_row = 1 + max((int(x) - int(e) + 7) // 8 for x, e in zip(lengths, q_end))
+    n_bf16 = Bm * bf16_row
+    bt = torch.arange(n_bf16, dtype=torch.int32, device=dev).view(Bm, bf16_row)
+    pos = torch.from_numpy(lengths.astype(np.int32)).to(dev)
+    seq_len = pos.clone()
+    qe = torch.from_numpy(q_end.astype(np.int32)).to(dev)
+    rope = lvq.lvq_rope_tables(Lmax + 1, D, 10000.0, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.seed_for(MIXED_CONFIG, synth.STREAM_K))
+    layers = []
+    for (T_, Tc_, G_) in MIXED_LAYERS:
+        c = G_ // Tc_
+        nblk, ng = T_ // Tc_, D // c
+        ip = torch.randint(0, 256, (pool, nblk, H, 2, 8, ng), generator=gen, dtype=torch.uint8, device=dev)
+        bp = torch.randn((n_bf16, T_, H, 2, 8, D), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+        cb = torch.randn((nblk, 2, H, ng, Tc_, 256, c), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+        q = [synth.gen_queries_torch(gen, Bm, H, D, device=dev) for _ in range(T_)]
+        shp = lvq.make_shape(Bm, H, H, D, T_, Tc_, G_, N_SINK, max_pages, bf16_row, pool, n_bf16, Lmax,
+                             Lmax + 1, 0)
+        ws = torch.empty(lvq.lvq_decode_attn_workspace_bytes(shp), dtype=torch.uint8, device=dev)
+        layers.append(dict(T=T_, Tc=Tc_, G=G_, ng=ng, ip=ip, bp=bp, cb=cb, q=q, shp=shp, ws=ws))
+    out = torch.empty((Bm, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((Bm, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(s, ev=None):
+        for li, Ly in enumerate(layers):
+            for t in range(Ly["T"]):
+                if ev is not None:
+                    ev[li][0].record()
+                lvq.lvq_decode_attn(Ly["q"][t], pt, Ly["ip"], Ly["bp"], bt, Ly["cb"], t, pos, seq_len, qe,
+                                    rope, Ly["shp"], out, lse, Ly["ws"])
+                if ev is not None:
+                    ev[li][1].record()
+        b0 = (8 * s) % Bm
+        src = bt[b0:b0 + 8, 1].contiguous()
+        dst = spare[b0:b0 + 8].contiguous()
+        for Ly in layers:
+            lvq.lvq_reencode_pages(Ly["bp"], src, dst, Ly["cb"], Ly["T"], Ly["Tc"], Ly["G"], Ly["ip"])
+
+    for w in range(warmup):
+        step(w)
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+           for _ in range(n_steps)]
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for s in range(n_steps):
+        step(s, evs[s])
+    s1.record()
+    torch.cuda.synchronize()
+    step_s = s0.elapsed_time(s1) * 1e-3 / n_steps
+    last_call = [sum(evs[s][li][0].elapsed_time(evs[s][li][1]) for s in range(n_steps)) * 1e-3 / n_steps
+                 for li in range(len(layers))]
+    sum_l = int(lengths.sum())
+    calls = sum(T_ for (T_, _, _) in MIXED_LAYERS)
+    # algorithmic bytes of one step's attention calls: index rows of the call's loop
+    # block, bf16 sink + recent tokens, the step's book slices, q/out/lse/page table
+    coded = int(sum(max(int(e) - N_SINK, 0) for e in q_end))
+    bf16_tok = int(sum(min(N_SINK, int(x)) + int(x) - int(e) for x, e in zip(lengths, q_end)))
+    small = Bm * H * D * 2 + Bm * H * (D + 1) * 4 + Bm * max_pages * 4
+    per_layer = []
+    for Ly in layers:
+        idx = coded * H * 2 * Ly["ng"]
+        per_call = idx + bf16_tok * H * 2 * D * 2 + H * 2 * 256 * D * 2 + small
+        per_layer.append(per_call)
+    algo_step = sum(Ly["T"] * b for Ly, b in zip(layers, per_layer))
+    gbs = algo_step / step_s / 1e9
+    log(f"mixed B={Bm}: step {step_s * 1e3:.3f} ms, {sum_l * calls / step_s:.3e} KV token-steps/s, "
+        f"{gbs:.0f} GB/s algorithmic ({gbs / HBM_PEAK_GBS * 100:.1f}% of peak)")
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": f"mixed serving decode: B={Bm}, L~U[{MIXED_LO},{MIXED_HI}] (sum {sum_l}), H={H}, "
+                        f"d={D}; per step 8 looped calls (T=8, Tc=4, G=32) + 1 prelude call (T=1, Tc=1, "
+                        f"G=32) + re-encode of 8 sequences' oldest recent page in both layers",
+            "steps": n_steps, "ms_per_step": round(step_s * 1e3, 4),
+            "kv_token_steps_per_s": round(sum_l * calls / step_s),
+            "algorithmic_bytes_per_step": algo_step, "achieved_gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "looped_call_us_last_t": round(last_call[0] * 1e6, 2),
+            "prelude_call_us": round(last_call[1] * 1e6, 2),
+            "looped_call_algorithmic_bytes": per_layer[0], "prelude_call_algorithmic_bytes": per_layer[1]}
+
+
+NEEDLE_L, NEEDLE_COPIES = 65536, 8
+
+
+def needle_bench(torch, lvq, synth, reps=60):
+    """One 65536-token sequence, H = 16, d = 128, T = 4, Tc = 2, G = 16, 4 sink + 64 recent:
+    the call time of lvq_decode_attn (attention + merge) rotating over 8 copies of the
+    index pool (536 MB, beyond twice the Infinity Cache)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    T_, Tc_, G_ = 4, 2, 16
+    c = G_ // Tc_
+    nblk, ng = T_ // Tc_, D // c
+    q_end = synth.prefill_q_end(NEEDLE_L, N_RECENT)
+    max_pages = NEEDLE_L // 8
+    rp = np.random.default_rng(synth.seed_for(3, synth.STREAM_PAGES))
+    pt_np, pool = synth.shuffled_page_table(rp, [q_end // 8], max_pages)
+    pt = torch.from_numpy(pt_np).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.seed_for(3, synth.STREAM_K))
+    ips = [torch.randint(0, 256, (pool, nblk, H, 2, 8, ng), generator=gen, dtype=torch.uint8, device=dev)
+           for _ in range(NEEDLE_COPIES)]
+    bf16_row = 1 + (NEEDLE_L - q_end + 7) // 8
+    bp = torch.randn((bf16_row, T_, H, 2, 8, D), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    bt = torch.arange(bf16_row, dtype=torch.int32, device=dev).view(1, bf16_row)
+    cb = torch.randn((nblk, 2, H, ng, Tc_, 256, c), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    q = synth.gen_queries_torch(gen, 1, H, D, device=dev)
+    one = torch.full((1,), NEEDLE_L, dtype=torch.int32, device=dev)
+    qe = torch.full((1,), q_end, dtype=torch.int32, device=dev)
+    rope = lvq.lvq_rope_tables(NEEDLE_L + 1, D, 10000.0, device=dev)
+    shp = lvq.make_shape(1, H, H, D, T_, Tc_, G_, N_SINK, max_pages, bf16_row, pool, bf16_row, NEEDLE_L,
+                         NEEDLE_L + 1, 0)
+    ws = torch.empty(lvq.lvq_decode_attn_workspace_bytes(shp), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, H), dtype=torch.float32, device=dev)
+
+    def call(i):
+        lvq.lvq_decode_attn(q, pt, ips[i % NEEDLE_COPIES], bp, bt, cb, 1, one, one, qe, rope, shp, out, lse, ws)
+
+    for i in range(5):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in evs)
+    med = ts[len(ts) // 2]
+    algo = (q_end - N_SINK) * H * 2 * ng + (N_SINK + NEEDLE_L - q_end) * H * 2 * D * 2 + H * 2 * 256 * D * 2 \
+        + H * D * 2 + H * (D + 1) * 4 + max_pages * 4
+    gbs = algo / med / 1e9
+    log(f"needle 64K: call {med * 1e6:.1f} us median, {gbs:.0f} GB/s algorithmic")
+    del ips
+    torch.cuda.empty_cache()
+    return {"workload": f"one sequence of {NEEDLE_L} tokens, H={H}, d={D}, T=4, Tc=2, G=16 (0.5 bit), "
+                        f"{N_SINK} sink + {N_RECENT} recent, shuffled pages, 8 pool copies rotated",
+            "call_us_p10": round(ts[len(ts) // 10] * 1e6, 2), "call_us_p50": round(med * 1e6, 2),
+            "call_us_p90": round(ts[(9 * len(ts)) // 10] * 1e6, 2),
+            "algorithmic_bytes_per_call": int(algo), "achieved_gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "kv_token_steps_per_s": round(NEEDLE_L / med)}
+
+
 def hbm_probe(torch):
     """Attainable HBM rates on this GPU: row sums of a 2 GiB float32 matrix with 4096-wide
     rows (a streaming read; the fastest of torch's reductions here) and a 2 GiB copy (read +
@@ -789,6 +963,14 @@ def main():
             res["decode_loop"] = decode_loop_bench(torch, lvq, inp)
         except Exception as e:  # report, never hide the headline
             res["decode_loop"] = {"error": repr(e)}
+        try:
+            res["needle_64k"] = needle_bench(torch, lvq, synth)
+        except Exception as e:  # report, never hide the headline
+            res["needle_64k"] = {"error": repr(e)}
+        try:
+            res["mixed_serving"] = mixed_bench(torch, lvq, synth)
+        except Exception as e:  # report, never hide the headline
+            res["mixed_serving"] = {"error": repr(e)}
     if not args.no_encode and not args.headline_only:
         try:
             res["encode"] = encode_bench(torch, lvq, synth, inp)

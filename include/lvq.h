@@ -193,9 +193,9 @@ typedef struct lvq_attn_shape {
   int32_t bf16_row;       /* row length of bf16_table */
   int32_t n_index_pages;  /* rows of index_pages (range check of page ids) */
   int32_t n_bf16_pages;   /* rows of bf16_pages */
-  int32_t max_seq_len;    /* upper bound of seq_len[b]; sizes the split grid */
+  int32_t max_seq_len;    /* upper bound of seq_len[b]; sizes the automatic split */
   int32_t rope_max_len;   /* max_len the rope table was built for; every pos and seq_len must be < it */
-  int32_t n_splits;       /* coded-token splits per (b, hq); 0 = automatic */
+  int32_t n_splits;       /* waves per query head; 0 = automatic (see lvq_decode_attn) */
   float scale;            /* softmax scale; 0 = 1/sqrt(d) */
 } lvq_attn_shape;
 
@@ -223,6 +223,12 @@ size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp);
  *   lse:         float32 [B][Hq] or NULL: natural log-sum-exp of the scaled scores.
  *   ws:          workspace of at least lvq_decode_attn_workspace_bytes(shp) bytes.
  * Each call overwrites the workspace; concurrent calls need distinct workspaces.
+ * Work split: per query head, the 16-token tiles of all sequences (coded tiles, then
+ * the bf16 sink and recent tiles, sequence by sequence) form one list that is cut
+ * into equal contiguous ranges, one per wave, whatever the mix of lengths; partial
+ * results are merged per (b, hq) by log-sum-exp.  n_splits > 0 sets the number of
+ * waves per query head (rounded up to whole workgroups of 12); 0 gives each head an
+ * equal share of the 256 compute units.
  * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.  With 8 or more
  * query heads per KV head at d = 128 the call runs on the multi-row kernel (see
  * lvq_rows_attn), which shares each key's reconstruction among those heads; the

@@ -44,34 +44,34 @@ int check_code_shape(int T, int Tc, int G, int d) {
 }
 
 struct SplitPlan {
-  int n_chunks;
-  int chunk_pages;
+  int n_waves;   // waves per query head (whole workgroups)
+  int n_rec;     // partial records per query head: n_waves + B
 };
 
-// Coded pages of a sequence are cut into chunks of whole 64-token tiles; one
-// wave works on one chunk.  Automatic sizing aims at about two waves per SIMD
-// of work (2048 chunks) while keeping a chunk at 16 tiles or more.
+constexpr int kComputeUnits = 256;   // MI355X: one resident decode workgroup per CU
+
+// Token-balanced split: every query head's work list (the 16-token tiles of all the
+// batch's sequences, coded and bf16) is cut into n_waves equal ranges, one per wave.
+// Automatic sizing gives each head an equal share of the compute units (one workgroup
+// each), but not more waves than about 4 tiles each of the largest possible work list.
+// n_splits > 0 asks for that many waves per head (rounded up to whole workgroups).
 SplitPlan plan_splits(const lvq_attn_shape& s) {
-  const int max_pages = (s.max_seq_len + lvq::kPage - 1) / lvq::kPage;
-  const int max_tiles = (max_pages + 7) / 8;
-  int n = s.n_splits;
-  if (n <= 0) {
-    const long items = (long)s.B * s.Hq;
-    n = (int)((2048 + items - 1) / items);
-    n = n < 1 ? 1 : n;
-    const int by_len = max_tiles / 16;
-    if (n > by_len) n = by_len < 1 ? 1 : by_len;
-    // whole workgroups of chunks
-    const int w = lvq::attn_waves_per_group();
-    if (n > w) n = (n + w - 1) / w * w;
+  const int w = lvq::attn_waves_per_group();
+  const int max_wph = (lvq::merge_max_records() - 1) / w;
+  int wph;
+  if (s.n_splits > 0) {
+    wph = (s.n_splits + w - 1) / w;
+  } else {
+    wph = kComputeUnits / s.Hq;
+    const long tiles_bound = (long)s.B * ((s.max_seq_len + 15) / 16 + 3);
+    const long by_work = (tiles_bound + 4L * w - 1) / (4L * w);
+    if (wph > by_work) wph = (int)by_work;
   }
-  if (n > max_tiles) n = max_tiles < 1 ? 1 : max_tiles;
-  if (n > 1023) n = 1023;                       // bound on splits per (b, query head)
-  const int tiles = (max_tiles + n - 1) / n;
+  if (wph < 1) wph = 1;
+  if (wph > max_wph) wph = max_wph;
   SplitPlan p;
-  p.chunk_pages = (tiles < 1 ? 1 : tiles) * 8;
-  p.n_chunks = (max_pages + p.chunk_pages - 1) / p.chunk_pages;
-  if (p.n_chunks < 1) p.n_chunks = 1;
+  p.n_waves = wph * w;
+  p.n_rec = p.n_waves + s.B;
   return p;
 }
 
@@ -185,7 +185,8 @@ lvq_rows_shape rows_shape_of(const lvq_attn_shape& s) {
 
 size_t workspace_bytes(const lvq_attn_shape& s) {
   const SplitPlan p = plan_splits(s);
-  const size_t dec = (size_t)s.B * s.Hq * p.n_chunks * (s.d + 2) * sizeof(float);
+  // partial records [Hq][n_rec][d + 2], then the sequences' first tiles [B + 1]
+  const size_t dec = (size_t)s.Hq * p.n_rec * (s.d + 2) * sizeof(float) + (size_t)(s.B + 1) * sizeof(int);
   if (!decode_on_rows(s)) return dec;
   const size_t rows = rows_workspace(rows_shape_of(s));
   return rows > dec ? rows : dec;
@@ -240,8 +241,9 @@ int run_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_
   a.n_bf16_pages = s.n_bf16_pages;
   a.max_seq_len = s.max_seq_len;
   a.rope_tiles = (s.rope_max_len + lvq::rope_tile() - 1) / lvq::rope_tile();
-  a.n_chunks = p.n_chunks;
-  a.chunk_pages = p.chunk_pages;
+  a.n_waves = p.n_waves;
+  a.n_rec = p.n_rec;
+  a.tile_start = (int*)((char*)ws + (size_t)s.Hq * p.n_rec * (s.d + 2) * sizeof(float));
   const float scale = s.scale > 0.f ? s.scale : 1.0f / sqrtf((float)s.d);
   a.scale_log2e = scale * 1.4426950408889634f;
   return device_status(lvq::launch_attn(a, (hipStream_t)stream), "lvq_decode_attn launch");
@@ -582,6 +584,7 @@ int lvq_rows_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
   m.Hq = s.Hq;
   m.d = s.d;
   m.n_chunks = p.n_chunks;
+  m.n_rec = p.n_chunks;
   return device_status(lvq::launch_merge(m, (hipStream_t)stream), "lvq_rows_attn merge launch");
 }
 

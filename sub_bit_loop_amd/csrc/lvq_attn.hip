@@ -52,7 +52,7 @@ constexpr float kNoMax = -1e30f;   // running maximum before the first valid sco
                                    // so an invalid score of -inf still gives weight 0)
 constexpr int kNW = 12;            // waves per workgroup
 constexpr int kWavesPerSimd = 3;   // occupancy the register budget is sized for
-constexpr int kBatch = 2;          // tiles per prefetch batch
+constexpr int kBatch = 1;          // tiles per prefetch batch
 constexpr int kTile = 16;          // positions per tile (RoPE table granularity)
 constexpr int kPtBatch = 128;      // page ids staged in LDS per wave at a time
 
@@ -63,7 +63,7 @@ constexpr int phase_buf_floats() { return 4 * (2 * (D / 8) + 4); }
 
 template <int D>
 constexpr size_t lds_bytes() {
-  return (size_t)2 * kCodes * D * 2 + (size_t)D * 4 + (size_t)kNW * (2 * phase_buf_floats<D>() * 4 + kPtBatch * 4);
+  return (size_t)2 * kCodes * D * 2 + (size_t)kNW * (2 * phase_buf_floats<D>() * 4 + kPtBatch * 4);
 }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -101,27 +101,90 @@ __device__ __forceinline__ float2 phase(const float* __restrict__ rope, int tile
 // Stage the step-tau [256][c] slices of all groups of book (beta, kv, h) into LDS as
 // float16, laid out [code][chunk][8]: chunk k of code x holds channels 8k..8k+7 of
 // code x's share.  A gather's LDS bank then depends on the chunk, not on the code.
+// The K and V slices are staged together with every 16-byte load of a thread in
+// flight before the first conversion (one memory latency, not one per load).
 template <int D, int C>
-__device__ __forceinline__ void stage_slice(const AttnArgs& a, int beta, int kv, int h, int tau,
-                                            _Float16* dst) {
+__device__ __forceinline__ void stage_slices(const AttnArgs& a, int beta, int h, int tau, _Float16* dst) {
   constexpr int NG = D / C;
   constexpr int NCH = D / 8;
-  const uint16_t* src = a.codebooks + ((((size_t)beta * 2 + kv) * a.H + h) * NG) * ((size_t)a.Tc * kCodes * C);
-  for (int e = threadIdx.x * 8; e < kCodes * D; e += kNW * 64 * 8) {
-    const int x = e / D, k = (e % D) / 8;                // destination code and chunk
-    const int g = (8 * k) / C, i = (8 * k) % C;
-    const u16x8 v = *(const u16x8*)(src + (((size_t)g * a.Tc + tau) * kCodes + x) * C + i);
-    f16x8 o;
+  constexpr int NTH = kNW * 64;
+  constexpr int PER = (kCodes * D / 8 + NTH - 1) / NTH;   // 16-byte pieces per thread and slice
+  u16x8 v[2][PER];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) o[q] = (_Float16)bf2f(v[q]);
-    *(f16x8*)(dst + ((size_t)x * NCH + k) * 8) = o;
+  for (int kv = 0; kv < 2; ++kv) {
+    const uint16_t* src = a.codebooks + ((((size_t)beta * 2 + kv) * a.H + h) * NG) * ((size_t)a.Tc * kCodes * C);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = (threadIdx.x + i * NTH) * 8;
+      if (e < kCodes * D) {
+        const int x = e / D, k = (e % D) / 8;                // destination code and chunk
+        const int g = (8 * k) / C, j = (8 * k) % C;
+        v[kv][i] = *(const u16x8*)(src + (((size_t)g * a.Tc + tau) * kCodes + x) * C + j);
+      }
+    }
+  }
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = (threadIdx.x + i * NTH) * 8;
+      if (e < kCodes * D) {
+        const int x = e / D, k = (e % D) / 8;
+        f16x8 o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = (_Float16)bf2f(v[kv][i][q]);
+        *(f16x8*)(dst + (size_t)kv * kCodes * D + ((size_t)x * NCH + k) * 8) = o;
+      }
+    }
   }
 }
 
 // ------------------------------------------------------------------ decode attention
+// Work units of sequence b in a query head's work list: one per coded tile (two pages
+// each), then kBfCost per bf16 virtual tile (the sink tile and the tiles over [r0, L)),
+// which read float32 keys and values from HBM and cost that much more than a coded tile.
+constexpr int kBfCost = 4;
+struct SeqTiles {
+  int coded;   // coded tiles (= their units)
+  int total;   // units
+};
+__device__ __forceinline__ SeqTiles seq_tiles(const AttnArgs& a, int b) {
+  const int L = max(min(a.seq_len[b], a.max_seq_len), 0);
+  const int qe = max(min(a.q_end[b] & ~7, L), 0);
+  const int ns = min(a.n_sink, L);
+  const int r0 = max(qe, a.n_sink);
+  const int vt_lo = r0 / kTile;
+  const int vt_hi = L > r0 ? (L - 1) / kTile + 1 : vt_lo;
+  const int coded = a.n_index_pages > 0 ? ((qe >> 3) + 1) >> 1 : 0;
+  return {coded, coded + kBfCost * ((ns > 0 ? 1 : 0) + (vt_hi - vt_lo))};
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    v += lane >= off ? u : 0;
+  }
+  return v;
+}
+
+// Token-balanced work split.  Every query head has the same work list: the units of
+// sequences 0..B-1 in order, total units in all.  The W waves of a head take equal
+// contiguous ranges [wg*total/W, (wg+1)*total/W) of it, crossing sequence boundaries;
+// a wave writes one partial record per sequence its range meets (empty if it takes no
+// tile there), at record wg + b of the head (distinct, since ranges and sequences are
+// both in order).
+__device__ __forceinline__ int range_lo(int wg, int total, int W) { return (int)((long)wg * total / W); }
+
 template <int D, int C, bool SCORES, bool WIDE>
 __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
-void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
+void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
   constexpr int NG = D / C;       // groups per head
   constexpr int HALF = D / 2;
   constexpr int QP = HALF / 4;    // channel pairs per lane (score)
@@ -132,50 +195,66 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
   constexpr int NV = QV / 8;      // value chunks per lane
   static_assert(NG >= 4 && QP % 8 == 0 && QV % 8 == 0, "shape outside the compiled set");
   extern __shared__ __align__(16) unsigned char smem[];
-  _Float16* kl = (_Float16*)smem;                          // [NG][256][C]
-  _Float16* vl = kl + (size_t)kCodes * D;                  // [NG][256][C]
-  float* qs = (float*)(vl + (size_t)kCodes * D);           // [D] rotated query
+  _Float16* kl = (_Float16*)smem;                          // [256][D/8][8]
+  _Float16* vl = kl + (size_t)kCodes * D;                  // [256][D/8][8]
   constexpr int ER = phase_buf_floats<D>();
-  float* e0buf = qs + D;                                   // [kNW][2][ER]
+  static_assert(2 * ER >= D, "the phase buffers also hold the rotated query");
+  float* e0buf = (float*)(vl + (size_t)kCodes * D);        // [kNW][2][ER]
   int* ptbuf = (int*)(e0buf + kNW * 2 * ER);               // [kNW][kPtBatch]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  int bid = blockIdx.x;
-  const int cg = bid % n_cg; bid /= n_cg;
-  const int hq = bid % a.Hq; bid /= a.Hq;
-  const int b = bid;
+  // block = kw * Hq + hq: with Hq a multiple of 8 a head's workgroups share one XCD (and its
+  // L2 copy of the head's codebook slices)
+  const int hq = blockIdx.x % a.Hq, kw = blockIdx.x / a.Hq;
   const int h = hq / (a.Hq / a.H);
   const int beta = a.t / a.Tc, tau = a.t % a.Tc;
   const int nblk = a.T / a.Tc;
-  const int chunk = cg * kNW + wave;
-  const int L = min(a.seq_len[b], a.max_seq_len);
-  const int qe = min(a.q_end[b] & ~7, L);
-  const int P_lo = chunk * a.chunk_pages;
-  const int P_hi = min(qe >> 3, P_lo + a.chunk_pages);
-  const bool active = chunk < a.n_chunks;
-  // bf16 tokens as virtual tiles: the sink tile [0, ns) and the tiles over [r0, L)
-  const int ns = min(a.n_sink, L);
-  const int r0 = max(qe, a.n_sink);
-  const int vt_lo = r0 / kTile;
-  const int vt_hi = L > r0 ? (L - 1) / kTile + 1 : vt_lo;
-  const int n_vt = (ns > 0 ? 1 : 0) + (vt_hi - vt_lo);
+  const int W = wph * kNW;          // waves on this query head
+  const int wg = kw * kNW + wave;   // this wave among them
 
-  stage_slice<D, C>(a, beta, 0, h, tau, kl);
-  stage_slice<D, C>(a, beta, 1, h, tau, vl);
-  // rotated query of this (b, hq), log2 units, pairs interleaved (one copy per workgroup)
-  float* qw = qs;
-  if (wave == 0 && lane < HALF) {
-    const int pq = min(max(a.pos[b], 0), a.rope_tiles * kTile - 1);
-    const uint16_t* qv = a.q + ((size_t)b * a.Hq + hq) * D;
-    const float2 cs = phase(rope, a.rope_tiles, D, pq, lane);
-    const float x = bf2f(qv[lane]), y = bf2f(qv[lane + HALF]);
-    qw[2 * lane] = (x * cs.x - y * cs.y) * a.scale_log2e;
-    qw[2 * lane + 1] = (y * cs.x + x * cs.y) * a.scale_log2e;
+  // the work list's length, and (one wave of the launch) the sequences' first tiles
+  int total = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int n = b < a.B ? seq_tiles(a, b).total : 0;
+    if (hq == 0 && wg == 0) {
+      const int incl = total + wave_incl_scan(n);
+      if (b < a.B) a.tile_start[b] = incl - n;
+    }
+    total += wave_sum_i(n);
   }
+  if (hq == 0 && wg == 0 && lane == 0) a.tile_start[a.B] = total;
+  total = __builtin_amdgcn_readfirstlane(total);   // wave-uniform: keep it in a scalar register
+  // a workgroup with no tiles leaves before staging the slices
+  if (range_lo(kw * kNW, total, W) == range_lo((kw + 1) * kNW, total, W)) return;
+  const int w_lo = __builtin_amdgcn_readfirstlane(range_lo(wg, total, W));
+  const int w_hi = __builtin_amdgcn_readfirstlane(range_lo(wg + 1, total, W));
+
+  stage_slices<D, C>(a, beta, h, tau, kl);
   __syncthreads();
-  if (!active) return;
+  if (w_lo == w_hi) return;
+
+  // the sequence holding tile w_lo, and its first tile
+  int b = 0, tb = 0;
+  {
+    int base = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int bb = b0 + lane;
+      const int n = bb < a.B ? seq_tiles(a, bb).total : 0;
+      const int incl = base + wave_incl_scan(n);
+      const uint64_t hit = __ballot(bb < a.B && incl - n <= w_lo && w_lo < incl);
+      if (hit) {
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        b = b0 + src;
+        tb = __shfl(incl - n, src);
+        break;
+      }
+      base = __shfl(incl, 63);
+    }
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  tb = __builtin_amdgcn_readfirstlane(tb);
 
   const int qt = lane & 3, t = lane >> 2;       // lane quarter, token in tile
   // Chunk order per lane, so the lanes of one LDS access phase hit distinct banks:
@@ -183,287 +262,317 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
   // token's parity), value block v holds chunk (v + vrot) mod NV.
   const int kswap = (KPC == 2) ? (t & 1) : 0;
   const int vrot = (NV == 4) ? ((t + 2 * (qt >> 1)) & 3) : (t & (NV - 1));
-  float m = kNoMax, l = 0.f;
-  float m_hi = kNoMax + kRescale;   // rescale threshold
-  float o[QV];
+  // byte offsets (4-aligned) of the index-row words holding this lane's codes
+  const int glo = (qt * QP) / C, ghi = (qt * QP + HALF) / C, gv = (qt * QV) / C;
+  const int wlo = glo & ~3, whi = ghi & ~3, wv = gv & ~3;
+  const int r = t & 7;
+  const size_t row_stride = (size_t)kPage * NG;
+  const size_t page_bytes = (size_t)nblk * a.H * 2 * row_stride;
+  // the rows of (beta, h) in page 0 (wave-uniform), and the lane's three index words
+  // as byte offsets from a page's start
+  const uint8_t* head_rows = a.index_pages + (((size_t)beta * a.H + h) * 2) * row_stride;
+  const uint32_t o_kl = r * NG + wlo, o_kh = r * NG + whi, o_v = (uint32_t)row_stride + r * NG + wv;
+  // Per-lane gather constants: bit offset of the code in its index word, and the LDS
+  // byte offset of the chunk (code x of chunk k sits at byte (x * NCH + k) * 16).
+  constexpr int kRowShift = (NCH == 16) ? 8 : 7;   // log2(NCH * 16)
+  // A partner chunk (channels + d/2) sits HALF / 8 chunks further on (an immediate
+  // offset of the LDS read) and its code is KSH bits further along in its index word
+  // than the low chunk's code in its own word (the same for every lane).
+  constexpr uint32_t kHighOff = (HALF / 8) * 16;
+  // HALF / C groups separate the two codes; with a multiple of 4 they sit at the same
+  // byte of their words, with 2 (the low code in byte 0 or 1) two bytes further on.
+  static_assert((HALF / C) % 4 == 0 || HALF / C == 2, "shape outside the compiled set");
+  constexpr uint32_t kHighShift = ((HALF / C) % 4 == 0) ? 0 : 8 * (HALF / C);
+  // With 256-byte code rows (d = 128) the gather address is one byte permute: byte 0 is
+  // the chunk offset, byte 1 the code taken from its index word, byte 2 the slice base
+  // (0 for keys, 1 for values at 64 KB).  Otherwise a bit-field extract and a shift.
+  constexpr bool kPermAddr = kRowShift == 8;
+  auto code_sel = [](uint32_t sh) -> uint32_t {
+    return kPermAddr ? (0x0c020000u | ((4u + sh / 8) << 8)) : sh;
+  };
+  uint32_t sell[KPC], selh[KPC], offl[KPC], selv[NV], offv[NV];
 #pragma unroll
-  for (int i = 0; i < QV; ++i) o[i] = 0.f;
+  for (int v = 0; v < KPC; ++v) {
+    const int cl = qt * QP + 8 * (v ^ kswap);
+    const uint32_t sh = 8 * (cl / C - wlo);
+    sell[v] = code_sel(sh);
+    selh[v] = code_sel(sh + kHighShift);
+    offl[v] = (uint32_t)(cl / 8) * 16;
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int cv = qt * QV + 8 * ((v + vrot) & (NV - 1));
+    selv[v] = code_sel(8 * (cv / C - wv));
+    offv[v] = (uint32_t)(kCodes * D * 2) + (uint32_t)(cv / 8) * 16;   // value slices follow the keys
+  }
+  auto gather = [&](uint32_t word, uint32_t sel, uint32_t off) -> uint32_t {
+    if constexpr (kPermAddr) return __builtin_amdgcn_perm(word, off, sel);
+    else return (__builtin_amdgcn_ubfe(word, sel, 8) << kRowShift) + off;
+  };
+  float* e0s = e0buf + wave * 2 * ER;
+  int* ptl = ptbuf + wave * kPtBatch;
 
-  const bool has_coded = P_lo < P_hi && a.n_index_pages > 0;
-  if (has_coded || chunk < n_vt) {
-    // F, G: the query turned back by the token's in-tile offset t, for this lane's pairs
-    float F[QP], Gc[QP];
-    {
-      const float* e1 = rope + (size_t)(a.rope_tiles + t) * D;
+  // ---- the sequences the range meets, one partial record each
+  int pos_t = w_lo;
+  while (pos_t < w_hi && b < a.B) {
+    const SeqTiles st = seq_tiles(a, b);
+    const int u_lo = pos_t - tb, u_hi = min(w_hi - tb, st.total);
+    if (u_lo < u_hi) {
+      const int L = max(min(a.seq_len[b], a.max_seq_len), 0);
+      const int qe = max(min(a.q_end[b] & ~7, L), 0);
+      const int ns = min(a.n_sink, L);
+      const int r0 = max(qe, a.n_sink);
+      const int vt_lo = r0 / kTile;
+      // F, G: the rotated query (log2 units) turned back by the token's in-tile offset t,
+      // for this lane's pairs
+      float F[QP], Gc[QP];
+      {
+        // lane j < d/2 rotates pair j of the query into the wave's phase buffer (free
+        // between tiles; the wave's LDS accesses complete in order)
+        float* qw = e0s;
+        if (lane < HALF) {
+          const int pq = min(max(a.pos[b], 0), a.rope_tiles * kTile - 1);
+          const uint16_t* qv = a.q + ((size_t)b * a.Hq + hq) * D;
+          const float2 cs = phase(rope, a.rope_tiles, D, pq, lane);
+          const float x = bf2f(qv[lane]), y = bf2f(qv[lane + HALF]);
+          qw[2 * lane] = (x * cs.x - y * cs.y) * a.scale_log2e;
+          qw[2 * lane + 1] = (y * cs.x + x * cs.y) * a.scale_log2e;
+        }
+        const float* e1 = rope + (size_t)(a.rope_tiles + t) * D;
 #pragma unroll
-      for (int jj = 0; jj < QP; ++jj) {
-        const int j = qt * QP + 8 * ((jj / 8) ^ kswap) + (jj % 8);
-        const float A = qw[2 * j], Bq = qw[2 * j + 1];
-        const float c1 = e1[2 * j], s1 = e1[2 * j + 1];
-        F[jj] = A * c1 + Bq * s1;
-        Gc[jj] = Bq * c1 - A * s1;
-      }
-    }
-    // byte offsets (4-aligned) of the index-row words holding this lane's codes
-    const int glo = (qt * QP) / C, ghi = (qt * QP + HALF) / C, gv = (qt * QV) / C;
-    const int wlo = glo & ~3, whi = ghi & ~3, wv = gv & ~3;
-    const int r = t & 7;
-    const size_t row_stride = (size_t)kPage * NG;
-    const size_t page_bytes = (size_t)nblk * a.H * 2 * row_stride;
-    // the rows of (beta, h) in page 0 (wave-uniform), and the lane's three index words
-    // as byte offsets from a page's start
-    const uint8_t* head_rows = a.index_pages + (((size_t)beta * a.H + h) * 2) * row_stride;
-    const uint32_t o_kl = r * NG + wlo, o_kh = r * NG + whi, o_v = (uint32_t)row_stride + r * NG + wv;
-    // Per-lane gather constants: bit offset of the code in its index word, and the LDS
-    // byte offset of the chunk (code x of chunk k sits at byte (x * NCH + k) * 16).
-    constexpr int kRowShift = (NCH == 16) ? 8 : 7;   // log2(NCH * 16)
-    // A partner chunk (channels + d/2) sits HALF / 8 chunks further on (an immediate
-    // offset of the LDS read) and its code is KSH bits further along in its index word
-    // than the low chunk's code in its own word (the same for every lane).
-    constexpr uint32_t kHighOff = (HALF / 8) * 16;
-    // HALF / C groups separate the two codes; with a multiple of 4 they sit at the same
-    // byte of their words, with 2 (the low code in byte 0 or 1) two bytes further on.
-    static_assert((HALF / C) % 4 == 0 || HALF / C == 2, "shape outside the compiled set");
-    constexpr uint32_t kHighShift = ((HALF / C) % 4 == 0) ? 0 : 8 * (HALF / C);
-    // With 256-byte code rows (d = 128) the gather address is one byte permute: byte 0 is
-    // the chunk offset, byte 1 the code taken from its index word, byte 2 the slice base
-    // (0 for keys, 1 for values at 64 KB).  Otherwise a bit-field extract and a shift.
-    constexpr bool kPermAddr = kRowShift == 8;
-    auto code_sel = [](uint32_t sh) -> uint32_t {
-      return kPermAddr ? (0x0c020000u | ((4u + sh / 8) << 8)) : sh;
-    };
-    uint32_t sell[KPC], selh[KPC], offl[KPC], selv[NV], offv[NV];
-#pragma unroll
-    for (int v = 0; v < KPC; ++v) {
-      const int cl = qt * QP + 8 * (v ^ kswap);
-      const uint32_t sh = 8 * (cl / C - wlo);
-      sell[v] = code_sel(sh);
-      selh[v] = code_sel(sh + kHighShift);
-      offl[v] = (uint32_t)(cl / 8) * 16;
-    }
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int cv = qt * QV + 8 * ((v + vrot) & (NV - 1));
-      selv[v] = code_sel(8 * (cv / C - wv));
-      offv[v] = (uint32_t)(kCodes * D * 2) + (uint32_t)(cv / 8) * 16;   // value slices follow the keys
-    }
-    auto gather = [&](uint32_t word, uint32_t sel, uint32_t off) -> uint32_t {
-      if constexpr (kPermAddr) return __builtin_amdgcn_perm(word, off, sel);
-      else return (__builtin_amdgcn_ubfe(word, sel, 8) << kRowShift) + off;
-    };
-    float* e0s = e0buf + wave * 2 * ER;
-    int* ptl = ptbuf + wave * kPtBatch;
-    const int* pt = a.page_table + (size_t)b * a.max_pages;
-    int pt_base = -kPtBatch;
-    // stage the page ids of pages [P, P + kPtBatch) into LDS (all loads in flight, one wait)
-    auto stage_pt = [&](int P) {
-      pt_base = P;
-      int v[kPtBatch / 64];
-#pragma unroll
-      for (int k = 0; k < kPtBatch / 64; ++k) v[k] = pt[min(P + k * 64 + lane, a.max_pages - 1)];
-#pragma unroll
-      for (int k = 0; k < kPtBatch / 64; ++k) {
-        const int q = P + k * 64 + lane;
-        ptl[k * 64 + lane] = (q < P_hi && v[k] >= 0 && v[k] < a.n_index_pages) ? v[k] : -1;
-      }
-    };
-    // everything a lane loads for the tile starting at page P0
-    struct TileIn {
-      int phys;
-      uint32_t kwl, kwh, vw;
-      float2 e0;
-    };
-    auto fetch = [&](int P0) -> TileIn {
-      TileIn in;
-      if (P0 + 1 >= pt_base + kPtBatch) stage_pt(P0);
-      in.phys = P0 < P_hi ? ptl[P0 - pt_base + (t >> 3)] : -1;
-      if constexpr (WIDE) {
-        const uint8_t* base = head_rows + (size_t)(uint32_t)max(in.phys, 0) * page_bytes;
-        in.kwl = *(const uint32_t*)(base + o_kl);
-        in.kwh = *(const uint32_t*)(base + o_kh);
-        in.vw = *(const uint32_t*)(base + o_v);
-      } else {
-        // the pool spans under 4 GiB and 2^24 pages: 32-bit offsets from a uniform base
-        const uint32_t po = __umul24((uint32_t)max(in.phys, 0), (uint32_t)page_bytes);
-        in.kwl = *(const uint32_t*)(head_rows + (po + o_kl));
-        in.kwh = *(const uint32_t*)(head_rows + (po + o_kh));
-        in.vw = *(const uint32_t*)(head_rows + (po + o_v));
-      }
-      const int tile_idx = min((8 * P0) / kTile, a.rope_tiles - 1);
-      in.e0 = *(const float2*)(rope + (size_t)tile_idx * D + 2 * (lane % HALF));
-      return in;
-    };
-    auto tile = [&](int P0, const TileIn& in, int buf) {
-      float* er = e0s + buf * ER;
-      if (lane < HALF) *(float2*)(er + (lane / QP) * (2 * QP + 4) + 2 * (lane % QP)) = in.e0;
-      const int p = 8 * P0 + t;
-      const bool valid = in.phys >= 0 && p >= a.n_sink;
-      // keys: low channels [qt*QP, qt*QP + QP) and the partners + d/2
-      f16x8 xl[QP / 8], xh[QP / 8];
-#pragma unroll
-      for (int v = 0; v < KPC; ++v) {
-        xl[v] = lds_read16(gather(in.kwl, sell[v], offl[v]));
-        xh[v] = lds_read16(gather(in.kwh, selh[v], offl[v]) + kHighOff);
-      }
-      float s0acc = 0.f, s1acc = 0.f;
-#pragma unroll
-      for (int v = 0; v < QP / 8; ++v) {
-#pragma unroll
-        for (int i4 = 0; i4 < 2; ++i4) {
-          const float* ep = er + qt * (2 * QP + 4) + 2 * (8 * (v ^ kswap) + 4 * i4);
-          const f32x4 e_a = *(const f32x4*)ep;
-          const f32x4 e_b = *(const f32x4*)(ep + 4);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int i = 4 * i4 + k, jj = 8 * v + i;
-            const float c0 = k < 2 ? e_a[2 * k] : e_b[2 * (k - 2)];
-            const float sn = k < 2 ? e_a[2 * k + 1] : e_b[2 * (k - 2) + 1];
-            const float u = c0 * F[jj] + sn * Gc[jj];
-            const float w_ = c0 * Gc[jj] - sn * F[jj];
-            if (i & 1) { s1acc = fmaf(u, (float)xl[v][i], s1acc); s1acc = fmaf(w_, (float)xh[v][i], s1acc); }
-            else       { s0acc = fmaf(u, (float)xl[v][i], s0acc); s0acc = fmaf(w_, (float)xh[v][i], s0acc); }
-          }
+        for (int jj = 0; jj < QP; ++jj) {
+          const int j = qt * QP + 8 * ((jj / 8) ^ kswap) + (jj % 8);
+          const float A = qw[2 * j], Bq = qw[2 * j + 1];
+          const float c1 = e1[2 * j], s1 = e1[2 * j + 1];
+          F[jj] = A * c1 + Bq * s1;
+          Gc[jj] = Bq * c1 - A * s1;
         }
       }
-      const float s = valid ? quad_sum(s0acc + s1acc) : -__builtin_inff();
-      if (SCORES && valid && qt == 0) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
-      if (__any(s > m_hi)) {
-        const float mn = fmaxf(m, wave_max(s));
-        const float f = __builtin_amdgcn_exp2f(m - mn);
+      float m = kNoMax, l = 0.f;
+      float m_hi = kNoMax + kRescale;   // rescale threshold
+      float o[QV];
 #pragma unroll
-        for (int i = 0; i < QV; ++i) o[i] *= f;
-        l *= f;
-        m = mn;
-        m_hi = mn + kRescale;
-      }
-      const float w = __builtin_amdgcn_exp2f(s - m);   // 0 for an invalid token (s = -inf)
-      l += w;   // every lane of a token adds the same weight; folded over tokens only
-      // values: output channels [qt*QV, qt*QV + QV)
+      for (int i = 0; i < QV; ++i) o[i] = 0.f;
+      const int P_lo = 2 * u_lo;
+      const int P_hi = min(2 * min(u_hi, st.coded), qe >> 3);
+      const int* pt = a.page_table + (size_t)b * a.max_pages;
+      int pt_base = -kPtBatch;
+      // stage the page ids of pages [P, P + kPtBatch) into LDS (all loads in flight, one wait)
+      auto stage_pt = [&](int P) {
+        pt_base = P;
+        int v[kPtBatch / 64];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const f16x8 x = lds_read16(gather(in.vw, selv[v], offv[v]));
+        for (int k = 0; k < kPtBatch / 64; ++k) v[k] = pt[min(P + k * 64 + lane, a.max_pages - 1)];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, (float)x[i], o[8 * v + i]);
-      }
-    };
-    // bf16 sink and recent tokens: virtual tile vt of (b, hq) runs on chunk vt mod n_chunks,
-    // with the same lane layout and RoPE factorisation; keys and values are read from the
-    // bf16 pages and used in float32 (a bf16 value need not fit float16).
-    for (int vt = chunk; vt < n_vt; vt += a.n_chunks) {
-      const bool sink_tile = ns > 0 && vt == 0;
-      const int a_tile = sink_tile ? 0 : vt_lo + vt - (ns > 0 ? 1 : 0);
-      const int lo = sink_tile ? 0 : r0, hi = sink_tile ? ns : L;
-      const int p = kTile * a_tile + t;
-      const uint16_t* krow = nullptr;
-      if (p >= lo && p < hi) {
-        const int slot = sink_tile ? 0 : 1 + (p >> 3) - (qe >> 3);
-        const int pg = slot < a.bf16_row ? a.bf16_table[(size_t)b * a.bf16_row + slot] : -1;
-        if (pg >= 0 && pg < a.n_bf16_pages)
-          krow = a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2) * kPage + (p & 7)) * D;
-      }
-      const bool valid = krow != nullptr;
-      float* er = e0s;   // buffer 0, before the coded tiles use both
-      if (lane < HALF) {
-        const int tile_idx = min(a_tile, a.rope_tiles - 1);
-        *(float2*)(er + (lane / QP) * (2 * QP + 4) + 2 * (lane % QP)) =
-            *(const float2*)(rope + (size_t)tile_idx * D + 2 * lane);
-      }
-      float s0acc = 0.f, s1acc = 0.f;
-      if (valid) {
-#pragma unroll
+        for (int k = 0; k < kPtBatch / 64; ++k) {
+          const int q = P + k * 64 + lane;
+          ptl[k * 64 + lane] = (q < P_hi && v[k] >= 0 && v[k] < a.n_index_pages) ? v[k] : -1;
+        }
+      };
+      // everything a lane loads for the tile starting at page P0
+      struct TileIn {
+        int phys;
+        uint32_t kwl, kwh, vw;
+        float2 e0;
+      };
+      auto fetch = [&](int P0) -> TileIn {
+        TileIn in;
+        if (P0 + 1 >= pt_base + kPtBatch) stage_pt(P0);
+        in.phys = P0 < P_hi ? ptl[P0 - pt_base + (t >> 3)] : -1;
+        if constexpr (WIDE) {
+          const uint8_t* base = head_rows + (size_t)(uint32_t)max(in.phys, 0) * page_bytes;
+          in.kwl = *(const uint32_t*)(base + o_kl);
+          in.kwh = *(const uint32_t*)(base + o_kh);
+          in.vw = *(const uint32_t*)(base + o_v);
+        } else {
+          // the pool spans under 4 GiB and 2^24 pages: 32-bit offsets from a uniform base
+          const uint32_t po = __umul24((uint32_t)max(in.phys, 0), (uint32_t)page_bytes);
+          in.kwl = *(const uint32_t*)(head_rows + (po + o_kl));
+          in.kwh = *(const uint32_t*)(head_rows + (po + o_kh));
+          in.vw = *(const uint32_t*)(head_rows + (po + o_v));
+        }
+        const int tile_idx = min((8 * P0) / kTile, a.rope_tiles - 1);
+        in.e0 = *(const float2*)(rope + (size_t)tile_idx * D + 2 * (lane % HALF));
+        return in;
+      };
+      auto tile = [&](int P0, const TileIn& in, int buf) {
+        float* er = e0s + buf * ER;
+        if (lane < HALF) *(float2*)(er + (lane / QP) * (2 * QP + 4) + 2 * (lane % QP)) = in.e0;
+        const int p = 8 * P0 + t;
+        const bool valid = in.phys >= 0 && p >= a.n_sink;
+        // keys: low channels [qt*QP, qt*QP + QP) and the partners + d/2
+        f16x8 xl[QP / 8], xh[QP / 8];
+  #pragma unroll
         for (int v = 0; v < KPC; ++v) {
-          const int cl = qt * QP + 8 * (v ^ kswap), ch = cl + HALF;
-          const u16x8 xlr = *(const u16x8*)(krow + cl);
-          const u16x8 xhr = *(const u16x8*)(krow + ch);
-#pragma unroll
+          xl[v] = lds_read16(gather(in.kwl, sell[v], offl[v]));
+          xh[v] = lds_read16(gather(in.kwh, selh[v], offl[v]) + kHighOff);
+        }
+        float s0acc = 0.f, s1acc = 0.f;
+  #pragma unroll
+        for (int v = 0; v < QP / 8; ++v) {
+  #pragma unroll
           for (int i4 = 0; i4 < 2; ++i4) {
             const float* ep = er + qt * (2 * QP + 4) + 2 * (8 * (v ^ kswap) + 4 * i4);
             const f32x4 e_a = *(const f32x4*)ep;
             const f32x4 e_b = *(const f32x4*)(ep + 4);
-#pragma unroll
+  #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const int i = 4 * i4 + k, jj = 8 * v + i;
               const float c0 = k < 2 ? e_a[2 * k] : e_b[2 * (k - 2)];
               const float sn = k < 2 ? e_a[2 * k + 1] : e_b[2 * (k - 2) + 1];
               const float u = c0 * F[jj] + sn * Gc[jj];
               const float w_ = c0 * Gc[jj] - sn * F[jj];
-              s0acc = fmaf(u, bf2f(xlr[i]), s0acc);
-              s1acc = fmaf(w_, bf2f(xhr[i]), s1acc);
+              if (i & 1) { s1acc = fmaf(u, (float)xl[v][i], s1acc); s1acc = fmaf(w_, (float)xh[v][i], s1acc); }
+              else       { s0acc = fmaf(u, (float)xl[v][i], s0acc); s0acc = fmaf(w_, (float)xh[v][i], s0acc); }
             }
           }
         }
-      }
-      const float s = valid ? quad_sum(s0acc + s1acc) : -__builtin_inff();
-      if (SCORES && valid && qt == 0) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
-      if (__any(s > m_hi)) {
-        const float mn = fmaxf(m, wave_max(s));
-        const float f = __builtin_amdgcn_exp2f(m - mn);
-#pragma unroll
-        for (int i = 0; i < QV; ++i) o[i] *= f;
-        l *= f;
-        m = mn;
-        m_hi = mn + kRescale;
-      }
-      const float w = __builtin_amdgcn_exp2f(s - m);   // 0 for an invalid token (s = -inf)
-      l += w;   // every lane of a token adds the same weight; folded over tokens only
-      if (valid) {
-        const uint16_t* vrow = krow + (size_t)kPage * D;
-#pragma unroll
+        const float s = valid ? quad_sum(s0acc + s1acc) : -__builtin_inff();
+        if (SCORES && valid && qt == 0) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
+        if (__any(s > m_hi)) {
+          const float mn = fmaxf(m, wave_max(s));
+          const float f = __builtin_amdgcn_exp2f(m - mn);
+  #pragma unroll
+          for (int i = 0; i < QV; ++i) o[i] *= f;
+          l *= f;
+          m = mn;
+          m_hi = mn + kRescale;
+        }
+        const float w = __builtin_amdgcn_exp2f(s - m);   // 0 for an invalid token (s = -inf)
+        l += w;   // every lane of a token adds the same weight; folded over tokens only
+        // values: output channels [qt*QV, qt*QV + QV)
+  #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          const u16x8 x = *(const u16x8*)(vrow + qt * QV + 8 * ((v + vrot) & (NV - 1)));
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, bf2f(x[i]), o[8 * v + i]);
+          const f16x8 x = lds_read16(gather(in.vw, selv[v], offv[v]));
+  #pragma unroll
+          for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, (float)x[i], o[8 * v + i]);
+        }
+      };
+      // Software pipeline in batches of NT tiles: each iteration loads the inputs of
+      // the next batch, computes the current batch, then moves next to current, so no
+      // load is in flight across the loop back-edge.
+      if (P_lo < P_hi) {
+        TileIn cur[NT], nxt[NT];
+  #pragma unroll
+        for (int i = 0; i < NT; ++i) cur[i] = fetch(P_lo + 2 * i);
+        for (int P0 = P_lo; P0 < P_hi; P0 += 2 * NT) {
+  #pragma unroll
+          for (int i = 0; i < NT; ++i) nxt[i] = fetch(P0 + 2 * NT + 2 * i);
+  #pragma unroll
+          for (int i = 0; i < NT; ++i) {
+            if (P0 + 2 * i < P_hi) tile(P0 + 2 * i, cur[i], i & 1);
+          }
+  #pragma unroll
+          for (int i = 0; i < NT; ++i) cur[i] = nxt[i];
         }
       }
-    }
-    // Software pipeline in batches of NT tiles: each iteration loads the inputs of
-    // the next batch, computes the current batch, then moves next to current, so no
-    // load is in flight across the loop back-edge.
-    if (has_coded) {
-      TileIn cur[NT], nxt[NT];
+      // bf16 sink and recent tokens (virtual tiles after the coded ones; a wave takes
+      // those whose first unit lies in its range), with the same lane layout and RoPE
+      // factorisation; keys and values are read from the bf16 pages and used in float32
+      // (a bf16 value need not fit float16).
+      const int vt_first = (max(u_lo, st.coded) - st.coded + kBfCost - 1) / kBfCost;
+      const int vt_end = u_hi > st.coded ? (u_hi - st.coded + kBfCost - 1) / kBfCost : 0;
+      for (int vt = vt_first; vt < vt_end; ++vt) {
+        const bool sink_tile = ns > 0 && vt == 0;
+        const int a_tile = sink_tile ? 0 : vt_lo + vt - (ns > 0 ? 1 : 0);
+        const int lo = sink_tile ? 0 : r0, hi = sink_tile ? ns : L;
+        const int p = kTile * a_tile + t;
+        const uint16_t* krow = nullptr;
+        if (p >= lo && p < hi) {
+          const int slot = sink_tile ? 0 : 1 + (p >> 3) - (qe >> 3);
+          const int pg = slot < a.bf16_row ? a.bf16_table[(size_t)b * a.bf16_row + slot] : -1;
+          if (pg >= 0 && pg < a.n_bf16_pages)
+            krow = a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2) * kPage + (p & 7)) * D;
+        }
+        const bool valid = krow != nullptr;
+        float* er = e0s;
+        if (lane < HALF) {
+          const int tile_idx = min(a_tile, a.rope_tiles - 1);
+          *(float2*)(er + (lane / QP) * (2 * QP + 4) + 2 * (lane % QP)) =
+              *(const float2*)(rope + (size_t)tile_idx * D + 2 * lane);
+        }
+        float s0acc = 0.f, s1acc = 0.f;
+        if (valid) {
+  #pragma unroll
+          for (int v = 0; v < KPC; ++v) {
+            const int cl = qt * QP + 8 * (v ^ kswap), ch = cl + HALF;
+            const u16x8 xlr = *(const u16x8*)(krow + cl);
+            const u16x8 xhr = *(const u16x8*)(krow + ch);
+  #pragma unroll
+            for (int i4 = 0; i4 < 2; ++i4) {
+              const float* ep = er + qt * (2 * QP + 4) + 2 * (8 * (v ^ kswap) + 4 * i4);
+              const f32x4 e_a = *(const f32x4*)ep;
+              const f32x4 e_b = *(const f32x4*)(ep + 4);
+  #pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const int i = 4 * i4 + k, jj = 8 * v + i;
+                const float c0 = k < 2 ? e_a[2 * k] : e_b[2 * (k - 2)];
+                const float sn = k < 2 ? e_a[2 * k + 1] : e_b[2 * (k - 2) + 1];
+                const float u = c0 * F[jj] + sn * Gc[jj];
+                const float w_ = c0 * Gc[jj] - sn * F[jj];
+                s0acc = fmaf(u, bf2f(xlr[i]), s0acc);
+                s1acc = fmaf(w_, bf2f(xhr[i]), s1acc);
+              }
+            }
+          }
+        }
+        const float s = valid ? quad_sum(s0acc + s1acc) : -__builtin_inff();
+        if (SCORES && valid && qt == 0) a.scores[((size_t)b * a.Hq + hq) * a.max_seq_len + p] = s * kLn2;
+        if (__any(s > m_hi)) {
+          const float mn = fmaxf(m, wave_max(s));
+          const float f = __builtin_amdgcn_exp2f(m - mn);
+  #pragma unroll
+          for (int i = 0; i < QV; ++i) o[i] *= f;
+          l *= f;
+          m = mn;
+          m_hi = mn + kRescale;
+        }
+        const float w = __builtin_amdgcn_exp2f(s - m);   // 0 for an invalid token (s = -inf)
+        l += w;   // every lane of a token adds the same weight; folded over tokens only
+        if (valid) {
+          const uint16_t* vrow = krow + (size_t)kPage * D;
+  #pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            const u16x8 x = *(const u16x8*)(vrow + qt * QV + 8 * ((v + vrot) & (NV - 1)));
+  #pragma unroll
+            for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, bf2f(x[i]), o[8 * v + i]);
+          }
+        }
+      }
+      // value block v holds chunk (v + vrot) mod NV: put chunk c back in block c
+      {
+        float ot[QV];
 #pragma unroll
-      for (int i = 0; i < NT; ++i) cur[i] = fetch(P_lo + 2 * i);
-      for (int P0 = P_lo; P0 < P_hi; P0 += 2 * NT) {
+        for (int c = 0; c < NV; ++c) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i) nxt[i] = fetch(P0 + 2 * NT + 2 * i);
+          for (int i = 0; i < 8; ++i) {
+            float val = o[8 * c + i];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          if (P0 + 2 * i < P_hi) tile(P0 + 2 * i, cur[i], i & 1);
+            for (int k = 1; k < NV; ++k) val = (vrot == k) ? o[8 * ((c - k) & (NV - 1)) + i] : val;
+            ot[8 * c + i] = val;
+          }
         }
 #pragma unroll
-        for (int i = 0; i < NT; ++i) cur[i] = nxt[i];
+        for (int i = 0; i < QV; ++i) o[i] = ot[i];
+      }
+      // fold the 16 token lanes of each quarter and write the partial (m, l, o)
+#pragma unroll
+      for (int off = 4; off < 64; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < QV; ++i) o[i] += __shfl_xor(o[i], off);
+      }
+#pragma unroll
+      for (int off = 4; off < 64; off <<= 1) l += __shfl_xor(l, off);
+      float* rec = a.part + ((size_t)hq * a.n_rec + wg + b) * (D + 2);
+      if (lane == 0) { rec[0] = m; rec[1] = l; }
+      if (t == 0) {
+#pragma unroll
+        for (int i = 0; i < QV; ++i) rec[2 + qt * QV + i] = o[i];
       }
     }
-  }
-  // value block v holds chunk (v + vrot) mod NV: put chunk c back in block c
-  {
-    float ot[QV];
-#pragma unroll
-    for (int c = 0; c < NV; ++c) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float val = o[8 * c + i];
-#pragma unroll
-        for (int k = 1; k < NV; ++k) val = (vrot == k) ? o[8 * ((c - k) & (NV - 1)) + i] : val;
-        ot[8 * c + i] = val;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < QV; ++i) o[i] = ot[i];
-  }
-  // fold the 16 token lanes of each quarter and write the partial (m, l, o)
-#pragma unroll
-  for (int off = 4; off < 64; off <<= 1) {
-#pragma unroll
-    for (int i = 0; i < QV; ++i) o[i] += __shfl_xor(o[i], off);
-  }
-#pragma unroll
-  for (int off = 4; off < 64; off <<= 1) l += __shfl_xor(l, off);
-  float* rec = a.part + (((size_t)b * a.Hq + hq) * a.n_chunks + chunk) * (D + 2);
-  if (lane == 0) { rec[0] = m; rec[1] = l; }
-  if (t == 0) {
-#pragma unroll
-    for (int i = 0; i < QV; ++i) rec[2 + qt * QV + i] = o[i];
+    pos_t = __builtin_amdgcn_readfirstlane(tb + u_hi);
+    tb = __builtin_amdgcn_readfirstlane(tb + st.total);
+    b = __builtin_amdgcn_readfirstlane(b + 1);
   }
 }
 
@@ -473,17 +582,42 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int n_cg) {
 // out = sum o_i 2^(m_i - m) / l, lse = (m + log2 l) ln 2.  The (m_i, l_i) pairs are
 // read in one round into LDS, the weights computed there, then each channel's S
 // partial values are loaded together.
-constexpr int kMergeMax = 1024;   // splits per (b, hq) at most (the planner caps them lower)
-__global__ __launch_bounds__(128) void merge_kernel(AttnArgs a) {
-  __shared__ float2 sml[kMergeMax];
-  __shared__ float s_w[kMergeMax];
+// With a.tile_start set (decode), the records of (b, hq) are those of the waves whose
+// token-balanced ranges meet sequence b's tiles: record wg + b of head hq for wg in a
+// window found from the tile counts, each checked (a wave with an empty intersection
+// wrote nothing there).  Otherwise the n_rec records of an item are consecutive.
+constexpr int kMergeMax = 4096;   // candidate records per (b, hq) at most (the host checks)
+__global__ __launch_bounds__(128) void merge_kernel(AttnArgs a, int cap) {
+  extern __shared__ __align__(16) unsigned char merge_smem[];
+  float2* sml = (float2*)merge_smem;            // [cap]
+  float* s_w = (float*)(sml + cap);             // [cap]
   __shared__ float s_ml[2];
   const int item = blockIdx.x;           // b * Hq + hq
-  const int S = a.n_chunks;
   const int D2 = a.d + 2;
-  const float* rec = a.part + (size_t)item * S * D2;
   const int tid = threadIdx.x;
-  for (int i = tid; i < S; i += blockDim.x) sml[i] = *(const float2*)(rec + (size_t)i * D2);
+  int S;
+  const float* rec;
+  if (a.tile_start) {
+    const int b = item / a.Hq, hq = item % a.Hq;
+    const int tb = a.tile_start[b], tb1 = a.tile_start[b + 1], total = a.tile_start[a.B];
+    const int W = a.n_waves;
+    int lo = 0, hi = -1;
+    if (tb < tb1) {   // then total > 0
+      lo = max(0, (int)(((long)(tb + 1) * W + total - 1) / total) - 2);
+      hi = min(W - 1, (int)(((long)tb1 * W + total - 1) / total));
+    }
+    S = min(hi - lo + 1, cap);   // hi - lo + 1 <= W + 1 = cap
+    rec = a.part + ((size_t)hq * a.n_rec + lo + b) * D2;
+    for (int i = tid; i < S; i += blockDim.x) {
+      const int wg = lo + i;
+      const bool meets = max(range_lo(wg, total, W), tb) < min(range_lo(wg + 1, total, W), tb1);
+      sml[i] = meets ? *(const float2*)(rec + (size_t)i * D2) : make_float2(-__builtin_inff(), 0.f);
+    }
+  } else {
+    S = min(a.n_rec, cap);
+    rec = a.part + (size_t)item * a.n_rec * D2;
+    for (int i = tid; i < S; i += blockDim.x) sml[i] = *(const float2*)(rec + (size_t)i * D2);
+  }
   __syncthreads();
   if (tid < 64) {
     float mloc = -__builtin_inff();
@@ -504,12 +638,15 @@ __global__ __launch_bounds__(128) void merge_kernel(AttnArgs a) {
   if (ch < a.d) {
     float acc0 = 0.f, acc1 = 0.f;
     int i = 0;
+    // records with weight 0 are not read (unwritten candidates may hold anything)
     for (; i + 1 < S; i += 2) {
-      const float o0 = rec[(size_t)i * D2 + 2 + ch], o1 = rec[(size_t)(i + 1) * D2 + 2 + ch];
-      acc0 = fmaf(o0, s_w[i], acc0);
-      acc1 = fmaf(o1, s_w[i + 1], acc1);
+      const float w0 = s_w[i], w1 = s_w[i + 1];
+      const float o0 = w0 != 0.f ? rec[(size_t)i * D2 + 2 + ch] : 0.f;
+      const float o1 = w1 != 0.f ? rec[(size_t)(i + 1) * D2 + 2 + ch] : 0.f;
+      acc0 = fmaf(o0, w0, acc0);
+      acc1 = fmaf(o1, w1, acc1);
     }
-    if (i < S) acc0 = fmaf(rec[(size_t)i * D2 + 2 + ch], s_w[i], acc0);
+    if (i < S && s_w[i] != 0.f) acc0 = fmaf(rec[(size_t)i * D2 + 2 + ch], s_w[i], acc0);
     a.out[(size_t)item * a.d + ch] = Ls > 0.f ? (acc0 + acc1) / Ls : 0.f;
   }
   if (a.lse && tid == 0) a.lse[item] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
@@ -543,13 +680,15 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
     attr_set = true;
   }
   const int n_items = a.B * a.Hq;
-  const int n_cg = (a.n_chunks + kNW - 1) / kNW;
-  const long grid = (long)n_cg * n_items;
+  const int wph = a.n_waves / kNW;   // workgroups per query head
+  if (wph < 1 || a.n_waves % kNW || a.n_waves + 1 > kMergeMax || a.n_rec != a.n_waves + a.B || !a.tile_start)
+    return hipErrorInvalidValue;
+  const long grid = (long)wph * a.Hq;
   hipLaunchKernelGGL((attn_kernel<D, C, SCORES, WIDE>), dim3((unsigned)grid), dim3(kNW * 64), lds, s, a,
-                     a.rope, n_cg);
+                     a.rope, wph);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(n_items), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, dim3(n_items), dim3(128), (size_t)(a.n_waves + 1) * 12, s, a, a.n_waves + 1);
   return hipGetLastError();
 }
 
@@ -569,6 +708,8 @@ int rope_tile() { return kTile; }
 
 int attn_waves_per_group() { return kNW; }
 
+int merge_max_records() { return kMergeMax; }
+
 bool attn_supported(int d, int c) {
   if (d == 128) return c == 8 || c == 16 || c == 32;
   if (d == 64) return c == 8 || c == 16;
@@ -576,7 +717,8 @@ bool attn_supported(int d, int c) {
 }
 
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, s, a);
+  if (a.n_rec > kMergeMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), (size_t)a.n_rec * 12, s, a, a.n_rec);
   return hipGetLastError();
 }
 

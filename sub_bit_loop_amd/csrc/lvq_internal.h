@@ -117,14 +117,18 @@ struct AttnArgs {
   float* scores;              // [B][Hq][max_seq_len] or null (probe)
   int t, B, H, Hq, d, T, Tc, G;
   int n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages, max_seq_len, rope_tiles;
-  int n_chunks;               // coded chunks per (b, hq)
-  int chunk_pages;            // pages per chunk, multiple of 8
+  int n_chunks;               // multi-row kernel: coded chunks per (row, hq)
+  int chunk_pages;            // multi-row kernel: pages per chunk, multiple of 8
+  int n_waves;                // decode kernel: waves per query head (token-balanced ranges)
+  int n_rec;                  // partial records per query head (decode) or per item (multi-row)
+  int* tile_start;            // decode: [B + 1] first tile of each sequence in the work list
   float scale_log2e;          // softmax scale * log2(e)
 };
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s);   // merge of a.part into a.out / a.lse
 bool attn_supported(int d, int c);
 int rope_tile();   // positions per row of the first RoPE table part
-int attn_waves_per_group();   // coded chunks (waves) per attention workgroup
+int attn_waves_per_group();   // waves per decode-attention workgroup
+int merge_max_records();      // candidate partial records per (b, query head) the merge accepts
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 }  // namespace lvq

@@ -105,14 +105,17 @@ def test_attn_validation(L):
 
 
 def test_workspace_size_covers_every_split(L):
+    """Records [Hq][W + B][d + 2] float32 and the tile table [B + 1] int32, W waves per head
+    in whole workgroups of 12: W = 12 * ceil(n_splits / 12), or automatically 256 / Hq
+    workgroups per head, capped at about 4 tiles per wave of the largest work list."""
     from sub_bit_loop_amd import _abi
-    for B, Hq, msl, ns in ((8, 16, 32768, 0), (1, 16, 65536, 0), (64, 16, 16384, 0), (1, 1, 512, 7),
-                           (2, 4, 100, 0)):
+    for B, Hq, msl, ns, W in ((8, 16, 32768, 0, 192), (1, 16, 65536, 0, 192), (64, 16, 16384, 0, 192),
+                              (1, 1, 512, 7, 12), (1, 1, 512, 0, 12), (2, 4, 100, 0, 12),
+                              (1, 1, 1 << 20, 0, 3072), (3, 2, 4096, 1000, 1008)):
         s = shape(B=B, H=Hq, Hq=Hq, max_seq_len=msl, rope_max_len=msl + 1, max_pages=(msl + 7) // 8,
                   n_splits=ns)
         nbytes = _abi.lvq_decode_attn_workspace_bytes(s)
-        per = B * Hq * 130 * 4           # one (m, l, o[128]) record per split
-        assert nbytes % per == 0 and nbytes // per >= 1
+        assert nbytes == Hq * (W + B) * 130 * 4 + (B + 1) * 4, (B, Hq, msl, ns, nbytes)
 
 
 def test_builder_validation(L):
