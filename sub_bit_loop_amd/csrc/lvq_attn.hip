@@ -12,28 +12,33 @@
 // combined with the bf16 part.
 //
 // Design (MI355X; MHA decode is bound by per-token VALU and LDS work, not HBM):
-//  * Workgroup = 8 waves (2 per SIMD) on one (sequence, query head); each wave
-//    owns one chunk of coded pages.  The step-t K and V slices of the head
+//  * Workgroup = 12 waves (3 per SIMD) on one query head; 256/Hq workgroups per
+//    head, one resident per CU.  The step-t K and V slices of the head
 //    (2 x 256 codes x d channels, 128 KB at d = 128) are staged once per
 //    workgroup in LDS as float16, which holds the bf16 codewords exactly.
+//  * Token-balanced split: a head's work list is the batch's 16-token tiles in
+//    sequence order (each sequence's coded tiles, then its bf16 tiles counted as
+//    kBfCost units); each wave takes an equal contiguous range of it, crossing
+//    sequence boundaries, and writes one partial (max, sum, output) record per
+//    sequence its range meets.  Mixed lengths and single long sequences keep every
+//    wave busy for the same time.
 //  * A tile is 16 positions (2 pages); four lanes share a token: lane quarter
 //    qt owns channel pairs [qt*d/8, (qt+1)*d/8) of the score and output channels
 //    [qt*d/4, (qt+1)*d/4) of the value sum.  Keys and values are gathered from
 //    LDS (16-byte reads), the value sum is accumulated in registers.
 //  * RoPE after dequantisation without per-token trigonometry: position
 //    16a + o has phase E(16a) * E(o); the lane folds E(o) and the query once per
-//    chunk into coefficients F, G, so per channel pair j the score gets
+//    sequence into coefficients F, G, so per channel pair j the score gets
 //    (c0 F_j + s0 G_j) k_j + (c0 G_j - s0 F_j) k_{j+d/2} with (c0, s0) = E(16a)
 //    read from a per-tile LDS row: six float32 operations, the key read by
 //    v_fma_mix straight from float16.
-//  * Index rows (only the bytes a lane needs) and tile phases of the next batch
-//    of 4 tiles are loaded while the current batch computes.
+//  * Index words (only the bytes a lane needs) and the tile phases of the next
+//    tile are loaded while the current tile computes.
 //  * Scores are kept in log2 units (scale * log2 e folded into the query); a
 //    running maximum is kept lazily (rescale only when a score passes it by
 //    more than 8 in log2 units).
-//  * The bf16 sink and recent tokens of a (b, query head) form a few virtual
-//    tiles (16 positions each) handed round-robin to the same chunk waves, read
-//    from the bf16 pages in float32: no separate workgroups, no extra partial.
+//  * The bf16 sink and recent tiles are read from the bf16 pages in float32 with
+//    the same lane layout and factorisation.
 //  * LDS layout [code][16-byte chunk] and a per-lane chunk order keep the lanes
 //    of an LDS access phase on distinct banks.
 #include "lvq_internal.h"
