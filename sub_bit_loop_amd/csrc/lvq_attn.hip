@@ -106,15 +106,21 @@ __device__ __forceinline__ float2 phase(const float* __restrict__ rope, int tile
 // Stage the step-tau [256][c] slices of all groups of book (beta, kv, h) into LDS as
 // float16, laid out [code][chunk][8]: chunk k of code x holds channels 8k..8k+7 of
 // code x's share.  A gather's LDS bank then depends on the chunk, not on the code.
-// The K and V slices are staged together with every 16-byte load of a thread in
-// flight before the first conversion (one memory latency, not one per load).
+// The K and V slices are staged together: load() puts every 16-byte piece of a thread
+// in flight (one memory latency, not one per load, overlapping the work-list scan);
+// store() converts and writes them.
 template <int D, int C>
-__device__ __forceinline__ void stage_slices(const AttnArgs& a, int beta, int h, int tau, _Float16* dst) {
-  constexpr int NG = D / C;
-  constexpr int NCH = D / 8;
-  constexpr int NTH = kNW * 64;
-  constexpr int PER = (kCodes * D / 8 + NTH - 1) / NTH;   // 16-byte pieces per thread and slice
+struct SliceStage {
+  static constexpr int NG = D / C;
+  static constexpr int NCH = D / 8;
+  static constexpr int NTH = kNW * 64;
+  static constexpr int PER = (kCodes * D / 8 + NTH - 1) / NTH;   // 16-byte pieces per thread and slice
   u16x8 v[2][PER];
+  __device__ __forceinline__ void load(const AttnArgs& a, int beta, int h, int tau);
+  __device__ __forceinline__ void store(_Float16* dst) const;
+};
+template <int D, int C>
+__device__ __forceinline__ void SliceStage<D, C>::load(const AttnArgs& a, int beta, int h, int tau) {
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     const uint16_t* src = a.codebooks + ((((size_t)beta * 2 + kv) * a.H + h) * NG) * ((size_t)a.Tc * kCodes * C);
@@ -128,6 +134,9 @@ __device__ __forceinline__ void stage_slices(const AttnArgs& a, int beta, int h,
       }
     }
   }
+}
+template <int D, int C>
+__device__ __forceinline__ void SliceStage<D, C>::store(_Float16* dst) const {
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
 #pragma unroll
@@ -218,36 +227,32 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
   const int W = wph * kNW;          // waves on this query head
   const int wg = kw * kNW + wave;   // this wave among them
 
-  // the work list's length, and (one wave of the launch) the sequences' first tiles
-  int total = 0;
+  SliceStage<D, C> slices;
+  slices.load(a, beta, h, tau);
+  // the work list's length, and (one wave of the launch) the sequences' first units;
+  // the first 64 sequences' counts and inclusive sums stay in registers
+  int total = 0, n_first = 0, incl_first = 0;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int b = b0 + lane;
     const int n = b < a.B ? seq_tiles(a, b).total : 0;
-    if (hq == 0 && wg == 0) {
-      const int incl = total + wave_incl_scan(n);
-      if (b < a.B) a.tile_start[b] = incl - n;
-    }
+    const int incl = total + wave_incl_scan(n);
+    if (b0 == 0) { n_first = n; incl_first = incl; }
+    if (hq == 0 && wg == 0 && b < a.B) a.tile_start[b] = incl - n;
     total += wave_sum_i(n);
   }
   if (hq == 0 && wg == 0 && lane == 0) a.tile_start[a.B] = total;
   total = __builtin_amdgcn_readfirstlane(total);   // wave-uniform: keep it in a scalar register
-  // a workgroup with no tiles leaves before staging the slices
-  if (range_lo(kw * kNW, total, W) == range_lo((kw + 1) * kNW, total, W)) return;
   const int w_lo = __builtin_amdgcn_readfirstlane(range_lo(wg, total, W));
   const int w_hi = __builtin_amdgcn_readfirstlane(range_lo(wg + 1, total, W));
 
-  stage_slices<D, C>(a, beta, h, tau, kl);
-  __syncthreads();
-  if (w_lo == w_hi) return;
-
-  // the sequence holding tile w_lo, and its first tile
+  // the sequence holding unit w_lo, and its first unit
   int b = 0, tb = 0;
-  {
+  if (w_lo < w_hi) {
     int base = 0;
     for (int b0 = 0; b0 < a.B; b0 += 64) {
       const int bb = b0 + lane;
-      const int n = bb < a.B ? seq_tiles(a, bb).total : 0;
-      const int incl = base + wave_incl_scan(n);
+      const int n = b0 == 0 ? n_first : (bb < a.B ? seq_tiles(a, bb).total : 0);
+      const int incl = b0 == 0 ? incl_first : base + wave_incl_scan(n);
       const uint64_t hit = __ballot(bb < a.B && incl - n <= w_lo && w_lo < incl);
       if (hit) {
         const int src = __ffsll((unsigned long long)hit) - 1;
@@ -260,6 +265,10 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
   }
   b = __builtin_amdgcn_readfirstlane(b);
   tb = __builtin_amdgcn_readfirstlane(tb);
+
+  slices.store(kl);
+  __syncthreads();
+  if (w_lo == w_hi) return;
 
   const int qt = lane & 3, t = lane >> 2;       // lane quarter, token in tile
   // Chunk order per lane, so the lanes of one LDS access phase hit distinct banks:
@@ -582,21 +591,22 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
 }
 
 // ------------------------------------------------------------------ merge
-// One workgroup per (b, hq), one thread per output channel.  The split partials
-// (m_i, l_i, o_i) are in log2 units: m = max m_i, l = sum l_i 2^(m_i - m),
-// out = sum o_i 2^(m_i - m) / l, lse = (m + log2 l) ln 2.  The (m_i, l_i) pairs are
-// read in one round into LDS, the weights computed there, then each channel's S
-// partial values are loaded together.
+// One workgroup per (b, hq).  The split partials (m_i, l_i, o_i) are in log2 units:
+// m = max m_i, l = sum l_i 2^(m_i - m), out = sum o_i 2^(m_i - m) / l,
+// lse = (m + log2 l) ln 2.  The (m_i, l_i) pairs are read in one round into LDS and the
+// weights computed there; then each (channel, record group) thread sums its records.
 // With a.tile_start set (decode), the records of (b, hq) are those of the waves whose
 // token-balanced ranges meet sequence b's tiles: record wg + b of head hq for wg in a
 // window found from the tile counts, each checked (a wave with an empty intersection
 // wrote nothing there).  Otherwise the n_rec records of an item are consecutive.
 constexpr int kMergeMax = 4096;   // candidate records per (b, hq) at most (the host checks)
-__global__ __launch_bounds__(128) void merge_kernel(AttnArgs a, int cap) {
+constexpr int kMergeThreads = 512;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int cap) {
   extern __shared__ __align__(16) unsigned char merge_smem[];
   float2* sml = (float2*)merge_smem;            // [cap]
   float* s_w = (float*)(sml + cap);             // [cap]
   __shared__ float s_ml[2];
+  __shared__ float s_part[kMergeThreads];       // per (record group, channel) sums
   const int item = blockIdx.x;           // b * Hq + hq
   const int D2 = a.d + 2;
   const int tid = threadIdx.x;
@@ -639,20 +649,33 @@ __global__ __launch_bounds__(128) void merge_kernel(AttnArgs a, int cap) {
   }
   __syncthreads();
   const float M = s_ml[0], Ls = s_ml[1];
-  const int ch = tid;
-  if (ch < a.d) {
-    float acc0 = 0.f, acc1 = 0.f;
-    int i = 0;
-    // records with weight 0 are not read (unwritten candidates may hold anything)
-    for (; i + 1 < S; i += 2) {
-      const float w0 = s_w[i], w1 = s_w[i + 1];
-      const float o0 = w0 != 0.f ? rec[(size_t)i * D2 + 2 + ch] : 0.f;
-      const float o1 = w1 != 0.f ? rec[(size_t)(i + 1) * D2 + 2 + ch] : 0.f;
-      acc0 = fmaf(o0, w0, acc0);
-      acc1 = fmaf(o1, w1, acc1);
+  // Thread (group, channel): record group g sums records g, g + NGR, ... with 8 loads in
+  // flight; the groups are then added in order.  Records with weight 0 are not read
+  // (unwritten candidates may hold anything).
+  const int NGR = kMergeThreads / a.d;
+  const int ch = tid % a.d, g = tid / a.d;
+  float acc = 0.f;
+  if (g < NGR) {
+    float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int i = g;
+    for (; i + 7 * NGR < S; i += 8 * NGR) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = s_w[i + u * NGR];
+        const float o = w != 0.f ? rec[(size_t)(i + u * NGR) * D2 + 2 + ch] : 0.f;
+        p[u] = fmaf(o, w, p[u]);
+      }
     }
-    if (i < S && s_w[i] != 0.f) acc0 = fmaf(rec[(size_t)i * D2 + 2 + ch], s_w[i], acc0);
-    a.out[(size_t)item * a.d + ch] = Ls > 0.f ? (acc0 + acc1) / Ls : 0.f;
+    for (; i < S; i += NGR)
+      if (s_w[i] != 0.f) p[0] = fmaf(rec[(size_t)i * D2 + 2 + ch], s_w[i], p[0]);
+    acc = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  }
+  s_part[tid] = acc;
+  __syncthreads();
+  if (tid < a.d) {
+    float sum = 0.f;
+    for (int k = 0; k < NGR; ++k) sum += s_part[k * a.d + tid];
+    a.out[(size_t)item * a.d + tid] = Ls > 0.f ? sum / Ls : 0.f;
   }
   if (a.lse && tid == 0) a.lse[item] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
 }
@@ -693,7 +716,8 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
                      a.rope, wph);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(n_items), dim3(128), (size_t)(a.n_waves + 1) * 12, s, a, a.n_waves + 1);
+  hipLaunchKernelGGL(merge_kernel, dim3(n_items), dim3(kMergeThreads), (size_t)(a.n_waves + 1) * 12, s, a,
+                     a.n_waves + 1);
   return hipGetLastError();
 }
 
@@ -723,7 +747,7 @@ bool attn_supported(int d, int c) {
 
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
   if (a.n_rec > kMergeMax) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), (size_t)a.n_rec * 12, s, a, a.n_rec);
+  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(kMergeThreads), (size_t)a.n_rec * 12, s, a, a.n_rec);
   return hipGetLastError();
 }
 
