@@ -92,6 +92,26 @@ def test_split_counts_and_page_permutation():
     np.testing.assert_array_equal(o3.cpu().numpy(), o2.cpu().numpy())
 
 
+def test_many_sequences_token_balanced_split():
+    """70 sequences (more than one 64-lane scan block) with lengths U[1, 400] and GQA 2:
+    every (b, head) against the oracle for automatic, one-workgroup and 1008-wave splits
+    (the last leaves most waves with empty ranges); the three agree closely."""
+    print("\ncase B=70 lengths U[1,400] splits 0/1/1000", flush=True)
+    rl_ = np.random.default_rng(synth.seed_for(40, synth.STREAM_LENGTHS))
+    lengths = synth.uniform_lengths(rl_, 70, 1, 400)
+    cache = build_cache(40, 70, lengths, 2, 128, 4, 4, 32, 4, 16, Hq=4, books="random", index="random")
+    dc = to_dev(cache)
+    t = 3
+    ro, rl = cache.oracle_attn(t)
+    outs = []
+    for S in (0, 1, 1000):
+        out, lse = gpu_attn(dc, t, n_splits=S)
+        check(out, lse, ro, rl, f"splits={S}")
+        outs.append(out.cpu().numpy())
+    for o in outs[1:]:
+        np.testing.assert_allclose(o, outs[0], rtol=2e-5, atol=2e-6)
+
+
 def test_index_pool_beyond_4gib():
     """An index pool over 4 GiB takes the kernel's 64-bit page addressing.  The same pages
     moved to the top of such a pool give the same bits as the compact pool (page
