@@ -182,13 +182,13 @@ def pmc_summary(fetch_dir, write_dir):
 
     cf, cw = calib(fetch), calib(write)
     sf, sw = CALIB_BYTES / cf, CALIB_BYTES / cw
-    af, na = per_launch(fetch, "attn_kernel<128, 8, false>")
-    aw, _ = per_launch(write, "attn_kernel<128, 8, false>")
+    af, na = per_launch(fetch, "attn_kernel<128, 8, false")
+    aw, _ = per_launch(write, "attn_kernel<128, 8, false")
     mf, nm = per_launch(fetch, "merge_kernel")
     mw, _ = per_launch(write, "merge_kernel")
     traffic = (af + mf) * sf + (aw + mw) * sw
     algo = algorithmic_bytes_per_call(synth_q_end())
-    print("# HBM traffic of one decode-attention call (attn_kernel<128, 8, false> + merge_kernel),")
+    print("# HBM traffic of one decode-attention call (attn_kernel<128, 8, false, false> + merge_kernel),")
     print("# Ouro-1.4B-shaped 32K decode bench\n")
     print("Commands (repository root $REPO on the GPU host):\n")
     for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -219,13 +219,13 @@ def pmc_instructions(directory):
     for c in INSTR_COUNTERS:
         d = _pmc_per_dispatch(directory, c)
         tot = 0.0
-        for key in ("attn_kernel<128, 8, false>", "merge_kernel"):
+        for key in ("attn_kernel<128, 8, false", "merge_kernel"):
             v = [x for k, xs in d.items() if key in k for x in xs]
             tot += sum(v) / len(v) if v else float("nan")
         per[c] = tot
     valu = per["SQ_INSTS_VALU"] - per["SQ_INSTS_MFMA"]
     bound_us = valu * VALU_CYCLES / SIMDS / (CLOCK_GHZ * 1e3)
-    print("# Instruction counts of one decode-attention call (attn_kernel<128, 8, false> + merge_kernel),")
+    print("# Instruction counts of one decode-attention call (attn_kernel<128, 8, false, false> + merge_kernel),")
     print("# Ouro-1.4B-shaped 32K decode bench\n")
     print("Command (repository root $REPO on the GPU host):\n")
     print(f"    cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {' '.join(INSTR_COUNTERS)} --output-format csv "

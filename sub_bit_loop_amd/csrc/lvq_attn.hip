@@ -352,14 +352,22 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
           qw[2 * lane] = (x * cs.x - y * cs.y) * a.scale_log2e;
           qw[2 * lane + 1] = (y * cs.x + x * cs.y) * a.scale_log2e;
         }
-        const float* e1 = rope + (size_t)(a.rope_tiles + t) * D;
+        // pairs j = qt*QP + 8*(v ^ kswap) + i of register block v, read at constant offsets
+        // from one base per block (no per-pair offsets held across the sequence loop)
+        // (32-bit element offsets from the uniform table base)
 #pragma unroll
-        for (int jj = 0; jj < QP; ++jj) {
-          const int j = qt * QP + 8 * ((jj / 8) ^ kswap) + (jj % 8);
-          const float A = qw[2 * j], Bq = qw[2 * j + 1];
-          const float c1 = e1[2 * j], s1 = e1[2 * j + 1];
-          F[jj] = A * c1 + Bq * s1;
-          Gc[jj] = Bq * c1 - A * s1;
+        for (int v = 0; v < KPC; ++v) {
+          const int jb = qt * QP + 8 * (v ^ kswap);
+          const float* qwv = qw + 2 * jb;
+          const uint32_t e1v = (uint32_t)((a.rope_tiles + t) * D + 2 * jb);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int jj = 8 * v + i;
+            const float A = qwv[2 * i], Bq = qwv[2 * i + 1];
+            const float c1 = rope[e1v + 2 * i], s1 = rope[e1v + 2 * i + 1];
+            F[jj] = A * c1 + Bq * s1;
+            Gc[jj] = Bq * c1 - A * s1;
+          }
         }
       }
       float m = kNoMax, l = 0.f;
@@ -406,7 +414,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
           in.vw = *(const uint32_t*)(head_rows + (po + o_v));
         }
         const int tile_idx = min((8 * P0) / kTile, a.rope_tiles - 1);
-        in.e0 = *(const float2*)(rope + (size_t)tile_idx * D + 2 * (lane % HALF));
+        in.e0 = *(const float2*)(rope + (uint32_t)(tile_idx * D + 2 * (lane % HALF)));
         return in;
       };
       auto tile = [&](int P0, const TileIn& in, int buf) {
