@@ -106,29 +106,35 @@ int check_attn(const void* q, const void* page_table, const void* index_pages,
 
 // ------------------------------------------------------------------ multi-row attention
 struct RowsPlan {
-  int n_rb, n_chunks, chunk_pages;
+  int n_rb;      // row blocks of 16 per KV head
+  int n_waves;   // waves per (KV head, row block) work list
+  int n_rec;     // records per list and row: n_waves + B
 };
 
+// Token-balanced split of the multi-row kernel: each (KV head, row block) work list
+// (every sequence's 16-key tiles) is cut into n_waves equal ranges.  Automatic sizing
+// gives each list an equal share of the compute units (one workgroup of 8 waves each),
+// but not more waves than about 4 tiles each of the largest possible list.
 RowsPlan plan_rows(const lvq_rows_shape& s) {
   RowsPlan p;
   const int g = s.Hq / s.H;
   p.n_rb = (s.NQ * g + 15) / 16;
-  const int coded_pages = (s.max_prefix + lvq::kPage - 1) / lvq::kPage;
   const int w = lvq::rows_waves_per_group();
-  int n = s.n_splits;
-  if (n <= 0) {
-    const long items = (long)s.B * s.H * p.n_rb;
-    n = (int)((2048 + items - 1) / items);
-    const int by_len = coded_pages / 16;            // at least 8 tiles per chunk
-    if (n > by_len) n = by_len;
+  const int lists = s.H * p.n_rb;
+  const int max_wph = (lvq::merge_max_records() - 1) / w;
+  int wph;
+  if (s.n_splits > 0) {
+    wph = (s.n_splits + w - 1) / w;
+  } else {
+    wph = kComputeUnits / lists;
+    const long tiles_bound = (long)s.B * ((s.max_prefix + 15) / 16 + 4L * (3 + (s.NQ + 15) / 16));
+    const long by_work = (tiles_bound + 4L * w - 1) / (4L * w);
+    if (wph > by_work) wph = (int)by_work;
   }
-  if (n < 1) n = 1;
-  n = (n + w - 1) / w * w;                         // whole workgroups
-  if (n > 1016) n = 1016;                          // bound on splits per row
-  int cp = (coded_pages + n - 1) / n;
-  cp = (cp + 1) / 2 * 2;
-  p.chunk_pages = cp < 2 ? 2 : cp;
-  p.n_chunks = n;
+  if (wph < 1) wph = 1;
+  if (wph > max_wph) wph = max_wph;
+  p.n_waves = wph * w;
+  p.n_rec = p.n_waves + s.B;
   return p;
 }
 
@@ -163,7 +169,9 @@ int check_rows(const void* q, const void* k_new, const void* v_new, const void* 
 
 size_t rows_workspace(const lvq_rows_shape& s) {
   const RowsPlan p = plan_rows(s);
-  return (size_t)s.B * s.NQ * s.Hq * p.n_chunks * (s.d + 2) * sizeof(float);
+  // records [H * n_rb][n_rec][16 rows][d + 2], then the row blocks' first units [n_rb][B + 1]
+  return (size_t)s.H * p.n_rb * p.n_rec * 16 * (s.d + 2) * sizeof(float) +
+         (size_t)p.n_rb * (s.B + 1) * sizeof(int);
 }
 
 // Decode with many query heads per KV head runs on the multi-row kernel: at 8 or more
@@ -570,8 +578,9 @@ int lvq_rows_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
   a.max_prefix = s.max_prefix;
   a.rope_tiles = (s.rope_max_len + lvq::rope_tile() - 1) / lvq::rope_tile();
   a.n_rb = p.n_rb;
-  a.n_chunks = p.n_chunks;
-  a.chunk_pages = p.chunk_pages;
+  a.n_waves = p.n_waves;
+  a.n_rec = p.n_rec;
+  a.tile_start = (int*)((char*)ws + (size_t)s.H * p.n_rb * p.n_rec * 16 * (s.d + 2) * sizeof(float));
   const float scale = s.scale > 0.f ? s.scale : 1.0f / sqrtf((float)s.d);
   a.scale_log2e = scale * 1.4426950408889634f;
   hipError_t e = lvq::launch_rows(a, (hipStream_t)stream);
@@ -580,11 +589,16 @@ int lvq_rows_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
   m.part = a.part;
   m.out = out;
   m.lse = lse;
-  m.B = s.B * s.NQ;
+  m.B = s.B;
+  m.NQ = s.NQ;
+  m.H = s.H;
   m.Hq = s.Hq;
   m.d = s.d;
-  m.n_chunks = p.n_chunks;
-  m.n_rec = p.n_chunks;
+  m.n_rb = p.n_rb;
+  m.n_waves = p.n_waves;
+  m.n_rec = p.n_rec;
+  m.tile_start = a.tile_start;
+  m.merge_rows = 1;
   return device_status(lvq::launch_merge(m, (hipStream_t)stream), "lvq_rows_attn merge launch");
 }
 

@@ -603,10 +603,12 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
 // m = max m_i, l = sum l_i 2^(m_i - m), out = sum o_i 2^(m_i - m) / l,
 // lse = (m + log2 l) ln 2.  The (m_i, l_i) pairs are read in one round into LDS and the
 // weights computed there; then each (channel, record group) thread sums its records.
-// With a.tile_start set (decode), the records of (b, hq) are those of the waves whose
-// token-balanced ranges meet sequence b's tiles: record wg + b of head hq for wg in a
-// window found from the tile counts, each checked (a wave with an empty intersection
-// wrote nothing there).  Otherwise the n_rec records of an item are consecutive.
+// The records of an item are those of the waves whose token-balanced ranges meet
+// sequence b's units in the item's work list: record wg + b of the list for wg in a
+// window found from the unit counts, each checked (a wave with an empty intersection
+// wrote nothing there).  Decode (merge_rows = 0): item b * Hq + hq, list hq, one row per
+// record.  Multi-row (merge_rows = 1): item (b * NQ + i) * Hq + hq, list = (KV head,
+// block of 16 rows), records hold 16 rows.
 constexpr int kMergeMax = 4096;   // candidate records per (b, hq) at most (the host checks)
 constexpr int kMergeThreads = 512;
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int cap) {
@@ -618,28 +620,35 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int ca
   const int item = blockIdx.x;           // b * Hq + hq
   const int D2 = a.d + 2;
   const int tid = threadIdx.x;
-  int S;
-  const float* rec;
-  if (a.tile_start) {
-    const int b = item / a.Hq, hq = item % a.Hq;
-    const int tb = a.tile_start[b], tb1 = a.tile_start[b + 1], total = a.tile_start[a.B];
-    const int W = a.n_waves;
-    int lo = 0, hi = -1;
-    if (tb < tb1) {   // then total > 0
-      lo = max(0, (int)(((long)(tb + 1) * W + total - 1) / total) - 2);
-      hi = min(W - 1, (int)(((long)tb1 * W + total - 1) / total));
-    }
-    S = min(hi - lo + 1, cap);   // hi - lo + 1 <= W + 1 = cap
-    rec = a.part + ((size_t)hq * a.n_rec + lo + b) * D2;
-    for (int i = tid; i < S; i += blockDim.x) {
-      const int wg = lo + i;
-      const bool meets = max(range_lo(wg, total, W), tb) < min(range_lo(wg + 1, total, W), tb1);
-      sml[i] = meets ? *(const float2*)(rec + (size_t)i * D2) : make_float2(-__builtin_inff(), 0.f);
-    }
+  int b, list, row = 0, rec_rows = 1;
+  const int* ts = a.tile_start;
+  if (a.merge_rows) {
+    const int hq = item % a.Hq, bi = item / a.Hq;
+    b = bi / a.NQ;
+    const int g = a.Hq / a.H;
+    const int r_abs = (bi % a.NQ) * g + hq % g;
+    list = (hq / g) * a.n_rb + r_abs / 16;
+    row = r_abs % 16;
+    rec_rows = 16;
+    ts += (size_t)(r_abs / 16) * (a.B + 1);
   } else {
-    S = min(a.n_rec, cap);
-    rec = a.part + (size_t)item * a.n_rec * D2;
-    for (int i = tid; i < S; i += blockDim.x) sml[i] = *(const float2*)(rec + (size_t)i * D2);
+    b = item / a.Hq;
+    list = item % a.Hq;
+  }
+  const int tb = ts[b], tb1 = ts[b + 1], total = ts[a.B];
+  const int W = a.n_waves;
+  int lo = 0, hi = -1;
+  if (tb < tb1) {   // then total > 0
+    lo = max(0, (int)(((long)(tb + 1) * W + total - 1) / total) - 2);
+    hi = min(W - 1, (int)(((long)tb1 * W + total - 1) / total));
+  }
+  const int S = min(hi - lo + 1, cap);   // hi - lo + 1 <= W + 1 = cap
+  const size_t rstride = (size_t)rec_rows * D2;   // between consecutive records of a list
+  const float* rec = a.part + (((size_t)list * a.n_rec + lo + b) * rec_rows + row) * D2;
+  for (int i = tid; i < S; i += blockDim.x) {
+    const int wg = lo + i;
+    const bool meets = max(range_lo(wg, total, W), tb) < min(range_lo(wg + 1, total, W), tb1);
+    sml[i] = meets ? *(const float2*)(rec + (size_t)i * rstride) : make_float2(-__builtin_inff(), 0.f);
   }
   __syncthreads();
   if (tid < 64) {
@@ -670,12 +679,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int ca
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float w = s_w[i + u * NGR];
-        const float o = w != 0.f ? rec[(size_t)(i + u * NGR) * D2 + 2 + ch] : 0.f;
+        const float o = w != 0.f ? rec[(size_t)(i + u * NGR) * rstride + 2 + ch] : 0.f;
         p[u] = fmaf(o, w, p[u]);
       }
     }
     for (; i < S; i += NGR)
-      if (s_w[i] != 0.f) p[0] = fmaf(rec[(size_t)i * D2 + 2 + ch], s_w[i], p[0]);
+      if (s_w[i] != 0.f) p[0] = fmaf(rec[(size_t)i * rstride + 2 + ch], s_w[i], p[0]);
     acc = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   }
   s_part[tid] = acc;
@@ -754,8 +763,10 @@ bool attn_supported(int d, int c) {
 }
 
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
-  if (a.n_rec > kMergeMax) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(kMergeThreads), (size_t)a.n_rec * 12, s, a, a.n_rec);
+  if (a.n_waves + 1 > kMergeMax || !a.tile_start || a.d > kMergeThreads || kMergeThreads % a.d) return hipErrorInvalidValue;
+  const int items = a.B * (a.merge_rows ? a.NQ : 1) * a.Hq;
+  hipLaunchKernelGGL(merge_kernel, dim3(items), dim3(kMergeThreads), (size_t)(a.n_waves + 1) * 12, s, a,
+                     a.n_waves + 1);
   return hipGetLastError();
 }
 

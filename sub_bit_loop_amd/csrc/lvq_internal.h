@@ -59,11 +59,13 @@ struct RowsArgs {
   const int32_t* prefix_len;  // [B] paged tokens, visible to every query
   const int32_t* q_end;       // [B]
   const float* rope;
-  float* part;                // [B * NQ][Hq][n_chunks][d + 2]
+  float* part;                // [H * n_rb][n_rec][16 rows][d + 2]
   int t, B, NQ, H, Hq, d, T, Tc, G;
   int n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages, max_prefix, rope_tiles;
-  int n_rb;                   // row blocks of 16 per (b, KV head)
-  int n_chunks, chunk_pages;  // key chunks per row block; coded pages per chunk (even)
+  int n_rb;                   // row blocks of 16 per KV head
+  int n_waves;                // waves per (KV head, row block) list
+  int n_rec;                  // records per list and row: n_waves + B
+  int* tile_start;            // [n_rb][B + 1] first unit of each sequence in a row block's list
   float scale_log2e;
 };
 bool rows_supported(int d, int c);
@@ -111,20 +113,20 @@ struct AttnArgs {
   const int32_t* seq_len;
   const int32_t* q_end;
   const float* rope;          // tile rows [ntile][d/2][2], offset rows [16][d/2][2], theta [d/2] (double)
-  float* part;                // partials [B][Hq][n_chunks][d + 2]
+  float* part;                // partial records [lists][n_rec][rows][d + 2]
   float* out;                 // [B][Hq][d]
   float* lse;                 // [B][Hq] or null
   float* scores;              // [B][Hq][max_seq_len] or null (probe)
   int t, B, H, Hq, d, T, Tc, G;
   int n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages, max_seq_len, rope_tiles;
-  int n_chunks;               // multi-row kernel: coded chunks per (row, hq)
-  int chunk_pages;            // multi-row kernel: pages per chunk, multiple of 8
-  int n_waves;                // decode kernel: waves per query head (token-balanced ranges)
-  int n_rec;                  // partial records per query head (decode) or per item (multi-row)
-  int* tile_start;            // decode: [B + 1] first tile of each sequence in the work list
+  int n_waves;                // waves per work list (token-balanced ranges)
+  int n_rec;                  // records per work list: n_waves + B
+  int* tile_start;            // [lists' row blocks][B + 1] first unit of each sequence
+  int merge_rows;             // merge input: 0 decode records, 1 multi-row records (16 rows)
+  int NQ, n_rb;               // multi-row merge: queries per sequence, row blocks per KV head
   float scale_log2e;          // softmax scale * log2(e)
 };
-hipError_t launch_merge(const AttnArgs& a, hipStream_t s);   // merge of a.part into a.out / a.lse
+hipError_t launch_merge(const AttnArgs& a, hipStream_t s);   // merge of multi-row records into a.out / a.lse
 bool attn_supported(int d, int c);
 int rope_tile();   // positions per row of the first RoPE table part
 int attn_waves_per_group();   // waves per decode-attention workgroup

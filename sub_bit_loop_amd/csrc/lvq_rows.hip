@@ -10,9 +10,11 @@
 // summary notes prefill runs slightly slower than bf16), and GQA decode, where the
 // query heads of one KV head are the rows.
 //
-// Design (MI355X): a workgroup owns 16 query rows of one (sequence, KV head) and 8
-// waves; each wave walks one chunk of keys, 16 keys per tile.  Each key is rebuilt and
-// rotated once per tile in float32 and shared by all 16 rows through v_mfma_f32_16x16x4f32:
+// Design (MI355X): a workgroup of 8 waves owns 16 query rows (a row block) of one KV
+// head; the (KV head, row block) work list -- every sequence's 16-key tiles in order --
+// is cut into equal ranges, one per wave (token-balanced, as in the decode kernel), so
+// mixed sequence lengths keep every wave busy.  Each key is rebuilt and rotated once per
+// tile in float32 and shared by all 16 rows through v_mfma_f32_16x16x4f32:
 //  * lane (key j, quarter k) holds key j's channel pairs [16k, 16k+16) with their
 //    partners + d/2, rebuilt by four 16-byte LDS gathers and rotated in registers (the
 //    rotation of a pair stays inside the lane); those 32 values are its B operands of
@@ -81,10 +83,49 @@ __device__ __forceinline__ float group16_sum(float v) {
   for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   return v;
 }
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    v += lane >= off ? u : 0;
+  }
+  return v;
+}
+
+// Token-balanced work split, as in the decode kernel.  The work list of one (KV head,
+// row block) is the units of sequences 0..B-1 in order: one per coded tile (two pages),
+// then kBfCostR per virtual tile (the bf16 sink and recent tiles, then the new-key tiles
+// the block's rows can see).  The W waves of a list take equal contiguous ranges
+// [wg*total/W, (wg+1)*total/W) and write one partial record per (row, sequence their
+// range meets), at record wg + b of the list.
+constexpr int kBfCostR = 4;
+struct RowSeq {
+  int coded;   // coded tiles (= their units)
+  int n_vt;    // virtual tiles
+  int total;   // units
+};
+__device__ __forceinline__ RowSeq row_seq(const RowsArgs& a, int b, int n_new) {
+  const int L = min(max(a.prefix_len[b], 0), a.max_prefix);
+  const int qe = max(min(a.q_end[b] & ~7, L), 0);
+  const int ns = min(a.n_sink, L);
+  const int r0 = max(qe, a.n_sink);
+  const int vt_lo = r0 / kKeys;
+  const int vt_hi = L > r0 ? (L - 1) / kKeys + 1 : vt_lo;
+  const int coded = a.n_index_pages > 0 ? ((qe >> 3) + 1) >> 1 : 0;
+  const int n_vt = (ns > 0 ? 1 : 0) + (vt_hi - vt_lo) + n_new;
+  return {coded, n_vt, coded + kBfCostR * n_vt};
+}
+__device__ __forceinline__ int range_lo(int wg, int total, int W) { return (int)((long)wg * total / W); }
 
 template <int C>
 __global__ __launch_bounds__(kRW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void rows_kernel(RowsArgs a, int n_cg) {
+void rows_kernel(RowsArgs a, int wph) {
   constexpr int D = kD, HALF = D / 2, NG = D / C, NCH = D / 8;
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* kl = (_Float16*)smem;
@@ -95,33 +136,77 @@ void rows_kernel(RowsArgs a, int n_cg) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int bid = blockIdx.x;
-  const int cg = bid % n_cg; bid /= n_cg;
-  const int rb = bid % a.n_rb; bid /= a.n_rb;
-  const int h = bid % a.H; bid /= a.H;
-  const int b = bid;
+  const int n_lists = a.H * a.n_rb;
+  const int list = blockIdx.x % n_lists, kw = blockIdx.x / n_lists;
+  const int h = list / a.n_rb, rb = list % a.n_rb;
   const int g = a.Hq / a.H;
   const int R = a.NQ * g;
   const int beta = a.t / a.Tc, tau = a.t % a.Tc, nblk = a.T / a.Tc;
-  const int chunk = cg * kRW + wave;
-  const int L = min(max(a.prefix_len[b], 0), a.max_prefix);
-  const int qe = min(a.q_end[b] & ~7, L);
-  const int P_lo = chunk * a.chunk_pages;
-  const int P_hi = a.n_index_pages > 0 ? min(qe >> 3, P_lo + a.chunk_pages) : P_lo;
-  const bool active = chunk < a.n_chunks;
-  const int ns = min(a.n_sink, L);
-  const int r0 = max(qe, a.n_sink);
-  const int vt_lo = r0 / kKeys;
-  const int vt_hi = L > r0 ? (L - 1) / kKeys + 1 : vt_lo;
+  const int W = wph * kRW;          // waves on this list
+  const int wg = kw * kRW + wave;   // this wave among them
   // new-key tiles: up to the largest query index among this block's rows
   const int i_max = min(a.NQ - 1, (rb * kRows + kRows - 1) / g);
   const int n_new = a.k_new ? i_max / kKeys + 1 : 0;
-  const int n_vt = (ns > 0 ? 1 : 0) + (vt_hi - vt_lo) + n_new;
+
+  // the list's length and (one wave per row block) the sequences' first units
+  int* tstart = a.tile_start + (size_t)rb * (a.B + 1);
+  int total = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int n = bb < a.B ? row_seq(a, bb, n_new).total : 0;
+    if (h == 0 && wg == 0) {
+      const int incl = total + wave_incl_scan(n);
+      if (bb < a.B) tstart[bb] = incl - n;
+    }
+    total += wave_sum_i(n);
+  }
+  if (h == 0 && wg == 0 && lane == 0) tstart[a.B] = total;
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int w_lo = __builtin_amdgcn_readfirstlane(range_lo(wg, total, W));
+  const int w_hi = __builtin_amdgcn_readfirstlane(range_lo(wg + 1, total, W));
 
   stage_slice_rows<C>(a, beta, 0, h, tau, kl);
   stage_slice_rows<C>(a, beta, 1, h, tau, vl);
   __syncthreads();
-  if (!active) return;
+  if (w_lo == w_hi) return;
+
+  // the sequence holding unit w_lo, and its first unit
+  int b = 0, tb = 0;
+  {
+    int base = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int bb = b0 + lane;
+      const int n = bb < a.B ? row_seq(a, bb, n_new).total : 0;
+      const int incl = base + wave_incl_scan(n);
+      const uint64_t hit = __ballot(bb < a.B && incl - n <= w_lo && w_lo < incl);
+      if (hit) {
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        b = b0 + src;
+        tb = __shfl(incl - n, src);
+        break;
+      }
+      base = __shfl(incl, 63);
+    }
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  tb = __builtin_amdgcn_readfirstlane(tb);
+
+  int pos_t = w_lo;
+  while (pos_t < w_hi && b < a.B) {
+  const RowSeq seq = row_seq(a, b, n_new);
+  const int u_lo = pos_t - tb, u_hi = min(w_hi - tb, seq.total);
+  if (u_lo < u_hi) {
+  const int L = min(max(a.prefix_len[b], 0), a.max_prefix);
+  const int qe = max(min(a.q_end[b] & ~7, L), 0);
+  const int P_lo = 2 * u_lo;
+  const int P_hi = min(2 * min(u_hi, seq.coded), qe >> 3);
+  const int ns = min(a.n_sink, L);
+  const int r0 = max(qe, a.n_sink);
+  const int vt_lo = r0 / kKeys;
+  const int vt_hi = L > r0 ? (L - 1) / kKeys + 1 : vt_lo;
+  // virtual tiles whose first unit lies in the range
+  const int vt_first = (max(u_lo, seq.coded) - seq.coded + kBfCostR - 1) / kBfCostR;
+  const int vt_end = u_hi > seq.coded ? (u_hi - seq.coded + kBfCostR - 1) / kBfCostR : 0;
 
   const int j = lane & 15, kq = lane >> 4;     // key in tile / quarter (B side); row / quarter (A side)
   // A operands: rotated query rows, pairs [16 kq, 16 kq + 16) then their partners
@@ -255,7 +340,7 @@ void rows_kernel(RowsArgs a, int n_cg) {
   };
 
   // ---- virtual tiles: bf16 sink, recent window, new keys
-  for (int vt = chunk; vt < n_vt; vt += a.n_chunks) {
+  for (int vt = vt_first; vt < vt_end; ++vt) {
     const bool sink_tile = ns > 0 && vt == 0;
     const int after_sink = vt - (ns > 0 ? 1 : 0);
     const bool new_tile = after_sink >= vt_hi - vt_lo;
@@ -433,8 +518,7 @@ void rows_kernel(RowsArgs a, int n_cg) {
     const float l = group16_sum(lp[r]);
     const int ra = rb * kRows + 4 * kq + r;
     if (ra < R) {
-      const int qi = ra / g, hq = h * g + ra % g;
-      float* rec = a.part + ((((size_t)b * a.NQ + qi) * a.Hq + hq) * a.n_chunks + chunk) * (D + 2);
+      float* rec = a.part + ((((size_t)list * a.n_rec + wg + b) * kRows) + 4 * kq + r) * (D + 2);
       if (j == 0) { rec[0] = m[r]; rec[1] = l; }
       f32x4 o0 = {O[0][r], O[1][r], O[2][r], O[3][r]};
       f32x4 o1 = {O[4][r], O[5][r], O[6][r], O[7][r]};
@@ -442,6 +526,11 @@ void rows_kernel(RowsArgs a, int n_cg) {
       *(f32x4*)(rec + 2 + 8 * j + 4) = o1;
     }
   }
+  }   // u_lo < u_hi
+  pos_t = __builtin_amdgcn_readfirstlane(tb + u_hi);
+  tb = __builtin_amdgcn_readfirstlane(tb + seq.total);
+  b = __builtin_amdgcn_readfirstlane(b + 1);
+  }   // sequences
 }
 
 template <int C>
@@ -454,9 +543,10 @@ hipError_t launch_rows_t(const RowsArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int n_cg = (a.n_chunks + kRW - 1) / kRW;
-  const long grid = (long)n_cg * a.n_rb * a.H * a.B;
-  hipLaunchKernelGGL((rows_kernel<C>), dim3((unsigned)grid), dim3(kRW * 64), lds, s, a, n_cg);
+  const int wph = a.n_waves / kRW;   // workgroups per (KV head, row block)
+  if (wph < 1 || a.n_waves % kRW || a.n_rec != a.n_waves + a.B || !a.tile_start) return hipErrorInvalidValue;
+  const long grid = (long)wph * a.n_rb * a.H;
+  hipLaunchKernelGGL((rows_kernel<C>), dim3((unsigned)grid), dim3(kRW * 64), lds, s, a, wph);
   return hipGetLastError();
 }
 

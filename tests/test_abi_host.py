@@ -177,5 +177,8 @@ def test_rows_shape_validation(L):
     assert call(rs(max_pages=62)) == 1                  # 62 pages hold fewer than 500 tokens
     assert call(rs(d=64, G=16, Tc=2)) == 2              # multi-row kernel compiled for d = 128 only
     need = L.lvq_rows_attn_workspace_bytes(ctypes.byref(rs()))
-    assert need > 0 and need % (4 * 130) == 0
+    # records [H * row blocks][W + B][16 rows][d + 2] float32 + first units [row blocks][B + 1]:
+    # 1 row block (4 queries x 2 heads per KV head), W = 16 waves (2 workgroups: about 4
+    # units per wave of 32 coded + 16 virtual units)
+    assert need == 2 * 1 * (16 + 1) * 16 * 130 * 4 + 1 * 2 * 4
     assert call(rs(), ws_bytes=need - 1) == 3
