@@ -792,6 +792,26 @@ def mixed_bench(torch, lvq, synth, n_steps=64, warmup=3):
         f"{gbs:.0f} GB/s algorithmic ({gbs / HBM_PEAK_GBS * 100:.1f}% of peak)")
     del layers
     torch.cuda.empty_cache()
+    # the looped layer's call with 16 query heads over 2 KV heads (GQA 8, the multi-row kernel)
+    T_, Tc_, G_ = MIXED_LAYERS[0]
+    Hk = 2
+    c = G_ // Tc_
+    nblk, ng = T_ // Tc_, D // c
+    ipg = torch.randint(0, 256, (pool, nblk, Hk, 2, 8, ng), generator=gen, dtype=torch.uint8, device=dev)
+    bpg = torch.randn((n_bf16, T_, Hk, 2, 8, D), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    cbg = torch.randn((nblk, 2, Hk, ng, Tc_, 256, c), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    qg = synth.gen_queries_torch(gen, Bm, H, D, device=dev)
+    shg = lvq.make_shape(Bm, Hk, H, D, T_, Tc_, G_, N_SINK, max_pages, bf16_row, pool, n_bf16, Lmax, Lmax + 1, 0)
+    wsg = torch.empty(lvq.lvq_decode_attn_workspace_bytes(shg), dtype=torch.uint8, device=dev)
+
+    def gqa_call():
+        lvq.lvq_decode_attn(qg, pt, ipg, bpg, bt, cbg, 1, pos, seq_len, qe, rope, shg, out, lse, wsg)
+
+    gqa_s = _event_time(torch, gqa_call, 20)
+    gqa_bytes = coded * Hk * 2 * ng + bf16_tok * Hk * 2 * D * 2 + Hk * 2 * 256 * D * 2 + small
+    log(f"mixed B={Bm} GQA 8 looped call: {gqa_s * 1e6:.1f} us")
+    del ipg, bpg, cbg, wsg
+    torch.cuda.empty_cache()
     return {"workload": f"mixed serving decode: B={Bm}, L~U[{MIXED_LO},{MIXED_HI}] (sum {sum_l}), H={H}, "
                         f"d={D}; per step 8 looped calls (T=8, Tc=4, G=32) + 1 prelude call (T=1, Tc=1, "
                         f"G=32) + re-encode of 8 sequences' oldest recent page in both layers",
@@ -801,7 +821,9 @@ def mixed_bench(torch, lvq, synth, n_steps=64, warmup=3):
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "looped_call_us_last_t": round(last_call[0] * 1e6, 2),
             "prelude_call_us": round(last_call[1] * 1e6, 2),
-            "looped_call_algorithmic_bytes": per_layer[0], "prelude_call_algorithmic_bytes": per_layer[1]}
+            "looped_call_algorithmic_bytes": per_layer[0], "prelude_call_algorithmic_bytes": per_layer[1],
+            "gqa8_looped_call_us": round(gqa_s * 1e6, 2), "gqa8_looped_call_algorithmic_bytes": gqa_bytes,
+            "gqa8_note": "16 query heads over 2 KV heads, loop step 1 of the looped layer, same lengths"}
 
 
 NEEDLE_L, NEEDLE_COPIES = 65536, 8
