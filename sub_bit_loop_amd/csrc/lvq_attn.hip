@@ -332,6 +332,13 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
     const SeqTiles st = seq_tiles(a, b);
     const int u_lo = pos_t - tb, u_hi = min(w_hi - tb, st.total);
     if (u_lo < u_hi) {
+      // the lane's layout values again, from an opaque copy of the lane id, so nothing
+      // derived from them for this sequence is held in registers across the loop
+      int lane_s = lane;
+      asm volatile("" : "+v"(lane_s));
+      const int qt = lane_s & 3, t = lane_s >> 2;
+      const int kswap = (KPC == 2) ? (t & 1) : 0;
+      const int vrot = (NV == 4) ? ((t + 2 * (qt >> 1)) & 3) : (t & (NV - 1));
       const int L = max(min(a.seq_len[b], a.max_seq_len), 0);
       const int qe = max(min(a.q_end[b] & ~7, L), 0);
       const int ns = min(a.n_sink, L);
