@@ -208,7 +208,11 @@ void rows_kernel(RowsArgs a, int wph) {
   const int vt_first = (max(u_lo, seq.coded) - seq.coded + kBfCostR - 1) / kBfCostR;
   const int vt_end = u_hi > seq.coded ? (u_hi - seq.coded + kBfCostR - 1) / kBfCostR : 0;
 
-  const int j = lane & 15, kq = lane >> 4;     // key in tile / quarter (B side); row / quarter (A side)
+  // the lane's layout values from an opaque copy of the lane id, so nothing derived from
+  // them for this sequence is held in registers across the sequence loop
+  int lane_s = lane;
+  asm volatile("" : "+v"(lane_s));
+  const int j = lane_s & 15, kq = lane_s >> 4;   // key in tile / quarter (B side); row / quarter (A side)
   // A operands: rotated query rows, pairs [16 kq, 16 kq + 16) then their partners
   float qf[32];
   int row_q[4];                                  // query index of the 4 rows this lane holds in D layout
