@@ -127,7 +127,7 @@ RowsPlan plan_rows(const lvq_rows_shape& s) {
     wph = (s.n_splits + w - 1) / w;
   } else {
     wph = kComputeUnits / lists;
-    const long tiles_bound = (long)s.B * ((s.max_prefix + 15) / 16 + 4L * (3 + (s.NQ + 15) / 16));
+    const long tiles_bound = (long)s.B * ((s.max_prefix + 15) / 16 + 3 + (s.NQ + 15) / 16);
     const long by_work = (tiles_bound + 4L * w - 1) / (4L * w);
     if (wph > by_work) wph = (int)by_work;
   }

@@ -101,10 +101,12 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // Token-balanced work split, as in the decode kernel.  The work list of one (KV head,
 // row block) is the units of sequences 0..B-1 in order: one per coded tile (two pages),
 // then kBfCostR per virtual tile (the bf16 sink and recent tiles, then the new-key tiles
-// the block's rows can see).  The W waves of a list take equal contiguous ranges
+// the block's rows can see).  Here a tile's cost is set by its 64 matrix instructions
+// whatever its source, so every tile is one unit (measured: heavier virtual tiles only
+// slowed the 512-token prefill).  The W waves of a list take equal contiguous ranges
 // [wg*total/W, (wg+1)*total/W) and write one partial record per (row, sequence their
 // range meets), at record wg + b of the list.
-constexpr int kBfCostR = 4;
+constexpr int kBfCostR = 1;
 struct RowSeq {
   int coded;   // coded tiles (= their units)
   int n_vt;    // virtual tiles
