@@ -195,347 +195,349 @@ void rows_kernel(RowsArgs a, int wph) {
 
   int pos_t = w_lo;
   while (pos_t < w_hi && b < a.B) {
-  const RowSeq seq = row_seq(a, b, n_new);
-  const int u_lo = pos_t - tb, u_hi = min(w_hi - tb, seq.total);
-  if (u_lo < u_hi) {
-  const int L = min(max(a.prefix_len[b], 0), a.max_prefix);
-  const int qe = max(min(a.q_end[b] & ~7, L), 0);
-  const int P_lo = 2 * u_lo;
-  const int P_hi = min(2 * min(u_hi, seq.coded), qe >> 3);
-  const int ns = min(a.n_sink, L);
-  const int r0 = max(qe, a.n_sink);
-  const int vt_lo = r0 / kKeys;
-  const int vt_hi = L > r0 ? (L - 1) / kKeys + 1 : vt_lo;
-  // virtual tiles whose first unit lies in the range
-  const int vt_first = (max(u_lo, seq.coded) - seq.coded + kBfCostR - 1) / kBfCostR;
-  const int vt_end = u_hi > seq.coded ? (u_hi - seq.coded + kBfCostR - 1) / kBfCostR : 0;
+    const RowSeq seq = row_seq(a, b, n_new);
+    const int u_lo = pos_t - tb, u_hi = min(w_hi - tb, seq.total);
+    if (u_lo < u_hi) {
+      const int L = min(max(a.prefix_len[b], 0), a.max_prefix);
+      const int qe = max(min(a.q_end[b] & ~7, L), 0);
+      const int P_lo = 2 * u_lo;
+      const int P_hi = min(2 * min(u_hi, seq.coded), qe >> 3);
+      const int ns = min(a.n_sink, L);
+      const int r0 = max(qe, a.n_sink);
+      const int vt_lo = r0 / kKeys;
+      const int vt_hi = L > r0 ? (L - 1) / kKeys + 1 : vt_lo;
+      // virtual tiles whose first unit lies in the range
+      const int vt_first = (max(u_lo, seq.coded) - seq.coded + kBfCostR - 1) / kBfCostR;
+      const int vt_end = u_hi > seq.coded ? (u_hi - seq.coded + kBfCostR - 1) / kBfCostR : 0;
 
-  // the lane's layout values from an opaque copy of the lane id, so nothing derived from
-  // them for this sequence is held in registers across the sequence loop
-  int lane_s = lane;
-  asm volatile("" : "+v"(lane_s));
-  const int j = lane_s & 15, kq = lane_s >> 4;   // key in tile / quarter (B side); row / quarter (A side)
-  // A operands: rotated query rows, pairs [16 kq, 16 kq + 16) then their partners
-  float qf[32];
-  int row_q[4];                                  // query index of the 4 rows this lane holds in D layout
-  {
-    const int r_abs = rb * kRows + j;
-    const bool row_ok = r_abs < R;
-    const int qi = row_ok ? r_abs / g : 0, hq = h * g + (row_ok ? r_abs % g : 0);
-    const int pq = min(max(a.pos[b] + qi, 0), a.rope_tiles * kKeys - 1);
-    const uint16_t* qv = a.q + (((size_t)b * a.NQ + qi) * a.Hq + hq) * D;
-    const float* e0 = a.rope + (size_t)(pq / kKeys) * D;
-    const float* e1 = a.rope + (size_t)(a.rope_tiles + pq % kKeys) * D;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int pr = 16 * kq + s;
-      const float c0 = e0[2 * pr], s0 = e0[2 * pr + 1], c1 = e1[2 * pr], s1 = e1[2 * pr + 1];
-      const float c = c0 * c1 - s0 * s1, sn = s0 * c1 + c0 * s1;
-      const float x = row_ok ? bf2f(qv[pr]) : 0.f, y = row_ok ? bf2f(qv[pr + HALF]) : 0.f;
-      qf[s] = (x * c - y * sn) * a.scale_log2e;
-      qf[16 + s] = (y * c + x * sn) * a.scale_log2e;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int ra = rb * kRows + 4 * kq + r;
-      row_q[r] = ra < R ? ra / g : -1;
-    }
-  }
-  // the in-tile offset phase of key j for this lane's pairs
-  float e1c[16], e1s[16];
-  {
-    const float* e1 = a.rope + (size_t)(a.rope_tiles + j) * D;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      e1c[s] = e1[2 * (16 * kq + s)];
-      e1s[s] = e1[2 * (16 * kq + s) + 1];
-    }
-  }
-  float m[4], lp[4];
-  f32x4 O[8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { m[r] = -__builtin_inff(); lp[r] = 0.f; }
-#pragma unroll
-  for (int c8 = 0; c8 < 8; ++c8) O[c8] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float* ptile = ptile_all + wave * kKeys * kRows;
-
-  const size_t row_stride = (size_t)kPage * NG;
-  const size_t page_bytes = (size_t)nblk * a.H * 2 * row_stride;
-  const uint8_t* head_rows = a.index_pages + (((size_t)beta * a.H + h) * 2) * row_stride;
-  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
-  const int32_t* bt = a.bf16_table + (size_t)b * a.bf16_row;
-
-  auto gather = [&](const _Float16* slice, uint32_t code, int ch) -> f16x8 {
-    return *(const f16x8*)(slice + ((size_t)code * NCH + ch) * 8);
-  };
-  auto gather_k = [&](uint32_t code, int ch) -> f16x8 {
-    return *(const f16x8*)(kl + ((size_t)code * NCH + (ch ^ (code & (NCH - 1)))) * 8);
-  };
-  // One tile: keys at positions pbase + 0..15 (pbase a multiple of 16).
-  //  kf: this lane's 32 raw key values (pairs of quarter kq, then partners), float32;
-  //  vraw[s2][0..7]: chunk j of the value of key 4 s2 + kq;
-  //  kok: the key of this lane is valid for every row; causal_base >= 0: new-key tile
-  //  whose key i' = causal_base + j is visible to rows with query index >= i'.
-  // rotate this lane's key values by position pbase + j (pbase a multiple of 16): the
-  // tile phase E(pbase) times the lane's offset phase E(j)
-  auto rotate_aligned = [&](int pbase, float (&kf)[32]) {
-    const int a_tile = min(pbase / kKeys, a.rope_tiles - 1);
-    const f32x4* e0 = (const f32x4*)(a.rope + (size_t)a_tile * D + 2 * 16 * kq);
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      const f32x4 e = e0[s2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int s = 2 * s2 + u;
-        const float c0 = e[2 * u], s0 = e[2 * u + 1];
-        const float c = c0 * e1c[s] - s0 * e1s[s], sn = s0 * e1c[s] + c0 * e1s[s];
-        const float lo = kf[s], hi = kf[16 + s];
-        kf[s] = lo * c - hi * sn;
-        kf[16 + s] = lo * sn + hi * c;
-      }
-    }
-  };
-  // Masks, online softmax and the transpose of the probabilities into the A layout of
-  // the value MFMAs: returns pa[s2] = P[row j][key 4 s2 + kq].
-  //  kok: the key of lane column j exists; causal_base >= 0: new-key tile whose key
-  //  i' = causal_base + j is visible to rows with query index >= i'.
-  auto softmax_step = [&](const f32x4& S, bool kok, int causal_base, float (&pa)[4]) {
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      bool ok = kok && row_q[r] >= 0;
-      if (causal_base >= 0) ok = ok && causal_base + j <= row_q[r];
-      sv[r] = ok ? S[r] : -__builtin_inff();
-    }
-    if (__any(sv[0] > m[0] + kRescaleR || sv[1] > m[1] + kRescaleR || sv[2] > m[2] + kRescaleR ||
-              sv[3] > m[3] + kRescaleR)) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float mn = fmaxf(m[r], group16_max(sv[r]));
-        const float f = mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m[r] - mn);
-        lp[r] *= f;
-#pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) O[c8][r] *= f;
-        m[r] = mn;
-      }
-    }
-    f32x4 P;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      P[r] = sv[r] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m[r]);
-      lp[r] += P[r];
-    }
-    *(f32x4*)(ptile + j * kRows + 4 * kq) = P;          // [key][row]
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) pa[s2] = ptile[(4 * s2 + kq) * kRows + j];
-    asm volatile("" ::: "memory");
-  };
-  // A tile of 16 rotated keys (kf: this lane's 32 values, pairs of quarter kq then the
-  // partners) and values (vraw[s2]: chunk j of key 4 s2 + kq) against the 16 rows.
-  auto tile = [&](const float (&kf)[32], const float (&vraw)[4][8], bool kok, int causal_base) {
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 32; ++s) S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], kf[s], S, 0, 0, 0);
-    float pa[4];
-    softmax_step(S, kok, causal_base, pa);
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8) O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], vraw[s2][c8], O[c8], 0, 0, 0);
-  };
-
-  // ---- virtual tiles: bf16 sink, recent window, new keys
-  for (int vt = vt_first; vt < vt_end; ++vt) {
-    const bool sink_tile = ns > 0 && vt == 0;
-    const int after_sink = vt - (ns > 0 ? 1 : 0);
-    const bool new_tile = after_sink >= vt_hi - vt_lo;
-    float kf[32], vraw[4][8];
-    bool kok = false;
-    int pbase = 0, causal = -1;
-    // this lane's key row (channels of quarter kq and their partners) as float32
-    auto load_krow = [&](const uint16_t* krow, float (&kf)[32]) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int ch0 = (u >> 1) * HALF + 16 * kq + 8 * (u & 1);
-        u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (krow) x = *(const u16x8*)(krow + ch0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kf[(u & 1) * 8 + (u >> 1) * 16 + i] = bf2f(x[i]);
-      }
-    };
-    if (new_tile) {
-      const int nt = after_sink - (vt_hi - vt_lo);
-      causal = nt * kKeys;
-      const int ik = causal + j;
-      kok = ik < a.NQ;
-      load_krow(kok ? a.k_new + (((size_t)b * a.NQ + ik) * a.H + h) * D : nullptr, kf);
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const int iv = causal + 4 * s2 + kq;
-        u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (iv < a.NQ) x = *(const u16x8*)(a.v_new + (((size_t)b * a.NQ + iv) * a.H + h) * D + 8 * j);
-#pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) vraw[s2][c8] = bf2f(x[c8]);
-      }
-      // new key i' sits at position L + i' (not tile aligned): its own phase E0 * E1
-      const int pc = min(L + ik, a.rope_tiles * kKeys - 1);
-      const float* e0 = a.rope + (size_t)(pc / kKeys) * D;
-      const float* e1 = a.rope + (size_t)(a.rope_tiles + pc % kKeys) * D;
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int pr = 16 * kq + s;
-        const float c0 = e0[2 * pr], s0 = e0[2 * pr + 1], c1 = e1[2 * pr], s1 = e1[2 * pr + 1];
-        const float c = c0 * c1 - s0 * s1, sn = s0 * c1 + c0 * s1;
-        const float lo = kf[s], hi = kf[16 + s];
-        kf[s] = lo * c - hi * sn;
-        kf[16 + s] = lo * sn + hi * c;
-      }
-    } else {
-      const int a_tile = sink_tile ? 0 : vt_lo + after_sink;
-      const int lo = sink_tile ? 0 : r0, hi = sink_tile ? ns : L;
-      pbase = kKeys * a_tile;
-      auto row_of = [&](int p) -> const uint16_t* {
-        if (p < lo || p >= hi) return nullptr;
-        const int slot = sink_tile ? 0 : 1 + (p >> 3) - (qe >> 3);
-        const int pg = slot < a.bf16_row ? bt[slot] : -1;
-        if (pg < 0 || pg >= a.n_bf16_pages) return nullptr;
-        return a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2) * kPage + (p & 7)) * D;
-      };
-      const uint16_t* krow = row_of(pbase + j);
-      kok = krow != nullptr;
-      load_krow(krow, kf);
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const uint16_t* vr = row_of(pbase + 4 * s2 + kq);
-        u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (vr) x = *(const u16x8*)(vr + (size_t)kPage * D + 8 * j);
-#pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) vraw[s2][c8] = bf2f(x[c8]);
-      }
-      rotate_aligned(pbase, kf);
-    }
-    tile(kf, vraw, kok, causal);
-  }
-
-  // ---- coded tiles: pages [P_lo, P_hi), two pages per tile; the index words and the
-  // tile phase of the next tile are loaded while the current one computes
-  {
-    float* erow = erow_all + wave * kErow;
-    int* ptl = ptl_all + wave * kPtR;
-    int pt_base = -kPtR;
-    auto stage_pt = [&](int P) {
-      pt_base = P;
-      int v[kPtR / 64];
-#pragma unroll
-      for (int k = 0; k < kPtR / 64; ++k) v[k] = pt[min(P + k * 64 + lane, a.max_pages - 1)];
-#pragma unroll
-      for (int k = 0; k < kPtR / 64; ++k) {
-        const int q = P + k * 64 + lane;
-        ptl[k * 64 + lane] = (q < P_hi && v[k] >= 0 && v[k] < a.n_index_pages) ? v[k] : -1;
-      }
-      asm volatile("" ::: "memory");
-    };
-    // index-word byte offsets and code shifts of this lane (key chunks 2kq, 2kq+1 share
-    // word wl, their partners word wh; value chunk j sits in word wv)
-    const int gl = (16 * kq) / C, gh = (HALF + 16 * kq) / C, gv = (8 * j) / C;
-    const int wl = gl & ~3, wh = gh & ~3, wv = gv & ~3;
-    uint32_t shk[4];
-    {
-      const int chs[4] = {2 * kq, 2 * kq + 1, NCH / 2 + 2 * kq, NCH / 2 + 2 * kq + 1};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) shk[u] = 8 * (((8 * chs[u]) / C) & 3);
-    }
-    const uint32_t shv = 8 * (gv & 3);
-    struct CIn {
-      uint32_t kwl, kwh, vw[4];
-      float2 e0;
-      int physk;
-    };
-    auto fetch = [&](int P0) -> CIn {
-      CIn in;
-      if (P0 + 2 > pt_base + kPtR) stage_pt(P0);
-      const int ph0 = P0 < P_hi ? ptl[P0 - pt_base] : -1;
-      const int ph1 = P0 + 1 < P_hi ? ptl[P0 + 1 - pt_base] : -1;
-      in.physk = (j >> 3) ? ph1 : ph0;
-      const uint8_t* kb = head_rows + (size_t)max(in.physk, 0) * page_bytes + (j & 7) * NG;
-      in.kwl = *(const uint32_t*)(kb + wl);
-      in.kwh = *(const uint32_t*)(kb + wh);
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const int kv = 4 * s2 + kq;
-        const int ph = (kv >> 3) ? ph1 : ph0;
-        const uint8_t* vb = head_rows + (size_t)max(ph, 0) * page_bytes + row_stride + (kv & 7) * NG;
-        in.vw[s2] = *(const uint32_t*)(vb + wv);
-      }
-      const int a_tile = min((8 * P0) / kKeys, a.rope_tiles - 1);
-      in.e0 = *(const float2*)(a.rope + (size_t)a_tile * D + 2 * lane);
-      return in;
-    };
-    auto coded_tile = [&](int P0, const CIn& in) {
-      const int pbase = 8 * P0;
-      *(float2*)(erow + 36 * (lane >> 4) + 2 * (lane & 15)) = in.e0;     // pair `lane`
-      asm volatile("" ::: "memory");
-      const bool kok = in.physk >= 0 && pbase + j >= a.n_sink;
-      f16x8 xk[4];
+      // the lane's layout values from an opaque copy of the lane id, so nothing derived from
+      // them for this sequence is held in registers across the sequence loop
+      int lane_s = lane;
+      asm volatile("" : "+v"(lane_s));
+      const int j = lane_s & 15, kq = lane_s >> 4;   // key in tile / quarter (B side); row / quarter (A side)
+      // A operands: rotated query rows, pairs [16 kq, 16 kq + 16) then their partners
+      float qf[32];
+      int row_q[4];                                  // query index of the 4 rows this lane holds in D layout
       {
-        const int chs[4] = {2 * kq, 2 * kq + 1, NCH / 2 + 2 * kq, NCH / 2 + 2 * kq + 1};
+        const int r_abs = rb * kRows + j;
+        const bool row_ok = r_abs < R;
+        const int qi = row_ok ? r_abs / g : 0, hq = h * g + (row_ok ? r_abs % g : 0);
+        const int pq = min(max(a.pos[b] + qi, 0), a.rope_tiles * kKeys - 1);
+        const uint16_t* qv = a.q + (((size_t)b * a.NQ + qi) * a.Hq + hq) * D;
+        const float* e0 = a.rope + (size_t)(pq / kKeys) * D;
+        const float* e1 = a.rope + (size_t)(a.rope_tiles + pq % kKeys) * D;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          xk[u] = gather_k(__builtin_amdgcn_ubfe(u < 2 ? in.kwl : in.kwh, shk[u], 8), chs[u]);
-      }
-      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 16; ++s) {
+          const int pr = 16 * kq + s;
+          const float c0 = e0[2 * pr], s0 = e0[2 * pr + 1], c1 = e1[2 * pr], s1 = e1[2 * pr + 1];
+          const float c = c0 * c1 - s0 * s1, sn = s0 * c1 + c0 * s1;
+          const float x = row_ok ? bf2f(qv[pr]) : 0.f, y = row_ok ? bf2f(qv[pr + HALF]) : 0.f;
+          qf[s] = (x * c - y * sn) * a.scale_log2e;
+          qf[16 + s] = (y * c + x * sn) * a.scale_log2e;
+        }
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) {
-        const f32x4 e = *(const f32x4*)(erow + 36 * kq + 4 * s2);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int s = 2 * s2 + u;
-          const float c0 = e[2 * u], s0 = e[2 * u + 1];
-          const float c = c0 * e1c[s] - s0 * e1s[s], sn = s0 * e1c[s] + c0 * e1s[s];
-          const float lo = (float)xk[s >> 3][s & 7], hi = (float)xk[2 + (s >> 3)][s & 7];
-          S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], lo * c - hi * sn, S, 0, 0, 0);
-          S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[16 + s], lo * sn + hi * c, S, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) {
+          const int ra = rb * kRows + 4 * kq + r;
+          row_q[r] = ra < R ? ra / g : -1;
         }
       }
-      float pa[4];
-      softmax_step(S, kok, -1, pa);
-      // invalid keys have P = 0 and finite codewords, so their values need no mask
+      // the in-tile offset phase of key j for this lane's pairs
+      float e1c[16], e1s[16];
+      {
+        const float* e1 = a.rope + (size_t)(a.rope_tiles + j) * D;
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const f16x8 x = gather(vl, __builtin_amdgcn_ubfe(in.vw[s2], shv, 8), j);
+        for (int s = 0; s < 16; ++s) {
+          e1c[s] = e1[2 * (16 * kq + s)];
+          e1s[s] = e1[2 * (16 * kq + s) + 1];
+        }
+      }
+      float m[4], lp[4];
+      f32x4 O[8];
 #pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], (float)x[c8], O[c8], 0, 0, 0);
-      }
-    };
-    if (P_lo < P_hi) {
-      CIn cur = fetch(P_lo);
-      for (int P0 = P_lo; P0 < P_hi; P0 += 2) {
-        const CIn nxt = fetch(P0 + 2);
-        coded_tile(P0, cur);
-        cur = nxt;
-      }
-    }
-  }
+      for (int r = 0; r < 4; ++r) { m[r] = -__builtin_inff(); lp[r] = 0.f; }
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8) O[c8] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float* ptile = ptile_all + wave * kKeys * kRows;
 
-  // ---- partial records of the 4 rows this lane holds
+      const size_t row_stride = (size_t)kPage * NG;
+      const size_t page_bytes = (size_t)nblk * a.H * 2 * row_stride;
+      const uint8_t* head_rows = a.index_pages + (((size_t)beta * a.H + h) * 2) * row_stride;
+      const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+      const int32_t* bt = a.bf16_table + (size_t)b * a.bf16_row;
+
+      auto gather = [&](const _Float16* slice, uint32_t code, int ch) -> f16x8 {
+        return *(const f16x8*)(slice + ((size_t)code * NCH + ch) * 8);
+      };
+      auto gather_k = [&](uint32_t code, int ch) -> f16x8 {
+        return *(const f16x8*)(kl + ((size_t)code * NCH + (ch ^ (code & (NCH - 1)))) * 8);
+      };
+      // One tile: keys at positions pbase + 0..15 (pbase a multiple of 16).
+      //  kf: this lane's 32 raw key values (pairs of quarter kq, then partners), float32;
+      //  vraw[s2][0..7]: chunk j of the value of key 4 s2 + kq;
+      //  kok: the key of this lane is valid for every row; causal_base >= 0: new-key tile
+      //  whose key i' = causal_base + j is visible to rows with query index >= i'.
+      // rotate this lane's key values by position pbase + j (pbase a multiple of 16): the
+      // tile phase E(pbase) times the lane's offset phase E(j)
+      auto rotate_aligned = [&](int pbase, float (&kf)[32]) {
+        const int a_tile = min(pbase / kKeys, a.rope_tiles - 1);
+        const f32x4* e0 = (const f32x4*)(a.rope + (size_t)a_tile * D + 2 * 16 * kq);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float l = group16_sum(lp[r]);
-    const int ra = rb * kRows + 4 * kq + r;
-    if (ra < R) {
-      float* rec = a.part + ((((size_t)list * a.n_rec + wg + b) * kRows) + 4 * kq + r) * (D + 2);
-      if (j == 0) { rec[0] = m[r]; rec[1] = l; }
-      f32x4 o0 = {O[0][r], O[1][r], O[2][r], O[3][r]};
-      f32x4 o1 = {O[4][r], O[5][r], O[6][r], O[7][r]};
-      *(f32x4*)(rec + 2 + 8 * j) = o0;
-      *(f32x4*)(rec + 2 + 8 * j + 4) = o1;
-    }
-  }
-  }   // u_lo < u_hi
-  pos_t = __builtin_amdgcn_readfirstlane(tb + u_hi);
-  tb = __builtin_amdgcn_readfirstlane(tb + seq.total);
-  b = __builtin_amdgcn_readfirstlane(b + 1);
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const f32x4 e = e0[s2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int s = 2 * s2 + u;
+            const float c0 = e[2 * u], s0 = e[2 * u + 1];
+            const float c = c0 * e1c[s] - s0 * e1s[s], sn = s0 * e1c[s] + c0 * e1s[s];
+            const float lo = kf[s], hi = kf[16 + s];
+            kf[s] = lo * c - hi * sn;
+            kf[16 + s] = lo * sn + hi * c;
+          }
+        }
+      };
+      // Masks, online softmax and the transpose of the probabilities into the A layout of
+      // the value MFMAs: returns pa[s2] = P[row j][key 4 s2 + kq].
+      //  kok: the key of lane column j exists; causal_base >= 0: new-key tile whose key
+      //  i' = causal_base + j is visible to rows with query index >= i'.
+      auto softmax_step = [&](const f32x4& S, bool kok, int causal_base, float (&pa)[4]) {
+        float sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bool ok = kok && row_q[r] >= 0;
+          if (causal_base >= 0) ok = ok && causal_base + j <= row_q[r];
+          sv[r] = ok ? S[r] : -__builtin_inff();
+        }
+        if (__any(sv[0] > m[0] + kRescaleR || sv[1] > m[1] + kRescaleR || sv[2] > m[2] + kRescaleR ||
+                  sv[3] > m[3] + kRescaleR)) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float mn = fmaxf(m[r], group16_max(sv[r]));
+            const float f = mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m[r] - mn);
+            lp[r] *= f;
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) O[c8][r] *= f;
+            m[r] = mn;
+          }
+        }
+        f32x4 P;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          P[r] = sv[r] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(sv[r] - m[r]);
+          lp[r] += P[r];
+        }
+        *(f32x4*)(ptile + j * kRows + 4 * kq) = P;          // [key][row]
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) pa[s2] = ptile[(4 * s2 + kq) * kRows + j];
+        asm volatile("" ::: "memory");
+      };
+      // A tile of 16 rotated keys (kf: this lane's 32 values, pairs of quarter kq then the
+      // partners) and values (vraw[s2]: chunk j of key 4 s2 + kq) against the 16 rows.
+      auto tile = [&](const float (&kf)[32], const float (&vraw)[4][8], bool kok, int causal_base) {
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 32; ++s) S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], kf[s], S, 0, 0, 0);
+        float pa[4];
+        softmax_step(S, kok, causal_base, pa);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+          for (int c8 = 0; c8 < 8; ++c8)
+            O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], vraw[s2][c8], O[c8], 0, 0, 0);
+      };
+
+      // ---- virtual tiles: bf16 sink, recent window, new keys
+      for (int vt = vt_first; vt < vt_end; ++vt) {
+        const bool sink_tile = ns > 0 && vt == 0;
+        const int after_sink = vt - (ns > 0 ? 1 : 0);
+        const bool new_tile = after_sink >= vt_hi - vt_lo;
+        float kf[32], vraw[4][8];
+        bool kok = false;
+        int pbase = 0, causal = -1;
+        // this lane's key row (channels of quarter kq and their partners) as float32
+        auto load_krow = [&](const uint16_t* krow, float (&kf)[32]) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ch0 = (u >> 1) * HALF + 16 * kq + 8 * (u & 1);
+            u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (krow) x = *(const u16x8*)(krow + ch0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kf[(u & 1) * 8 + (u >> 1) * 16 + i] = bf2f(x[i]);
+          }
+        };
+        if (new_tile) {
+          const int nt = after_sink - (vt_hi - vt_lo);
+          causal = nt * kKeys;
+          const int ik = causal + j;
+          kok = ik < a.NQ;
+          load_krow(kok ? a.k_new + (((size_t)b * a.NQ + ik) * a.H + h) * D : nullptr, kf);
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const int iv = causal + 4 * s2 + kq;
+            u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (iv < a.NQ) x = *(const u16x8*)(a.v_new + (((size_t)b * a.NQ + iv) * a.H + h) * D + 8 * j);
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) vraw[s2][c8] = bf2f(x[c8]);
+          }
+          // new key i' sits at position L + i' (not tile aligned): its own phase E0 * E1
+          const int pc = min(L + ik, a.rope_tiles * kKeys - 1);
+          const float* e0 = a.rope + (size_t)(pc / kKeys) * D;
+          const float* e1 = a.rope + (size_t)(a.rope_tiles + pc % kKeys) * D;
+#pragma unroll
+          for (int s = 0; s < 16; ++s) {
+            const int pr = 16 * kq + s;
+            const float c0 = e0[2 * pr], s0 = e0[2 * pr + 1], c1 = e1[2 * pr], s1 = e1[2 * pr + 1];
+            const float c = c0 * c1 - s0 * s1, sn = s0 * c1 + c0 * s1;
+            const float lo = kf[s], hi = kf[16 + s];
+            kf[s] = lo * c - hi * sn;
+            kf[16 + s] = lo * sn + hi * c;
+          }
+        } else {
+          const int a_tile = sink_tile ? 0 : vt_lo + after_sink;
+          const int lo = sink_tile ? 0 : r0, hi = sink_tile ? ns : L;
+          pbase = kKeys * a_tile;
+          auto row_of = [&](int p) -> const uint16_t* {
+            if (p < lo || p >= hi) return nullptr;
+            const int slot = sink_tile ? 0 : 1 + (p >> 3) - (qe >> 3);
+            const int pg = slot < a.bf16_row ? bt[slot] : -1;
+            if (pg < 0 || pg >= a.n_bf16_pages) return nullptr;
+            return a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2) * kPage + (p & 7)) * D;
+          };
+          const uint16_t* krow = row_of(pbase + j);
+          kok = krow != nullptr;
+          load_krow(krow, kf);
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const uint16_t* vr = row_of(pbase + 4 * s2 + kq);
+            u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (vr) x = *(const u16x8*)(vr + (size_t)kPage * D + 8 * j);
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8) vraw[s2][c8] = bf2f(x[c8]);
+          }
+          rotate_aligned(pbase, kf);
+        }
+        tile(kf, vraw, kok, causal);
+      }
+
+      // ---- coded tiles: pages [P_lo, P_hi), two pages per tile; the index words and the
+      // tile phase of the next tile are loaded while the current one computes
+      {
+        float* erow = erow_all + wave * kErow;
+        int* ptl = ptl_all + wave * kPtR;
+        int pt_base = -kPtR;
+        auto stage_pt = [&](int P) {
+          pt_base = P;
+          int v[kPtR / 64];
+#pragma unroll
+          for (int k = 0; k < kPtR / 64; ++k) v[k] = pt[min(P + k * 64 + lane, a.max_pages - 1)];
+#pragma unroll
+          for (int k = 0; k < kPtR / 64; ++k) {
+            const int q = P + k * 64 + lane;
+            ptl[k * 64 + lane] = (q < P_hi && v[k] >= 0 && v[k] < a.n_index_pages) ? v[k] : -1;
+          }
+          asm volatile("" ::: "memory");
+        };
+        // index-word byte offsets and code shifts of this lane (key chunks 2kq, 2kq+1 share
+        // word wl, their partners word wh; value chunk j sits in word wv)
+        const int gl = (16 * kq) / C, gh = (HALF + 16 * kq) / C, gv = (8 * j) / C;
+        const int wl = gl & ~3, wh = gh & ~3, wv = gv & ~3;
+        uint32_t shk[4];
+        {
+          const int chs[4] = {2 * kq, 2 * kq + 1, NCH / 2 + 2 * kq, NCH / 2 + 2 * kq + 1};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) shk[u] = 8 * (((8 * chs[u]) / C) & 3);
+        }
+        const uint32_t shv = 8 * (gv & 3);
+        struct CIn {
+          uint32_t kwl, kwh, vw[4];
+          float2 e0;
+          int physk;
+        };
+        auto fetch = [&](int P0) -> CIn {
+          CIn in;
+          if (P0 + 2 > pt_base + kPtR) stage_pt(P0);
+          const int ph0 = P0 < P_hi ? ptl[P0 - pt_base] : -1;
+          const int ph1 = P0 + 1 < P_hi ? ptl[P0 + 1 - pt_base] : -1;
+          in.physk = (j >> 3) ? ph1 : ph0;
+          const uint8_t* kb = head_rows + (size_t)max(in.physk, 0) * page_bytes + (j & 7) * NG;
+          in.kwl = *(const uint32_t*)(kb + wl);
+          in.kwh = *(const uint32_t*)(kb + wh);
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const int kv = 4 * s2 + kq;
+            const int ph = (kv >> 3) ? ph1 : ph0;
+            const uint8_t* vb = head_rows + (size_t)max(ph, 0) * page_bytes + row_stride + (kv & 7) * NG;
+            in.vw[s2] = *(const uint32_t*)(vb + wv);
+          }
+          const int a_tile = min((8 * P0) / kKeys, a.rope_tiles - 1);
+          in.e0 = *(const float2*)(a.rope + (size_t)a_tile * D + 2 * lane);
+          return in;
+        };
+        auto coded_tile = [&](int P0, const CIn& in) {
+          const int pbase = 8 * P0;
+          *(float2*)(erow + 36 * (lane >> 4) + 2 * (lane & 15)) = in.e0;     // pair `lane`
+          asm volatile("" ::: "memory");
+          const bool kok = in.physk >= 0 && pbase + j >= a.n_sink;
+          f16x8 xk[4];
+          {
+            const int chs[4] = {2 * kq, 2 * kq + 1, NCH / 2 + 2 * kq, NCH / 2 + 2 * kq + 1};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              xk[u] = gather_k(__builtin_amdgcn_ubfe(u < 2 ? in.kwl : in.kwh, shk[u], 8), chs[u]);
+          }
+          f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s2 = 0; s2 < 8; ++s2) {
+            const f32x4 e = *(const f32x4*)(erow + 36 * kq + 4 * s2);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int s = 2 * s2 + u;
+              const float c0 = e[2 * u], s0 = e[2 * u + 1];
+              const float c = c0 * e1c[s] - s0 * e1s[s], sn = s0 * e1c[s] + c0 * e1s[s];
+              const float lo = (float)xk[s >> 3][s & 7], hi = (float)xk[2 + (s >> 3)][s & 7];
+              S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], lo * c - hi * sn, S, 0, 0, 0);
+              S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[16 + s], lo * sn + hi * c, S, 0, 0, 0);
+            }
+          }
+          float pa[4];
+          softmax_step(S, kok, -1, pa);
+          // invalid keys have P = 0 and finite codewords, so their values need no mask
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const f16x8 x = gather(vl, __builtin_amdgcn_ubfe(in.vw[s2], shv, 8), j);
+#pragma unroll
+            for (int c8 = 0; c8 < 8; ++c8)
+              O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], (float)x[c8], O[c8], 0, 0, 0);
+          }
+        };
+        if (P_lo < P_hi) {
+          CIn cur = fetch(P_lo);
+          for (int P0 = P_lo; P0 < P_hi; P0 += 2) {
+            const CIn nxt = fetch(P0 + 2);
+            coded_tile(P0, cur);
+            cur = nxt;
+          }
+        }
+      }
+
+      // ---- partial records of the 4 rows this lane holds
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float l = group16_sum(lp[r]);
+        const int ra = rb * kRows + 4 * kq + r;
+        if (ra < R) {
+          float* rec = a.part + ((((size_t)list * a.n_rec + wg + b) * kRows) + 4 * kq + r) * (D + 2);
+          if (j == 0) { rec[0] = m[r]; rec[1] = l; }
+          f32x4 o0 = {O[0][r], O[1][r], O[2][r], O[3][r]};
+          f32x4 o1 = {O[4][r], O[5][r], O[6][r], O[7][r]};
+          *(f32x4*)(rec + 2 + 8 * j) = o0;
+          *(f32x4*)(rec + 2 + 8 * j + 4) = o1;
+        }
+      }
+    }   // u_lo < u_hi
+    pos_t = __builtin_amdgcn_readfirstlane(tb + u_hi);
+    tb = __builtin_amdgcn_readfirstlane(tb + seq.total);
+    b = __builtin_amdgcn_readfirstlane(b + 1);
   }   // sequences
 }
 
