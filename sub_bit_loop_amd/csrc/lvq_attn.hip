@@ -285,7 +285,10 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
   // the rows of (beta, h) in page 0 (wave-uniform), and the lane's three index words
   // as byte offsets from a page's start
   const uint8_t* head_rows = a.index_pages + (((size_t)beta * a.H + h) * 2) * row_stride;
-  const uint32_t o_kl = r * NG + wlo, o_kh = r * NG + whi, o_v = (uint32_t)row_stride + r * NG + wv;
+  uint32_t o_kl = r * NG + wlo, o_kh = r * NG + whi, o_v = (uint32_t)row_stride + r * NG + wv;
+  // opaque copies: three independent 32-bit offsets from the uniform base (otherwise the
+  // compiler derives one load's address from another's with 64-bit arithmetic)
+  asm volatile("" : "+v"(o_kl), "+v"(o_kh), "+v"(o_v));
   // Per-lane gather constants: bit offset of the code in its index word, and the LDS
   // byte offset of the chunk (code x of chunk k sits at byte (x * NCH + k) * 16).
   constexpr int kRowShift = (NCH == 16) ? 8 : 7;   // log2(NCH * 16)
@@ -421,7 +424,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
           in.vw = *(const uint32_t*)(head_rows + (po + o_v));
         }
         const int tile_idx = min((8 * P0) / kTile, a.rope_tiles - 1);
-        in.e0 = *(const float2*)(rope + (uint32_t)(tile_idx * D + 2 * (lane % HALF)));
+        in.e0 = *(const float2*)((const char*)rope + (uint32_t)(4 * (tile_idx * D + 2 * (lane % HALF))));
         return in;
       };
       auto tile = [&](int P0, const TileIn& in, int buf) {
