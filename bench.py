@@ -325,12 +325,13 @@ def run_decode(args, torch, lvq, inp):
     # After a token's forward pass, every 8 tokens each sequence encodes its oldest recent
     # page (all loop steps, heads, K and V) in every layer; with 8 sequences that is one
     # sequence's page per step on average: step s re-encodes sequence s mod B.
+    pools = [(Ly["bp"], Ly["cb"], Ly["ip"]) for Ly in layers]
+
     def reencode(s_idx):
         b = s_idx % B
         src = inp["bt"][b, 1:2].contiguous()
         dst = inp["spare"][b:b + 1].contiguous()
-        for Ly in layers:
-            lvq.lvq_reencode_pages(Ly["bp"], src, dst, Ly["cb"], T, TC, G, Ly["ip"])
+        lvq.lvq_reencode_pages_layers(pools, src, dst, T, TC, G)   # every layer, one launch
 
     def step(s_idx, events=None):
         k = 0
@@ -407,8 +408,9 @@ def manager_bench(torch, lvq, inp, n_tokens=64):
     cache = lvq.PagedCache(B, max_pages, N_SINK, N_RECENT, n_index, B * 12)
     cache.prefill(torch.full((B,), L, dtype=torch.int32, device=dev))
     nl = len(inp["layers"])
-    ip = torch.zeros((n_index, nblk, H, 2, 8, ng), dtype=torch.uint8, device=dev)   # one pool, all layers
+    ips = [torch.zeros((n_index, nblk, H, 2, 8, ng), dtype=torch.uint8, device=dev) for _ in range(nl)]
     bps = [torch.zeros((B * 12, T, H, 2, 8, D), dtype=torch.bfloat16, device=dev) for _ in range(nl)]
+    pools = [(bps[layer], inp["layers"][layer]["cb"], ips[layer]) for layer in range(nl)]
     gen = torch.Generator(device=dev)
     gen.manual_seed(77)
     kv = [torch.randn((2, 1, B, H, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(4)]
@@ -421,9 +423,7 @@ def manager_bench(torch, lvq, inp, n_tokens=64):
                 cache.append(t, k[0], k[1], bps[layer])
         cache.end_token()
         if reencode:
-            for layer in range(nl):
-                lvq.lvq_reencode_pages(bps[layer], cache.re_src, cache.re_dst, inp["layers"][layer]["cb"],
-                                       T, TC, G, ip)
+            lvq.lvq_reencode_pages_layers(pools, cache.re_src, cache.re_dst, T, TC, G)
         cache.commit()
 
     res = {}
@@ -593,6 +593,7 @@ def decode_loop_bench(torch, lvq, inp, n_tokens=24):
     ips = [torch.randint(0, 256, (n_index, nblk, H, 2, 8, ng), generator=gen, device=dev, dtype=torch.uint8)
            for _ in range(nl)]
     bps = [torch.randn((n_bf16, T, H, 2, 8, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(nl)]
+    pools = [(bps[layer], inp["layers"][layer]["cb"], ips[layer]) for layer in range(nl)]
     kvs = [torch.randn((2, 1, B, H, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(4)]
     max_len = L + 2 * n_tokens + 8
     rope = lvq.lvq_rope_tables(max_len + 1, D, 10000.0, device=dev)
@@ -615,9 +616,7 @@ def decode_loop_bench(torch, lvq, inp, n_tokens=24):
                                     Ly["cb"], t, pos, cache.seq_len, cache.q_end, rope, shp, out=out, lse=lse,
                                     ws=ws)
         cache.end_token()
-        for layer in range(nl):
-            lvq.lvq_reencode_pages(bps[layer], cache.re_src, cache.re_dst, inp["layers"][layer]["cb"], T, TC, G,
-                                   ips[layer])
+        lvq.lvq_reencode_pages_layers(pools, cache.re_src, cache.re_dst, T, TC, G)
         cache.commit()
 
     token()
@@ -704,7 +703,7 @@ def mixed_bench(torch, lvq, synth, n_steps=64, warmup=3):
     layer's 8 loop-step calls (T = 8, Tc = 4, G = 32), the prelude layer's call (T = 1,
     Tc = 1, G = 32: c = 32, 4 groups) and the batched page re-encode of the 8 sequences
     whose recent window reaches 72 tokens at that step (round robin; both layers, K and V,
-    one launch per layer).  Index pools hold uniform random codes (time does not depend on
+    one launch per layer shape).  Index pools hold uniform random codes (time does not depend on
     their values); the looped pool alone is larger than twice the 256 MB Infinity Cache."""
     import numpy as np
     dev = torch.device("cuda:0")
@@ -741,6 +740,9 @@ def mixed_bench(torch, lvq, synth, n_steps=64, warmup=3):
                              Lmax + 1, 0)
         ws = torch.empty(lvq.lvq_decode_attn_workspace_bytes(shp), dtype=torch.uint8, device=dev)
         layers.append(dict(T=T_, Tc=Tc_, G=G_, ng=ng, ip=ip, bp=bp, cb=cb, q=q, shp=shp, ws=ws))
+    groups = {}
+    for Ly in layers:
+        groups.setdefault((Ly["T"], Ly["Tc"], Ly["G"]), []).append((Ly["bp"], Ly["cb"], Ly["ip"]))
     out = torch.empty((Bm, H, D), dtype=torch.float32, device=dev)
     lse = torch.empty((Bm, H), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -757,8 +759,8 @@ def mixed_bench(torch, lvq, synth, n_steps=64, warmup=3):
         b0 = (8 * s) % Bm
         src = bt[b0:b0 + 8, 1].contiguous()
         dst = spare[b0:b0 + 8].contiguous()
-        for Ly in layers:
-            lvq.lvq_reencode_pages(Ly["bp"], src, dst, Ly["cb"], Ly["T"], Ly["Tc"], Ly["G"], Ly["ip"])
+        for (T_, Tc_, G_), pools in groups.items():     # one launch per layer shape
+            lvq.lvq_reencode_pages_layers(pools, src, dst, T_, Tc_, G_)
 
     for w in range(warmup):
         step(w)

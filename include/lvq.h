@@ -133,6 +133,34 @@ int lvq_reencode_pages(const uint16_t* bf16_pages, const int32_t* src_pages,
                        uint8_t* index_pages, void* stream);
 
 /*
+ * lvq_reencode_pages_layers -- lvq_reencode_pages for several layers at once: the
+ * same page ids (a page id names the same page in every layer's pools) re-encoded
+ * in every listed layer, each with its own pools and codebooks, in one launch per
+ * 48 layers instead of one per layer.  Every 8 generated tokens a sequence's oldest
+ * recent page is coded in all layers (the summary, section "전제와 한계"), so this
+ * is the per-token re-encode of a whole model.
+ *   layers:      host array [n_layers], read during the call only; per layer its
+ *                bf16 pool ([n_bf16_pages][T][H][2][8][d]), codebooks
+ *                ([nblk][2][H][ng][Tc][256][c]) and coded pool
+ *                ([n_index_pages][nblk][H][2][8][ng], in/out), device pointers.
+ *   src_pages, dst_pages: int32 [n] device arrays as in lvq_reencode_pages.
+ * T, Tc, G, H, d are shared by all layers.  Results are bit-identical to one
+ * lvq_reencode_pages call per layer.  Ids out of range are skipped; n = 0 or
+ * n_layers = 0 is a no-op.  Any invalid layer fails the call before any launch.
+ */
+typedef struct lvq_reencode_layer {
+  const uint16_t* bf16_pages;
+  const uint16_t* codebooks;
+  uint8_t* index_pages;
+  int32_t n_bf16_pages;
+  int32_t n_index_pages;
+} lvq_reencode_layer;
+
+int lvq_reencode_pages_layers(const lvq_reencode_layer* layers, int n_layers,
+                              const int32_t* src_pages, const int32_t* dst_pages, int n, int T,
+                              int Tc, int G, int H, int d, void* stream);
+
+/*
  * lvq_build_codebooks -- learn the 256-word codebooks of one of K / V from sample
  * tokens on the device: k-means on calibration keys and values (the summary,
  * section "어떻게 쓰나"), Fisher-weighted when weights are given (section "무엇과
@@ -325,8 +353,9 @@ int lvq_rows_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
  *
  * One decode token, in order: lvq_cache_begin_token; for each loop step t and
  * layer: lvq_cache_append (that layer's K/V at step t), then lvq_decode_attn;
- * lvq_cache_end_token; for each layer lvq_reencode_pages(bf16 pool, re_src,
- * re_dst, B, ...); lvq_cache_commit.  All calls on one stream.
+ * lvq_cache_end_token; lvq_reencode_pages_layers over every layer's pools with
+ * re_src, re_dst, B (or lvq_reencode_pages per layer); lvq_cache_commit.  All calls
+ * on one stream.
  */
 typedef struct lvq_cache {
   int32_t B;              /* sequence slots */

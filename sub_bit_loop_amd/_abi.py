@@ -50,6 +50,12 @@ class CacheDesc(ctypes.Structure):
                                    "counters", "re_src", "re_dst")]
 
 
+class ReencodeLayer(ctypes.Structure):
+    """Mirror of lvq_reencode_layer."""
+    _fields_ = [("bf16_pages", _vp), ("codebooks", _vp), ("index_pages", _vp), ("n_bf16_pages", _i32),
+                ("n_index_pages", _i32)]
+
+
 _CP = ctypes.POINTER(CacheDesc)
 
 _SIGS = {
@@ -58,6 +64,8 @@ _SIGS = {
     "lvq_encode": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "lvq_encode_pages": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
     "lvq_reencode_pages": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "lvq_reencode_pages_layers": (_i32, [ctypes.POINTER(ReencodeLayer), _i32, _vp, _vp, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _vp]),
     "lvq_build_codebooks_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "lvq_build_codebooks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                    _sz, _vp]),
@@ -184,6 +192,30 @@ def lvq_reencode_pages(bf16_pages, src_pages, dst_pages, codebooks, T: int, Tc: 
                                     bf16_pages.shape[0], index_pages.shape[0], _ptr(index_pages),
                                     _stream(bf16_pages)))
     return index_pages
+
+
+def lvq_reencode_pages_layers(layers, src_pages, dst_pages, T: int, Tc: int, G: int) -> None:
+    """lvq_reencode_pages for every (bf16_pages, codebooks, index_pages) triple in layers, in one launch."""
+    _dev(src_pages, "src_pages", I32, 1)
+    _dev(dst_pages, "dst_pages", I32, 1)
+    if src_pages.numel() != dst_pages.numel():
+        raise ValueError("src_pages and dst_pages differ in length")
+    layers = list(layers)
+    tab = (ReencodeLayer * max(1, len(layers)))()
+    H = d = 0
+    for i, (bp, cb, ip) in enumerate(layers):
+        _dev(bp, "bf16_pages", BF16, 6)
+        _dev(cb, "codebooks", BF16, 7)
+        _dev(ip, "index_pages", U8, 6)
+        if i == 0:
+            _, _, H, _, _, d = bp.shape
+        elif (bp.shape[2], bp.shape[5]) != (H, d):
+            raise ValueError("layers differ in heads or head dimension")
+        tab[i] = ReencodeLayer(_ptr(bp), _ptr(cb), _ptr(ip), bp.shape[0], ip.shape[0])
+    if not layers:
+        return
+    _check(lib().lvq_reencode_pages_layers(tab, len(layers), _ptr(src_pages), _ptr(dst_pages),
+                                           src_pages.numel(), T, Tc, G, H, d, _stream(layers[0][0])))
 
 
 def lvq_build_codebooks(samples, draws, kv_sel: int, T: int, Tc: int, G: int, n_iter: int,

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 
 #include "lvq_internal.h"
@@ -388,6 +389,47 @@ int lvq_reencode_pages(const uint16_t* bf16_pages, const int32_t* src_pages,
   a.n_dst_pages = n_index_pages;
   a.tokens_per_block = 512;
   return device_status(lvq::launch_encode(a, (hipStream_t)stream), "lvq_reencode_pages launch");
+}
+
+int lvq_reencode_pages_layers(const lvq_reencode_layer* layers, int n_layers,
+                              const int32_t* src_pages, const int32_t* dst_pages, int n, int T,
+                              int Tc, int G, int H, int d, void* stream) {
+  if (n < 0 || n_layers < 0) return fail(LVQ_EINVAL, "n=%d and n_layers=%d must be >= 0", n, n_layers);
+  if (n_layers > 0 && !layers) return fail(LVQ_EINVAL, "null layer array");
+  for (int l = 0; l < n_layers; ++l) {
+    const lvq_reencode_layer& L = layers[l];
+    int st = check_encode_common(L.bf16_pages, L.codebooks, T, Tc, G, lvq::kPage * n, H, d);
+    if (st) return st;
+    if (!L.index_pages) return fail(LVQ_EINVAL, "layer %d: null index_pages", l);
+    if (L.n_bf16_pages < 0 || L.n_index_pages < 0)
+      return fail(LVQ_EINVAL, "layer %d: pool sizes must be >= 0", l);
+  }
+  if (n > 0 && n_layers > 0 && (!src_pages || !dst_pages)) return fail(LVQ_EINVAL, "null pointer argument");
+  if (n == 0 || n_layers == 0) return ok();
+  lvq::EncodeArgs a{};
+  a.src_pages = src_pages;
+  a.dst_pages = dst_pages;
+  a.src_mode = lvq::kSrcPages;
+  a.dst_mode = lvq::kDstPages;
+  a.kv_sel = -1;
+  a.T = T; a.Tc = Tc; a.G = G; a.N = lvq::kPage * n; a.H = H; a.d = d;
+  a.tokens_per_block = 512;
+  // The layer table travels as a kernel argument, so larger models take several launches.
+  for (int l0 = 0; l0 < n_layers; l0 += lvq::kMaxReencodeLayers) {
+    lvq::ReencodeLayers tab{};
+    tab.n = std::min(lvq::kMaxReencodeLayers, n_layers - l0);
+    for (int i = 0; i < tab.n; ++i) {
+      const lvq_reencode_layer& L = layers[l0 + i];
+      tab.layer[i] = {L.bf16_pages, L.codebooks, L.index_pages, L.n_bf16_pages, L.n_index_pages};
+    }
+    a.src = tab.layer[0].bf16_pages;
+    a.codebooks = tab.layer[0].codebooks;
+    a.out = tab.layer[0].index_pages;
+    int st = device_status(lvq::launch_encode(a, (hipStream_t)stream, &tab),
+                           "lvq_reencode_pages_layers launch");
+    if (st) return st;
+  }
+  return ok();
 }
 
 size_t lvq_build_codebooks_workspace_bytes(int T, int Tc, int G, int S, int H, int d) {

@@ -36,6 +36,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <type_traits>
 
 namespace lvq {
 namespace {
@@ -166,13 +167,20 @@ constexpr int waves_per_group_block() { return D / C < 4 ? D / C : 4; }
 // dispatch) at the same time and each row is fetched from HBM once.
 constexpr int kXcds = 8;
 
+// Per-layer pools and books of a pages -> pages launch (the decode-time re-encode of
+// several layers at once); the other modes take none.
+struct NoLayers {};
+template <int MODE>
+using LayersArg = typename std::conditional<MODE == 2, ReencodeLayers, NoLayers>::type;
+
 // MODE: 0 dense source and destination, 1 dense source into coded pages,
-// 2 bf16 pages into coded pages.  Occupancy: 3 waves per SIMD at G = 32 (the
-// codebook takes 64 VGPRs), 4 at G = 16.  The grid is persistent: each workgroup
-// loads a codebook once per item and streams the item's whole token range.
+// 2 bf16 pages into coded pages (items of all layers in one grid, the layer
+// outermost).  Occupancy: 3 waves per SIMD at G = 32 (the codebook takes 64
+// VGPRs), 4 at G = 16.  The grid is persistent: each workgroup loads a codebook
+// once per item and streams the item's whole token range.
 template <int G, int C, int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 32 ? 3 : 4, 8)))
-void encode_kernel(EncodeArgs a, int n_items) {
+void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
   constexpr bool kDenseSrc = MODE != 2;
   constexpr bool kDenseDst = MODE == 0;
   constexpr int NG = D / C;
@@ -188,11 +196,14 @@ void encode_kernel(EncodeArgs a, int n_items) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int H = a.H, N = a.N;
-  const int nblk = a.T / TC;
-  const int tpi = a.tokens_per_block;
+  const int H = a0.H, N = a0.N;
+  const int nblk = a0.T / TC;
+  const int tpi = a0.tokens_per_block;
   const int nparts = (N + tpi - 1) / tpi;
-  const int nrest = nparts * H * nblk * (a.kv_sel >= 0 ? 1 : 2);
+  const int nrest_layer = nparts * H * nblk * (a0.kv_sel >= 0 ? 1 : 2);
+  int n_layers = 1;
+  if constexpr (MODE == 2) n_layers = layers.n;
+  const int nrest = nrest_layer * n_layers;
   const int q4 = lane >> 4, col = lane & 15;
   const int e0 = EPL * q4;
   const int tau0 = e0 / C, i0 = e0 % C;
@@ -203,6 +214,16 @@ void encode_kernel(EncodeArgs a, int n_items) {
     const int gb = r8 % NGB;
     int rest = (r8 / NGB) * kXcds + xcd;
     if (rest >= nrest) continue;   // padding to whole XCD rounds (uniform per workgroup)
+    EncodeArgs a = a0;
+    if constexpr (MODE == 2) {     // the item's layer: its pools and books
+      const ReencodeLayer& L = layers.layer[rest / nrest_layer];
+      rest %= nrest_layer;
+      a.src = L.bf16_pages;
+      a.codebooks = L.codebooks;
+      a.out = L.index_pages;
+      a.n_src_pages = L.n_bf16_pages;
+      a.n_dst_pages = L.n_index_pages;
+    }
     const int part = rest % nparts; rest /= nparts;
     const int h = rest % H;         rest /= H;
     const int beta = rest % nblk;   rest /= nblk;
@@ -404,7 +425,7 @@ int resident_workgroups(K kernel, int threads) {
 }
 
 template <int G, int C, int D, int MODE>
-hipError_t launch_mode(const EncodeArgs& args, hipStream_t s) {
+hipError_t launch_mode(const EncodeArgs& args, const LayersArg<MODE>& layers, int n_layers, hipStream_t s) {
   constexpr int NG = D / C;
   constexpr int WPG = waves_per_group_block<D, C>();
   constexpr int NGB = NG / WPG;
@@ -422,27 +443,37 @@ hipError_t launch_mode(const EncodeArgs& args, hipStream_t s) {
   long tpi = (args.N + parts - 1) / parts;
   tpi = (tpi + 15) / 16 * 16;
   parts = (args.N + tpi - 1) / tpi;
-  const long nrest = parts * sets;
+  const long nrest = parts * sets * n_layers;
   const long items = (nrest + kXcds - 1) / kXcds * kXcds * NGB;
   if (items > INT32_MAX) return hipErrorInvalidValue;
   const long grid = items < slots ? items : slots;
   EncodeArgs a = args;
   a.tokens_per_block = (int)tpi;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(WPG * 64), 0, s, a, (int)items);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(WPG * 64), 0, s, a, (int)items, layers);
   return hipGetLastError();
 }
 
 template <int G, int C, int D>
-hipError_t launch_one(const EncodeArgs& a, hipStream_t s) {
-  if (a.src_mode == kSrcPages) return launch_mode<G, C, D, 2>(a, s);
-  if (a.dst_mode == kDstPages) return launch_mode<G, C, D, 1>(a, s);
-  return launch_mode<G, C, D, 0>(a, s);
+hipError_t launch_one(const EncodeArgs& a, const ReencodeLayers* layers, hipStream_t s) {
+  if (a.src_mode == kSrcPages) {
+    // pages -> pages: the given layers, or the single layer the arguments name
+    ReencodeLayers one{};
+    if (!layers) {
+      one.n = 1;
+      one.layer[0] = {a.src, a.codebooks, a.out, a.n_src_pages, a.n_dst_pages};
+      layers = &one;
+    }
+    if (layers->n < 1 || layers->n > kMaxReencodeLayers) return hipErrorInvalidValue;
+    return launch_mode<G, C, D, 2>(a, *layers, layers->n, s);
+  }
+  if (a.dst_mode == kDstPages) return launch_mode<G, C, D, 1>(a, NoLayers{}, 1, s);
+  return launch_mode<G, C, D, 0>(a, NoLayers{}, 1, s);
 }
 
 template <int G, int C>
-hipError_t by_d(const EncodeArgs& a, hipStream_t s) {
-  if (a.d == 64) return launch_one<G, C, 64>(a, s);
-  return launch_one<G, C, 128>(a, s);
+hipError_t by_d(const EncodeArgs& a, const ReencodeLayers* layers, hipStream_t s) {
+  if (a.d == 64) return launch_one<G, C, 64>(a, layers, s);
+  return launch_one<G, C, 128>(a, layers, s);
 }
 
 }  // namespace
@@ -454,16 +485,16 @@ bool encode_supported(int G, int c, int d) {
   return false;
 }
 
-hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t s, const ReencodeLayers* layers) {
   const int c = a.G / a.Tc;
   if (a.G == 32) {
-    if (c == 8) return by_d<32, 8>(a, s);
-    if (c == 16) return by_d<32, 16>(a, s);
-    return by_d<32, 32>(a, s);
+    if (c == 8) return by_d<32, 8>(a, layers, s);
+    if (c == 16) return by_d<32, 16>(a, layers, s);
+    return by_d<32, 32>(a, layers, s);
   }
-  if (c == 4) return by_d<16, 4>(a, s);
-  if (c == 8) return by_d<16, 8>(a, s);
-  return by_d<16, 16>(a, s);
+  if (c == 4) return by_d<16, 4>(a, layers, s);
+  if (c == 8) return by_d<16, 8>(a, layers, s);
+  return by_d<16, 16>(a, layers, s);
 }
 
 }  // namespace lvq

@@ -27,8 +27,21 @@ struct EncodeArgs {
   int n_src_pages, n_dst_pages;
   int tokens_per_block;       // multiple of 16
 };
+// The pools and books of one layer in a multi-layer re-encode (pages -> pages).
+struct ReencodeLayer {
+  const uint16_t* bf16_pages;
+  const uint16_t* codebooks;
+  uint8_t* index_pages;
+  int n_bf16_pages, n_index_pages;
+};
+constexpr int kMaxReencodeLayers = 48;   // layers per launch (passed by value as kernel arguments)
+struct ReencodeLayers {
+  int n;
+  ReencodeLayer layer[kMaxReencodeLayers];
+};
 bool encode_supported(int G, int c, int d);
-hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
+// layers: for a pages -> pages launch, the layers to encode (null: the one a names)
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t s, const ReencodeLayers* layers = nullptr);
 
 // ---------------------------------------------------------------- codebook builder
 constexpr int kMaxKmeansSamples = 8192;   // samples per book (float64 D^2 and running sums in LDS)

@@ -65,6 +65,29 @@ def test_encode_validation(L):
     assert L.lvq_reencode_pages(FAKE, FAKE, FAKE, 0, FAKE, 4, 2, 16, 1, 64, 4, 4, FAKE, NUL) == 0
 
 
+def test_reencode_layers_validation(L):
+    from sub_bit_loop_amd import _abi
+    tab = (_abi.ReencodeLayer * 2)()
+    tab[0] = _abi.ReencodeLayer(FAKE, FAKE, FAKE, 4, 4)
+    tab[1] = _abi.ReencodeLayer(FAKE, FAKE, FAKE, 4, 4)
+    args = (FAKE, FAKE, 3, 4, 2, 16, 1, 64, NUL)
+    assert L.lvq_reencode_pages_layers(tab, -1, *args) == 1
+    assert L.lvq_reencode_pages_layers(None, 2, *args) == 1
+    assert L.lvq_reencode_pages_layers(tab, 2, FAKE, FAKE, -1, 4, 2, 16, 1, 64, NUL) == 1
+    assert L.lvq_reencode_pages_layers(tab, 2, NUL, FAKE, 3, 4, 2, 16, 1, 64, NUL) == 1
+    assert L.lvq_reencode_pages_layers(tab, 2, FAKE, FAKE, 3, 4, 3, 16, 1, 64, NUL) == 1   # Tc does not divide T
+    tab[1] = _abi.ReencodeLayer(FAKE, NUL, FAKE, 4, 4)                                      # second layer bad
+    assert L.lvq_reencode_pages_layers(tab, 2, *args) == 1
+    tab[1] = _abi.ReencodeLayer(FAKE, FAKE, NUL, 4, 4)
+    assert L.lvq_reencode_pages_layers(tab, 2, *args) == 1
+    tab[1] = _abi.ReencodeLayer(FAKE, FAKE, FAKE, -1, 4)
+    assert L.lvq_reencode_pages_layers(tab, 2, *args) == 1
+    assert b"layer 1" in L.lvq_last_error()
+    tab[1] = _abi.ReencodeLayer(FAKE, FAKE, FAKE, 4, 4)
+    assert L.lvq_reencode_pages_layers(tab, 0, *args) == 0                                  # no layers: no-op
+    assert L.lvq_reencode_pages_layers(tab, 2, FAKE, FAKE, 0, 4, 2, 16, 1, 64, NUL) == 0    # no pages: no-op
+
+
 def test_rope_table_sizes(L):
     assert L.lvq_rope_table_bytes(512, 64) == (32 + 16) * 32 * 2 * 4 + 32 * 8
     assert L.lvq_rope_table_bytes(513, 64) == (33 + 16) * 32 * 2 * 4 + 32 * 8

@@ -189,8 +189,7 @@ def _decode_token(m, cache, ips, bps, cbs, attn_at=None):
                 assert np.abs(lse.cpu().numpy()[live] - rl[live]).max() < 2e-3
                 worst = (max(worst[0], mabs), max(worst[1], mrel))
     cache.end_token()
-    for layer in range(len(ips)):
-        lvq.lvq_reencode_pages(bps[layer], cache.re_src, cache.re_dst, cbs[layer], T, Tc, G, ips[layer])
+    lvq.lvq_reencode_pages_layers(list(zip(bps, cbs, ips)), cache.re_src, cache.re_dst, T, Tc, G)
     cache.commit()
     m.end_token()
     torch.cuda.synchronize()
@@ -319,8 +318,7 @@ def test_manager_decode_token_replays_in_a_hip_graph():
                     lvq.lvq_decode_attn(q, cache.page_table, ips[0], bps[0], cache.bf16_table, cbs[0], t, pos,
                                         cache.seq_len, cache.q_end, rope, shp, out=out, lse=lse, ws=ws)
         cache.end_token()
-        for layer in range(n_layers):
-            lvq.lvq_reencode_pages(bps[layer], cache.re_src, cache.re_dst, cbs[layer], T, Tc, G, ips[layer])
+        lvq.lvq_reencode_pages_layers(list(zip(bps, cbs, ips)), cache.re_src, cache.re_dst, T, Tc, G)
         cache.commit()
 
     def outs():

@@ -209,3 +209,47 @@ def test_encode_pages_and_reencode():
         assert (r.n_near <= 1).all()
         orc.scatter_index_pages(r.idx, kv, np.array(dst, np.int32), ref2)
     np.testing.assert_array_equal(got, ref2)
+
+
+def test_reencode_layers_matches_per_layer_and_oracle():
+    """lvq_reencode_pages_layers over 50 layers (two launches of at most 48) writes
+    exactly what one lvq_reencode_pages call per layer writes, honours each layer's
+    own pool bounds, and matches the oracle."""
+    import sub_bit_loop_amd as lvq
+    T, Tc, G, d, H = 4, 2, 16, 64, 1
+    c = G // Tc
+    nblk, ng = T // Tc, d // c
+    n_layers = 50
+    rng = np.random.default_rng(11)
+    src = np.array([3, 0, 5, -1, 2, 1], np.int32)
+    dst = np.array([7, 1, 2, 4, 9, 3], np.int32)   # page 9 exists in odd layers only
+    layers, host = [], []
+    for l in range(n_layers):
+        n_bf, n_ix = 6, 9 + (l % 2)
+        scales = synth.channel_scales(rng, H, d)
+        toks = np.stack([synth.f32_to_bf16_bits(synth.gen_kv(rng, T, 8, H, d, scales)) for _ in range(2 * n_bf)])
+        bp = toks.reshape(n_bf, 2, T, 8, H, d).transpose(0, 2, 4, 1, 3, 5).copy()   # [P][T][H][2][8][d]
+        cb = synth.random_codebooks(rng, T, Tc, G, H, d)
+        ip0 = rng.integers(0, 256, size=(n_ix, nblk, H, 2, 8, ng), dtype=np.uint8)
+        layers.append((dev(bp), dev(cb), dev(ip0)))
+        host.append((bp, cb, ip0))
+    per_layer = [torch.from_numpy(h[2]).cuda() for h in host]
+    s_d, d_d = dev(src), dev(dst)
+    print(f"\ncase layers={n_layers} T={T} Tc={Tc} G={G} d={d} H={H} pages={len(src)}", flush=True)
+    lvq.lvq_reencode_pages_layers(layers, s_d, d_d, T, Tc, G)
+    for l in range(n_layers):
+        lvq.lvq_reencode_pages(layers[l][0], s_d, d_d, layers[l][1], T, Tc, G, per_layer[l])
+    torch.cuda.synchronize()
+    for l in range(n_layers):
+        np.testing.assert_array_equal(layers[l][2].cpu().numpy(), per_layer[l].cpu().numpy(),
+                                      err_msg=f"layer {l}")
+    for l in (0, 1, 47, 48, 49):
+        bp, cb, ip0 = host[l]
+        ref = ip0.copy()
+        ok = [(s, t) for s, t in zip(src, dst) if 0 <= s < bp.shape[0] and 0 <= t < ref.shape[0]]
+        for kv in (0, 1):
+            allt = np.concatenate([bp[s, :, :, kv].transpose(0, 2, 1, 3) for s, _ in ok], axis=1)
+            r = orc.encode(allt, cb, kv, T, Tc, G)
+            assert (r.n_near <= 1).all()
+            orc.scatter_index_pages(r.idx, kv, np.array([t for _, t in ok], np.int32), ref)
+        np.testing.assert_array_equal(layers[l][2].cpu().numpy(), ref, err_msg=f"layer {l} vs oracle")
