@@ -333,31 +333,38 @@ def run_decode(args, torch, lvq, inp):
         dst = inp["spare"][b:b + 1].contiguous()
         lvq.lvq_reencode_pages_layers(pools, src, dst, T, TC, G)   # every layer, one launch
 
+    # An event pair around a call costs about 5 us of queue time at each of its two ends, so
+    # timing all 96 calls would add about 1 ms to a 10 ms step.  Each step times one call per
+    # loop step instead: the call of layer (s mod layers) at every t, so the steps together
+    # sample every (layer, loop step) position once per 24 steps.
+    def sampled(s_idx):
+        return {t * len(layers) + s_idx % len(layers) for t in range(T)}
+
     def step(s_idx, events=None):
         k = 0
         for t in range(T):
             for layer in range(len(layers)):
-                if events is not None:
-                    events[k][0].record()
+                ev = events.get(k) if events is not None else None
+                if ev is not None:
+                    ev[0].record()
                 call(layer, t)
-                if events is not None:
-                    events[k][1].record()
+                if ev is not None:
+                    ev[1].record()
                 k += 1
         reencode(s_idx)
 
     for w in range(args.warmup):
         step(w)
     torch.cuda.synchronize()
-    ncall = T * len(layers)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(ncall)] for _ in range(args.steps)]
+    evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in sampled(s)}
+           for s in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(s, evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_call = [evs[s][k][0].elapsed_time(evs[s][k][1]) * 1e-3 for s in range(args.steps) for k in range(ncall)]
+    per_call = [a.elapsed_time(b) * 1e-3 for e in evs for a, b in e.values()]
     return wall, per_call
 
 

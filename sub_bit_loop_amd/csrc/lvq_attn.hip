@@ -660,6 +660,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int ca
     const bool meets = max(range_lo(wg, total, W), tb) < min(range_lo(wg + 1, total, W), tb1);
     sml[i] = meets ? *(const float2*)(rec + (size_t)i * rstride) : make_float2(-__builtin_inff(), 0.f);
   }
+  // Thread (group, channel): record group g takes records g, g + NGR, ...  Its first 8
+  // records' values are loaded now, so their latency overlaps that of the (m, l) pairs.
+  // Every slot below S exists in the list; a record with weight 0 (possibly never
+  // written, so holding anything) is discarded by a select, never multiplied.
+  const int NGR = kMergeThreads / a.d;
+  const int ch = tid % a.d, g = tid / a.d;
+  float pre[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = g + u * NGR;
+    pre[u] = (g < NGR && i < S) ? rec[(size_t)i * rstride + 2 + ch] : 0.f;
+  }
   __syncthreads();
   if (tid < 64) {
     float mloc = -__builtin_inff();
@@ -676,15 +688,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int ca
   }
   __syncthreads();
   const float M = s_ml[0], Ls = s_ml[1];
-  // Thread (group, channel): record group g sums records g, g + NGR, ... with 8 loads in
-  // flight; the groups are then added in order.  Records with weight 0 are not read
-  // (unwritten candidates may hold anything).
-  const int NGR = kMergeThreads / a.d;
-  const int ch = tid % a.d, g = tid / a.d;
+  // Record group g sums its records with 8 loads in flight (the first 8 preloaded); the
+  // groups are then added in order.  Beyond the first 8, records with weight 0 are not
+  // read.
   float acc = 0.f;
   if (g < NGR) {
-    float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int i = g;
+    float p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = g + u * NGR;
+      const float w = i < S ? s_w[i] : 0.f;
+      p[u] = w != 0.f ? pre[u] * w : 0.f;
+    }
+    int i = g + 8 * NGR;
     for (; i + 7 * NGR < S; i += 8 * NGR) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
