@@ -57,7 +57,6 @@ constexpr float kNoMax = -1e30f;   // running maximum before the first valid sco
                                    // so an invalid score of -inf still gives weight 0)
 constexpr int kNW = 12;            // waves per workgroup
 constexpr int kWavesPerSimd = 3;   // occupancy the register budget is sized for
-constexpr int kBatch = 1;          // tiles per prefetch batch
 constexpr int kTile = 16;          // positions per tile (RoPE table granularity)
 constexpr int kPtBatch = 128;      // page ids staged in LDS per wave at a time
 
@@ -203,7 +202,6 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
   constexpr int HALF = D / 2;
   constexpr int QP = HALF / 4;    // channel pairs per lane (score)
   constexpr int QV = D / 4;       // output channels per lane (value sum)
-  constexpr int NT = kBatch;      // tiles per prefetch batch
   constexpr int NCH = D / 8;      // 16-byte chunks per codeword row in LDS
   constexpr int KPC = QP / 8;     // key chunks per lane in each half
   constexpr int NV = QV / 8;      // value chunks per lane
@@ -480,22 +478,18 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
           for (int i = 0; i < 8; ++i) o[8 * v + i] = fmaf(w, (float)x[i], o[8 * v + i]);
         }
       };
-      // Software pipeline in batches of NT tiles: each iteration loads the inputs of
-      // the next batch, computes the current batch, then moves next to current, so no
-      // load is in flight across the loop back-edge.
+      // Software pipeline, two tiles per iteration: each tile's inputs are loaded while
+      // the tile before it is computed, into the other of two register sets, so the
+      // sets alternate without copies.
       if (P_lo < P_hi) {
-        TileIn cur[NT], nxt[NT];
-  #pragma unroll
-        for (int i = 0; i < NT; ++i) cur[i] = fetch(P_lo + 2 * i);
-        for (int P0 = P_lo; P0 < P_hi; P0 += 2 * NT) {
-  #pragma unroll
-          for (int i = 0; i < NT; ++i) nxt[i] = fetch(P0 + 2 * NT + 2 * i);
-  #pragma unroll
-          for (int i = 0; i < NT; ++i) {
-            if (P0 + 2 * i < P_hi) tile(P0 + 2 * i, cur[i], i & 1);
-          }
-  #pragma unroll
-          for (int i = 0; i < NT; ++i) cur[i] = nxt[i];
+        TileIn in0 = fetch(P_lo);
+        for (int P0 = P_lo;; P0 += 4) {
+          const TileIn in1 = fetch(P0 + 2);
+          tile(P0, in0, 0);
+          if (P0 + 2 >= P_hi) break;
+          in0 = fetch(P0 + 4);
+          tile(P0 + 2, in1, 1);
+          if (P0 + 4 >= P_hi) break;
         }
       }
       // bf16 sink and recent tokens (virtual tiles after the coded ones; a wave takes
