@@ -510,12 +510,16 @@ void rows_kernel(RowsArgs a, int wph) {
               O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], (float)x[c8], O[c8], 0, 0, 0);
           }
         };
+        // two tiles per iteration, each prefetched into the other register set
         if (P_lo < P_hi) {
-          CIn cur = fetch(P_lo);
-          for (int P0 = P_lo; P0 < P_hi; P0 += 2) {
-            const CIn nxt = fetch(P0 + 2);
-            coded_tile(P0, cur);
-            cur = nxt;
+          CIn in0 = fetch(P_lo);
+          for (int P0 = P_lo;; P0 += 4) {
+            const CIn in1 = fetch(P0 + 2);
+            coded_tile(P0, in0);
+            if (P0 + 2 >= P_hi) break;
+            in0 = fetch(P0 + 4);
+            coded_tile(P0 + 2, in1);
+            if (P0 + 4 >= P_hi) break;
           }
         }
       }
