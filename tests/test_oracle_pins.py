@@ -3,6 +3,8 @@ invariants, special cases that reduce to library routines, brute force.
 
 Each test names the mistake it is there to catch.
 """
+import os
+
 import numpy as np
 import pytest
 import scipy.cluster.vq as scvq
@@ -43,13 +45,26 @@ def textbook_attention(q, K, V, pos_q, pos_k, base, scale):
 # ----------------------------------------------------------------------------
 # P1: bit budget
 # ----------------------------------------------------------------------------
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden_rows(name):
+    """The data lines of a fixture under tests/golden (comments start with '#')."""
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [line.split() for line in f if line.strip() and not line.startswith("#")]
+
+
+BIT_RATES = {int(g): float(bpe) for _, g, bpe in golden_rows("bit_rates.txt")}
+
+
 @pytest.mark.parametrize("Tc,G", [(1, 16), (2, 16), (4, 32), (1, 32), (2, 32), (4, 16)])
 def test_p1_bits_per_element_independent_of_Tc(Tc, G):
-    """One byte per (block, head, group, K/V): 8/G bits per element whatever Tc is.
-    Catches a layout that stores one row per step instead of one per block."""
+    """One byte per (block, head, group, K/V): the pages' 0.5 (G = 16) and 0.25 (G = 32)
+    bits per element whatever Tc is.  Catches a layout that stores one row per step
+    instead of one per block."""
     T, H, d = 8, 4, 128
     nbytes = orc.index_bytes_per_token(T, Tc, G, H, d)
-    assert nbytes * 8 / (2 * T * H * d) == pytest.approx(8.0 / G)
+    assert nbytes * 8 / (2 * T * H * d) == pytest.approx(BIT_RATES[G])
     # and the encoder's own output has exactly that many bytes per token
     rng = np.random.default_rng(1)
     kv = synth.f32_to_bf16_bits(rng.standard_normal((T, 3, H, d)))

@@ -1,4 +1,6 @@
 """The synthetic workload generator lands on its stated statistics and is reproducible."""
+import os
+
 import numpy as np
 import torch
 
@@ -15,20 +17,30 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(back, torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().numpy())
 
 
+def golden_values(name):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    with open(path) as f:
+        return {k: float(v) for k, v in (line.split() for line in f if line.strip() and not line.startswith("#"))}
+
+
 def test_loop_and_channel_correlations():
+    """The generator's loop-step and cross-channel correlations are the ones the pages
+    report for Ouro-1.4B (tests/golden/loop_statistics.txt)."""
+    pages = golden_values("loop_statistics.txt")
     rng = np.random.default_rng(1)
     H, d, N = 2, 64, 20000
     sc = np.ones((H, d))
     for T in (4, 8):
         X = synth.gen_kv(rng, T, N, H, d, sc).astype(np.float64)
         rho = synth.loop_rhos(T)
-        assert rho[0] == 0.69 and abs(rho[-1] - 0.94) < 1e-12
+        assert rho[0] == pages["first_pair_step_correlation"]
+        assert abs(rho[-1] - pages["last_pair_step_correlation"]) < 1e-12
         for t in range(1, T):
             r = np.mean([np.corrcoef(X[t - 1, :, 0, j], X[t, :, 0, j])[0, 1] for j in range(8)])
             assert abs(r - rho[t - 1]) < 0.02
         cc = np.corrcoef(X[T - 1, :, 1, :8].T)
         off = cc[~np.eye(8, dtype=bool)].mean()
-        assert abs(off - 0.16) < 0.02
+        assert abs(off - pages["cross_channel_correlation"]) < 0.02
 
 
 def test_scales_and_outliers():
