@@ -243,7 +243,8 @@ size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp);
  *   codebooks:   see above.
  *   t:           loop step, 0 <= t < T; block t/Tc, step slice t%Tc are read.
  *   pos:         int32 [B], RoPE position of the query.
- *   seq_len:     int32 [B], cached tokens L_b (positions 0 .. L_b-1).
+ *   seq_len:     int32 [B], cached tokens L_b (positions 0 .. L_b-1).  L_b = 0 (an
+ *                empty slot of the batch) gives out = 0 and lse = -inf for its heads.
  *   q_end:       int32 [B], multiple of 8: tokens [n_sink, q_end) are coded,
  *                [0, n_sink) and [q_end, L_b) are bf16 (sink wins where both apply).
  *   rope_tab:    table built by lvq_rope_tables for this d and base.
@@ -298,7 +299,8 @@ int lvq_decode_scores(const uint16_t* q, const int32_t* page_table, const uint8_
  *                 step t, or both NULL.
  *   page_table, index_pages, bf16_pages, bf16_table, codebooks, t, q_end, rope_tab:
  *                 as lvq_decode_attn.
- *   prefix_len:   int32 [B], paged tokens visible to every query.
+ *   prefix_len:   int32 [B], paged tokens visible to every query.  A row that sees no
+ *                 key at all (prefix_len 0 and no new keys) gets out = 0, lse = -inf.
  *   out:          float32 [B][NQ][Hq][d]; lse: float32 [B][NQ][Hq] or NULL.
  *   ws:           lvq_rows_attn_workspace_bytes(shp) bytes.
  * Scores and the value sum run on float32 matrix cores (products exact in float32).

@@ -289,7 +289,14 @@ def reconstruct_kv(shp: AttnShape, b: int, h: int, t: int, L: int, q_end: int,
 
 
 def attend(qr: np.ndarray, Kr: np.ndarray, V: np.ndarray, scale: float):
-    """Softmax attention of one rotated query over rotated keys: (out, lse, scores)."""
+    """Softmax attention of one rotated query over rotated keys: (out, lse, scores).
+
+    With no keys (an empty sequence) the weighted sum and the sum of weights are both
+    empty: the output is the zero vector and lse = log 0 = -inf (a reading; the pages
+    do not speak of empty sequences).
+    """
+    if len(Kr) == 0:
+        return np.zeros(V.shape[1]), -np.inf, np.zeros(0)
     s = (Kr @ qr) * scale
     m = s.max()
     w = np.exp(s - m)

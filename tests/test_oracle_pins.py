@@ -380,6 +380,27 @@ def test_p12_single_token():
                 assert lse[b, h] == sc[(b, h)][0]
 
 
+def test_p13_empty_sequence_is_the_merge_identity():
+    """L = 0 (an empty batch slot): out = 0 and lse = -inf, the partial that the
+    log-sum-exp merge leaves every other partial unchanged with (scipy's logsumexp of
+    [x, -inf] is x), and an empty slot changes no other sequence's result."""
+    with_empty = build_cache(37, 3, [0, 45, 0], 2, 128, 4, 4, 32, 4, 16, books="random", index="random")
+    out, lse = with_empty.oracle_attn(1)
+    for b in (0, 2):
+        np.testing.assert_array_equal(out[b], 0.0)
+        assert np.isneginf(lse[b]).all()
+    assert np.isfinite(lse[1]).all()
+    for h in range(2):
+        assert logsumexp([lse[1, h], lse[0, h]]) == pytest.approx(lse[1, h], abs=0, rel=1e-15)
+    # the same sequence alone, same inputs: only slot 1 of the batch above
+    c = with_empty
+    alone = orc.decode_attn(orc.AttnShape(1, 2, 2, 128, 4, 4, 32, 4), c.q[1][1:2], c.page_table[1:2],
+                            c.index_pages, c.bf16_pages, c.bf16_table[1:2], c.codebooks, 1,
+                            c.pos[1:2], c.seq_len[1:2], c.q_end[1:2])
+    np.testing.assert_array_equal(alone[0][0], out[1])
+    np.testing.assert_array_equal(alone[1][0], lse[1])
+
+
 def test_boundary_conventions():
     """First 4 and last 16 of 512 tokens bf16 leaves 492 coded tokens; sink wins over recent."""
     assert synth.prefill_q_end(512, 16) == 496
