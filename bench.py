@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--headline-only", action="store_true",
                     help="only the decode-attention measurement (for counter runs): no HBM probe, "
                          "multi-row, cache-manager or encoder legs")
+    ap.add_argument("--encode-only", action="store_true",
+                    help="only the encoder measurement (for counter runs): prints its JSON object")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-instructions", metavar="DIR",
                     help="summarise a rocprofv3 --pmc run of the SQ instruction counters of this bench "
@@ -676,7 +678,7 @@ def encode_bench(torch, lvq, synth, inp):
     rk = np.random.default_rng(synth.seed_for(4, synth.STREAM_K))
     sc = synth.channel_scales(rk, H, D)
     for (tc, g) in ((4, 32), (2, 16)):
-        if (tc, g) == (TC, G):
+        if (tc, g) == (TC, G) and inp.get("cb0") is not None:
             cb = inp["cb0"]
         else:
             cb, _ = build_books(torch, lvq, synth, tc, g, sc, sc, synth.seed_for(4, synth.STREAM_BOOKS))
@@ -951,6 +953,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.encode_only:
+        print(json.dumps({"encode": encode_bench(torch, lvq, synth, {})}), flush=True)
+        return
     inp = build_inputs(args, torch, lvq, synth)
     wall, per_call = run_decode(args, torch, lvq, inp)
     ncall = T * args.layers
