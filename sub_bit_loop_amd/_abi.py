@@ -140,6 +140,33 @@ U8 = (torch.uint8,)
 F32 = (torch.float32,)
 
 
+def _coded_dims(T: int, Tc: int, G: int, d: int):
+    """(nblk, ng, c) of a valid (T, Tc, G, d), else None (the library then rejects the call)."""
+    if min(T, Tc, G, d) <= 0 or T % Tc or G % Tc or d % (G // Tc):
+        return None
+    c = G // Tc
+    return T // Tc, d // c, c
+
+
+def _expect(t: torch.Tensor, name: str, shape) -> None:
+    """The kernels index these arrays by the call's sizes: a tensor of another shape
+    would be read or written out of bounds, so it is refused here."""
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, the call needs {tuple(shape)}")
+
+
+def _book_shape(T: int, Tc: int, G: int, H: int, d: int):
+    """[nblk][2][H][ng][Tc][256][c], or None for sizes the library rejects."""
+    dims = _coded_dims(T, Tc, G, d)
+    return None if dims is None else (dims[0], 2, H, dims[1], Tc, NCODES, dims[2])
+
+
+def _index_pool_shape(P: int, T: int, Tc: int, G: int, H: int, d: int):
+    """[P][nblk][H][2][8][ng], or None for sizes the library rejects."""
+    dims = _coded_dims(T, Tc, G, d)
+    return None if dims is None else (P, dims[0], H, 2, PAGE, dims[1])
+
+
 def lvq_version() -> int:
     return lib().lvq_version()
 
@@ -153,9 +180,12 @@ def lvq_encode(kv, codebooks, kv_sel: int, T: int, Tc: int, G: int, idx=None) ->
         raise ValueError("kv.shape[0] != T")
     c = G // Tc if Tc > 0 else 0
     ng = d // c if c > 0 else 0
+    _expect(codebooks, "codebooks", _book_shape(T, Tc, G, H, d))
     if idx is None:
         idx = torch.empty((max(T // max(Tc, 1), 0), N, H, ng), dtype=torch.uint8, device=kv.device)
     _dev(idx, "idx", U8)
+    dims = _coded_dims(T, Tc, G, d)
+    _expect(idx, "idx", None if dims is None else (dims[0], N, H, dims[1]))
     _check(lib().lvq_encode(_ptr(kv), _ptr(codebooks), kv_sel, T, Tc, G, N, H, d, _ptr(idx), _stream(kv)))
     return idx
 
@@ -168,8 +198,12 @@ def lvq_encode_pages(kv, codebooks, kv_sel: int, T: int, Tc: int, G: int, chunk_
     _dev(chunk_page, "chunk_page", I32, 1)
     _dev(index_pages, "index_pages", U8, 6)
     T_, N, H, d = kv.shape
+    if T_ != T:
+        raise ValueError("kv.shape[0] != T")
     if chunk_page.numel() * PAGE < N:
         raise ValueError("chunk_page too short")
+    _expect(codebooks, "codebooks", _book_shape(T, Tc, G, H, d))
+    _expect(index_pages, "index_pages", _index_pool_shape(index_pages.shape[0], T, Tc, G, H, d))
     _check(lib().lvq_encode_pages(_ptr(kv), _ptr(codebooks), kv_sel, T, Tc, G, N, H, d,
                                   _ptr(chunk_page), index_pages.shape[0], _ptr(index_pages),
                                   _stream(kv)))
@@ -187,6 +221,9 @@ def lvq_reencode_pages(bf16_pages, src_pages, dst_pages, codebooks, T: int, Tc: 
     if src_pages.numel() != dst_pages.numel():
         raise ValueError("src_pages and dst_pages differ in length")
     _, T_, H, _, _, d = bf16_pages.shape
+    _expect(bf16_pages, "bf16_pages", (bf16_pages.shape[0], T, H, 2, PAGE, d))
+    _expect(codebooks, "codebooks", _book_shape(T, Tc, G, H, d))
+    _expect(index_pages, "index_pages", _index_pool_shape(index_pages.shape[0], T, Tc, G, H, d))
     _check(lib().lvq_reencode_pages(_ptr(bf16_pages), _ptr(src_pages), _ptr(dst_pages),
                                     src_pages.numel(), _ptr(codebooks), T, Tc, G, H, d,
                                     bf16_pages.shape[0], index_pages.shape[0], _ptr(index_pages),
@@ -211,6 +248,9 @@ def lvq_reencode_pages_layers(layers, src_pages, dst_pages, T: int, Tc: int, G: 
             _, _, H, _, _, d = bp.shape
         elif (bp.shape[2], bp.shape[5]) != (H, d):
             raise ValueError("layers differ in heads or head dimension")
+        _expect(bp, f"layer {i} bf16_pages", (bp.shape[0], T, H, 2, PAGE, d))
+        _expect(cb, f"layer {i} codebooks", _book_shape(T, Tc, G, H, d))
+        _expect(ip, f"layer {i} index_pages", _index_pool_shape(ip.shape[0], T, Tc, G, H, d))
         tab[i] = ReencodeLayer(_ptr(bp), _ptr(cb), _ptr(ip), bp.shape[0], ip.shape[0])
     if not layers:
         return
@@ -240,6 +280,7 @@ def lvq_build_codebooks(samples, draws, kv_sel: int, T: int, Tc: int, G: int, n_
     if codebooks is None:
         codebooks = torch.zeros((nblk, 2, H, ng, Tc, NCODES, c), dtype=torch.bfloat16, device=samples.device)
     _dev(codebooks, "codebooks", BF16, 7)
+    _expect(codebooks, "codebooks", _book_shape(T, Tc, G, H, d))
     need = lib().lvq_build_codebooks_workspace_bytes(T, Tc, G, S, H, d)
     if ws is None:
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=samples.device)
@@ -290,6 +331,12 @@ def _attn_call(fn, q, page_table, index_pages, bf16_pages, bf16_table, codebooks
         raise ValueError("pool sizes do not match the shape")
     if rope_tab.numel() * 4 < lvq_rope_table_bytes(shp.rope_max_len, shp.d):
         raise ValueError("rope table too small")
+    _expect(q, "q", (shp.B, shp.Hq, shp.d))
+    for name, x in (("pos", pos), ("seq_len", seq_len), ("q_end", q_end)):
+        _expect(x, name, (shp.B,))
+    _expect(index_pages, "index_pages", _index_pool_shape(shp.n_index_pages, shp.T, shp.Tc, shp.G, shp.H, shp.d))
+    _expect(bf16_pages, "bf16_pages", (shp.n_bf16_pages, shp.T, shp.H, 2, PAGE, shp.d))
+    _expect(codebooks, "codebooks", _book_shape(shp.T, shp.Tc, shp.G, shp.H, shp.d))
     dev = q.device
     if out is None:
         out = torch.empty((shp.B, shp.Hq, shp.d), dtype=torch.float32, device=dev)
@@ -300,11 +347,14 @@ def _attn_call(fn, q, page_table, index_pages, bf16_pages, bf16_table, codebooks
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
     _dev(out, "out", F32)
     _dev(lse, "lse", F32)
+    _expect(out, "out", (shp.B, shp.Hq, shp.d))
+    _expect(lse, "lse", (shp.B, shp.Hq))
     args = [_ptr(q), _ptr(page_table), _ptr(index_pages), _ptr(bf16_pages), _ptr(bf16_table),
             _ptr(codebooks), int(t), _ptr(pos), _ptr(seq_len), _ptr(q_end), _ptr(rope_tab),
             ctypes.byref(shp), _ptr(out), _ptr(lse)]
     if scores is not None:
         _dev(scores, "scores", F32)
+        _expect(scores, "scores", (shp.B, shp.Hq, shp.max_seq_len))
         args.append(_ptr(scores))
     args += [_ptr(ws), ws.numel() * ws.element_size(), _stream(q)]
     _check(fn(*args))
@@ -450,11 +500,27 @@ def lvq_rows_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebooks,
         _dev(v_new, "v_new", BF16, 4)
     if tuple(q.shape) != (shp.B, shp.NQ, shp.Hq, shp.d):
         raise ValueError("q must be [B][NQ][Hq][d] of the shape")
+    if k_new is not None:
+        _expect(k_new, "k_new", (shp.B, shp.NQ, shp.H, shp.d))
+        _expect(v_new, "v_new", (shp.B, shp.NQ, shp.H, shp.d))
+    _expect(page_table, "page_table", (shp.B, shp.max_pages))
+    _expect(bf16_table, "bf16_table", (shp.B, shp.bf16_row))
+    for name, x in (("pos", pos), ("prefix_len", prefix_len), ("q_end", q_end)):
+        _expect(x, name, (shp.B,))
+    _expect(index_pages, "index_pages", _index_pool_shape(shp.n_index_pages, shp.T, shp.Tc, shp.G, shp.H, shp.d))
+    _expect(bf16_pages, "bf16_pages", (shp.n_bf16_pages, shp.T, shp.H, 2, PAGE, shp.d))
+    _expect(codebooks, "codebooks", _book_shape(shp.T, shp.Tc, shp.G, shp.H, shp.d))
+    if rope_tab.numel() * 4 < lvq_rope_table_bytes(shp.rope_max_len, shp.d):
+        raise ValueError("rope table too small")
     dev = q.device
     if out is None:
         out = torch.empty((shp.B, shp.NQ, shp.Hq, shp.d), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((shp.B, shp.NQ, shp.Hq), dtype=torch.float32, device=dev)
+    _dev(out, "out", F32)
+    _dev(lse, "lse", F32)
+    _expect(out, "out", (shp.B, shp.NQ, shp.Hq, shp.d))
+    _expect(lse, "lse", (shp.B, shp.NQ, shp.Hq))
     need = lvq_rows_attn_workspace_bytes(shp)
     if ws is None:
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)

@@ -205,3 +205,20 @@ def test_rows_shape_validation(L):
     # units per wave of 32 coded + 16 virtual units)
     assert need == 2 * 1 * (16 + 1) * 16 * 130 * 4 + 1 * 2 * 4
     assert call(rs(), ws_bytes=need - 1) == 3
+
+
+def test_binding_shape_helpers():
+    """The binding derives the shapes the kernels index by from the call's sizes, and
+    refuses other tensors before anything is launched."""
+    import torch
+    from sub_bit_loop_amd import _abi
+    assert _abi._coded_dims(4, 4, 32, 128) == (1, 16, 8)
+    assert _abi._coded_dims(4, 2, 16, 64) == (2, 8, 8)
+    assert _abi._coded_dims(4, 3, 32, 128) is None      # Tc does not divide T: the library rejects
+    assert _abi._coded_dims(4, 0, 32, 128) is None
+    assert _abi._book_shape(4, 2, 16, 3, 64) == (2, 2, 3, 8, 2, 256, 8)
+    assert _abi._index_pool_shape(7, 8, 4, 32, 2, 128) == (7, 2, 2, 2, 8, 16)
+    _abi._expect(torch.zeros(2, 3), "x", (2, 3))
+    _abi._expect(torch.zeros(2, 3), "x", None)
+    with pytest.raises(ValueError, match="needs"):
+        _abi._expect(torch.zeros(2, 3), "x", (3, 2))

@@ -253,3 +253,25 @@ def test_reencode_layers_matches_per_layer_and_oracle():
             assert (r.n_near <= 1).all()
             orc.scatter_index_pages(r.idx, kv, np.array([t for _, t in ok], np.int32), ref)
         np.testing.assert_array_equal(layers[l][2].cpu().numpy(), ref, err_msg=f"layer {l} vs oracle")
+
+
+def test_binding_refuses_mismatched_shapes():
+    """Tensors whose shape does not match the call's sizes are refused before a launch."""
+    import sub_bit_loop_amd as lvq
+    T, Tc, G, d, H, N = 4, 4, 32, 128, 2, 16
+    kv = torch.zeros((T, N, H, d), dtype=torch.int16, device="cuda")
+    good = torch.zeros((1, 2, H, 16, Tc, 256, 8), dtype=torch.int16, device="cuda")
+    bad = torch.zeros((1, 2, H, 8, Tc, 256, 8), dtype=torch.int16, device="cuda")     # ng = 8, not 16
+    with pytest.raises(ValueError, match="codebooks"):
+        lvq.lvq_encode(kv, bad, 0, T, Tc, G)
+    with pytest.raises(ValueError, match="idx"):
+        lvq.lvq_encode(kv, good, 0, T, Tc, G, idx=torch.empty((1, N, H, 8), dtype=torch.uint8, device="cuda"))
+    bp = torch.zeros((3, T, H, 2, 8, d), dtype=torch.int16, device="cuda")
+    ip_bad = torch.zeros((3, 1, H, 2, 8, 8), dtype=torch.uint8, device="cuda")
+    pages = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="index_pages"):
+        lvq.lvq_reencode_pages_layers([(bp, good, ip_bad)], pages, pages, T, Tc, G)
+    with pytest.raises(ValueError, match="bf16_pages"):
+        lvq.lvq_reencode_pages(bp[:, :2].contiguous(), pages, pages, good, T, Tc, G,
+                               torch.zeros((3, 1, H, 2, 8, 16), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
