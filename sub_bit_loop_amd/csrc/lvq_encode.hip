@@ -436,9 +436,10 @@ hipError_t launch_mode(const EncodeArgs& args, const LayersArg<MODE>& layers, in
   const int round = kXcds * NGB;
   slots = slots / round * round;
   if (slots < round) slots = round;
-  // split every (head, block, K/V) codebook set into enough token ranges to fill the slots
+  // split every (layer, head, block, K/V) codebook set into enough token ranges to fill
+  // the slots (each range loads its codebook once, so no more ranges than that)
   const long sets = (long)args.H * (args.T / args.Tc) * (args.kv_sel < 0 ? 2 : 1);
-  long parts = slots / (sets * NGB);
+  long parts = slots / (sets * NGB * n_layers);
   if (parts < 1) parts = 1;
   long tpi = (args.N + parts - 1) / parts;
   tpi = (tpi + 15) / 16 * 16;
