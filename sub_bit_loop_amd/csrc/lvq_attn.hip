@@ -33,7 +33,8 @@
 //    read from a per-tile LDS row: six float32 operations, the key read by
 //    v_fma_mix straight from float16.
 //  * Index words (only the bytes a lane needs) and the tile phases of the next
-//    tile are loaded while the current tile computes.
+//    tile are loaded while the current tile computes, into the other of two
+//    register sets (the loop body holds two tiles, so nothing is copied).
 //  * Scores are kept in log2 units (scale * log2 e folded into the query); a
 //    running maximum is kept lazily (rescale only when a score passes it by
 //    more than 8 in log2 units).
