@@ -29,7 +29,10 @@
  *    reached that point.  Entry points are thread-safe; the only state is the
  *    calling thread's last error string.
  *  - The return value is a status code.  Every argument check happens on the
- *    host before anything is enqueued, so on a non-zero status nothing ran.
+ *    host before anything is enqueued, so on LVQ_EINVAL, LVQ_EUNSUPPORTED or
+ *    LVQ_ENOSPC nothing ran.  LVQ_EDEVICE reports a failed launch; a call made of
+ *    several launches may have run the earlier ones, and its outputs are then
+ *    unspecified.
  *    LVQ_EINVAL: a null pointer, a size <= 0 where one is required, Tc not
  *    dividing T or G, c = G/Tc not dividing d, t >= T, Hq not a multiple of H,
  *    n_sink > 8, a table too small for the requested lengths.
