@@ -616,12 +616,16 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
 // block of 16 rows), records hold 16 rows.
 constexpr int kMergeMax = 4096;   // candidate records per (b, hq) at most (the host checks)
 constexpr int kMergeThreads = 512;
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int cap) {
+// THREADS threads per item, each record group's first PRE records loaded with the (m, l)
+// pairs: 512 / 8 where an item has few records, 1024 / 16 where one sequence spans many
+// waves (up to 128 records in the first round of loads at d = 128).
+template <int THREADS, int PRE>
+__global__ __launch_bounds__(THREADS) void merge_kernel(AttnArgs a, int cap) {
   extern __shared__ __align__(16) unsigned char merge_smem[];
   float2* sml = (float2*)merge_smem;            // [cap]
   float* s_w = (float*)(sml + cap);             // [cap]
   __shared__ float s_ml[2];
-  __shared__ float s_part[kMergeThreads];       // per (record group, channel) sums
+  __shared__ float s_part[THREADS];             // per (record group, channel) sums
   const int item = blockIdx.x;           // b * Hq + hq
   const int D2 = a.d + 2;
   const int tid = threadIdx.x;
@@ -655,15 +659,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int ca
     const bool meets = max(range_lo(wg, total, W), tb) < min(range_lo(wg + 1, total, W), tb1);
     sml[i] = meets ? *(const float2*)(rec + (size_t)i * rstride) : make_float2(-__builtin_inff(), 0.f);
   }
-  // Thread (group, channel): record group g takes records g, g + NGR, ...  Its first 8
+  // Thread (group, channel): record group g takes records g, g + NGR, ...  Its first PRE
   // records' values are loaded now, so their latency overlaps that of the (m, l) pairs.
   // Every slot below S exists in the list; a record with weight 0 (possibly never
   // written, so holding anything) is discarded by a select, never multiplied.
-  const int NGR = kMergeThreads / a.d;
+  const int NGR = THREADS / a.d;
   const int ch = tid % a.d, g = tid / a.d;
-  float pre[8];
+  float pre[PRE];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < PRE; ++u) {
     const int i = g + u * NGR;
     pre[u] = (g < NGR && i < S) ? rec[(size_t)i * rstride + 2 + ch] : 0.f;
   }
@@ -683,19 +687,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a, int ca
   }
   __syncthreads();
   const float M = s_ml[0], Ls = s_ml[1];
-  // Record group g sums its records with 8 loads in flight (the first 8 preloaded); the
-  // groups are then added in order.  Beyond the first 8, records with weight 0 are not
-  // read.
+  // Record group g sums its records with 8 loads in flight (the first PRE preloaded);
+  // the groups are then added in order.  Beyond the first PRE, records with weight 0 are
+  // not read.
   float acc = 0.f;
   if (g < NGR) {
     float p[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 8; ++u) p[u] = 0.f;
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
       const int i = g + u * NGR;
       const float w = i < S ? s_w[i] : 0.f;
-      p[u] = w != 0.f ? pre[u] * w : 0.f;
+      p[u % 8] = w != 0.f ? fmaf(pre[u], w, p[u % 8]) : p[u % 8];
     }
-    int i = g + 8 * NGR;
+    int i = g + PRE * NGR;
     for (; i + 7 * NGR < S; i += 8 * NGR) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -754,8 +760,14 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
                      a.rope, wph);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(n_items), dim3(kMergeThreads), (size_t)(a.n_waves + 1) * 12, s, a,
-                     a.n_waves + 1);
+  // records per item: the waves over one sequence's share of the list, plus one
+  const bool many = a.n_waves / (a.B > 0 ? a.B : 1) + 1 > 8 * (kMergeThreads / D);
+  if (many)
+    hipLaunchKernelGGL((merge_kernel<2 * kMergeThreads, 16>), dim3(n_items), dim3(2 * kMergeThreads),
+                       (size_t)(a.n_waves + 1) * 12, s, a, a.n_waves + 1);
+  else
+    hipLaunchKernelGGL((merge_kernel<kMergeThreads, 8>), dim3(n_items), dim3(kMergeThreads),
+                       (size_t)(a.n_waves + 1) * 12, s, a, a.n_waves + 1);
   return hipGetLastError();
 }
 
@@ -786,8 +798,8 @@ bool attn_supported(int d, int c) {
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
   if (a.n_waves + 1 > kMergeMax || !a.tile_start || a.d > kMergeThreads || kMergeThreads % a.d) return hipErrorInvalidValue;
   const int items = a.B * (a.merge_rows ? a.NQ : 1) * a.Hq;
-  hipLaunchKernelGGL(merge_kernel, dim3(items), dim3(kMergeThreads), (size_t)(a.n_waves + 1) * 12, s, a,
-                     a.n_waves + 1);
+  hipLaunchKernelGGL((merge_kernel<kMergeThreads, 8>), dim3(items), dim3(kMergeThreads),
+                     (size_t)(a.n_waves + 1) * 12, s, a, a.n_waves + 1);
   return hipGetLastError();
 }
 
