@@ -1,0 +1,36 @@
+"""The benchmark's algorithmic byte and flop models (the numerators of its roofline
+figures) reproduce the per-call workload figures derived independently from the
+method: index rows of every coded token, bf16 sink and recent tokens, the step-t
+codebook slices once, and 7 d flops per cached (token, head).  No GPU needed."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402  (the module imports torch only inside main())
+
+
+def test_decode_call_bytes_at_the_ouro_shape():
+    q_end = bench.synth_q_end()
+    assert q_end == 32704                          # 8 * floor((32768 - 64) / 8)
+    coded = q_end - bench.N_SINK                   # 32700 coded tokens per sequence
+    ng = bench.D // (bench.G // bench.TC)          # 16 groups
+    idx = bench.B * coded * bench.H * 2 * ng       # one byte per (token, head, group, K/V)
+    bf = bench.B * (bench.N_SINK + bench.L - q_end) * bench.H * 2 * bench.D * 2
+    books = bench.H * 2 * 256 * bench.D * 2
+    assert idx == pytest.approx(133.94e6, rel=1e-4)
+    assert bf == pytest.approx(4.46e6, rel=1e-3)
+    assert books == pytest.approx(2.10e6, rel=1e-2)
+    total = bench.algorithmic_bytes_per_call(q_end)
+    assert total == pytest.approx(140.7e6, rel=1e-3)
+    assert 0 < total - (idx + bf + books) < 0.3e6   # query, output, lse and page ids
+
+
+def test_decode_call_flops_at_the_ouro_shape():
+    # per (token, head): d/2 pairs rotated (6 flops each), q.k (2 d), p.v (2 d)
+    per = (bench.D // 2) * 6 + 2 * bench.D + 2 * bench.D
+    assert per == 7 * bench.D == 896
+    assert bench.algorithmic_flops_per_call() == bench.B * bench.H * bench.L * per
+    assert bench.algorithmic_flops_per_call() == pytest.approx(3.758e9, rel=1e-3)
