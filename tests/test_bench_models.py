@@ -34,3 +34,12 @@ def test_decode_call_flops_at_the_ouro_shape():
     assert per == 7 * bench.D == 896
     assert bench.algorithmic_flops_per_call() == bench.B * bench.H * bench.L * per
     assert bench.algorithmic_flops_per_call() == pytest.approx(3.758e9, rel=1e-3)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """The library has no multi-GPU path: --gpus N > 1 exits at once (no GPU touched)."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
