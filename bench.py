@@ -41,6 +41,7 @@ N_SINK, N_RECENT = 4, 64
 CONFIG_ID = 2
 CALIB_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_ouro_b8_l32k_traffic.txt")
+KSTATS_FILE = os.path.join(ROOT, "profiles", "decode_attn_ouro_b8_l32k_kernel_stats.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "sub_bit_loop_amd", "csrc", f) for f in ("lvq_attn.hip", "lvq_internal.h")]
 
 
@@ -58,10 +59,17 @@ def parse():
                          "multi-row, cache-manager or encoder legs")
     ap.add_argument("--encode-only", action="store_true",
                     help="only the encoder measurement (for counter runs): prints its JSON object")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="wall-time bound of the CPU oracle baseline")
     ap.add_argument("--pmc-instructions", metavar="DIR",
                     help="summarise a rocprofv3 --pmc run of the SQ instruction counters of this bench "
                          "into the instruction record the bench line reports")
+    ap.add_argument("--kernel-stats-summary", metavar="DIR",
+                    help="summarise a rocprofv3 --kernel-trace --stats run of the headline measurement "
+                         "into the kernel-time record the bench line reports")
+    ap.add_argument("--cpu-worker", metavar="DIR", help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-cores", type=int, default=0,
+                    help="worker processes of the CPU oracle baseline (0 = the host's cores, at most 16)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench "
                          "into the HBM-traffic record the bench line reports")
@@ -297,6 +305,71 @@ def algorithmic_flops_per_call():
     return B * H * L * 7 * D
 
 
+# Float32 lane operations that exact attention over the coded cache needs per cached
+# (token, head): the rotated score takes 6 operations per channel pair (the key pair
+# times the query-side phase coefficients) and the value sum one FMA per channel.
+VALU_OPS_PER_TOKEN_HEAD = 6 * (D // 2) + D
+LANE_OPS_PER_S = 256 * 64 * CLOCK_GHZ * 1e9    # non-packed float32: 64 lanes per CU per clock
+
+
+def valu_floor_us():
+    """Time of the essential float32 lane operations of one call at the non-packed rate."""
+    return B * H * L * VALU_OPS_PER_TOKEN_HEAD / LANE_OPS_PER_S * 1e6
+
+
+def recorded_kernel_us():
+    """attn_kernel + merge_kernel average (us) from the committed rocprofv3 statistics
+    record, or None if the attention sources changed since it was taken."""
+    try:
+        text = open(KSTATS_FILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and not line.startswith(" "))
+    if fields.get("source_sha256", "").strip() != attn_source_hash():
+        return None
+    try:
+        return float(fields["call_kernel_us"].split()[0])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_stats_summary(directory):
+    """The library's kernels in a rocprofv3 --kernel-trace --stats csv run of the headline
+    measurement, and the average kernel time of one decode call (attention + merge)."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    lib = ("attn_kernel", "merge_kernel", "encode_kernel", "seed_kernel", "update_kernel", "round_kernel",
+           "rope_kernel", "rows_kernel", "cache_")
+    out = []
+    for r in rows:
+        name = r["Name"]
+        if not any(k in name for k in lib):
+            continue
+        short = name.split("(")[0].replace("lvq::(anonymous namespace)::", "").replace("void ", "")
+        out.append((short, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                    float(r["MaxNs"]) / 1e3, float(r.get("StdDev", 0) or 0) / 1e3))
+    out.sort(key=lambda x: -x[1] * x[2])
+    attn = [x for x in out if x[0].startswith("attn_kernel<128, 8, false")]
+    merge = [x for x in out if x[0].startswith("merge_kernel")]
+    call_us = (sum(x[1] * x[2] for x in attn) / max(1, sum(x[1] for x in attn)) +
+               sum(x[1] * x[2] for x in merge) / max(1, sum(x[1] for x in merge)))
+    print("# Kernels of the Ouro-1.4B-shaped 32K decode bench (headline measurement only)\n")
+    print("Command (repository root $REPO on the GPU host):\n")
+    print(f"    cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+          f"-d {directory} -o bench -- python3 $REPO/bench.py --no-cpu --headline-only")
+    print(f"    python3 $REPO/bench.py --kernel-stats-summary {directory}\n")
+    print(f"source_sha256: {attn_source_hash()}")
+    print(f"call_kernel_us: {call_us:.2f}  (attn_kernel + merge_kernel averages)")
+    print(f"algorithmic_bytes_per_call: {algorithmic_bytes_per_call(synth_q_end())}\n")
+    print(f"{'kernel':<62}{'calls':>7}{'avg_us':>10}{'min_us':>10}{'max_us':>10}{'stddev_us':>10}")
+    for n, c, a, lo, hi, sd in out:
+        print(f"{n[:61]:<62}{c:>7}{a:>10.2f}{lo:>10.2f}{hi:>10.2f}{sd:>10.2f}")
+
+
 N_BOOK_SAMPLES, N_LLOYD = 4096, 10
 
 
@@ -381,37 +454,105 @@ def run_decode(args, torch, lvq, inp):
     return wall, per_call
 
 
-def cpu_baseline(args, torch, inp):
-    """The float64 oracle on a bounded sample of the same workload: (b, head) pairs of one
-    (layer 0, loop step 1) call at full context, single thread."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_cores(asked=0):
+    """Worker processes for the CPU baseline: the cores this process may run on, at most 16
+    (the host share of one GPU)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    n = min(n, 16)
+    return max(1, min(asked, n) if asked > 0 else n)
+
+
+def _oracle_pairs(job):
+    """Worker: the oracle on a list of (b, head) pairs of the saved call; returns the count."""
+    directory, pairs = job
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import lvq_oracle as orc
-    Ly = inp["layers"][0]
-    t = 1
-    host = dict(
-        ip=Ly["ip"].cpu().numpy(), bp=Ly["bp"].cpu().numpy().view(np.uint16),
-        cb=Ly["cb"].cpu().numpy().view(np.uint16), q=Ly["q"][t].cpu().view(torch.int16).numpy().view(np.uint16),
-    )
-    shp = orc.AttnShape(B, H, H, D, T, TC, G, N_SINK)
-    pt = inp["pt_np"]
-    bt = inp["bt"].cpu().numpy()
-    pos = np.full(B, L)
-    qe = np.full(B, inp["q_end"])
-    pairs = [(b, h) for h in range(H) for b in range(B)]
+    z = {k: np.load(os.path.join(directory, k + ".npy"), mmap_mode="r") for k in
+         ("ip", "bp", "cb", "q", "pt", "bt", "pos", "qe", "meta")}
+    Bm, Hm, Dm, Tm, TCm, Gm, NS, t = (int(x) for x in z["meta"])
+    shp = orc.AttnShape(Bm, Hm, Hm, Dm, Tm, TCm, Gm, NS)
+    with threadpool_limits(limits=1):
+        orc.decode_attn(shp, np.asarray(z["q"]), z["pt"], z["ip"], z["bp"], z["bt"], np.asarray(z["cb"]), t,
+                        np.asarray(z["pos"]), np.asarray(z["pos"]), np.asarray(z["qe"]), pairs=pairs)
+    return len(pairs)
+
+
+def cpu_worker(directory, cores, seconds):
+    """Runs in a child process that never touches the GPU: the oracle over every (b, head)
+    pair of the saved call, one pair per task, on `cores` forked worker processes; pairs
+    not started within `seconds` are skipped.  Returns the pairs done and the wall time."""
+    import multiprocessing as mp
+    import numpy as np
+    meta = np.load(os.path.join(directory, "meta.npy"))
+    Bm, Hm = int(meta[0]), int(meta[1])
+    pairs = [(b, h) for h in range(Hm) for b in range(Bm)]
+    n = host_cores(cores)
     done = 0
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while done < len(pairs) and time.perf_counter() - t0 < args.cpu_seconds:
-            orc.decode_attn(shp, host["q"], pt, host["ip"], host["bp"], bt, host["cb"], t, pos, pos, qe,
-                            pairs=[pairs[done]])
-            done += 1
-    el = time.perf_counter() - t0
+    with mp.get_context("fork").Pool(n) as pool:
+        pending = [pool.apply_async(_oracle_pairs, ((directory, [p]),)) for p in pairs]
+        for r in pending:
+            left = seconds - (time.perf_counter() - t0)
+            if left <= 0:
+                break
+            try:
+                done += r.get(timeout=left)
+            except mp.TimeoutError:
+                break
+        el = time.perf_counter() - t0
+        pool.terminate()
+    return {"pairs": done, "of": len(pairs), "seconds": el, "cores": n}
+
+
+def cpu_baseline(args, torch, inp):
+    """The float64 oracle on a bounded sample of the same workload: the (b, head) pairs of
+    one (layer 0, loop step 1) call at full context, spread over the host's cores.  The
+    oracle runs in a child process (and its forked workers) that never touches the GPU;
+    the call's inputs reach it through .npy files."""
+    import shutil
+    import subprocess
+    import tempfile
+    import numpy as np
+    Ly = inp["layers"][0]
+    t = 1
+    d = tempfile.mkdtemp(prefix="lvq_cpu_")
+    try:
+        arrays = dict(
+            ip=Ly["ip"].cpu().numpy(), bp=Ly["bp"].cpu().numpy().view(np.uint16),
+            cb=Ly["cb"].cpu().numpy().view(np.uint16),
+            q=Ly["q"][t].cpu().view(torch.int16).numpy().view(np.uint16),
+            pt=inp["pt_np"], bt=inp["bt"].cpu().numpy(), pos=np.full(B, L), qe=np.full(B, inp["q_end"]),
+            meta=np.array([B, H, D, T, TC, G, N_SINK, t]))
+        for k, v in arrays.items():
+            np.save(os.path.join(d, k + ".npy"), np.ascontiguousarray(v))
+        cmd = [sys.executable, os.path.abspath(__file__), "--cpu-worker", d, "--cpu-cores", str(args.cpu_cores),
+               "--cpu-seconds", str(args.cpu_seconds)]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=args.cpu_seconds + 120)
+        if r.returncode != 0:
+            return {"error": r.stderr[-2000:]}
+        w = json.loads(r.stdout.strip().splitlines()[-1])
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
     # one (b, head) pair over L tokens is L/H token-steps of the all-head metric
-    value = done * L / H / el
-    return {"value": value, "unit": "KV token-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (sequence, head) pairs of one (layer, loop step) call at L={L}, "
-                      f"float64 numpy, 1 thread, {el:.1f}s"}
+    value = w["pairs"] * L / H / w["seconds"]
+    return {"value": value, "unit": "KV token-steps/s", "cores": w["cores"], "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{w['pairs']} of the {w['of']} (sequence, head) pairs of one (layer, loop step) call "
+                      f"at L={L} (float64 numpy oracle, one pair per task, {w['cores']} worker processes of "
+                      f"one thread each, {w['seconds']:.1f}s wall); not extrapolated: the value is the "
+                      f"sample's own rate"}
 
 
 def manager_bench(torch, lvq, inp, n_tokens=64):
@@ -959,6 +1100,12 @@ def main():
     if args.pmc_instructions:
         pmc_instructions(args.pmc_instructions)
         return
+    if args.kernel_stats_summary:
+        kernel_stats_summary(args.kernel_stats_summary)
+        return
+    if args.cpu_worker:
+        print(json.dumps(cpu_worker(args.cpu_worker, args.cpu_cores, args.cpu_seconds)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -987,25 +1134,36 @@ def main():
     probe = None if args.headline_only else hbm_probe(torch)
     pc = sorted(per_call)
     pct = {f"p{q}": round(pc[min(len(pc) - 1, int(q / 100 * len(pc)))] * 1e6, 2) for q in (10, 50, 90)}
-    # The call is bound by float32 vector arithmetic (the per-token rotation after
-    # dequantisation), so its roofline is the ALU one; the HBM fraction the metric names
-    # is reported beside it.
+    # The metric names the HBM fraction, so the roofline reports the call against the HBM
+    # peak (algorithmic bytes / event-timed call time / 8 TB/s).  The float32 vector work
+    # of the per-token rotation after dequantisation is what actually binds the call; its
+    # figures (VALU floor, issue bound, ALU fraction) sit beside it as flat fields.
     flops = algorithmic_flops_per_call()
     achieved_tflops = flops / call_avg / 1e12
-    roof = {"bound": "alu", "achieved": round(achieved_tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+    kern_us = recorded_kernel_us()
+    floor_us = valu_floor_us()
+    roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
-            "algorithmic_flops_per_call": flops,
-            "peak_unpacked": FP32_VECTOR_UNPACKED_TFLOPS,
-            "frac_of_unpacked_peak": round(achieved_tflops / FP32_VECTOR_UNPACKED_TFLOPS, 4),
+            "algorithmic_bytes_per_call": algo,
+            "traffic_over_algorithmic": None if traffic is None else round(traffic / algo, 3),
+            "kernel": "lvq_decode_attn call: attn_kernel<128,8> + merge_kernel, one (layer, loop step)",
+            "avg_call_us": round(call_avg * 1e6, 2), "call_us_percentiles": pct,
+            "frac_event_timed": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "kernel_us_rocprof": kern_us,
+            "frac_kernel_only": None if kern_us is None else round(algo / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "attainable_read_gbs": None if probe is None else probe["read_gbs"],
+            "attainable_copy_gbs": None if probe is None else probe["copy_gbs"],
+            "frac_of_attainable_read": None if probe is None else round(achieved_gbs / probe["read_gbs"], 4),
+            "valu_floor_us": round(floor_us, 2),
+            "frac_of_valu_floor": round(floor_us / (call_avg * 1e6), 4),
             "valu_issue_bound_us": valu_bound,
             "frac_of_valu_issue_bound": None if valu_bound is None else round(valu_bound / (call_avg * 1e6), 4),
-            "hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": algo,
-                    "attainable": probe,
-                    "frac_of_attainable_read": None if probe is None else round(achieved_gbs / probe["read_gbs"], 4)},
-            "kernel": "lvq_decode_attn call: attn_kernel<128,8> + merge_kernel, one (layer, loop step)",
-            "avg_call_us": round(call_avg * 1e6, 2), "call_us_percentiles": pct}
+            "alu_achieved_tflops": round(achieved_tflops, 2), "alu_peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
+            "alu_frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "alu_peak_unpacked_tflops": FP32_VECTOR_UNPACKED_TFLOPS,
+            "alu_frac_of_unpacked_peak": round(achieved_tflops / FP32_VECTOR_UNPACKED_TFLOPS, 4),
+            "algorithmic_flops_per_call": flops}
     res = {
         "metric": METRIC, "value": value, "unit": "KV token-steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,

@@ -166,9 +166,10 @@ int lvq_reencode_pages_layers(const lvq_reencode_layer* layers, int n_layers,
 /*
  * lvq_build_codebooks -- learn the 256-word codebooks of one of K / V from sample
  * tokens on the device: k-means on calibration keys and values (the summary,
- * section "어떻게 쓰나"), Fisher-weighted when weights are given (section "무엇과
- * 다른가": the codebooks start from Fisher-weighted k-means; the Fisher information
- * needs model gradients, so the weights are an input).  Every book (loop block,
+ * section "전제와 한계", experiments paragraph: k-means calibration on 16
+ * calibration sequences of 2,048 tokens), Fisher-weighted when weights are given
+ * (section "무엇과 다른가": the codebooks start from Fisher-weighted k-means; the
+ * Fisher information needs model gradients, so the weights are an input).  Every book (loop block,
  * head, group) is built at once.
  *   samples:   bf16 [T][S][H][d], S sample tokens (pre-RoPE keys or values), the
  *              encoder's input layout.  1 <= S <= 8192.
@@ -198,8 +199,10 @@ int lvq_build_codebooks(const uint16_t* samples, const double* draws, const doub
                         uint16_t* codebooks, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * RoPE phase tables (rotate-half convention: channel j pairs with j + d/2 and
- * turns by the angle p * theta_j, theta_j = base^(-2j/d)).  Phases are formed
+ * RoPE phase tables.  Keys are coded before RoPE and attention rotates the
+ * reconstructed keys (the summary, section "무엇과 다른가"), so the decode kernel
+ * needs the phase of every cached position.  Rotate-half convention: channel j
+ * pairs with j + d/2 and turns by the angle p * theta_j, theta_j = base^(-2j/d).  Phases are formed
  * in float64 (angle and cos/sin); the table holds, in order:
  *   float32 rows 0 .. ntile-1:       (cos, sin)(16 a * theta_j), j < d/2   (a = p / 16)
  *   float32 rows ntile .. ntile+15:  (cos, sin)(o * theta_j),    j < d/2   (o = p % 16)
@@ -222,19 +225,28 @@ typedef struct lvq_attn_shape {
   int32_t n_sink;         /* bf16 sink tokens (<= 8), read from the bf16 copy of page 0 */
   int32_t max_pages;      /* row length of page_table */
   int32_t bf16_row;       /* row length of bf16_table */
-  int32_t n_index_pages;  /* rows of index_pages (range check of page ids) */
-  int32_t n_bf16_pages;   /* rows of bf16_pages */
+  int32_t n_index_pages;  /* rows of index_pages (range check of page ids), >= 1 even when
+                             every token is bf16; a coded token whose page id is outside
+                             [0, n_index_pages) is left out of the attention */
+  int32_t n_bf16_pages;   /* rows of bf16_pages, >= 1 */
   int32_t max_seq_len;    /* upper bound of seq_len[b]; sizes the automatic split */
   int32_t rope_max_len;   /* max_len the rope table was built for; every pos and seq_len must be < it */
   int32_t n_splits;       /* waves per query head; 0 = automatic (see lvq_decode_attn) */
   float scale;            /* softmax scale; 0 = 1/sqrt(d) */
 } lvq_attn_shape;
 
-/* Workspace bytes of lvq_decode_attn / lvq_decode_scores for this shape. */
+/* Workspace bytes of lvq_decode_attn / lvq_decode_scores for this shape: the
+ * partial (max, sum, output) records of the Flash-Decoding split that the
+ * log-sum-exp merge combines (the summary, section "전제와 한계"). */
 size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp);
 
 /*
- * lvq_decode_attn -- decode attention at loop step t over the paged cache.
+ * lvq_decode_attn -- decode attention at loop step t over the paged cache (the
+ * summary, section "전제와 한계": the kernel reads only the loop-step-t codebook
+ * slice, splits the coded tokens Flash-Decoding style and merges the parts by
+ * log-sum-exp; section "무엇과 다른가": RoPE on the reconstructed keys; the rit.work
+ * article, section "Когда LoopVQ меняет план развёртывания": keys and values are
+ * rebuilt from the codebooks and merged with the uncompressed bf16 tokens).
  *   q:           bf16 [B][Hq][d], pre-RoPE query of loop step t.
  *   page_table:  int32 [B][max_pages], logical page -> coded page id.  Entries of
  *                logical pages 0 .. q_end[b]/8 - 1 are read.
@@ -274,8 +286,10 @@ int lvq_decode_attn(const uint16_t* q, const int32_t* page_table, const uint8_t*
 
 /*
  * lvq_decode_scores -- test probe: same inputs and device code as
- * lvq_decode_attn, but also writes the scaled scores q'.k' * scale (natural
- * units) of every cached token to scores: float32 [B][Hq][max_seq_len]
+ * lvq_decode_attn (same passages), but also writes the scaled scores q'.k' * scale
+ * (natural units) of every cached token to scores, from which the attention mass
+ * of a span of positions (the long-context retrieval check of the summary, section
+ * "전제와 한계", RULER needle tasks) follows as sum exp(s_p - lse): float32 [B][Hq][max_seq_len]
  * (entries at p >= seq_len[b] are left untouched).  out and lse are produced too.
  */
 int lvq_decode_scores(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,

@@ -401,9 +401,9 @@ def needle_mass(scores: np.ndarray, lse: float, lo: int, hi: int) -> float:
 # ----------------------------------------------------------------------------
 # codebook builder: k-means++ seeding and Lloyd iterations
 # ----------------------------------------------------------------------------
-# The summary (section "어떻게 쓰나") learns the codebooks by k-means on
-# calibration K/V, and (section "무엇과 다른가") initialises them by Fisher-weighted
-# k-means; the pages fix neither the seeding, the weights nor the precision.
+# The summary (section "전제와 한계", experiments paragraph) calibrates the
+# codebooks by k-means on calibration K/V, and (section "무엇과 다른가") initialises
+# them by Fisher-weighted k-means; the pages fix neither the seeding, the weights nor the precision.
 # Readings: one non-negative weight per joint vector, given as an input (the Fisher
 # information itself needs model gradients); k-means++ seeding (weighted D^2
 # sampling) driven by draws passed in; Lloyd iterations whose assignment uses the

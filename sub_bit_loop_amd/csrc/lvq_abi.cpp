@@ -95,7 +95,9 @@ int check_attn(const void* q, const void* page_table, const void* index_pages,
   if ((long)s.max_pages * lvq::kPage < s.max_seq_len)
     return fail(LVQ_EINVAL, "max_pages=%d too small for max_seq_len=%d", s.max_pages, s.max_seq_len);
   if (s.bf16_row < 1) return fail(LVQ_EINVAL, "bf16_row must be >= 1");
-  if (s.n_index_pages < 0 || s.n_bf16_pages <= 0) return fail(LVQ_EINVAL, "pool sizes must be positive");
+  // an all-bf16 cache still passes a coded pool of at least one page: a zero-page pool
+  // would make every coded token's page id out of range, and those tokens are skipped
+  if (s.n_index_pages <= 0 || s.n_bf16_pages <= 0) return fail(LVQ_EINVAL, "pool sizes must be positive");
   if (s.rope_max_len <= s.max_seq_len)
     return fail(LVQ_EINVAL, "rope_max_len=%d must exceed max_seq_len=%d", s.rope_max_len, s.max_seq_len);
   if (!(s.scale >= 0.f) || isinf(s.scale)) return fail(LVQ_EINVAL, "scale must be finite and >= 0");
@@ -159,7 +161,9 @@ int check_rows(const void* q, const void* k_new, const void* v_new, const void* 
   if ((long)s.max_pages * lvq::kPage < s.max_prefix)
     return fail(LVQ_EINVAL, "max_pages=%d too small for max_prefix=%d", s.max_pages, s.max_prefix);
   if (s.bf16_row < 1) return fail(LVQ_EINVAL, "bf16_row must be >= 1");
-  if (s.n_index_pages < 0 || s.n_bf16_pages <= 0) return fail(LVQ_EINVAL, "pool sizes must be positive");
+  // an all-bf16 cache still passes a coded pool of at least one page: a zero-page pool
+  // would make every coded token's page id out of range, and those tokens are skipped
+  if (s.n_index_pages <= 0 || s.n_bf16_pages <= 0) return fail(LVQ_EINVAL, "pool sizes must be positive");
   if ((long)s.rope_max_len < (long)s.max_prefix + s.NQ)
     return fail(LVQ_EINVAL, "rope_max_len=%d below max_prefix + NQ = %ld", s.rope_max_len, (long)s.max_prefix + s.NQ);
   if (!(s.scale >= 0.f) || isinf(s.scale)) return fail(LVQ_EINVAL, "scale must be finite and >= 0");

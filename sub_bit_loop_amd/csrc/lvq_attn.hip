@@ -744,13 +744,12 @@ __global__ void rope_kernel(int ntile, int d, double base, float* tab) {
 template <int D, int C, bool SCORES, bool WIDE>
 hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   constexpr size_t lds = lds_bytes<D>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, C, SCORES, WIDE>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_set{0};
+  hipError_t ea = once_per_device(attr_set, [&] {
+    return hipFuncSetAttribute((const void*)attn_kernel<D, C, SCORES, WIDE>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (ea != hipSuccess) return ea;
   const int n_items = a.B * a.Hq;
   const int wph = a.n_waves / kNW;   // workgroups per query head
   if (wph < 1 || a.n_waves % kNW || a.n_waves + 1 > kMergeMax || a.n_rec != a.n_waves + a.B || !a.tile_start)

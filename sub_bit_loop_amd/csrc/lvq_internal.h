@@ -4,9 +4,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "lvq.h"
 
 namespace lvq {
+
+// Runs set() (a kernel attribute such as its dynamic-LDS limit, which applies to the
+// current device) the first time it is needed on each device.  Flags are per device
+// and atomic; two first calls racing on one device both run set(), which is
+// idempotent.  Devices beyond 64 run set() on every call.
+template <typename F>
+inline hipError_t once_per_device(std::atomic<uint64_t>& done, F&& set) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = set();
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 constexpr int kPage = 8;
 constexpr int kCodes = 256;

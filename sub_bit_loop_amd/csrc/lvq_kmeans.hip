@@ -1,8 +1,8 @@
 // LoopVQ codebook builder for gfx950: k-means++ seeding and Lloyd iterations.
 //
 // What it computes (LoopVQ summary, onedev.kr/papers/1681, section "무엇과 다른가":
-// the codebooks are initialised by Fisher-weighted k-means; section "어떻게 쓰나":
-// they are learned on calibration keys and values): for every book (loop block beta,
+// the codebooks are initialised by Fisher-weighted k-means; section "전제와 한계",
+// experiments paragraph: a k-means calibration on calibration sequences, timed per model): for every book (loop block beta,
 // head h, group g) of one of K / V, the 256 codewords of the joint vectors
 // x_s[tau*c + i] = X[beta*Tc + tau][s][h][g*c + i] of S sample tokens, each with a
 // weight w_s >= 0 (all 1 when no weights are given; the weights stand in for the
@@ -451,17 +451,16 @@ hipError_t build_t(const KmeansArgs& a, hipStream_t s) {
   const int Sp = (a.S + 2 * kChain - 1) / (2 * kChain) * (2 * kChain);
   const size_t seed_lds = (size_t)(Sp + Sp / kChain) * sizeof(double);
   const size_t upd_lds = update_lds_bytes(G, a.S);
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<uint64_t> attr_set{0};
+  hipError_t ea = once_per_device(attr_set, [&] {
     hipError_t e = hipFuncSetAttribute((const void*)seed_kernel<G, C, kSeedMaxPer, false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)((kMaxKmeansSamples + kMaxKmeansSamples / kChain) * sizeof(double)));
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)update_kernel<G, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)update_lds_bytes(G, kMaxKmeansSamples));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return hipFuncSetAttribute((const void*)update_kernel<G, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)update_lds_bytes(G, kMaxKmeansSamples));
+  });
+  if (ea != hipSuccess) return ea;
   if (a.S <= kSeedRegPer * kSeedThreads)
     hipLaunchKernelGGL((seed_kernel<G, C, kSeedRegPer, true>), dim3(a.n_books), dim3(kSeedThreads), seed_lds, s, a);
   else

@@ -548,13 +548,12 @@ void rows_kernel(RowsArgs a, int wph) {
 template <int C>
 hipError_t launch_rows_t(const RowsArgs& a, hipStream_t s) {
   constexpr size_t lds = rows_lds_bytes();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)rows_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_set{0};
+  hipError_t ea = once_per_device(attr_set, [&] {
+    return hipFuncSetAttribute((const void*)rows_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds);
+  });
+  if (ea != hipSuccess) return ea;
   const int wph = a.n_waves / kRW;   // workgroups per (KV head, row block)
   if (wph < 1 || a.n_waves % kRW || a.n_rec != a.n_waves + a.B || !a.tile_start) return hipErrorInvalidValue;
   const long grid = (long)wph * a.n_rb * a.H;

@@ -166,3 +166,70 @@ def build_cache_light(config: int, B: int, lengths, H: int, d: int, T: int, Tc: 
     q = synth.gen_queries(rq, T, B, Hq, d)
     return Cache(B, H, Hq, d, T, Tc, G, n_sink, n_recent, lengths.copy(), q_end, lengths.copy(),
                  pt, ip, bp, lay.bf16_table, cb, q)
+
+
+def build_cache_generated(config: int, B: int, lengths, H: int, d: int, T: int, Tc: int, G: int,
+                          n_sink: int, n_recent: int, book_samples: int = 4096) -> Cache:
+    """Full-size cache from the generator's own tokens, built with torch on the GPU (input
+    preparation only, none of the library's kernels): AR(1) keys and values per sequence,
+    k-means++ / 10-Lloyd codebooks fitted on `book_samples` seeded samples, and every coded
+    token's index the nearest codeword by torch's float32 distance matmul and argmin.  The
+    indices are therefore realistic codes (not uniform draws); where float32 rounding picks
+    a near-tied neighbour the cache is still a valid input, since attention parity reads the
+    same pages on both sides."""
+    import torch
+    dev = torch.device("cuda")
+    lengths = np.asarray(lengths, dtype=np.int32)
+    rk = np.random.default_rng(synth.seed_for(config, synth.STREAM_K))
+    rv = np.random.default_rng(synth.seed_for(config, synth.STREAM_V))
+    sc_k = synth.channel_scales(rk, H, d)
+    sc_v = synth.channel_scales(rv, H, d)
+    c = G // Tc
+    ng, nblk = d // c, T // Tc
+    rb = np.random.default_rng(synth.seed_for(config, synth.STREAM_BOOKS))
+    books = []
+    for kv, sc in ((0, sc_k), (1, sc_v)):
+        s = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(synth.gen_kv(rb, T, book_samples, H, d, sc)))
+        books.append(synth.codebooks_from_samples(s, Tc, G, config * 7 + 1 + kv, device="cuda",
+                                                  dtype=torch.float32))
+    cb = np.ascontiguousarray(np.stack(books, axis=1))                 # [nblk][2][H][ng][Tc][256][c]
+    cbf = torch.from_numpy(synth.bf16_bits_to_f32(cb).astype(np.float32)).to(dev)
+    # joint codewords [nblk][2][H][ng][256][G], step-major inside the joint vector
+    Cj = cbf.permute(0, 1, 2, 3, 5, 4, 6).reshape(nblk, 2, H, ng, 256, G).contiguous()
+    cn = (Cj * Cj).sum(-1)                                              # [nblk][2][H][ng][256]
+    q_end = np.array([synth.prefill_q_end(int(L), n_recent) for L in lengths], dtype=np.int32)
+    n_pages = [int(qe) // 8 for qe in q_end]
+    max_pages = max(1, max((int(L) + 7) // 8 for L in lengths))
+    rp = np.random.default_rng(synth.seed_for(config, synth.STREAM_PAGES))
+    pt, pool = synth.shuffled_page_table(rp, n_pages, max_pages)
+    ip = np.zeros((max(pool, 1), nblk, H, 2, 8, ng), dtype=np.uint8)
+    gen = torch.Generator(device=dev)
+    fk, fv, rk_, rv_ = [], [], [], []
+    for b in range(B):
+        L, qe = int(lengths[b]), int(q_end[b])
+        base = (qe // 8) * 8
+        for kv, sc, first, rec in ((0, sc_k, fk, rk_), (1, sc_v, fv, rv_)):
+            gen.manual_seed(synth.seed_for(config, kv) * 1009 + b)
+            x = synth.gen_kv_torch(gen, T, L, H, d, sc, device=dev)     # bf16 [T][L][H][d]
+            first.append(x[:, :min(8, L)].view(torch.int16).cpu().numpy().view(np.uint16))
+            rec.append(x[:, base:L].view(torch.int16).cpu().numpy().view(np.uint16))
+            if qe == 0:
+                continue
+            xf = x[:, :qe].float().reshape(nblk, Tc, qe, H, ng, c)
+            J = xf.permute(0, 3, 4, 2, 1, 5).reshape(nblk, H, ng, qe, G)   # [nblk][H][ng][qe][G]
+            idx = torch.empty((nblk, H, ng, qe), dtype=torch.uint8, device=dev)
+            for beta in range(nblk):
+                for h in range(H):
+                    A = J[beta, h].contiguous()                          # [ng][qe][G]
+                    Ct = Cj[beta, kv, h].transpose(1, 2).contiguous()    # [ng][G][256]
+                    dist = cn[beta, kv, h][:, None, :] - 2.0 * torch.bmm(A, Ct)
+                    idx[beta, h] = dist.argmin(-1).to(torch.uint8)
+            idx = idx.view(nblk, H, ng, qe // 8, 8).permute(3, 0, 1, 4, 2).cpu().numpy()  # [pg][nblk][H][8][ng]
+            ip[pt[b, :qe // 8], :, :, kv] = idx
+            del x, xf, J, idx
+    torch.cuda.empty_cache()
+    bp, lay = synth.pack_bf16_pages_parts(fk, fv, rk_, rv_, q_end, lengths, T, H, d, rng=rp)
+    rq = np.random.default_rng(synth.seed_for(config, synth.STREAM_Q))
+    q = synth.gen_queries(rq, T, B, H, d)
+    return Cache(B, H, H, d, T, Tc, G, n_sink, n_recent, lengths.copy(), q_end, lengths.copy(),
+                 pt, ip, bp, lay.bf16_table, cb, q)

@@ -64,12 +64,15 @@ def gpu_attn(dc: DevCache, t: int, n_splits: int = 0, scores: bool = False, q=No
     return res
 
 
-def attn_close(got, ref, atol=2e-3, rtol=1e-2):
-    """Element passes if |d| <= atol or |d| <= rtol * |ref|; returns (ok, max_abs, max_rel)."""
+def attn_close(got, ref, atol=2e-3, rtol=1e-2, rel_floor=0.2):
+    """The attention acceptance: max-abs <= atol over every element AND max-rel <= rtol
+    over the elements with |ref| >= rel_floor (a relative error means nothing near zero).
+    Returns (ok, max_abs, max_rel)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     err = np.abs(got - ref)
-    ok = (err <= atol) | (err <= rtol * np.abs(ref))
-    big = np.abs(ref) >= 0.2
+    big = np.abs(ref) >= rel_floor
+    mabs = float(err.max()) if err.size else 0.0
     mrel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
-    return bool(ok.all()), float(err.max()), mrel
+    ok = bool(np.isfinite(got).all()) and mabs <= atol and mrel <= rtol
+    return ok, mabs, mrel

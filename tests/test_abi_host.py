@@ -119,6 +119,8 @@ def test_attn_validation(L):
     assert attn(L, shape(n_sink=9)) == 1
     assert attn(L, shape(max_pages=10)) == 1
     assert attn(L, shape(rope_max_len=512)) == 1
+    assert attn(L, shape(n_index_pages=0)) == 1   # an all-bf16 cache still passes one coded page
+    assert attn(L, shape(n_bf16_pages=0)) == 1
     assert attn(L, shape(d=96, G=16, Tc=2)) == 2
     assert attn(L, shape(G=16, Tc=4)) == 2       # c = 4 not compiled for decode
     assert attn(L, shape(d=64, G=32, Tc=1)) == 2  # c = 32 at d = 64 not compiled
@@ -198,6 +200,7 @@ def test_rows_shape_validation(L):
     assert call(rs(Hq=3)) == 1
     assert call(rs(rope_max_len=503)) == 1              # below max_prefix + NQ
     assert call(rs(max_pages=62)) == 1                  # 62 pages hold fewer than 500 tokens
+    assert call(rs(n_index_pages=0)) == 1               # coded pool must hold a page
     assert call(rs(d=64, G=16, Tc=2)) == 2              # multi-row kernel compiled for d = 128 only
     need = L.lvq_rows_attn_workspace_bytes(ctypes.byref(rs()))
     # records [H * row blocks][W + B][16 rows][d + 2] float32 + first units [row blocks][B + 1]:

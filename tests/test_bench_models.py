@@ -43,3 +43,30 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_valu_floor_at_the_ouro_shape():
+    """512 float32 lane operations per cached (token, head) at d = 128 (6 per channel pair
+    for the rotated score, one FMA per channel for the value sum) over 4.19 M (token, head)
+    at 256 CUs x 64 lanes x 2.4 GHz: 54.6 us."""
+    assert bench.VALU_OPS_PER_TOKEN_HEAD == 512
+    assert bench.valu_floor_us() == pytest.approx(54.6, abs=0.05)
+
+
+def test_cpu_baseline_worker_runs_every_pair_of_a_small_call(tmp_path):
+    """The CPU baseline's worker (a child process with forked oracle workers, no GPU)
+    covers every (b, head) pair of a saved call and reports its cores."""
+    import numpy as np
+    from cachebuild import build_cache
+    c = build_cache(41, 2, [200, 77], 2, 64, 4, 2, 16, 4, 16, books="random", index="random")
+    t = 1
+    arrays = dict(ip=c.index_pages, bp=c.bf16_pages, cb=c.codebooks, q=c.q[t], pt=c.page_table,
+                  bt=c.bf16_table, pos=c.seq_len, qe=c.q_end,
+                  meta=np.array([c.B, c.H, c.d, c.T, c.Tc, c.G, c.n_sink, t]))
+    for k, v in arrays.items():
+        np.save(tmp_path / f"{k}.npy", np.ascontiguousarray(v))
+    w = bench.cpu_worker(str(tmp_path), 2, 60.0)
+    assert w["pairs"] == w["of"] == c.B * c.H
+    assert w["cores"] == 2 and w["seconds"] > 0
+    assert bench.host_cores(0) >= 1 and bench.host_cores(100) <= 16
+    assert isinstance(bench.cpu_model(), str)

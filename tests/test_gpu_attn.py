@@ -1,9 +1,11 @@
 """GPU decode-attention parity against the float64 oracle, through the C ABI.
 
-Tolerance (element-wise): |gpu - oracle| <= 2e-3 or <= 1e-2 * |oracle|, on the
-float32 output; lse within 1e-4 absolute.  Full context lengths are run on the
-GPU in the launch configuration the benchmark uses; the oracle checks sampled
-(sequence, head) pairs.
+Tolerance: max-abs <= 2e-3 over every output element and max-rel <= 1e-2 over
+the elements with |oracle| >= 0.2, on the float32 output; lse within 1e-4
+absolute.  Full context lengths run on the GPU in the launch configuration the
+benchmark uses; the oracle checks every (sequence, head) pair of the Ouro-shaped
+call and every head of the 64K needle call.  Each case's figures go to the
+parity record (parity_log).
 """
 import dataclasses
 
@@ -15,6 +17,7 @@ import synth
 from cachebuild import build_cache, build_cache_light
 from gpu_helpers import attn_close, gpu_attn, to_dev
 from oracle import lvq_oracle as orc
+import parity_log as plog
 
 pytestmark = pytest.mark.gpu
 
@@ -32,15 +35,17 @@ def check(out, lse, ref_out, ref_lse, label, pairs=None):
     empty = np.isneginf(ref_lse)
     np.testing.assert_array_equal(np.isneginf(l), empty, err_msg=f"{label}: -inf lse pattern")
     lerr = float(np.abs(l[~empty] - ref_lse[~empty]).max()) if (~empty).any() else 0.0
-    print(f"  {label}: max-abs {mabs:.2e} max-rel {mrel:.2e} lse err {lerr:.2e}", flush=True)
-    assert ok, f"{label}: output outside tolerance (max-abs {mabs:.3e})"
+    n_rows = int(np.prod(o.shape[:-1]))
+    plog.line(f"{label}: {n_rows} (b, head) rows x {o.shape[-1]} channels, max-abs {mabs:.3e}, "
+              f"max-rel {mrel:.3e} (|ref| >= 0.2), lse max-abs {lerr:.3e}")
+    assert ok, f"{label}: output outside tolerance (max-abs {mabs:.3e}, max-rel {mrel:.3e})"
     assert lerr <= 1e-4, f"{label}: lse error {lerr:.3e}"
 
 
 def test_tiny_config_all_steps():
     """The tiny configuration end to end: oracle-encoded pages, k-means books, every step."""
-    print("\ncase tiny d=64 H=1 T=4 Tc=2 G=16 L=512", flush=True)
-    cache = build_cache(1, 1, [512], 1, 64, 4, 2, 16, 4, 16, book_samples=1024)
+    plog.case("attention, tiny configuration: d=64 H=1 T=4 Tc=2 G=16 L=512, k-means books on 4096 samples")
+    cache = build_cache(1, 1, [512], 1, 64, 4, 2, 16, 4, 16, book_samples=4096)
     dc = to_dev(cache)
     for t in range(4):
         out, lse = gpu_attn(dc, t)
@@ -62,7 +67,8 @@ EDGE = [  # config, B, lengths, H, Hq, d, T, Tc, G, n_sink, n_recent
 
 @pytest.mark.parametrize("cfg,B,lengths,H,Hq,d,T,Tc,G,ns,nr", EDGE)
 def test_edge_cases(cfg, B, lengths, H, Hq, d, T, Tc, G, ns, nr):
-    print(f"\ncase edge cfg={cfg} B={B} L={lengths} H={H} Hq={Hq} d={d} T={T} Tc={Tc} G={G}", flush=True)
+    plog.case(f"attention edge case cfg={cfg} B={B} L={lengths} H={H} Hq={Hq} d={d} T={T} Tc={Tc} G={G} "
+              f"n_sink={ns} n_recent={nr}")
     cache = build_cache(cfg, B, lengths, H, d, T, Tc, G, ns, nr, Hq=Hq, books="random",
                         index="random")
     dc = to_dev(cache)
@@ -75,7 +81,7 @@ def test_edge_cases(cfg, B, lengths, H, Hq, d, T, Tc, G, ns, nr):
 def test_split_counts_and_page_permutation():
     """Splits 1, 2, 7 and one per tile agree with the oracle and with each other; a page
     table over an identity pool gives the same bits as the shuffled one."""
-    print("\ncase splits / permutation", flush=True)
+    plog.case("attention split counts 1/2/7/1000 and page permutation, B=2 L=[2000, 1111]")
     kw = dict(books="random", index="oracle")
     cache = build_cache(37, 2, [2000, 1111], 2, 128, 4, 4, 32, 4, 64, **kw)
     dc = to_dev(cache)
@@ -101,7 +107,7 @@ def test_many_sequences_token_balanced_split():
     """70 sequences (more than one 64-lane scan block) with lengths U[1, 400] and GQA 2:
     every (b, head) against the oracle for automatic, one-workgroup and 1008-wave splits
     (the last leaves most waves with empty ranges); the three agree closely."""
-    print("\ncase B=70 lengths U[1,400] splits 0/1/1000", flush=True)
+    plog.case("attention token-balanced split, B=70 lengths U[1,400], GQA 2, splits 0/1/1000")
     rl_ = np.random.default_rng(synth.seed_for(40, synth.STREAM_LENGTHS))
     lengths = synth.uniform_lengths(rl_, 70, 1, 400)
     cache = build_cache(40, 70, lengths, 2, 128, 4, 4, 32, 4, 16, Hq=4, books="random", index="random")
@@ -121,7 +127,7 @@ def test_index_pool_beyond_4gib():
     """An index pool over 4 GiB takes the kernel's 64-bit page addressing.  The same pages
     moved to the top of such a pool give the same bits as the compact pool (page
     placement invariance), so the 32-bit and 64-bit address paths agree."""
-    print("\ncase index pool over 4 GiB", flush=True)
+    plog.case("attention, index pool over 4 GiB (64-bit page addressing): bit-identical to the compact pool")
     cache = build_cache(39, 1, [2000], 2, 128, 4, 4, 32, 4, 64, books="random", index="random")
     dc = to_dev(cache)
     ref, ref_lse = gpu_attn(dc, 1)
@@ -158,19 +164,40 @@ def test_step_slice_locality_on_gpu():
         np.testing.assert_array_equal(o1.cpu().numpy(), o2.cpu().numpy())
 
 
-def test_ouro_shape_full_context_sampled():
+ALL_PAIRS_C2 = [(b, h) for b in range(8) for h in range(16)]
+
+
+def test_ouro_shape_full_context_all_pairs():
     """Ouro-1.4B-shaped call: B=8, 32768 tokens, 16 heads, d=128, T=4, Tc=4, G=32,
-    4 sink + 64 recent, shuffled pages; all heads on the GPU, 6 (b, h) pairs checked."""
-    print("\ncase ouro-shaped B=8 L=32768", flush=True)
-    cache = build_cache_light(2, 8, [32768] * 8, 16, 128, 4, 4, 32, 4, 64, books="random")
+    4 sink + 64 recent, shuffled pages, in the benchmark's launch configuration.  The
+    cache holds the generator's own tokens coded against k-means books (realistic codes
+    and value scales); every (b, head) pair at every loop step is checked."""
+    plog.case("attention, Ouro-shaped B=8 L=32768 H=16 d=128 T=4 Tc=4 G=32: generated tokens, "
+              "k-means books (4096 samples), nearest-codeword indices; all 128 (b, head) pairs")
+    from cachebuild import build_cache_generated
+    cache = build_cache_generated(2, 8, [32768] * 8, 16, 128, 4, 4, 32, 4, 64)
     dc = to_dev(cache)
-    pairs = [(0, 0), (3, 7), (7, 15), (5, 2), (1, 11), (6, 9)]
-    for t in (0, 3):
+    for t in range(4):
         out, lse = gpu_attn(dc, t)
         ro, rl = orc.decode_attn(cache.shape(), cache.q[t], cache.page_table, cache.index_pages,
                                  cache.bf16_pages, cache.bf16_table, cache.codebooks, t, cache.pos,
-                                 cache.seq_len, cache.q_end, pairs=pairs)
-        check(out, lse, ro, rl, f"t={t}", pairs=pairs)
+                                 cache.seq_len, cache.q_end, pairs=ALL_PAIRS_C2)
+        check(out, lse, ro, rl, f"t={t}", pairs=ALL_PAIRS_C2)
+
+
+def test_ouro_shape_uniform_codes_all_pairs():
+    """The same shape with uniform random codes over Gaussian books on the data's channel
+    scales (every codeword equally likely, so every LDS gather pattern occurs); all 128
+    (b, head) pairs at the first loop step."""
+    plog.case("attention, Ouro-shaped B=8 L=32768: uniform random codes, Gaussian books; all 128 pairs")
+    cache = build_cache_light(2, 8, [32768] * 8, 16, 128, 4, 4, 32, 4, 64, books="random")
+    dc = to_dev(cache)
+    t = 0
+    out, lse = gpu_attn(dc, t)
+    ro, rl = orc.decode_attn(cache.shape(), cache.q[t], cache.page_table, cache.index_pages,
+                             cache.bf16_pages, cache.bf16_table, cache.codebooks, t, cache.pos,
+                             cache.seq_len, cache.q_end, pairs=ALL_PAIRS_C2)
+    check(out, lse, ro, rl, f"t={t}", pairs=ALL_PAIRS_C2)
 
 
 def plant_needle(cache, lo, span, rng):
@@ -207,42 +234,51 @@ def plant_needle(cache, lo, span, rng):
 
 def test_needle_64k():
     """Long-context retrieval shape: B=1, 65536 tokens, 16 heads, T=4, Tc=2, G=16, split-K
-    over the coded tokens; the needle's attention mass matches the oracle."""
+    over the coded tokens; every head at every loop step: output, lse, every score and the
+    needle's attention mass against the oracle."""
     import sub_bit_loop_amd as lvq  # noqa: F401
-    print("\ncase needle L=65536", flush=True)
+    plog.case("attention, 64K needle B=1 L=65536 H=16 d=128 T=4 Tc=2 G=16: all 16 heads, all 4 steps")
     cache = build_cache_light(3, 1, [65536], 16, 128, 4, 2, 16, 4, 64, books="kmeans",
                               book_samples=1024)
     rng = np.random.default_rng(synth.seed_for(3, synth.STREAM_NEEDLE))
     lo = int(rng.integers(1000, 60000)) // 8 * 8
     plant_needle(cache, lo, 16, rng)
     dc = to_dev(cache)
-    heads = [0, 5, 13]
-    for t in (0, 3):
+    heads = list(range(16))
+    pairs = [(0, h) for h in heads]
+    for t in range(4):
         out, lse, sc = gpu_attn(dc, t, scores=True)
         ro, rl, rs = orc.decode_attn(cache.shape(), cache.q[t], cache.page_table, cache.index_pages,
                                      cache.bf16_pages, cache.bf16_table, cache.codebooks, t,
                                      cache.pos, cache.seq_len, cache.q_end, return_scores=True,
-                                     heads=heads)
-        pairs = [(0, h) for h in heads]
+                                     pairs=pairs)
         check(out, lse, ro, rl, f"t={t}", pairs=pairs)
         s = sc.cpu().numpy()
         l = lse.cpu().numpy()
+        worst_mass, worst_score = 0.0, 0.0
         for h in heads:
             m_gpu = float(np.exp(s[0, h, lo:lo + 16].astype(np.float64) - l[0, h]).sum())
             m_ref = orc.needle_mass(rs[(0, h)], rl[0, h], lo, lo + 16)
-            print(f"  needle mass h={h}: gpu {m_gpu:.6f} oracle {m_ref:.6f}", flush=True)
             assert m_ref > 0.5          # the needle dominates (uniform mass would be 2.4e-4)
-            assert abs(m_gpu - m_ref) <= 2e-3
+            assert abs(m_gpu - m_ref) <= 2e-3, f"t={t} h={h}: needle mass gpu {m_gpu} oracle {m_ref}"
             np.testing.assert_allclose(s[0, h], rs[(0, h)], atol=2e-3, rtol=1e-4)
+            worst_mass = max(worst_mass, abs(m_gpu - m_ref))
+            worst_score = max(worst_score, float(np.abs(s[0, h] - rs[(0, h)]).max()))
+            if h in (0, 15):
+                plog.line(f"t={t} h={h}: needle mass gpu {m_gpu:.6f} oracle {m_ref:.6f}")
+        plog.line(f"t={t}: 16 heads, needle mass max |gpu - oracle| {worst_mass:.3e}, "
+                  f"65536 scores per head max-abs {worst_score:.3e}")
 
 
 def test_mixed_serving_batch_sampled():
     """Mixed batch: 64 sequences with lengths U[1024, 16384], T=8, Tc=4, G=32, plus the
     prelude layer coded per step (T=1, Tc=1, G=32); sampled (b, h) pairs."""
-    print("\ncase mixed batch B=64", flush=True)
+    plog.case("attention, mixed batch B=64 lengths U[1024,16384], looped T=8 Tc=4 G=32 and prelude "
+              "T=1 Tc=1 G=32: 16 sampled (b, head) pairs per step")
     rl_ = np.random.default_rng(synth.seed_for(5, synth.STREAM_LENGTHS))
     lengths = synth.uniform_lengths(rl_, 64, 1024, 16384)
-    pairs = [(0, 0), (17, 4), (40, 15), (63, 9)]
+    prs = np.random.default_rng(55)
+    pairs = [(int(b), int(h)) for b, h in zip(prs.integers(0, 64, 16), prs.integers(0, 16, 16))]
     for (T, Tc, G) in ((8, 4, 32), (1, 1, 32)):
         cache = build_cache_light(5, 64, lengths, 16, 128, T, Tc, G, 4, 64, books="random")
         dc = to_dev(cache)

@@ -3,7 +3,8 @@ oracle, through the C ABI.
 
 Query i of a chunk is the oracle's decode attention over the prefix plus the chunk's
 tokens 0 .. i (appended as bf16 tokens after the prefix), at position prefix + i.
-Tolerance as for decode: |gpu - oracle| <= 2e-3 or <= 1e-2 |oracle|; lse within 1e-4.
+Tolerance as for decode: max-abs <= 2e-3 over every element and max-rel <= 1e-2 over
+the elements with |oracle| >= 0.2; lse within 1e-4.
 """
 import numpy as np
 import pytest
@@ -13,6 +14,7 @@ import synth
 from cachebuild import build_cache, build_cache_light
 from gpu_helpers import attn_close, to_dev
 from oracle import lvq_oracle as orc
+import parity_log as plog
 
 pytestmark = pytest.mark.gpu
 
@@ -103,7 +105,8 @@ def compare(got, ref, label):
     sel = ~np.isnan(rl)
     ok, mabs, mrel = attn_close(o[sel], ro[sel])
     lerr = float(np.abs(l[sel] - rl[sel]).max())
-    print(f"  {label}: {int(sel.sum())} rows, max-abs {mabs:.2e} max-rel {mrel:.2e} lse err {lerr:.2e}", flush=True)
+    plog.line(f"{label}: {int(sel.sum())} rows, max-abs {mabs:.3e} max-rel {mrel:.3e} (|ref| >= 0.2), "
+              f"lse max-abs {lerr:.3e}")
     assert ok, f"{label}: output outside tolerance (max-abs {mabs:.3e})"
     assert lerr <= 1e-4, f"{label}: lse error {lerr:.3e}"
 
@@ -123,7 +126,7 @@ def _chunk(seed, B, T, NQ, H, d, Hq):
     (43, [5, 61], 18, 1, 1, 1, 1, 32, 4, 16, (0,)),          # c = 32; a prefix shorter than a page
 ])
 def test_prefill_chunk_matches_oracle(cfg, lengths, NQ, H, Hq, T, Tc, G, ns, nr, steps):
-    print(f"\ncase prefill chunk cfg={cfg} L={lengths} NQ={NQ} H={H} Hq={Hq} T={T} Tc={Tc} G={G}", flush=True)
+    plog.case(f"multi-row attention: prefill chunk cfg={cfg} L={lengths} NQ={NQ} H={H} Hq={Hq} T={T} Tc={Tc} G={G}")
     cache = build_cache(cfg, len(lengths), lengths, H, 128, T, Tc, G, ns, nr, Hq=Hq, books="random")
     dc = to_dev(cache, max_seq_len=int(max(lengths)) + NQ)
     ck, cv, q = _chunk(cfg, len(lengths), T, NQ, H, 128, Hq)
@@ -136,7 +139,7 @@ def test_prefill_chunk_matches_oracle(cfg, lengths, NQ, H, Hq, T, Tc, G, ns, nr,
     (45, [17, 700], 1, 16, 1, 1, 32),                        # 16 heads on one KV head, c = 32
 ])
 def test_gqa_decode_matches_oracle(cfg, lengths, H, Hq, T, Tc, G):
-    print(f"\ncase GQA decode cfg={cfg} L={lengths} H={H} Hq={Hq}", flush=True)
+    plog.case(f"multi-row attention: GQA decode cfg={cfg} L={lengths} H={H} Hq={Hq}")
     cache = build_cache(cfg, len(lengths), lengths, H, 128, T, Tc, G, 4, 64, Hq=Hq, books="random")
     dc = to_dev(cache)
     q = np.ascontiguousarray(cache.q[T - 1][:, None])                    # [B][1][Hq][d]
@@ -155,25 +158,27 @@ def test_rows_split_count_does_not_change_the_result():
 
 def test_prefill_chunk_at_32k_sampled():
     """512 new tokens over a 32768-token coded prefix (Ouro-shaped head, 16 heads, MHA), the
-    launch the bench times; the oracle checks three query positions of two heads."""
-    print("\ncase prefill chunk 512 over 32K", flush=True)
+    launch the bench times; the oracle checks eight query positions of four heads."""
+    plog.case("multi-row attention: prefill chunk 512 over 32K")
     NQ = 512
     cache = build_cache_light(47, 1, [32768], 16, 128, 4, 4, 32, 4, 64)
     dc = to_dev(cache, max_seq_len=32768 + NQ)
     ck, cv, q = _chunk(47, 1, 4, NQ, 16, 128, 16)
     got = gpu_rows(dc, cache, q, 1, ck, cv)
-    ref = oracle_rows(cache, q, 1, ck, cv, queries=(0, 255, 511), pairs=[(0, 3), (0, 12)])
+    ref = oracle_rows(cache, q, 1, ck, cv, queries=(0, 1, 15, 16, 255, 256, 500, 511),
+                      pairs=[(0, 0), (0, 3), (0, 12), (0, 15)])
     compare(got, ref, "t=1")
 
 
 def test_gqa_decode_at_32k_sampled():
-    """GQA decode at 32K: 8 sequences, 4 KV heads x 4 query heads; sampled pairs."""
-    print("\ncase GQA decode B=8 L=32K H=4 Hq=16", flush=True)
+    """GQA decode at 32K: 8 sequences, 4 KV heads x 4 query heads; every query head of
+    sequences 0, 3 and 7."""
+    plog.case("multi-row attention: GQA decode B=8 L=32K H=4 Hq=16")
     cache = build_cache_light(48, 8, [32768] * 8, 4, 128, 4, 4, 32, 4, 64, Hq=16)
     dc = to_dev(cache)
     q = np.ascontiguousarray(cache.q[2][:, None])
     got = gpu_rows(dc, cache, q, 2)
-    ref = oracle_rows(cache, q, 2, pairs=[(0, 0), (3, 7), (7, 15)])
+    ref = oracle_rows(cache, q, 2, pairs=[(b, h) for b in (0, 3, 7) for h in range(16)])
     compare(got, ref, "t=2")
 
 
@@ -198,7 +203,7 @@ def test_decode_attn_routes_wide_groups_to_the_rows_kernel():
     """lvq_decode_attn with 8 query heads per KV head (d = 128) runs on the multi-row kernel;
     the result is the oracle's and the workspace query covers it."""
     from gpu_helpers import gpu_attn
-    print("\ncase decode attn, 8 query heads per KV head", flush=True)
+    plog.case("multi-row attention: decode attn, 8 query heads per KV head")
     cache = build_cache(50, 2, [77, 640], 2, 128, 4, 2, 32, 4, 64, Hq=16, books="random")
     dc = to_dev(cache)
     out, lse = gpu_attn(dc, 3)
@@ -210,7 +215,7 @@ def test_decode_attn_routes_wide_groups_to_the_rows_kernel():
 
 def test_prefill_chunk_with_an_empty_prefix_and_single_queries():
     """prefix_len = 0 (the chunk attends only to itself) next to a one-token chunk."""
-    print("\ncase prefill chunk, empty prefix / one token", flush=True)
+    plog.case("multi-row attention: prefill chunk, empty prefix / one token")
     for cfg, lengths, NQ in ((51, [0, 45], 23), (52, [33], 1)):
         cache = build_cache(cfg, len(lengths), [max(L, 1) for L in lengths], 2, 128, 4, 4, 32, 4, 16, Hq=2,
                             books="random")

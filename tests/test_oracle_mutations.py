@@ -23,6 +23,7 @@ PINS = [
     pins.test_p10_rope_relative_invariance_and_closed_forms,
     pins.test_p12_single_token,
     pins.test_boundary_conventions,
+    pins.test_p14_needle_mass,
 ]
 
 
@@ -120,6 +121,15 @@ def _reconstruct_step_from_block_start(shp, b, h, t, L, q_end, *a):
 
 orc_reconstruct_orig = orc.reconstruct_kv
 
+
+def _mass_inclusive_end(scores, lse, lo, hi):
+    return float(np.exp(scores[lo:hi + 1] - lse).sum())
+
+
+def _mass_over_max(scores, lse, lo, hi):
+    # normalises by the largest score instead of the log-sum-exp
+    return float(np.exp(scores[lo:hi] - np.max(scores)).sum())
+
 MUTANTS = {
     "rope_sign": ("rope", _rope_sign_flipped),
     "rope_interleaved_pairs": ("rope", _rope_interleaved),
@@ -131,6 +141,8 @@ MUTANTS = {
     "merge_no_rescale": ("lse_merge", _merge_no_rescale),
     "recent_overrides_sink": ("token_classes", _classes_recent_wins),
     "wrong_step_slice": ("reconstruct_kv", _reconstruct_step_from_block_start),
+    "mass_inclusive_end": ("needle_mass", _mass_inclusive_end),
+    "mass_over_max": ("needle_mass", _mass_over_max),
 }
 
 

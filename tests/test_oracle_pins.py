@@ -410,3 +410,32 @@ def test_boundary_conventions():
     assert (cls == 0).sum() == 4 and (cls == 2).sum() == 16
     assert synth.prefill_q_end(10, 16) == 0
     assert synth.prefill_q_end(32768, 64) == 32704
+
+
+# ----------------------------------------------------------------------------
+# P14: attention mass of a span of positions (the needle check)
+# ----------------------------------------------------------------------------
+def test_p14_needle_mass():
+    """needle_mass(s, lse, lo, hi) is the softmax mass of positions [lo, hi): it equals
+    scipy's softmax summed over the span, the whole range has mass 1, disjoint spans add,
+    an empty span has mass 0, and a hand case: scores (0, ln 3) give the second position
+    3/4 of the mass."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(14)
+    s = rng.standard_normal(300) * 4.0
+    s[120:136] += 9.0                                   # a needle span that dominates
+    lse = float(logsumexp(s))
+    for lo, hi in ((120, 136), (0, 300), (0, 1), (299, 300), (7, 200)):
+        assert orc.needle_mass(s, lse, lo, hi) == pytest.approx(softmax(s)[lo:hi].sum(), rel=1e-12, abs=1e-15)
+    assert orc.needle_mass(s, lse, 0, 300) == pytest.approx(1.0, rel=1e-13)
+    assert orc.needle_mass(s, lse, 0, 50) + orc.needle_mass(s, lse, 50, 300) == pytest.approx(1.0, rel=1e-13)
+    assert orc.needle_mass(s, lse, 40, 40) == 0.0
+    hand = np.array([0.0, np.log(3.0)])
+    assert orc.needle_mass(hand, np.log(4.0), 1, 2) == pytest.approx(0.75, rel=1e-15)
+    assert orc.needle_mass(hand, np.log(4.0), 0, 1) == pytest.approx(0.25, rel=1e-15)
+    # with the oracle's own scores and lse of a planted span: the same as scipy on those scores
+    cache = build_cache(18, 1, [260], 1, 64, 4, 2, 16, 4, 16, books="random", index="random")
+    out, lse_o, sc = cache.oracle_attn(2, return_scores=True)
+    scores = sc[(0, 0)]
+    assert lse_o[0, 0] == pytest.approx(logsumexp(scores), rel=1e-14)
+    assert orc.needle_mass(scores, lse_o[0, 0], 30, 46) == pytest.approx(softmax(scores)[30:46].sum(), rel=1e-12)
