@@ -76,6 +76,21 @@ __device__ __forceinline__ float key_med3(float a, float b, float c) {
   return r;
 }
 
+// Exchange with lane ^ 16 (v_permlane16_swap) or lane ^ 32 (v_permlane32_swap), VALU
+// instructions with no LDS round trip.  Each lane gets its own value and its partner's
+// as (lo, hi), where lo is the value of the pair's lower lane on both lanes, so an
+// operation of (lo, hi) gives bit-identical results in the two lanes.
+__device__ __forceinline__ void pair16(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
 template <int EPL>
 using raw_t = typename std::conditional<EPL == 8, u16x8, u16x4>::type;
 
@@ -189,7 +204,6 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
   constexpr int EPL = (G == 32) ? 8 : 4; // elements per lane per MFMA operand
   constexpr int TC = G / C;
   constexpr int kPart = 4;               // MFMAs issued before their results are folded
-  constexpr bool kBiasAhead = true;      // read the next group's |C_k|^2 during the fold
   constexpr int kRing = 3;               // tiles in flight
   using R = raw_t<EPL>;
   __shared__ __attribute__((aligned(16))) float s_bias[WPG][kCodes];
@@ -200,24 +214,32 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
   const int nblk = a0.T / TC;
   const int tpi = a0.tokens_per_block;
   const int nparts = (N + tpi - 1) / tpi;
-  const int nrest_layer = nparts * H * nblk * (a0.kv_sel >= 0 ? 1 : 2);
+  // Items of one "combo" (token range, block of HB heads, loop block, K/V, layer) run on
+  // one XCD: its HB x NGB workgroups read every 128-byte row of their tokens and write
+  // every dense index row of them (HB heads x ng groups), so rows meet in that XCD's L2.
+  const int HB = a0.head_block;
+  const int nhb = H / HB;
+  const int ncombo_layer = nparts * nhb * nblk * (a0.kv_sel >= 0 ? 1 : 2);
   int n_layers = 1;
   if constexpr (MODE == 2) n_layers = layers.n;
-  const int nrest = nrest_layer * n_layers;
+  const int ncombo = ncombo_layer * n_layers;
+  const int per_combo = HB * NGB;
   const int q4 = lane >> 4, col = lane & 15;
   const int e0 = EPL * q4;
   const int tau0 = e0 / C, i0 = e0 % C;
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int xcd = item % kXcds;
-    const int r8 = item / kXcds;
-    const int gb = r8 % NGB;
-    int rest = (r8 / NGB) * kXcds + xcd;
-    if (rest >= nrest) continue;   // padding to whole XCD rounds (uniform per workgroup)
+    const int j = item / kXcds;
+    const int inner = j % per_combo;
+    int rest = (j / per_combo) * kXcds + xcd;   // the combo
+    if (rest >= ncombo) continue;   // padding to whole XCD rounds (uniform per workgroup)
+    const int gb = inner % NGB;
+    const int hh = inner / NGB;
     EncodeArgs a = a0;
     if constexpr (MODE == 2) {     // the item's layer: its pools and books
-      const ReencodeLayer& L = layers.layer[rest / nrest_layer];
-      rest %= nrest_layer;
+      const ReencodeLayer& L = layers.layer[rest / ncombo_layer];
+      rest %= ncombo_layer;
       a.src = L.bf16_pages;
       a.codebooks = L.codebooks;
       a.out = L.index_pages;
@@ -225,7 +247,7 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
       a.n_dst_pages = L.n_index_pages;
     }
     const int part = rest % nparts; rest /= nparts;
-    const int h = rest % H;         rest /= H;
+    const int h = (rest % nhb) * HB + hh; rest /= nhb;
     const int beta = rest % nblk;   rest /= nblk;
     const int kv = (a.kv_sel >= 0) ? a.kv_sel : rest;
     const int g = gb * WPG + wave;
@@ -301,66 +323,77 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
         const bf16x2 two = __builtin_bit_cast(bf16x2, (uint32_t)B[e] | ((uint32_t)B[e + 1] << 16));
         xx = __builtin_amdgcn_fdot2_f32_bf16(two, two, xx, false);
       }
-      xx += __shfl_xor(xx, 16);
-      xx += __shfl_xor(xx, 32);
+      {
+        float lo, hi;
+        pair16(xx, lo, hi);
+        xx = lo + hi;
+        pair32(xx, lo, hi);
+        xx = lo + hi;
+      }
 
       // The lane's 64 candidates (codes 16m + 4 q4 + r) become keys: D'_k with its six
       // low mantissa bits replaced by 63 - (4m + r).  A smaller key is a smaller D' at
-      // key precision, and every key of the lane is distinct.  Keys are folded three
-      // at a time into the smallest b1 and second smallest b2 of two alternating
-      // chains: t1 = min3, t2 = med3 of the triple, b2 = min3(max(b1, t1), b2, t2),
-      // b1 = min(b1, t1); the chains merge afterwards.
+      // key precision, and every key of the lane is distinct.  Two chains (rows 0-1 and
+      // rows 2-3 of each MFMA) fold their keys a pair (x, y) at a time: the smallest key
+      // b1 becomes min3(b1, x, y), and med3(b1, x, y) -- the second smallest of
+      // {b1, x, y} -- is a candidate for the second smallest overall, which is the
+      // minimum of these candidates (taken two at a time); 2.25 VALU per key.
       float c1[2] = {__builtin_inff(), __builtin_inff()};
       float c2[2] = {__builtin_inff(), __builtin_inff()};
-      float kq[3];
-      // |C_k|^2 of the next group of MFMAs is read from LDS while the current group folds
-      f32x4 bq[kPart];
+      float pend[2] = {__builtin_inff(), __builtin_inff()};
+      auto key = [](float v, int idx) {
+        return __uint_as_float((__float_as_uint(v) & ~63u) | (63u - (uint32_t)idx));
+      };
+      auto fold = [&](const f32x4& acc, int m) {   // m: compile-time MFMA number
 #pragma unroll
-      for (int mm = 0; mm < kPart; ++mm) bq[mm] = *(const f32x4*)(bias + 16 * mm);
-#pragma unroll
-      for (int part = 0; part < 16 / kPart; ++part) {
-        f32x4 acc[kPart];
-#pragma unroll
-        for (int mm = 0; mm < kPart; ++mm) {
-          const int m = kPart * part + mm;
-          if (!kBiasAhead && part > 0) bq[mm] = *(const f32x4*)(bias + 16 * m);
-          acc[mm] = mfma_bf16<EPL>(A[m], B, bq[mm]);
+        for (int ch = 0; ch < 2; ++ch) {
+          const float x = key(acc[2 * ch], 4 * m + 2 * ch);
+          const float y = key(acc[2 * ch + 1], 4 * m + 2 * ch + 1);
+          const float p = key_med3(c1[ch], x, y);
+          c1[ch] = key_min3(c1[ch], x, y);
+          if (m & 1) c2[ch] = key_min3(c2[ch], pend[ch], p);
+          else pend[ch] = p;
         }
-        if (kBiasAhead && part + 1 < 16 / kPart) {
+      };
+      // MFMA groups of kPart codes-blocks, software-pipelined: group p + 1 is issued
+      // before group p is folded.  Each group's accumulators start as |C_k|^2, read from
+      // LDS one group ahead.
+      constexpr int NP = 16 / kPart;
+      f32x4 acc[2][kPart];
 #pragma unroll
-          for (int mm = 0; mm < kPart; ++mm) bq[mm] = *(const f32x4*)(bias + 16 * (kPart * (part + 1) + mm));
+      for (int mm = 0; mm < kPart; ++mm) acc[0][mm] = *(const f32x4*)(bias + 16 * mm);
+#pragma unroll
+      for (int mm = 0; mm < kPart; ++mm) acc[0][mm] = mfma_bf16<EPL>(A[mm], B, acc[0][mm]);
+#pragma unroll
+      for (int part = 0; part < NP; ++part) {
+        const int cur = part & 1;
+        if (part + 1 < NP) {
+#pragma unroll
+          for (int mm = 0; mm < kPart; ++mm)
+            acc[cur ^ 1][mm] = *(const f32x4*)(bias + 16 * (kPart * (part + 1) + mm));
+#pragma unroll
+          for (int mm = 0; mm < kPart; ++mm)
+            acc[cur ^ 1][mm] = mfma_bf16<EPL>(A[kPart * (part + 1) + mm], B, acc[cur ^ 1][mm]);
         }
 #pragma unroll
-        for (int mm = 0; mm < kPart; ++mm) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int idx = 4 * (kPart * part + mm) + r;   // 0..63, compile time
-            kq[idx % 3] = __uint_as_float((__float_as_uint(acc[mm][r]) & ~63u) | (63u - (uint32_t)idx));
-            if (idx % 3 == 2) {
-              const int ch = (idx / 3) & 1;
-              const float t1 = key_min3(kq[0], kq[1], kq[2]);
-              const float t2 = key_med3(kq[0], kq[1], kq[2]);
-              c2[ch] = key_min3(key_max(c1[ch], t1), c2[ch], t2);
-              c1[ch] = key_min(c1[ch], t1);
-            } else if (idx == 63) {
-              c2[0] = key_med3(c1[0], c2[0], kq[0]);
-              c1[0] = key_min(c1[0], kq[0]);
-            }
-          }
-        }
+        for (int mm = 0; mm < kPart; ++mm) fold(acc[cur][mm], kPart * part + mm);
       }
       float b1 = key_min(c1[0], c1[1]);
-      float b2 = key_min(key_max(c1[0], c1[1]), key_min(c2[0], c2[1]));
-      // Merge the four lanes of the vector: smallest and second smallest key overall.
-      // The lane whose own smallest key survives holds the winning code; equal keys in
-      // two lanes make b2 == b1, which sends the vector to the float64 pass.
+      float b2 = key_min3(key_max(c1[0], c1[1]), c2[0], c2[1]);
+      // Merge the four lanes of the vector (lane ^ 16, then lane ^ 32): smallest and second
+      // smallest key overall, the same in all four lanes.  The lane whose own smallest key
+      // survives holds the winning code.
       const float own = b1;
-  #pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-        const float o1 = __shfl_xor(b1, off);
-        const float o2 = __shfl_xor(b2, off);
-        b2 = key_min(key_max(b1, o1), key_min(b2, o2));
-        b1 = key_min(b1, o1);
+      {
+        float lo1, hi1, lo2, hi2;
+        pair16(b1, lo1, hi1);
+        pair16(b2, lo2, hi2);
+        b1 = key_min(lo1, hi1);
+        b2 = key_min3(key_max(lo1, hi1), lo2, hi2);
+        pair32(b1, lo1, hi1);
+        pair32(b2, lo2, hi2);
+        b1 = key_min(lo1, hi1);
+        b2 = key_min3(key_max(lo1, hi1), lo2, hi2);
       }
       const bool owner = own == b1;
       // Float32 error bound for two expanded distances (33 or 17 rounded terms, each
@@ -444,12 +477,16 @@ hipError_t launch_mode(const EncodeArgs& args, const LayersArg<MODE>& layers, in
   long tpi = (args.N + parts - 1) / parts;
   tpi = (tpi + 15) / 16 * 16;
   parts = (args.N + tpi - 1) / tpi;
-  const long nrest = parts * sets * n_layers;
-  const long items = (nrest + kXcds - 1) / kXcds * kXcds * NGB;
+  // heads whose dense index rows share 128-byte lines go to one XCD together
+  int hb = args.H < 8 ? args.H : 8;
+  while (args.H % hb) --hb;
+  const long ncombo = parts * (sets / hb) * n_layers;
+  const long items = (ncombo + kXcds - 1) / kXcds * kXcds * hb * NGB;
   if (items > INT32_MAX) return hipErrorInvalidValue;
   const long grid = items < slots ? items : slots;
   EncodeArgs a = args;
   a.tokens_per_block = (int)tpi;
+  a.head_block = hb;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(WPG * 64), 0, s, a, (int)items, layers);
   return hipGetLastError();
 }

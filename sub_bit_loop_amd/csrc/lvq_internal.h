@@ -44,6 +44,7 @@ struct EncodeArgs {
   int T, Tc, G, N, H, d;
   int n_src_pages, n_dst_pages;
   int tokens_per_block;       // multiple of 16
+  int head_block;             // heads whose items share an XCD (a divisor of H, at most 8)
 };
 // The pools and books of one layer in a multi-layer re-encode (pages -> pages).
 struct ReencodeLayer {
