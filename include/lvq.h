@@ -285,6 +285,28 @@ int lvq_decode_attn(const uint16_t* q, const int32_t* page_table, const uint8_t*
                     float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * lvq_decode_attn_noalloc -- lvq_decode_attn for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, kernels and results as lvq_decode_attn, without the
+ * workspace: the partial records live in a fixed device array of the library,
+ * LVQ_NOALLOC_SCRATCH_BYTES per device, that each device keeps from its first use
+ * until the process ends.  The call allocates nothing and calls no allocating routine.
+ * A shape whose lvq_decode_attn_workspace_bytes() exceeds that size returns
+ * LVQ_ENOSPC before anything is enqueued.  Every call on one device shares that
+ * device's array, so calls whose work overlaps on one device (concurrent streams, or
+ * host threads on one device without ordering) race on it and give undefined
+ * results; calls ordered on one stream are safe.  The array keeps the last call's
+ * contents, which no call reads before writing them.
+ */
+#define LVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lvq_decode_attn_noalloc(const uint16_t* q, const int32_t* page_table,
+                            const uint8_t* index_pages, const uint16_t* bf16_pages,
+                            const int32_t* bf16_table, const uint16_t* codebooks, int t,
+                            const int32_t* pos, const int32_t* seq_len, const int32_t* q_end,
+                            const float* rope_tab, const lvq_attn_shape* shp, float* out,
+                            float* lse, void* stream);
+
+/*
  * lvq_decode_scores -- test probe: same inputs and device code as
  * lvq_decode_attn (same passages), but also writes the scaled scores q'.k' * scale
  * (natural units) of every cached token to scores, from which the attention mass

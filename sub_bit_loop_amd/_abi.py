@@ -74,6 +74,8 @@ _SIGS = {
     "lvq_decode_attn_workspace_bytes": (_sz, [ctypes.POINTER(AttnShape)]),
     "lvq_decode_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                ctypes.POINTER(AttnShape), _vp, _vp, _vp, _sz, _vp]),
+    "lvq_decode_attn_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
+                                       ctypes.POINTER(AttnShape), _vp, _vp, _vp]),
     "lvq_decode_scores": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                  ctypes.POINTER(AttnShape), _vp, _vp, _vp, _vp, _sz, _vp]),
     "lvq_rows_attn_workspace_bytes": (_sz, [ctypes.POINTER(RowsShape)]),
@@ -315,7 +317,7 @@ def lvq_decode_attn_workspace_bytes(shp: AttnShape) -> int:
 
 
 def _attn_call(fn, q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos, seq_len,
-               q_end, rope_tab, shp: AttnShape, out, lse, ws, scores=None):
+               q_end, rope_tab, shp: AttnShape, out, lse, ws, scores=None, noalloc=False):
     _dev(q, "q", BF16, 3)
     _dev(page_table, "page_table", I32, 2)
     _dev(index_pages, "index_pages", U8, 6)
@@ -342,9 +344,8 @@ def _attn_call(fn, q, page_table, index_pages, bf16_pages, bf16_table, codebooks
         out = torch.empty((shp.B, shp.Hq, shp.d), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((shp.B, shp.Hq), dtype=torch.float32, device=dev)
-    need = lvq_decode_attn_workspace_bytes(shp)
-    if ws is None:
-        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    if ws is None and not noalloc:
+        ws = torch.empty(max(lvq_decode_attn_workspace_bytes(shp), 4), dtype=torch.uint8, device=dev)
     _dev(out, "out", F32)
     _dev(lse, "lse", F32)
     _expect(out, "out", (shp.B, shp.Hq, shp.d))
@@ -356,7 +357,9 @@ def _attn_call(fn, q, page_table, index_pages, bf16_pages, bf16_table, codebooks
         _dev(scores, "scores", F32)
         _expect(scores, "scores", (shp.B, shp.Hq, shp.max_seq_len))
         args.append(_ptr(scores))
-    args += [_ptr(ws), ws.numel() * ws.element_size(), _stream(q)]
+    if not noalloc:
+        args += [_ptr(ws), ws.numel() * ws.element_size()]
+    args.append(_stream(q))
     _check(fn(*args))
     return out, lse
 
@@ -366,6 +369,16 @@ def lvq_decode_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebook
     """Decode attention at loop step t; returns (out [B][Hq][d] f32, lse [B][Hq] f32)."""
     return _attn_call(lib().lvq_decode_attn, q, page_table, index_pages, bf16_pages, bf16_table,
                       codebooks, t, pos, seq_len, q_end, rope_tab, shp, out, lse, ws)
+
+
+def lvq_decode_attn_noalloc(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos,
+                            seq_len, q_end, rope_tab, shp: AttnShape, out, lse):
+    """lvq_decode_attn without a workspace (the library's fixed scratch array): the caller
+    passes the outputs, so the call allocates nothing.  Returns (out, lse)."""
+    if out is None or lse is None:
+        raise ValueError("lvq_decode_attn_noalloc needs the caller's out and lse tensors")
+    return _attn_call(lib().lvq_decode_attn_noalloc, q, page_table, index_pages, bf16_pages, bf16_table,
+                      codebooks, t, pos, seq_len, q_end, rope_tab, shp, out, lse, None, noalloc=True)
 
 
 def lvq_decode_scores(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos,

@@ -29,6 +29,22 @@ int ok() {
   return LVQ_OK;
 }
 
+}  // namespace
+
+namespace lvq {
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+}  // namespace lvq
+
+namespace {
+
 int device_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(LVQ_EDEVICE, "%s: %s", what, hipGetErrorString(e));

@@ -29,6 +29,12 @@ inline hipError_t once_per_device(std::atomic<uint64_t>& done, F&& set) {
 constexpr int kPage = 8;
 constexpr int kCodes = 256;
 
+// Sets the calling thread's error text (printf format) and returns code.
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Size of the fixed device scratch array behind lvq_decode_attn_noalloc.
+constexpr size_t kNoAllocScratchBytes = LVQ_NOALLOC_SCRATCH_BYTES;
+
 // ---------------------------------------------------------------- encoder
 enum EncodeSrc { kSrcDense = 0, kSrcPages = 1 };
 enum EncodeDst { kDstDense = 0, kDstPages = 1 };

@@ -225,3 +225,14 @@ def test_binding_shape_helpers():
     _abi._expect(torch.zeros(2, 3), "x", None)
     with pytest.raises(ValueError, match="needs"):
         _abi._expect(torch.zeros(2, 3), "x", (3, 2))
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(L):
+    """lvq_decode_attn_noalloc refuses, before touching a device, a shape whose partial
+    records exceed the fixed scratch array (LVQ_ENOSPC), and reports invalid shapes as the
+    workspace entry point does."""
+    big = shape(B=4096, Hq=64, H=64)
+    assert L.lvq_decode_attn_workspace_bytes(ctypes.byref(big)) > 32 << 20
+    rc = L.lvq_decode_attn_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
+                                   ctypes.byref(big), FAKE, NUL, NUL)
+    assert rc == 3 and b"scratch" in L.lvq_last_error()
