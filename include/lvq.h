@@ -172,7 +172,8 @@ int lvq_reencode_pages_layers(const lvq_reencode_layer* layers, int n_layers,
  * Fisher information needs model gradients, so the weights are an input).  Every book (loop block,
  * head, group) is built at once.
  *   samples:   bf16 [T][S][H][d], S sample tokens (pre-RoPE keys or values), the
- *              encoder's input layout.  1 <= S <= 8192.
+ *              encoder's input layout.  1 <= S <= 32768 (the summary's calibration set
+ *              is 16 sequences of 2,048 tokens: 32,768 sample tokens).
  *   draws:     float64 [nblk][H][ng][256], uniform numbers in [0, 1) that drive the
  *              k-means++ seeding of each book.  Draw k picks the first sample s whose
  *              running sum of terms (sample order, float64) exceeds u_k times the
@@ -190,7 +191,7 @@ int lvq_reencode_pages_layers(const lvq_reencode_layer* layers, int n_layers,
  *   codebooks: out, bf16 [nblk][2][H][ng][Tc][256][c]; only half kv_sel is written,
  *              the final centers rounded to bf16 through float32.
  *   ws:        device workspace of lvq_build_codebooks_workspace_bytes() bytes.
- * Same shapes as lvq_encode (status 2 outside them, or for S > 8192).  The result
+ * Same shapes as lvq_encode (status 2 outside them, or for S > 32768).  The result
  * is bit-reproducible: every float64 step has a fixed order.
  */
 size_t lvq_build_codebooks_workspace_bytes(int T, int Tc, int G, int S, int H, int d);

@@ -458,7 +458,11 @@ size_t lvq_build_codebooks_workspace_bytes(int T, int Tc, int G, int S, int H, i
   const size_t nblk = (size_t)(T / Tc), ng = (size_t)(d / (G / Tc));
   const size_t centers = nblk * H * ng * lvq::kCodes * (size_t)G * sizeof(double);
   const size_t assign = nblk * (size_t)S * H * ng;
-  return (centers + 255) / 256 * 256 + assign;
+  // centers (256-byte aligned), assignments, and above the LDS seeding limit one float64
+  // D^2 per (book, sample) after the assignments (256-byte aligned)
+  const size_t head = (centers + 255) / 256 * 256;
+  if (S <= lvq::kMaxKmeansSamplesLds) return head + assign;
+  return head + (assign + 255) / 256 * 256 + nblk * H * ng * (size_t)((S + 31) / 32 * 32) * sizeof(double);
 }
 
 int lvq_build_codebooks(const uint16_t* samples, const double* draws, const double* weights,
@@ -487,6 +491,8 @@ int lvq_build_codebooks(const uint16_t* samples, const double* draws, const doub
   const size_t centers = (size_t)a.n_books * lvq::kCodes * G * sizeof(double);
   a.centers = (double*)ws;
   a.assign = (uint8_t*)ws + (centers + 255) / 256 * 256;
+  const size_t assign = (size_t)(T / Tc) * S * H * (d / (G / Tc));
+  a.d2 = S > lvq::kMaxKmeansSamplesLds ? (double*)(a.assign + (assign + 255) / 256 * 256) : nullptr;
   return device_status(lvq::launch_build_codebooks(a, (hipStream_t)stream), "lvq_build_codebooks launch");
 }
 

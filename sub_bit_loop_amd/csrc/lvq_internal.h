@@ -69,7 +69,8 @@ bool encode_supported(int G, int c, int d);
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s, const ReencodeLayers* layers = nullptr);
 
 // ---------------------------------------------------------------- codebook builder
-constexpr int kMaxKmeansSamples = 8192;   // samples per book (float64 D^2 and running sums in LDS)
+constexpr int kMaxKmeansSamples = 32768;     // samples per book (the update's member lists fit LDS)
+constexpr int kMaxKmeansSamplesLds = 8192;   // up to here the seeding keeps D^2 and running sums in LDS
 struct KmeansArgs {
   const uint16_t* samples;    // bf16 [T][S][H][d]
   const double* draws;        // [n_books][256] uniform in [0, 1), book = (beta * H + h) * ng + g
@@ -77,6 +78,7 @@ struct KmeansArgs {
   uint16_t* codebooks;        // bf16 [nblk][2][H][ng][Tc][256][c]; half kv_sel is written
   double* centers;            // workspace [n_books][256][G]
   uint8_t* assign;            // workspace [nblk][S][H][ng]
+  double* d2;                 // workspace [n_books][S rounded up to 32] (S > kMaxKmeansSamplesLds), else null
   int kv_sel, T, Tc, G, S, H, d, n_iter, n_books;
 };
 hipError_t launch_build_codebooks(const KmeansArgs& a, hipStream_t s);

@@ -95,7 +95,7 @@ __device__ __forceinline__ int draw_index(double u, int S) {
 constexpr int kSeedThreads = 512;
 constexpr int kSeedWaves = kSeedThreads / 64;
 constexpr int kSeedRegPer = 8;     // samples per thread kept in registers (S <= 4096)
-constexpr int kSeedMaxPer = kMaxKmeansSamples / kSeedThreads;
+constexpr int kSeedMaxPer = kMaxKmeansSamplesLds / kSeedThreads;
 
 // C bf16 values at p (8-byte aligned, 16-byte when 8 divides C) -> C/2 packed words
 template <int C>
@@ -315,6 +315,161 @@ __global__ __launch_bounds__(kSeedThreads) void seed_kernel(KmeansArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ seeding, large S
+// Above kMaxKmeansSamplesLds samples a book's D^2 live in the workspace (one float64 per
+// sample) instead of registers and LDS.  Each draw streams the terms w_s D^2_s through
+// a two-chunk LDS ring: waves 1..7 load and form chunk i + 1 while lane 0 of wave 0
+// adds chunk i in sample order (the same chain of float64 adds as the kernel above,
+// only batch-end sums kept), then the workgroup finds the crossing batch, lane 0 redoes
+// its sums from the workspace, and every thread refreshes the D^2 of its samples
+// against the new center, re-reading their joint vectors.
+constexpr int kWalkChunk = 2048;   // terms per LDS chunk (a multiple of 2 kChain)
+
+constexpr size_t seed_ws_lds_bytes(int S) {
+  return ((size_t)2 * kWalkChunk + (size_t)((S + 2 * kChain - 1) / (2 * kChain) * (2 * kChain)) / kChain) *
+         sizeof(double);
+}
+
+template <int G, int C>
+__global__ __launch_bounds__(kSeedThreads) void seed_kernel_ws(KmeansArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int S = a.S;
+  const int Sp = (S + 2 * kChain - 1) / (2 * kChain) * (2 * kChain);
+  double* ring = (double*)smem;                 // [2][kWalkChunk] terms of the walk
+  double* ckpt = ring + 2 * kWalkChunk;         // [Sp / kChain] running sum at each batch end
+  __shared__ double cen[G];
+  __shared__ double s_total;
+  __shared__ int s_first[kSeedWaves], s_pick;
+  const int book = book_of_block(blockIdx.x, a.n_books);
+  const Book bk = book_at<G, C>(a, book);
+  const double* u = a.draws + (size_t)book * kCodes;
+  double* centers = a.centers + (size_t)book * kCodes * G;
+  double* d2 = a.d2 + (size_t)book * Sp;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunk = (Sp + kWalkChunk - 1) / kWalkChunk;
+
+  auto term_of = [&](int s) -> double {
+    if (s >= S) return 0.0;
+    const double dd = d2[s];
+    return a.weights ? __dmul_rn(a.weights[bk.wbase + (size_t)s * bk.wstride], dd) : dd;
+  };
+  // chunk i into ring slot i & 1, by threads first .. kSeedThreads - 1
+  auto load_chunk = [&](int i, int first) {
+    double* dst = ring + (i & 1) * kWalkChunk;
+    const int c0 = i * kWalkChunk, n = min(kWalkChunk, Sp - c0);
+    for (int j = tid - first; j < n; j += kSeedThreads - first) dst[j] = term_of(c0 + j);
+  };
+
+  for (int s = tid; s < Sp; s += kSeedThreads) d2[s] = 1.0;   // draw 0 takes every distance as 1
+  __syncthreads();
+  for (int k = 0; k < kCodes; ++k) {
+    load_chunk(0, 0);
+    __syncthreads();
+    double acc = 0.0;
+    for (int i = 0; i < nchunk; ++i) {
+      if (wave == 0) {
+        if (lane == 0) {
+          // running sum in sample order, two register batches alternating as above
+          const double* run = ring + (i & 1) * kWalkChunk;
+          const int n = min(kWalkChunk, Sp - i * kWalkChunk);
+          double ba[kChain], bb[kChain];
+#pragma unroll
+          for (int j = 0; j < kChain; ++j) ba[j] = run[j];
+          for (int s0 = 0; s0 < n; s0 += 2 * kChain) {
+            const int nb = s0 + kChain;
+#pragma unroll
+            for (int j = 0; j < kChain; ++j) bb[j] = run[nb + j];
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < kChain; ++j) acc = __dadd_rn(acc, ba[j]);
+            ckpt[(i * kWalkChunk + s0) / kChain] = acc;
+            const int na = s0 + 2 * kChain < n ? s0 + 2 * kChain : 0;
+#pragma unroll
+            for (int j = 0; j < kChain; ++j) ba[j] = run[na + j];
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < kChain; ++j) acc = __dadd_rn(acc, bb[j]);
+            ckpt[(i * kWalkChunk + nb) / kChain] = acc;
+          }
+        }
+      } else if (i + 1 < nchunk) {
+        load_chunk(i + 1, 64);
+      }
+      __syncthreads();
+    }
+    if (tid == 0) s_total = acc;
+    __syncthreads();
+    const double total = s_total;
+    int pick;
+    if (total > 0.0) {
+      const double target = __dmul_rn(u[k], total);
+      int fb = INT32_MAX;
+      for (int b = tid; b < Sp / kChain; b += kSeedThreads)
+        if (ckpt[b] > target) {
+          fb = b;
+          break;
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) fb = min(fb, __shfl_xor(fb, off));
+      if (lane == 0) s_first[wave] = fb;
+      __syncthreads();
+      if (tid == 0) {
+        int f = INT32_MAX;
+#pragma unroll
+        for (int v = 0; v < kSeedWaves; ++v) f = min(f, s_first[v]);
+        int p;
+        if (f != INT32_MAX) {
+          // redo that batch's sums from the previous batch's last one: same values as the chain
+          double acc2 = f > 0 ? ckpt[f - 1] : 0.0;
+          p = f * kChain + kChain - 1;
+          for (int j = 0; j < kChain; ++j) {
+            acc2 = __dadd_rn(acc2, term_of(f * kChain + j));
+            if (acc2 > target) {
+              p = f * kChain + j;
+              break;
+            }
+          }
+        } else {
+          // rounding left no crossing: the last sample with a positive term (one exists,
+          // since the total is positive)
+          p = 0;
+          for (int s = S - 1; s >= 0; --s)
+            if (term_of(s) > 0.0) {
+              p = s;
+              break;
+            }
+        }
+        s_pick = p < S ? p : S - 1;
+      }
+      __syncthreads();
+      pick = s_pick;
+    } else {
+      pick = draw_index(u[k], S);
+    }
+    if (tid < G) {
+      const int tau = tid / C, i = tid % C;
+      const double v = bf2d(bk.base[((size_t)tau * S + pick) * a.H * a.d + i]);
+      cen[tid] = v;
+      centers[(size_t)k * G + tid] = v;
+    }
+    __syncthreads();
+    if (k + 1 == kCodes) break;
+    // D^2 against the new center, squares added in element order
+    for (int s = tid; s < S; s += kSeedThreads) {
+      uint32_t xw[G / 2];
+      load_packed<G, C>(a, bk, s, xw);
+      double dn = 0.0;
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        const double df = __dsub_rn(packed_elem(xw, e), cen[e]);
+        dn = __dadd_rn(dn, __dmul_rn(df, df));
+      }
+      if (k == 0 || dn < d2[s]) d2[s] = dn;
+    }
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ bf16 rounding
 // centers [book][256][G] (float64) -> codebooks [nblk][2][H][ng][Tc][256][c], half kv_sel
 __global__ void round_kernel(KmeansArgs a, int G, int C) {
@@ -449,13 +604,16 @@ __global__ __launch_bounds__(kKmThreads) void update_kernel(KmeansArgs a) {
 template <int G, int C>
 hipError_t build_t(const KmeansArgs& a, hipStream_t s) {
   const int Sp = (a.S + 2 * kChain - 1) / (2 * kChain) * (2 * kChain);
-  const size_t seed_lds = (size_t)(Sp + Sp / kChain) * sizeof(double);
+  const size_t seed_lds = a.S <= kMaxKmeansSamplesLds ? (size_t)(Sp + Sp / kChain) * sizeof(double) : 0;
   const size_t upd_lds = update_lds_bytes(G, a.S);
   static std::atomic<uint64_t> attr_set{0};
   hipError_t ea = once_per_device(attr_set, [&] {
     hipError_t e = hipFuncSetAttribute((const void*)seed_kernel<G, C, kSeedMaxPer, false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)((kMaxKmeansSamples + kMaxKmeansSamples / kChain) * sizeof(double)));
+                                       (int)((kMaxKmeansSamplesLds + kMaxKmeansSamplesLds / kChain) * sizeof(double)));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)seed_kernel_ws<G, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)seed_ws_lds_bytes(kMaxKmeansSamples));
     if (e != hipSuccess) return e;
     return hipFuncSetAttribute((const void*)update_kernel<G, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)update_lds_bytes(G, kMaxKmeansSamples));
@@ -463,9 +621,13 @@ hipError_t build_t(const KmeansArgs& a, hipStream_t s) {
   if (ea != hipSuccess) return ea;
   if (a.S <= kSeedRegPer * kSeedThreads)
     hipLaunchKernelGGL((seed_kernel<G, C, kSeedRegPer, true>), dim3(a.n_books), dim3(kSeedThreads), seed_lds, s, a);
-  else
+  else if (a.S <= kMaxKmeansSamplesLds)
     hipLaunchKernelGGL((seed_kernel<G, C, kSeedMaxPer, false>), dim3(a.n_books), dim3(kSeedThreads), seed_lds, s,
                        a);
+  else if (a.d2)
+    hipLaunchKernelGGL((seed_kernel_ws<G, C>), dim3(a.n_books), dim3(kSeedThreads), seed_ws_lds_bytes(a.S), s, a);
+  else
+    return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rgrid = (int)((a.n_books * (size_t)kCodes * G + 255) / 256);

@@ -150,7 +150,11 @@ def test_builder_validation(L):
     assert L.lvq_build_codebooks(FAKE, NUL, NUL, 0, 4, 2, 16, 100, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 1
     assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 2, 4, 2, 16, 100, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 1
     assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 0, 4, 2, 16, 0, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 1
-    assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 0, 4, 2, 16, 8193, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 2
+    assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 0, 4, 2, 16, 32769, 1, 64, 1, FAKE, ws, 1 << 30, NUL) == 2
+    # above the LDS seeding limit the workspace also holds one float64 D^2 per (book, sample)
+    small = L.lvq_build_codebooks_workspace_bytes(4, 2, 16, 8192, 1, 64)
+    big = L.lvq_build_codebooks_workspace_bytes(4, 2, 16, 8200, 1, 64)
+    assert big - small >= 2 * 8 * 8224 * 8
     assert L.lvq_build_codebooks(FAKE, FAKE, NUL, 0, 4, 2, 16, 100, 1, 64, 1001, FAKE, ws, 1 << 30, NUL) == 1
     need = L.lvq_build_codebooks_workspace_bytes(4, 2, 16, 100, 1, 64)
     # centers (2 blocks x 8 groups x 256 x 16 float64, 256-aligned) + assignments

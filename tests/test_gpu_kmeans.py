@@ -28,6 +28,10 @@ def _gpu_build(bits, draws, kv_sel, T, Tc, G, n_iter, codebooks=None, weights=No
     return out.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def books_desc(nblk, ng):
+    return f"(block, head, group) in [0, {nblk}) x [0, 16) x [0, {ng})"
+
+
 def _compare(gpu_half, ref, books):
     for (beta, h, g) in books:
         got, want = gpu_half[beta, h, g], ref[beta, h, g]
@@ -97,8 +101,8 @@ def test_weighted_builder_matches_oracle(T, Tc, G, S, H, d, n_iter):
     _compare(out[:, 1], ref, [(b, h, g) for b in range(nblk) for h in range(H) for g in range(ng)])
 
 
-def test_builder_at_the_sample_limit():
-    """S = 8192 (the largest supported: the seeding keeps 2 x 8192 float64 in LDS)."""
+def test_builder_at_the_lds_seeding_limit():
+    """S = 8192, the largest count whose seeding keeps D^2 and running sums in LDS."""
     T, Tc, G, S, H, d = 4, 4, 32, 8192, 1, 64
     print("\ncase build S=8192", flush=True)
     bits, rng = _samples(66, T, S, H, d)
@@ -106,6 +110,37 @@ def test_builder_at_the_sample_limit():
     out = _gpu_build(bits, draws, 0, T, Tc, G, 2)
     books = [(0, 0, 0), (0, 0, 5)]
     _compare(out[:, 0], orc.build_codebooks(bits, draws, Tc, G, 2, books=books), books)
+
+
+@pytest.mark.parametrize("Tc,G,S,weighted", [(4, 32, 32768, False), (2, 16, 8200, True)])
+def test_builder_at_calibration_scale(Tc, G, S, weighted):
+    """S = 32768 sample tokens per book (16 calibration sequences of 2048 tokens), above
+    the LDS seeding limit (D^2 in the workspace), Ouro-shaped layer (16 heads, d = 128),
+    10 Lloyd iterations; sampled books bit-exact against the oracle.  A weighted case
+    just above the limit covers the weighted terms of that path."""
+    import time
+    T, H, d = 4, 16, 128
+    nblk, ng = T // Tc, d // (G // Tc)
+    print(f"\ncase build calibration scale Tc={Tc} G={G} S={S} weighted={weighted}", flush=True)
+    bits, rng = _samples(67, T, S, H, d)
+    draws = rng.random((nblk, H, ng, 256))
+    w = None
+    if weighted:
+        w = 10.0 ** rng.uniform(-1, 1, (nblk, S, H, ng))
+        w[rng.random(w.shape) < 0.25] = 0.0
+    _gpu_build(bits, draws, 0, T, Tc, G, 1, weights=w)    # warm-up
+    t0 = time.perf_counter()
+    out = _gpu_build(bits, draws, 0, T, Tc, G, 10, weights=w)
+    dt = time.perf_counter() - t0
+    import parity_log as plog
+    plog.case(f"codebook builder at calibration scale: Tc={Tc} G={G} S={S} weighted={weighted}, "
+              f"{nblk * H * ng} books, 10 Lloyd iterations")
+    plog.line(f"build time {dt * 1e3:.1f} ms (host-timed, one call); sampled books {books_desc(nblk, ng)} "
+              f"compared bit for bit below")
+    books = [(0, 0, 0), (nblk - 1, 9, ng - 1)]
+    ref = orc.build_codebooks(bits, draws, Tc, G, 10, books=books, weights=w)
+    _compare(out[:, 0], ref, books)
+    plog.line(f"books {books}: bit-exact against the oracle")
 
 
 def test_weighted_builder_unit_weights_is_unweighted():
@@ -130,6 +165,6 @@ def test_builder_rejects_bad_arguments():
     with pytest.raises(ValueError):
         lvq.lvq_build_codebooks(x, u, 0, 4, 2, 16, 1,
                                 weights=torch.ones((2, 15, 1, 8), dtype=torch.float64, device=dev))
-    big = torch.zeros((4, 8193, 1, 64), dtype=torch.bfloat16, device=dev)
+    big = torch.zeros((4, 32769, 1, 64), dtype=torch.bfloat16, device=dev)
     with pytest.raises(lvq.LvqError):
-        lvq.lvq_build_codebooks(big, u, 0, 4, 2, 16, 1)          # S above 8192
+        lvq.lvq_build_codebooks(big, u, 0, 4, 2, 16, 1)          # S above 32768
