@@ -91,79 +91,72 @@ __device__ __forceinline__ void pair32(float v, float& lo, float& hi) {
   hi = __uint_as_float(r[1]);
 }
 
-template <int EPL>
-using raw_t = typename std::conditional<EPL == 8, u16x8, u16x4>::type;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int EPL>
-__device__ __forceinline__ f32x4 mfma_bf16(raw_t<EPL> a, raw_t<EPL> b, f32x4 c) {
-  if constexpr (EPL == 8) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+// Loads the lane's 8 joint-vector elements e = e0 .. e0 + 7 (a multiple of 8) of one
+// vector whose step-tau channel slices start at row(tau) (element tau * C + i is
+// row(tau)[i]): one 16-byte load when 8 divides C, two 8-byte loads when C = 4.
+template <int C, typename RowFn>
+__device__ __forceinline__ u16x8 load8(RowFn row, int e0) {
+  if constexpr (C % 8 == 0) {
+    return *(const u16x8*)(row(e0 / C) + e0 % C);
   } else {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+    const u16x4 lo = *(const u16x4*)(row(e0 / C));
+    const u16x4 hi = *(const u16x4*)(row(e0 / C + 1));
+    u16x8 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { v[q] = lo[q]; v[q + 4] = hi[q]; }
+    return v;
   }
 }
 
-// Row of channels of (loop step t, token n, head h) in the source, or null if the token is absent.
-__device__ __forceinline__ const uint16_t* src_row(const EncodeArgs& a, int t, int n, int h, int kv) {
-  if (a.src_mode == kSrcDense) {
-    return a.src + ((size_t)((size_t)t * a.N + n) * a.H + h) * a.d;
-  }
-  const int P = a.src_pages[n >> 3];
-  if (P < 0 || P >= a.n_src_pages) return nullptr;
-  return a.src + (((((size_t)P * a.T + t) * a.H + h) * 2 + kv) * kPage + (n & 7)) * a.d;
-}
-
-__device__ __forceinline__ uint8_t* dst_byte(const EncodeArgs& a, int beta, int n, int h, int g,
-                                             int kv, int ng) {
-  const int nblk = a.T / a.Tc;
-  if (a.dst_mode == kDstDense) {
-    return a.out + ((size_t)((size_t)beta * a.N + n) * a.H + h) * ng + g;
-  }
-  const int P = a.dst_pages[n >> 3];
-  if (P < 0 || P >= a.n_dst_pages) return nullptr;
-  return a.out + (((((size_t)P * nblk + beta) * a.H + h) * 2 + kv) * kPage + (n & 7)) * ng + g;
+__device__ __forceinline__ f32x16 mfma32(const u16x8& a, const u16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
 }
 
 // Float64 direct-difference nearest codeword of vector column cv of the current tile,
-// computed from registers: the wave holds the codebook as MFMA operand (A[m] = -2 C,
-// exact) and the tile as operand B (lane (q4, col) holds elements e0..e0+EPL-1 of
-// vector col).  Lane (q4, col) sums its EPL elements for codes 16m + col, the four
-// lanes of a column add their parts (the same sum in every lane), and the 16 columns
-// compare.  Ties resolve to the lowest code.
-template <int EPL, typename R>
-__device__ __forceinline__ int exact_in_registers(const R (&A)[16], const R& B, int cv, int lane) {
-  const int q4 = lane >> 4, col = lane & 15;
-  const int src = (q4 << 4) | cv;
-  double x[EPL];
+// computed from registers.  The wave holds the codebook as MFMA operand A: lane
+// (kk, col) holds elements 16 hh + 8 kk .. + 7 of codeword 32 b + col, times -2 (exact);
+// the tile is operand B: lane (kk, col) holds the same elements of vector col.  Each lane
+// sums its elements for codes 32 b + col, the lane pair (kk = 0, 1) adds its parts (the
+// same sum in both lanes), and the 32 columns compare.  Ties resolve to the lowest code.
+template <int NH, int NB>
+__device__ __forceinline__ int exact_in_registers(const u16x8 (&A)[NB][NH], const u16x8 (&B)[NH], int cv,
+                                                  int lane) {
+  const int kk = lane >> 5, col = lane & 31;
+  const int src = (kk << 5) | cv;
+  double x[NH][8];
 #pragma unroll
-  for (int e = 0; e < EPL; e += 2) {
-    const uint32_t w = (uint32_t)__shfl((int)((uint32_t)B[e] | ((uint32_t)B[e + 1] << 16)), src);
-    x[e] = (double)bf2f((uint16_t)(w & 0xffffu));
-    x[e + 1] = (double)bf2f((uint16_t)(w >> 16));
-  }
+  for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t w = (uint32_t)__shfl((int)((uint32_t)B[hh][e] | ((uint32_t)B[hh][e + 1] << 16)), src);
+      x[hh][e] = (double)bf2f((uint16_t)(w & 0xffffu));
+      x[hh][e + 1] = (double)bf2f((uint16_t)(w >> 16));
+    }
   double best = __builtin_inf();
   int bidx = 0;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
+  for (int b = 0; b < NB; ++b) {
     double part = 0.0;
 #pragma unroll
-    for (int e = 0; e < EPL; e += 2) {
-      // opaque copy: keeps the conversions here instead of hoisted out of the token loop
-      uint32_t w = (uint32_t)A[m][e] | ((uint32_t)A[m][e + 1] << 16);
-      asm volatile("" : "+v"(w));
-      const double d0 = fma(0.5, (double)bf2f((uint16_t)(w & 0xffffu)), x[e]);   // x - C, A = -2 C
-      const double d1 = fma(0.5, (double)bf2f((uint16_t)(w >> 16)), x[e + 1]);
-      part = fma(d0, d0, part);
-      part = fma(d1, d1, part);
-    }
-    part += __shfl_xor(part, 16);
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        // opaque copy: keeps the conversions here instead of hoisted out of the token loop
+        uint32_t w = (uint32_t)A[b][hh][e] | ((uint32_t)A[b][hh][e + 1] << 16);
+        asm volatile("" : "+v"(w));
+        const double d0 = fma(0.5, (double)bf2f((uint16_t)(w & 0xffffu)), x[hh][e]);   // x - C, A = -2 C
+        const double d1 = fma(0.5, (double)bf2f((uint16_t)(w >> 16)), x[hh][e + 1]);
+        part = fma(d0, d0, part);
+        part = fma(d1, d1, part);
+      }
     part += __shfl_xor(part, 32);
-    if (part < best) { best = part; bidx = 16 * m + col; }   // m ascending: lowest code kept
+    if (part < best) { best = part; bidx = 32 * b + col; }   // b ascending: lowest code kept
   }
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
+  for (int off = 1; off < 32; off <<= 1) {
     const double ob = __shfl_xor(best, off);
     const int oi = __shfl_xor(bidx, off);
     if (ob < best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
@@ -176,11 +169,12 @@ template <int D, int C>
 constexpr int waves_per_group_block() { return D / C < 4 ? D / C : 4; }
 
 // Work items are (token range, channel-group block, head, loop block, K/V).  The
-// items of one (token range, head, loop block, K/V) that read the same 128-byte
-// rows differ only in the group block and are numbered 8 apart, so with a grid that
-// is a multiple of 8 x (group blocks) they run on the same XCD (round-robin
-// dispatch) at the same time and each row is fetched from HBM once.
+// items of one (token range, head, loop block, K/V) that read the same 128-byte rows
+// differ only in the group block and are numbered 8 apart, so with a grid that is a
+// multiple of 8 x (group blocks) they run on the same XCD (round-robin dispatch) at
+// the same time and each row is fetched from HBM once.
 constexpr int kXcds = 8;
+constexpr int kTileTokens = 32;   // vectors per MFMA tile (the 32 columns)
 
 // Per-layer pools and books of a pages -> pages launch (the decode-time re-encode of
 // several layers at once); the other modes take none.
@@ -201,11 +195,10 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
   constexpr int NG = D / C;
   constexpr int WPG = waves_per_group_block<D, C>();   // waves (groups) per workgroup
   constexpr int NGB = NG / WPG;
-  constexpr int EPL = (G == 32) ? 8 : 4; // elements per lane per MFMA operand
   constexpr int TC = G / C;
-  constexpr int kPart = 4;               // MFMAs issued before their results are folded
-  constexpr int kRing = 3;               // tiles in flight
-  using R = raw_t<EPL>;
+  constexpr int NH = G / 16;             // 16-element K halves: MFMAs per block of 32 codes
+  constexpr int NB = kCodes / 32;        // blocks of 32 codes (the MFMA rows)
+  constexpr int kRing = 2;               // tiles in flight
   __shared__ __attribute__((aligned(16))) float s_bias[WPG][kCodes];
 
   const int lane = threadIdx.x & 63;
@@ -224,9 +217,9 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
   if constexpr (MODE == 2) n_layers = layers.n;
   const int ncombo = ncombo_layer * n_layers;
   const int per_combo = HB * NGB;
-  const int q4 = lane >> 4, col = lane & 15;
-  const int e0 = EPL * q4;
-  const int tau0 = e0 / C, i0 = e0 % C;
+  // MFMA 32x32x16 lane roles: operand A row / operand B column / result column col,
+  // K elements 8 kk .. 8 kk + 7 of each 16-element half; result rows 8 jj + 4 kk + r
+  const int kk = lane >> 5, col = lane & 31;
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int xcd = item % kXcds;
@@ -235,7 +228,7 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
     int rest = (j / per_combo) * kXcds + xcd;   // the combo
     if (rest >= ncombo) continue;   // padding to whole XCD rounds (uniform per workgroup)
     const int gb = inner % NGB;
-    const int hh = inner / NGB;
+    const int hh0 = inner / NGB;
     EncodeArgs a = a0;
     if constexpr (MODE == 2) {     // the item's layer: its pools and books
       const ReencodeLayer& L = layers.layer[rest / ncombo_layer];
@@ -247,7 +240,7 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
       a.n_dst_pages = L.n_index_pages;
     }
     const int part = rest % nparts; rest /= nparts;
-    const int h = (rest % nhb) * HB + hh; rest /= nhb;
+    const int h = (rest % nhb) * HB + hh0; rest /= nhb;
     const int beta = rest % nblk;   rest /= nblk;
     const int kv = (a.kv_sel >= 0) ? a.kv_sel : rest;
     const int g = gb * WPG + wave;
@@ -256,54 +249,63 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
 
     // ---- the codebook as MFMA A operand, scaled by -2 (exact); |C_k|^2 in float64, rounded once
     const uint16_t* cb = a.codebooks + ((((size_t)beta * 2 + kv) * H + h) * NG + g) * ((size_t)TC * kCodes * C);
-    R A[16];
+    u16x8 A[NB][NH];
     float cmax2 = 0.f;
   #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const R v = *(const R*)(cb + ((size_t)tau0 * kCodes + 16 * m + col) * C + i0);
-      R w;
+    for (int b = 0; b < NB; ++b) {
+      const int code = 32 * b + col;
       double s = 0.0;
   #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float f = bf2f(v[e]);
-        s = fma((double)f, (double)f, s);
-        w[e] = (uint16_t)(__float_as_uint(-2.f * f) >> 16);
+      for (int hh = 0; hh < NH; ++hh) {
+        const u16x8 v = load8<C>([&](int tau) { return cb + ((size_t)tau * kCodes + code) * C; }, 16 * hh + 8 * kk);
+        u16x8 w;
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = bf2f(v[e]);
+          s = fma((double)f, (double)f, s);
+          w[e] = (uint16_t)(__float_as_uint(-2.f * f) >> 16);
+        }
+        A[b][hh] = w;
       }
-      A[m] = w;
-      s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
       const float sf = (float)s;
       cmax2 = fmaxf(cmax2, sf);
-      if (q4 == 0) s_bias[wave][16 * m + col] = sf;
+      if (kk == 0) s_bias[wave][code] = sf;
     }
   #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) cmax2 = fmaxf(cmax2, __shfl_xor(cmax2, off));
-    const float* bias = &s_bias[wave][4 * q4];
-    // Dense rows of the lane's (loop step, channel slice) start at src_base + n * H * d;
-    // the lane's source and destination pointers advance by one tile (16 tokens) per step.
+    for (int off = 1; off < 32; off <<= 1) cmax2 = fmaxf(cmax2, __shfl_xor(cmax2, off));
+    const float* bias = &s_bias[wave][4 * kk];   // + 32 b + 8 jj: codes 32 b + 8 jj + 4 kk + r
+    // Dense rows of (loop step tau, token n) start at src_base + tau * N * H * d + n * H * d.
     const size_t src_stride = (size_t)H * a.d;
+    const size_t step_stride = (size_t)N * H * a.d;
     const size_t dst_stride = (size_t)H * NG;
-    const uint16_t* src_base = a.src + ((size_t)(beta * TC + tau0) * N * H + h) * a.d + g * C + i0;
-    const uint16_t* src_any = src_base + (size_t)nb0 * src_stride;   // a readable row of this block
-    const uint16_t* src_lane = src_base + (size_t)(nb0 + col) * src_stride;
+    const uint16_t* src_base = a.src + ((size_t)beta * TC * N * H + h) * a.d + g * C;
     uint8_t* dst_lane = a.out + ((size_t)beta * N * H + h) * NG + g + (size_t)(nb0 + col) * dst_stride;
 
-    // Load the lane's channel slice of tile n0 (and its destination page id).  Every load
-    // is unconditional, a slot past the range reading a row of this block and a missing
-    // bf16 page reading the codebook, so the compiler can count the loads in flight; ok
-    // says whether the slot is a real token.
-    auto fetch = [&](int n0, R& v, bool& ok, int& pg) {
+    // Load the lane's elements of tile n0's vector col (and its destination page id).
+    // Every load is unconditional, a slot past the range reading a row of this block and
+    // a missing bf16 page reading the codebook, so the compiler can count the loads in
+    // flight; ok says whether the slot is a real token.
+    auto fetch = [&](int n0, u16x8 (&v)[NH], bool& ok, int& pg) {
       const int n = n0 + col;
       ok = n < nb1;
-      const uint16_t* ptr;
       if constexpr (kDenseSrc) {
-        ptr = ok ? src_lane + (size_t)(n0 - nb0) * src_stride : src_any;
+        const uint16_t* rowp = src_base + (size_t)(ok ? n : nb0) * src_stride;
+  #pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+          v[hh] = load8<C>([&](int tau) { return rowp + (size_t)tau * step_stride; }, 16 * hh + 8 * kk);
       } else {
-        const uint16_t* r = src_row(a, beta * TC + tau0, ok ? n : nb0, h, kv);
-        ok = ok && r != nullptr;
-        ptr = r ? r + g * C + i0 : cb;
+        const int P = a.src_pages[(ok ? n : nb0) >> 3];
+        const bool have = P >= 0 && P < a.n_src_pages;
+        ok = ok && have;
+        const uint16_t* pb = a.src + ((((size_t)(have ? P : 0) * a.T + beta * TC) * H + h) * 2 + kv) * kPage * a.d +
+                             (size_t)((ok ? n : nb0) & 7) * a.d + g * C;
+        const size_t pstep = (size_t)H * 2 * kPage * a.d;
+  #pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+          v[hh] = have ? load8<C>([&](int tau) { return pb + (size_t)tau * pstep; }, 16 * hh + 8 * kk)
+                       : *(const u16x8*)cb;
       }
-      v = *(const R*)ptr;
       if constexpr (kDenseDst) {
         pg = 0;
       } else {
@@ -311,85 +313,103 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
       }
     };
 
-    // One 16-token tile: distances, argmin, certification, index write or deferral.
-    auto tile = [&](int n0, bool ok, const R& B, int pg) {
-      // keep the |C_k|^2 reads from LDS inside the tile (hoisted, they would take 64 VGPRs)
+    // One 32-token tile: distances, argmin, certification, index write or deferral.
+    auto tile = [&](int n0, bool ok, const u16x8 (&B)[NH], int pg) {
+      // keep the |C_k|^2 reads from LDS inside the tile (hoisted, they would take 128 VGPRs)
       asm volatile("" ::: "memory");
       const int n = n0 + col;
       // |x|^2 of the vector, only for the error bound
       float xx = 0.f;
   #pragma unroll
-      for (int e = 0; e < EPL; e += 2) {
-        const bf16x2 two = __builtin_bit_cast(bf16x2, (uint32_t)B[e] | ((uint32_t)B[e + 1] << 16));
-        xx = __builtin_amdgcn_fdot2_f32_bf16(two, two, xx, false);
-      }
+      for (int hh = 0; hh < NH; ++hh)
+  #pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 two = __builtin_bit_cast(bf16x2, (uint32_t)B[hh][e] | ((uint32_t)B[hh][e + 1] << 16));
+          xx = __builtin_amdgcn_fdot2_f32_bf16(two, two, xx, false);
+        }
       {
         float lo, hi;
-        pair16(xx, lo, hi);
-        xx = lo + hi;
         pair32(xx, lo, hi);
         xx = lo + hi;
       }
 
-      // The lane's 64 candidates (codes 16m + 4 q4 + r) become keys: D'_k with its six
-      // low mantissa bits replaced by 63 - (4m + r).  A smaller key is a smaller D' at
-      // key precision, and every key of the lane is distinct.  Two chains (rows 0-1 and
-      // rows 2-3 of each MFMA) fold their keys a pair (x, y) at a time: the smallest key
-      // b1 becomes min3(b1, x, y), and med3(b1, x, y) -- the second smallest of
-      // {b1, x, y} -- is a candidate for the second smallest overall, which is the
-      // minimum of these candidates (taken two at a time); 2.25 VALU per key.
-      float c1[2] = {__builtin_inff(), __builtin_inff()};
-      float c2[2] = {__builtin_inff(), __builtin_inff()};
-      float pend[2] = {__builtin_inff(), __builtin_inff()};
+      // The lane's 128 candidates (codes 32 b + 8 jj + 4 kk + r) become keys in two halves
+      // of four blocks: D'_k with its six low mantissa bits replaced by
+      // 63 - (16 (b mod 4) + 4 jj + r) (an inline constant, so one v_and_or_b32 per key).
+      // A smaller key is a smaller D' at key precision.  Four chains (half, pair parity)
+      // fold their keys a pair (x, y) at a time: the smallest key b1 becomes
+      // min3(b1, x, y), and med3(b1, x, y) -- the second smallest of {b1, x, y} -- is a
+      // candidate for the second smallest overall, which is the minimum of these
+      // candidates (taken two at a time); 2.25 VALU per key.
+      float c1[4], c2[4], pend[4];
+  #pragma unroll
+      for (int ch = 0; ch < 4; ++ch) c1[ch] = c2[ch] = pend[ch] = __builtin_inff();
       auto key = [](float v, int idx) {
         return __uint_as_float((__float_as_uint(v) & ~63u) | (63u - (uint32_t)idx));
       };
-      auto fold = [&](const f32x4& acc, int m) {   // m: compile-time MFMA number
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          const float x = key(acc[2 * ch], 4 * m + 2 * ch);
-          const float y = key(acc[2 * ch + 1], 4 * m + 2 * ch + 1);
+      // pairs [p0, p1) of block b (b, p0, p1 compile-time)
+      auto fold = [&](const f32x16& acc, int b, int p0, int p1) {
+  #pragma unroll
+        for (int pi = p0; pi < p1; ++pi) {
+          const int ch = 2 * (b >> 2) + (pi & 1);
+          const float x = key(acc[2 * pi], 16 * (b & 3) + 2 * pi);
+          const float y = key(acc[2 * pi + 1], 16 * (b & 3) + 2 * pi + 1);
           const float p = key_med3(c1[ch], x, y);
           c1[ch] = key_min3(c1[ch], x, y);
-          if (m & 1) c2[ch] = key_min3(c2[ch], pend[ch], p);
+          if (pi & 2) c2[ch] = key_min3(c2[ch], pend[ch], p);
           else pend[ch] = p;
         }
       };
-      // MFMA groups of kPart codes-blocks, software-pipelined: group p + 1 is issued
-      // before group p is folded.  Each group's accumulators start as |C_k|^2, read from
-      // LDS one group ahead.
-      constexpr int NP = 16 / kPart;
-      f32x4 acc[2][kPart];
-#pragma unroll
-      for (int mm = 0; mm < kPart; ++mm) acc[0][mm] = *(const f32x4*)(bias + 16 * mm);
-#pragma unroll
-      for (int mm = 0; mm < kPart; ++mm) acc[0][mm] = mfma_bf16<EPL>(A[mm], B, acc[0][mm]);
-#pragma unroll
-      for (int part = 0; part < NP; ++part) {
-        const int cur = part & 1;
-        if (part + 1 < NP) {
-#pragma unroll
-          for (int mm = 0; mm < kPart; ++mm)
-            acc[cur ^ 1][mm] = *(const f32x4*)(bias + 16 * (kPart * (part + 1) + mm));
-#pragma unroll
-          for (int mm = 0; mm < kPart; ++mm)
-            acc[cur ^ 1][mm] = mfma_bf16<EPL>(A[kPart * (part + 1) + mm], B, acc[cur ^ 1][mm]);
+      // Blocks of 32 codes, software-pipelined: each block's accumulators start as
+      // |C_k|^2, read from LDS before the first half of the previous block's fold; its
+      // MFMAs issue between the two halves, so neither the LDS read nor the MFMAs sit
+      // on the critical path (the scheduling barriers keep that order).
+      auto bias_of = [&](int b) {
+        f32x16 c;
+  #pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 q = *(const f32x4*)(bias + 32 * b + 8 * jj);
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) c[4 * jj + r] = q[r];
         }
-#pragma unroll
-        for (int mm = 0; mm < kPart; ++mm) fold(acc[cur][mm], kPart * part + mm);
+        return c;
+      };
+      auto mfmas = [&](int b, f32x16 c) {
+  #pragma unroll
+        for (int hh = 0; hh < NH; ++hh) c = mfma32(A[b][hh], B[hh], c);
+        return c;
+      };
+      f32x16 acc[2];
+      acc[0] = mfmas(0, bias_of(0));
+  #pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int cur = b & 1;
+        if (b + 1 < NB) acc[cur ^ 1] = bias_of(b + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(acc[cur], b, 0, 4);
+        __builtin_amdgcn_sched_barrier(0);
+        if (b + 1 < NB) acc[cur ^ 1] = mfmas(b + 1, acc[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        fold(acc[cur], b, 4, 8);
       }
-      float b1 = key_min(c1[0], c1[1]);
-      float b2 = key_min3(key_max(c1[0], c1[1]), c2[0], c2[1]);
-      // Merge the four lanes of the vector (lane ^ 16, then lane ^ 32): smallest and second
-      // smallest key overall, the same in all four lanes.  The lane whose own smallest key
-      // survives holds the winning code.
+      // the halves' smallest and second smallest, then the lane's (keys of the two halves
+      // share index bits: the half of the winner is kept aside; equal keys make b2 == b1)
+      float m1[2], m2[2];
+  #pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        m1[hf] = key_min(c1[2 * hf], c1[2 * hf + 1]);
+        m2[hf] = key_min3(key_max(c1[2 * hf], c1[2 * hf + 1]), c2[2 * hf], c2[2 * hf + 1]);
+      }
+      const int half = m1[1] < m1[0] ? 1 : 0;
+      float b1 = key_min(m1[0], m1[1]);
+      float b2 = key_min3(key_max(m1[0], m1[1]), m2[0], m2[1]);
+      // Merge the two lanes of the vector (lane ^ 32): smallest and second smallest key
+      // overall, the same in both lanes.  The lane whose own smallest key survives holds
+      // the winning code; equal keys in the two lanes make b2 == b1, which sends the
+      // vector to the float64 pass.
       const float own = b1;
       {
         float lo1, hi1, lo2, hi2;
-        pair16(b1, lo1, hi1);
-        pair16(b2, lo2, hi2);
-        b1 = key_min(lo1, hi1);
-        b2 = key_min3(key_max(lo1, hi1), lo2, hi2);
         pair32(b1, lo1, hi1);
         pair32(b2, lo2, hi2);
         b1 = key_min(lo1, hi1);
@@ -410,39 +430,41 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
       }
       if (ok && owner && !need_exact && o) {
         const uint32_t p = 63u - (__float_as_uint(b1) & 63u);
-        *o = (uint8_t)(16 * (int)(p >> 2) + 4 * q4 + (int)(p & 3u));
+        *o = (uint8_t)(32 * (4 * half + (int)(p >> 4)) + 8 * (int)((p >> 2) & 3u) + 4 * kk + (int)(p & 3u));
       }
       // Vectors whose float32 decision is not certain: float64 from registers, one at a time.
-      uint64_t todo = __ballot(need_exact && q4 == 0);   // bits = vector columns
+      uint64_t todo = __ballot(need_exact && kk == 0);   // bits = vector columns
       while (todo) {
         const int cv = (int)__builtin_ctzll(todo);
         todo &= todo - 1;
-        const int ex = exact_in_registers<EPL>(A, B, cv, lane);
+        const int ex = exact_in_registers<NH, NB>(A, B, cv, lane);
         if (lane == cv && o) *o = (uint8_t)ex;
       }
     };
 
     // Buffer j is refilled right after its tile is consumed and used again kRing - 1
     // tiles later, so each load overlaps that much work.
-    R Bq[kRing];
+    u16x8 Bq[kRing][NH];
     bool okq[kRing];
     int pgq[kRing];
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) fetch(nb0 + 16 * j, Bq[j], okq[j], pgq[j]);
-    for (int n0 = nb0; n0 < nb1; n0 += 16 * kRing) {
+    for (int jt = 0; jt < kRing; ++jt) fetch(nb0 + kTileTokens * jt, Bq[jt], okq[jt], pgq[jt]);
+    for (int n0 = nb0; n0 < nb1; n0 += kTileTokens * kRing) {
 #pragma unroll
-      for (int j = 0; j < kRing; ++j) {
-        if (n0 + 16 * j < nb1) tile(n0 + 16 * j, okq[j], Bq[j], pgq[j]);
-        fetch(n0 + 16 * (j + kRing), Bq[j], okq[j], pgq[j]);
+      for (int jt = 0; jt < kRing; ++jt) {
+        if (n0 + kTileTokens * jt < nb1) tile(n0 + kTileTokens * jt, okq[jt], Bq[jt], pgq[jt]);
+        fetch(n0 + kTileTokens * (jt + kRing), Bq[jt], okq[jt], pgq[jt]);
       }
     }
   }
 }
 
-// Workgroups per CU the kernel reaches and the device's CU count, cached per device.
+// Workgroups the device holds at once: the CU count times the workgroups per CU that
+// the kernel's VGPR count allows (512 per SIMD lane, at most 8 waves per SIMD; a
+// workgroup of W waves puts W / 4 waves on each SIMD), or the runtime's occupancy figure
+// if that is higher.  Cached per device in the caller's cache (one per kernel instance).
 template <typename K>
-int resident_workgroups(K kernel, int threads) {
-  static std::atomic<int> cache[64];
+int resident_workgroups(K kernel, int threads, std::atomic<int> (&cache)[64]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
   if (dev < 64) {
@@ -452,6 +474,15 @@ int resident_workgroups(K kernel, int threads) {
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  hipFuncAttributes fa{};
+  if (hipFuncGetAttributes(&fa, (const void*)kernel) == hipSuccess && fa.numRegs > 0) {
+    const int vgprs = (fa.numRegs + 7) / 8 * 8;
+    int waves_per_simd = 512 / vgprs;
+    if (waves_per_simd > 8) waves_per_simd = 8;
+    const int wg_waves = (threads + 63) / 64;
+    const int by_regs = 4 * waves_per_simd / wg_waves;
+    if (by_regs > per_cu) per_cu = by_regs;
+  }
   const int v = per_cu * cus;
   if (v > 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
   return v;
@@ -464,7 +495,8 @@ hipError_t launch_mode(const EncodeArgs& args, const LayersArg<MODE>& layers, in
   constexpr int NGB = NG / WPG;
   if (args.N <= 0) return hipSuccess;
   auto kernel = encode_kernel<G, C, D, MODE>;
-  int slots = resident_workgroups(kernel, WPG * 64);
+  static std::atomic<int> slot_cache[64];   // this kernel instance's, per device
+  int slots = resident_workgroups(kernel, WPG * 64, slot_cache);
   if (slots <= 0) slots = 256;
   const int round = kXcds * NGB;
   slots = slots / round * round;
@@ -475,7 +507,7 @@ hipError_t launch_mode(const EncodeArgs& args, const LayersArg<MODE>& layers, in
   long parts = slots / (sets * NGB * n_layers);
   if (parts < 1) parts = 1;
   long tpi = (args.N + parts - 1) / parts;
-  tpi = (tpi + 15) / 16 * 16;
+  tpi = (tpi + kTileTokens - 1) / kTileTokens * kTileTokens;
   parts = (args.N + tpi - 1) / tpi;
   // heads whose dense index rows share 128-byte lines go to one XCD together
   int hb = args.H < 8 ? args.H : 8;
