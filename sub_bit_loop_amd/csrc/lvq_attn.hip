@@ -162,15 +162,19 @@ struct SeqTiles {
   int coded;   // coded tiles (= their units)
   int total;   // units
 };
-__device__ __forceinline__ SeqTiles seq_tiles(const AttnArgs& a, int b) {
-  const int L = max(min(a.seq_len[b], a.max_seq_len), 0);
-  const int qe = max(min(a.q_end[b] & ~7, L), 0);
+// from sequence b's seq_len and q_end entries
+__device__ __forceinline__ SeqTiles seq_tiles_of(const AttnArgs& a, int len, int q_end) {
+  const int L = max(min(len, a.max_seq_len), 0);
+  const int qe = max(min(q_end & ~7, L), 0);
   const int ns = min(a.n_sink, L);
   const int r0 = max(qe, a.n_sink);
   const int vt_lo = r0 / kTile;
   const int vt_hi = L > r0 ? (L - 1) / kTile + 1 : vt_lo;
   const int coded = a.n_index_pages > 0 ? ((qe >> 3) + 1) >> 1 : 0;
   return {coded, coded + kBfCost * ((ns > 0 ? 1 : 0) + (vt_hi - vt_lo))};
+}
+__device__ __forceinline__ SeqTiles seq_tiles(const AttnArgs& a, int b) {
+  return seq_tiles_of(a, a.seq_len[b], a.q_end[b]);
 }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -226,6 +230,13 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
   const int W = wph * kNW;          // waves on this query head
   const int wg = kw * kNW + wave;   // this wave among them
 
+  // The first 64 sequences' lengths are loaded before the slices: vector loads return
+  // in order, so loaded after them the scan below would wait for every slice load.
+  // (unconditional loads at a clamped index: a load under a lane mask is waited for at
+  // the end of its branch; a.B >= 1 for every launch)
+  const int b_first = min(lane, a.B - 1);
+  const int len_first = a.seq_len[b_first];
+  const int qe_first = a.q_end[b_first];
   SliceStage<D, C> slices;
   slices.load(a, beta, h, tau);
   // the work list's length, and (one wave of the launch) the sequences' first units;
@@ -233,7 +244,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
   int total = 0, n_first = 0, incl_first = 0;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int b = b0 + lane;
-    const int n = b < a.B ? seq_tiles(a, b).total : 0;
+    const int n = b < a.B ? (b0 == 0 ? seq_tiles_of(a, len_first, qe_first) : seq_tiles(a, b)).total : 0;
     const int incl = total + wave_incl_scan(n);
     if (b0 == 0) { n_first = n; incl_first = incl; }
     if (hq == 0 && wg == 0 && b < a.B) a.tile_start[b] = incl - n;
@@ -617,8 +628,9 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
 constexpr int kMergeMax = 4096;   // candidate records per (b, hq) at most (the host checks)
 constexpr int kMergeThreads = 512;
 // THREADS threads per item, each record group's first PRE records loaded with the (m, l)
-// pairs: 512 / 8 where an item has few records, 1024 / 16 where one sequence spans many
-// waves (up to 128 records in the first round of loads at d = 128).
+// pairs: 512 / 8 where an item has few records, 1024 / 32 where one sequence spans many
+// waves (up to 256 records in the first round of loads at d = 128, so an item of a single
+// sequence over a whole launch of 16 query heads is merged in one round).
 template <int THREADS, int PRE>
 __global__ __launch_bounds__(THREADS) void merge_kernel(AttnArgs a, int cap) {
   extern __shared__ __align__(16) unsigned char merge_smem[];
@@ -762,7 +774,7 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
   // records per item: the waves over one sequence's share of the list, plus one
   const bool many = a.n_waves / (a.B > 0 ? a.B : 1) + 1 > 8 * (kMergeThreads / D);
   if (many)
-    hipLaunchKernelGGL((merge_kernel<2 * kMergeThreads, 16>), dim3(n_items), dim3(2 * kMergeThreads),
+    hipLaunchKernelGGL((merge_kernel<2 * kMergeThreads, 32>), dim3(n_items), dim3(2 * kMergeThreads),
                        (size_t)(a.n_waves + 1) * 12, s, a, a.n_waves + 1);
   else
     hipLaunchKernelGGL((merge_kernel<kMergeThreads, 8>), dim3(n_items), dim3(kMergeThreads),
