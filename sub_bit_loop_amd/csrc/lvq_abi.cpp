@@ -203,6 +203,44 @@ bool decode_on_rows(const lvq_attn_shape& s) {
   return s.Hq / s.H >= kRowsMinGroup && lvq::rows_supported(s.d, s.G / s.Tc);
 }
 
+// Decode with 4 query heads per KV head (d = 128) runs on the grouped kernel: the four
+// heads share each key's dequantisation and rotation.  lvq_decode_scores keeps the
+// per-head kernel (it writes per-head scores).
+bool decode_on_group(const lvq_attn_shape& s) {
+  return s.Hq == lvq::kGroupHeads * s.H && lvq::attn_group_supported(s.d, s.G / s.Tc);
+}
+
+// Token-balanced split of a KV head's work list over quads of waves: automatic sizing
+// gives each KV head an equal share of the compute units (one workgroup each), but not
+// more quads than about 4 tiles each of the largest possible work list.  n_splits > 0
+// asks for that many waves per KV head (rounded up to whole workgroups).
+SplitPlan plan_group_splits(const lvq_attn_shape& s) {
+  const int w = lvq::attn_group_waves_per_group();
+  const int quads_per_wg = w / lvq::kGroupQuad;
+  const int max_wpl = (lvq::merge_max_records() / lvq::kGroupQuad - 1) / quads_per_wg;
+  int wpl;
+  if (s.n_splits > 0) {
+    wpl = (s.n_splits + w - 1) / w;
+  } else {
+    wpl = kComputeUnits / s.H;
+    const long tiles_bound = (long)s.B * ((s.max_seq_len + 15) / 16 + 3);
+    const long by_work = (tiles_bound + 4L * quads_per_wg - 1) / (4L * quads_per_wg);
+    if (wpl > by_work) wpl = (int)by_work;
+  }
+  if (wpl < 1) wpl = 1;
+  if (wpl > max_wpl) wpl = max_wpl;
+  SplitPlan p;
+  p.n_waves = wpl * w;
+  p.n_rec = p.n_waves + lvq::kGroupQuad * s.B;
+  return p;
+}
+
+size_t group_workspace(const lvq_attn_shape& s) {
+  const SplitPlan p = plan_group_splits(s);
+  // records [H][n_rec][Hq / H rows][d + 2], then the sequences' first tiles [B + 1]
+  return (size_t)s.H * p.n_rec * lvq::kGroupHeads * (s.d + 2) * sizeof(float) + (size_t)(s.B + 1) * sizeof(int);
+}
+
 lvq_rows_shape rows_shape_of(const lvq_attn_shape& s) {
   lvq_rows_shape r{};
   r.B = s.B; r.NQ = 1; r.H = s.H; r.Hq = s.Hq; r.d = s.d; r.T = s.T; r.Tc = s.Tc; r.G = s.G;
@@ -216,6 +254,10 @@ size_t workspace_bytes(const lvq_attn_shape& s) {
   const SplitPlan p = plan_splits(s);
   // partial records [Hq][n_rec][d + 2], then the sequences' first tiles [B + 1]
   const size_t dec = (size_t)s.Hq * p.n_rec * (s.d + 2) * sizeof(float) + (size_t)(s.B + 1) * sizeof(int);
+  if (decode_on_group(s)) {
+    const size_t grp = group_workspace(s);
+    return grp > dec ? grp : dec;
+  }
   if (!decode_on_rows(s)) return dec;
   const size_t rows = rows_workspace(rows_shape_of(s));
   return rows > dec ? rows : dec;
@@ -239,7 +281,8 @@ int run_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_
     return lvq_rows_attn(q, nullptr, nullptr, page_table, index_pages, bf16_pages, bf16_table, codebooks, t,
                          pos, seq_len, q_end, rope_tab, &rs, out, lse, ws, ws_bytes, stream);
   }
-  const SplitPlan p = plan_splits(s);
+  const bool group = !scores && decode_on_group(s);
+  const SplitPlan p = group ? plan_group_splits(s) : plan_splits(s);
   lvq::AttnArgs a{};
   a.q = q;
   a.page_table = page_table;
@@ -272,9 +315,12 @@ int run_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_
   a.rope_tiles = (s.rope_max_len + lvq::rope_tile() - 1) / lvq::rope_tile();
   a.n_waves = p.n_waves;
   a.n_rec = p.n_rec;
-  a.tile_start = (int*)((char*)ws + (size_t)s.Hq * p.n_rec * (s.d + 2) * sizeof(float));
+  const size_t rec_floats = group ? (size_t)s.H * p.n_rec * lvq::kGroupHeads * (s.d + 2)
+                                  : (size_t)s.Hq * p.n_rec * (s.d + 2);
+  a.tile_start = (int*)((char*)ws + rec_floats * sizeof(float));
   const float scale = s.scale > 0.f ? s.scale : 1.0f / sqrtf((float)s.d);
   a.scale_log2e = scale * 1.4426950408889634f;
+  if (group) return device_status(lvq::launch_attn_group(a, (hipStream_t)stream), "lvq_decode_attn launch");
   return device_status(lvq::launch_attn(a, (hipStream_t)stream), "lvq_decode_attn launch");
 }
 

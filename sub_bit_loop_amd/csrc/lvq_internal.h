@@ -162,7 +162,8 @@ struct AttnArgs {
   int n_waves;                // waves per work list (token-balanced ranges)
   int n_rec;                  // records per work list: n_waves + B
   int* tile_start;            // [lists' row blocks][B + 1] first unit of each sequence
-  int merge_rows;             // merge input: 0 decode records, 1 multi-row records (16 rows)
+  int merge_rows;             // merge input: 0 decode records, 1 multi-row records (16 rows),
+                              // 2 grouped decode records (Hq / H rows, kGroupQuad per range)
   int NQ, n_rb;               // multi-row merge: queries per sequence, row blocks per KV head
   float scale_log2e;          // softmax scale * log2(e)
 };
@@ -172,5 +173,15 @@ int rope_tile();   // positions per row of the first RoPE table part
 int attn_waves_per_group();   // waves per decode-attention workgroup
 int merge_max_records();      // candidate partial records per (b, query head) the merge accepts
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// Grouped-query decode: kGroupHeads query heads per KV head share each key's
+// dequantisation and rotation; a range of a KV head's work list belongs to a quad of
+// kGroupQuad waves, each of which writes a record per sequence (n_rec = n_waves +
+// kGroupQuad * B per list).
+constexpr int kGroupQuad = 4;
+constexpr int kGroupHeads = 4;
+bool attn_group_supported(int d, int c);
+int attn_group_waves_per_group();   // waves per grouped-decode workgroup
+hipError_t launch_attn_group(const AttnArgs& a, hipStream_t s);
 
 }  // namespace lvq
