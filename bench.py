@@ -644,8 +644,9 @@ def rows_bench(torch, lvq, inp, nq=512):
       step 1, 16 heads), causal within the chunk; flops 4 d per (query, visible key) per
       head on fp32 matrix cores.  Context: the same attention in bf16 with torch matmuls on
       dense K/V (not the path).
-    gqa: decode over 8 x 32768 tokens with 4 KV heads x 4 query heads: the multi-row kernel
-      against the decode kernel on the same cache."""
+    gqa: decode over 8 x 32768 tokens with 16 query heads over 4, 2 and 1 KV heads:
+      lvq_decode_attn (the grouped kernel at 4 heads per KV head, the multi-row kernel at 8
+      and 16) and the multi-row kernel against the per-head kernel on the same cache."""
     dev = torch.device("cuda:0")
     Ly = inp["layers"][0]
     gen = torch.Generator(device=dev)
@@ -702,10 +703,13 @@ def rows_bench(torch, lvq, inp, nq=512):
     qg = torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
     res["gqa_decode"] = {"workload": f"B={B}, L={L}, {Hq} query heads over Hk KV heads, d={D}, Tc={TC}, G={G}, "
                                      f"one (layer, step)"}
-    # the decode kernel serves 16 query heads per KV-head group below 8 heads per KV head (at 8
-    # and above lvq_decode_attn itself runs on the multi-row kernel); its cost does not depend
-    # on the grouping, so the 4-KV-head run is the per-head baseline for every group size
+    # lvq_decode_attn runs the grouped kernel at 4 query heads per KV head and the multi-row
+    # kernel at 8 and 16.  The per-head kernel is timed through lvq_decode_scores, which runs
+    # it on the same call and also writes every score (B x 16 x L float32, 16.8 MB); its cost
+    # does not depend on the grouping, so the 4-KV-head run is the per-head baseline for
+    # every group size
     base_us = None
+    sbuf = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     for Hk in (4, 2, 1):
         ip = torch.randint(0, 256, (pool, T // TC, Hk, 2, 8, ng), generator=gen, device=dev, dtype=torch.uint8)
         bp = torch.randn((nbf, T, Hk, 2, 8, D), generator=gen, device=dev).to(torch.bfloat16)
@@ -725,11 +729,25 @@ def rows_bench(torch, lvq, inp, nq=512):
                                          out=o2, lse=l2, ws=rws)
         ds, rs = _event_time(torch, dec, 20), _event_time(torch, rows, 20)
         if base_us is None:
-            base_us = ds
-        res["gqa_decode"][f"g{Hq // Hk}"] = {
+            o3 = torch.empty_like(o1)
+            l3 = torch.empty_like(l1)
+            per_head = lambda: lvq.lvq_decode_scores(qg, pt, ip, bp, inp["bt"], cb, 2, posg, posg, qeg, inp["rope"],
+                                                     dshp, out=o3, lse=l3, ws=dws, scores=sbuf)
+            base_us = _event_time(torch, per_head, 20)
+            diff_ph = float((o1 - o3).abs().max())
+        g = Hq // Hk
+        res["gqa_decode"][f"g{g}"] = {
+            "route": "grouped kernel" if g == 4 else "multi-row kernel",
             "rows_us": round(rs * 1e6, 1), "lvq_decode_attn_us": round(ds * 1e6, 1),
-            "per_head_kernel_us": round(base_us * 1e6, 1), "speedup_vs_per_head": round(base_us / rs, 2),
+            "per_head_kernel_us": round(base_us * 1e6, 1),
+            "speedup_vs_per_head": round(base_us / ds, 2),
+            "rows_speedup_vs_per_head": round(base_us / rs, 2),
             "max_abs_diff_decode_vs_rows": float((o1 - o2[:, 0]).abs().max())}
+        if g == 4:
+            res["gqa_decode"]["g4"]["max_abs_diff_grouped_vs_per_head"] = diff_ph
+    del sbuf
+    res["gqa_decode"]["per_head_note"] = ("per-head kernel timed through lvq_decode_scores on the 4-KV-head call "
+                                          "(it also writes 16.8 MB of scores)")
     return res
 
 

@@ -232,7 +232,8 @@ typedef struct lvq_attn_shape {
   int32_t n_bf16_pages;   /* rows of bf16_pages, >= 1 */
   int32_t max_seq_len;    /* upper bound of seq_len[b]; sizes the automatic split */
   int32_t rope_max_len;   /* max_len the rope table was built for; every pos and seq_len must be < it */
-  int32_t n_splits;       /* waves per query head; 0 = automatic (see lvq_decode_attn) */
+  int32_t n_splits;       /* waves per query head (per KV head on the grouped route);
+                             0 = automatic (see lvq_decode_attn) */
   float scale;            /* softmax scale; 0 = 1/sqrt(d) */
 } lvq_attn_shape;
 
@@ -274,10 +275,13 @@ size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp);
  * results are merged per (b, hq) by log-sum-exp.  n_splits > 0 sets the number of
  * waves per query head (rounded up to whole workgroups of 12); 0 gives each head an
  * equal share of the 256 compute units.
- * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.  With 8 or more
- * query heads per KV head at d = 128 the call runs on the multi-row kernel (see
- * lvq_rows_attn), which shares each key's reconstruction among those heads; the
- * workspace size accounts for it.
+ * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.  With exactly 4
+ * query heads per KV head at d = 128 the call runs on the grouped kernel, which
+ * dequantises and rotates each key once for the four heads; the list is then per KV
+ * head, its ranges go to quads of 4 waves, and n_splits counts waves per KV head
+ * (whole workgroups of 16).  With 8 or more query heads per KV head at d = 128 it runs
+ * on the multi-row kernel (see lvq_rows_attn), which shares each key's reconstruction
+ * among those heads.  The workspace size accounts for either route.
  */
 int lvq_decode_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
                     const uint16_t* bf16_pages, const int32_t* bf16_table,
@@ -308,8 +312,9 @@ int lvq_decode_attn_noalloc(const uint16_t* q, const int32_t* page_table,
                             float* lse, void* stream);
 
 /*
- * lvq_decode_scores -- test probe: same inputs and device code as
- * lvq_decode_attn (same passages), but also writes the scaled scores q'.k' * scale
+ * lvq_decode_scores -- test probe: same inputs as lvq_decode_attn (same passages),
+ * always on the per-head kernel (the grouped and multi-row routes of lvq_decode_attn
+ * do not apply), which also writes the scaled scores q'.k' * scale
  * (natural units) of every cached token to scores, from which the attention mass
  * of a span of positions (the long-context retrieval check of the summary, section
  * "전제와 한계", RULER needle tasks) follows as sum exp(s_p - lse): float32 [B][Hq][max_seq_len]

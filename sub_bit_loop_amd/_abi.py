@@ -382,9 +382,11 @@ def lvq_decode_attn_noalloc(q, page_table, index_pages, bf16_pages, bf16_table, 
 
 
 def lvq_decode_scores(q, page_table, index_pages, bf16_pages, bf16_table, codebooks, t, pos,
-                      seq_len, q_end, rope_tab, shp: AttnShape, out=None, lse=None, ws=None):
-    """Test probe: (out, lse, scores [B][Hq][max_seq_len] f32, NaN where not written)."""
-    scores = torch.full((shp.B, shp.Hq, shp.max_seq_len), math.nan, dtype=torch.float32, device=q.device)
+                      seq_len, q_end, rope_tab, shp: AttnShape, out=None, lse=None, ws=None, scores=None):
+    """Test probe: (out, lse, scores [B][Hq][max_seq_len] f32).  Without a scores tensor
+    one is allocated NaN-filled, so positions the call does not write stay NaN."""
+    if scores is None:
+        scores = torch.full((shp.B, shp.Hq, shp.max_seq_len), math.nan, dtype=torch.float32, device=q.device)
     out, lse = _attn_call(lib().lvq_decode_scores, q, page_table, index_pages, bf16_pages,
                           bf16_table, codebooks, t, pos, seq_len, q_end, rope_tab, shp, out, lse,
                           ws, scores=scores)
