@@ -42,7 +42,8 @@ CONFIG_ID = 2
 CALIB_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_ouro_b8_l32k_traffic.txt")
 KSTATS_FILE = os.path.join(ROOT, "profiles", "decode_attn_ouro_b8_l32k_kernel_stats.txt")
-ATTN_SOURCES = [os.path.join(ROOT, "sub_bit_loop_amd", "csrc", f) for f in ("lvq_attn.hip", "lvq_internal.h")]
+ATTN_SOURCES = [os.path.join(ROOT, "sub_bit_loop_amd", "csrc", f)
+                for f in ("lvq_attn.hip", "lvq_attn_common.h", "lvq_internal.h")]
 
 
 def parse():
@@ -342,7 +343,7 @@ def kernel_stats_summary(directory):
     for f in glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
-    lib = ("attn_kernel", "merge_kernel", "encode_kernel", "seed_kernel", "update_kernel", "round_kernel",
+    lib = ("attn_kernel", "attn_group_kernel", "merge_kernel", "encode_kernel", "seed_kernel", "update_kernel", "round_kernel",
            "rope_kernel", "rows_kernel", "cache_")
     out = []
     for r in rows:

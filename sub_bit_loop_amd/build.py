@@ -13,8 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblvq.so")
-SOURCES = ["lvq_abi.cpp", "lvq_encode.hip", "lvq_attn.hip", "lvq_kmeans.hip", "lvq_cache.hip", "lvq_rows.hip",
-           "lvq_noalloc.hip"]
+SOURCES = ["lvq_abi.cpp", "lvq_encode.hip", "lvq_attn.hip", "lvq_attn_group.hip", "lvq_kmeans.hip", "lvq_cache.hip",
+           "lvq_rows.hip", "lvq_noalloc.hip"]
 
 # Packed float32 VALU forms are switched off: the kernels are written for
 # plain float32 FMA and mixed float16/float32 FMA.

@@ -168,6 +168,9 @@ struct AttnArgs {
   float scale_log2e;          // softmax scale * log2(e)
 };
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s);   // merge of multi-row records into a.out / a.lse
+// Merge of decode records (merge_rows 0 or 2) into m.out / m.lse: cap candidate records
+// per (b, hq), about per_item of them written (it picks the merge's width).
+hipError_t launch_merge_records(const AttnArgs& m, int cap, int per_item, hipStream_t s);
 bool attn_supported(int d, int c);
 int rope_tile();   // positions per row of the first RoPE table part
 int attn_waves_per_group();   // waves per decode-attention workgroup
