@@ -350,7 +350,7 @@ def kernel_stats_summary(directory):
         name = r["Name"]
         if not any(k in name for k in lib):
             continue
-        short = name.split("(")[0].replace("lvq::(anonymous namespace)::", "").replace("void ", "")
+        short = name.replace("lvq::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
         out.append((short, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                     float(r["MaxNs"]) / 1e3, float(r.get("StdDev", 0) or 0) / 1e3))
     out.sort(key=lambda x: -x[1] * x[2])

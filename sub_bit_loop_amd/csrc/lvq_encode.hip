@@ -10,28 +10,30 @@
 //
 // Design (MI355X):
 //  * One wave owns one codebook for a whole token range.  The 256 codewords,
-//    pre-scaled by -2 (exact in bf16), sit in VGPRs as the A operand of 16
-//    MFMAs (rows = codes); a 16-token tile of joint vectors is the B operand
-//    (columns = vectors), loaded straight from the cache in the layout the
-//    MFMA wants (8 or 4 contiguous channels of one loop step per lane).  The
-//    accumulator input is |C_k|^2, so each MFMA returns D'_k = |C_k|^2 - 2 x.C_k
-//    = |x - C_k|^2 - |x|^2 for 16 codes x 16 vectors, float32.
-//  * Argmin: each lane holds 64 candidates of one vector (16 MFMAs x 4 rows).
+//    pre-scaled by -2 (exact in bf16), sit in VGPRs as the A operand of
+//    v_mfma_f32_32x32x16_bf16 (8 blocks of 32 codes, G/16 K-halves each); a
+//    32-token tile of joint vectors is the B operand (columns = vectors), loaded
+//    straight from the cache in the layout the MFMA wants (8 or 4 contiguous
+//    channels of one loop step per lane).  The accumulator input is |C_k|^2, so each
+//    block returns D'_k = |C_k|^2 - 2 x.C_k = |x - C_k|^2 - |x|^2 for 32 codes x 32
+//    vectors, float32.
+//  * Argmin: each lane holds 128 candidates of one vector (8 blocks x 16 rows).
 //    Each becomes a key, D' with its six low mantissa bits replaced by the
-//    candidate's position; keys are folded three at a time (v_min3, v_med3)
-//    into the lane's smallest and second smallest key, then the four lanes of
-//    the vector merge.
+//    candidate's position; keys are folded a pair at a time (v_min3, v_med3) into
+//    the smallest and second smallest key (2.25 VALU per candidate), then the two
+//    lanes of the vector (lane ^ 32) merge through v_permlane32_swap.
 //  * Exactness: a vector is recomputed in float64 by direct differences over
 //    all 256 codewords (the definition itself) when its second smallest key is
 //    within the float32 error bound of the smallest.  So the chosen index is the
 //    float64 nearest codeword with lowest-index ties: float32 decides only where
 //    no other candidate can be within rounding of the winner.
-//  * Input tiles (16 tokens) are loaded two tiles ahead of their use; the |C_k|^2
-//    of the next group of MFMAs is read from LDS while the current group folds.
+//  * Input tiles (32 tokens) are loaded two tiles ahead of their use; the |C_k|^2
+//    of the next block of MFMAs is read from LDS while the current block folds.
 //  * A workgroup holds the waves of up to 4 consecutive groups of one
 //    (block, head); the workgroups that read the other halves of the same
-//    128-byte cache rows run on the same XCD at the same time, so the K/V
-//    bytes are fetched from HBM once.
+//    128-byte cache rows run on the same XCD at the same time, and the waves of a
+//    workgroup meet at a barrier every two tiles, so a row line stays in L2 until
+//    its readers have taken it (the input is read from memory about 1.2-1.3 times).
 #include "lvq_internal.h"
 
 #include <atomic>
@@ -443,7 +445,12 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
     };
 
     // Buffer j is refilled right after its tile is consumed and used again kRing - 1
-    // tiles later, so each load overlaps that much work.
+    // tiles later, so each load overlaps that much work.  The workgroup's waves meet at a
+    // barrier once per kRing tiles: every 128-byte line of a token's row is read by the
+    // four waves of this workgroup and by those of the workgroup of the neighbouring
+    // groups, and waves left to drift apart over a long token range find the line evicted
+    // from L2 between its readers (2.5 times the input read from memory at G = 32, 1.3
+    // with the barrier).
     u16x8 Bq[kRing][NH];
     bool okq[kRing];
     int pgq[kRing];
@@ -453,6 +460,7 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
 #pragma unroll
       for (int jt = 0; jt < kRing; ++jt) {
         if (n0 + kTileTokens * jt < nb1) tile(n0 + kTileTokens * jt, okq[jt], Bq[jt], pgq[jt]);
+        if (jt == kRing - 1) __syncthreads();   // n0, nb1: the same in every wave of the workgroup
         fetch(n0 + kTileTokens * (jt + kRing), Bq[jt], okq[jt], pgq[jt]);
       }
     }
