@@ -195,19 +195,22 @@ size_t rows_workspace(const lvq_rows_shape& s) {
          (size_t)p.n_rb * (s.B + 1) * sizeof(int);
 }
 
-// Decode with many query heads per KV head runs on the multi-row kernel: at 8 or more
-// heads per KV head it is the faster of the two (one key rebuild for all the heads).
-constexpr int kRowsMinGroup = 8;
+// Decode with 16 or more query heads per KV head runs on the multi-row kernel (one key
+// rebuild for all the heads, scores and values on the matrix cores); from 2 to 8 the
+// grouped kernel below is the faster.
+constexpr int kRowsMinGroup = 16;
 
 bool decode_on_rows(const lvq_attn_shape& s) {
   return s.Hq / s.H >= kRowsMinGroup && lvq::rows_supported(s.d, s.G / s.Tc);
 }
 
-// Decode with 4 query heads per KV head (d = 128) runs on the grouped kernel: the four
+// Decode with 2, 4 or 8 query heads per KV head (d = 128) runs on the grouped kernel: the
 // heads share each key's dequantisation and rotation.  lvq_decode_scores keeps the
 // per-head kernel (it writes per-head scores).
+int group_heads(const lvq_attn_shape& s) { return s.H > 0 && s.Hq % s.H == 0 ? s.Hq / s.H : 0; }
+
 bool decode_on_group(const lvq_attn_shape& s) {
-  return s.Hq == lvq::kGroupHeads * s.H && lvq::attn_group_supported(s.d, s.G / s.Tc);
+  return !decode_on_rows(s) && group_heads(s) > 1 && lvq::attn_group_supported(s.d, s.G / s.Tc, group_heads(s));
 }
 
 // Token-balanced split of a KV head's work list over quads of waves: automatic sizing
@@ -215,7 +218,7 @@ bool decode_on_group(const lvq_attn_shape& s) {
 // more quads than about 4 tiles each of the largest possible work list.  n_splits > 0
 // asks for that many waves per KV head (rounded up to whole workgroups).
 SplitPlan plan_group_splits(const lvq_attn_shape& s) {
-  const int w = lvq::attn_group_waves_per_group();
+  const int w = lvq::attn_group_waves_per_group(group_heads(s));
   const int quads_per_wg = w / lvq::kGroupQuad;
   const int max_wpl = (lvq::merge_max_records() / lvq::kGroupQuad - 1) / quads_per_wg;
   int wpl;
@@ -238,7 +241,7 @@ SplitPlan plan_group_splits(const lvq_attn_shape& s) {
 size_t group_workspace(const lvq_attn_shape& s) {
   const SplitPlan p = plan_group_splits(s);
   // records [H][n_rec][Hq / H rows][d + 2], then the sequences' first tiles [B + 1]
-  return (size_t)s.H * p.n_rec * lvq::kGroupHeads * (s.d + 2) * sizeof(float) + (size_t)(s.B + 1) * sizeof(int);
+  return (size_t)s.H * p.n_rec * group_heads(s) * (s.d + 2) * sizeof(float) + (size_t)(s.B + 1) * sizeof(int);
 }
 
 lvq_rows_shape rows_shape_of(const lvq_attn_shape& s) {
@@ -315,7 +318,7 @@ int run_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_
   a.rope_tiles = (s.rope_max_len + lvq::rope_tile() - 1) / lvq::rope_tile();
   a.n_waves = p.n_waves;
   a.n_rec = p.n_rec;
-  const size_t rec_floats = group ? (size_t)s.H * p.n_rec * lvq::kGroupHeads * (s.d + 2)
+  const size_t rec_floats = group ? (size_t)s.H * p.n_rec * group_heads(s) * (s.d + 2)
                                   : (size_t)s.Hq * p.n_rec * (s.d + 2);
   a.tile_start = (int*)((char*)ws + rec_floats * sizeof(float));
   const float scale = s.scale > 0.f ? s.scale : 1.0f / sqrtf((float)s.d);

@@ -3,31 +3,35 @@
 // "전제와 한계" and "무엇과 다른가"; rit.work article, section "Когда LoopVQ меняет
 // план развёртывания").
 //
-// kGroupHeads (4) query heads per KV head share each key's dequantisation and tile
+// QH query heads per KV head (2, 4 or 8) share each key's dequantisation and tile
 // rotation.  A quad of four waves covers the 16 positions of a tile: member m of the quad
 // takes in-tile offsets 4m..4m+3, one per 16-lane row r (offset o = 4m + r), so a lane's
-// offset never changes and its query coefficients F, G (4 heads x 4 channel pairs) are set
-// once per sequence.  Lane s of a row owns channel pairs 4s..4s+3 of the score (channels
-// 4s.. and d/2 + 4s..) and output channels 8s..8s+7 of the value sum, for all four heads.
-// Per token the lane rotates its four key pairs by the tile phase E(16a) once (four mixed
-// float16/float32 operations per pair) and forms the four partial scores (two FMAs per
-// pair and head); a transposing reduction over the row (eleven DPP and select operations
-// for the four heads) leaves the score of head s/4 in the lanes 4(s/4)..4(s/4)+3, which
-// keep that head's running maximum and sum, and three DPP row rotations give every lane
-// the four weights for the value sum.  About 7 lane operations per (token, head) against
-// 10.4 for the per-head kernel.  The work list of a KV head is the same as a query
-// head's; its ranges go to quads, and each wave of a quad writes its own partial record
-// (four rows, one per head) per sequence its range meets.
+// offset never changes and its query coefficients F, G (QH heads x 4 channel pairs) are
+// set once per sequence.  Lane s of a row owns channel pairs 4s..4s+3 of the score
+// (channels 4s.. and d/2 + 4s..) and output channels 8s..8s+7 of the value sum, for all
+// QH heads.  Per token the lane rotates its four key pairs by the tile phase E(16a) once
+// (four mixed float16/float32 operations per pair) and forms the QH partial scores (two
+// FMAs per pair and head); a transposing reduction over the row (lanes trading halves of
+// their heads) leaves the score of head s / (16 / QH) in the 16 / QH lanes that keep that
+// head's running maximum and sum, and QH - 1 DPP row rotations give every lane the QH
+// weights for the value sum.  At QH = 4, about 7 lane operations per (token, head)
+// against 10.4 for the per-head kernel.  The work list of a KV head is the same as a
+// query head's; its ranges go to quads, and each wave of a quad writes its own partial
+// record (QH rows, one per head) per sequence its range meets.  Four waves per SIMD at
+// QH = 2 and 4 (16-wave workgroups); the 64 coefficient and 64 output registers of
+// QH = 8 leave two (8-wave workgroups).
 #include "lvq_attn_common.h"
 
 namespace lvq {
 namespace {
-constexpr int kGW = 16;     // waves per workgroup: four quads, four waves per SIMD
+// waves per workgroup: four quads (four waves per SIMD), two at QH = 8 (two per SIMD)
+template <int QH>
+constexpr int group_waves() { return QH == 8 ? 8 : 16; }
 constexpr int kGPh = 128;   // floats per phase row: 64 pairs of (cos, sin)
 
-template <int D>
+template <int D, int NW>
 constexpr size_t group_lds_bytes() {
-  return (size_t)2 * kCodes * D * 2 + (size_t)kGW * (2 * kGPh * 4 + kPtBatch * 4);
+  return (size_t)2 * kCodes * D * 2 + (size_t)NW * (2 * kGPh * 4 + kPtBatch * 4);
 }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -35,34 +39,81 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef const f16x4 __attribute__((address_space(3)))* lds_f16x4_ptr;
 __device__ __forceinline__ f16x4 lds_read8(uint32_t addr) { return *(lds_f16x4_ptr)(size_t)addr; }
 
-// DPP lane moves within 16-lane rows (every lane of the wave active)
-constexpr int kDppRowRor4 = 0x124, kDppRowRor8 = 0x128, kDppRowRor12 = 0x12C;
-constexpr int kDppHalfMirror = 0x141, kDppQuad1032 = 0xB1, kDppQuad2301 = 0x4E;
+// DPP lane moves within 16-lane rows (every lane of the wave active): row rotations by
+// 2..14 lanes, the half-row mirror and quad permutes
+constexpr int kDppRowRor0 = 0x120;
+constexpr int kDppRowRor8 = kDppRowRor0 + 8;
+constexpr int kDppHalfMirror = 0x141, kDppQuad1032 = 0xB1, kDppQuad2301 = 0x4E, kDppQuad3210 = 0x1B;
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// Sum of the four per-lane partial scores p[0..3] over a 16-lane row.  Lanes s and s ^ 8
-// trade a pair of heads (s < 8 keeps heads 0, 1), then s and s ^ 7 a single head (bit 2
-// of s picks the odd one), then the quad adds its four lanes: every lane of quad s / 4
-// ends with the whole row sum of head s / 4.
-__device__ __forceinline__ float row_scores4(const float p[4], bool hi, bool b2) {
-  const float a0 = (hi ? p[2] : p[0]) + dpp_f<kDppRowRor8>(hi ? p[0] : p[2]);
-  const float a1 = (hi ? p[3] : p[1]) + dpp_f<kDppRowRor8>(hi ? p[1] : p[3]);
-  float v = (b2 ? a1 : a0) + dpp_f<kDppHalfMirror>(b2 ? a0 : a1);
-  v += dpp_f<kDppQuad1032>(v);
-  v += dpp_f<kDppQuad2301>(v);
-  return v;
+// Sum of the QH per-lane partial scores p[] over a 16-lane row, by lanes trading halves
+// of their heads: s and s ^ 8 (row rotation by 8) first, then s and the half-row mirror
+// of s (bit 2 differs), then s and s ^ 3 (bit 1), and the rest of the row by quad
+// permutes.  Every lane ends with the whole row sum of head s / (16 / QH).
+template <int QH>
+__device__ __forceinline__ float row_scores(const float (&p)[QH], int s) {
+  const bool hi = (s & 8) != 0, b2 = (s & 4) != 0, b1 = (s & 2) != 0;
+  if constexpr (QH == 2) {
+    float v = (hi ? p[1] : p[0]) + dpp_f<kDppRowRor8>(hi ? p[0] : p[1]);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppQuad2301>(v);
+    v += dpp_f<kDppQuad1032>(v);
+    return v;
+  } else if constexpr (QH == 4) {
+    const float a0 = (hi ? p[2] : p[0]) + dpp_f<kDppRowRor8>(hi ? p[0] : p[2]);
+    const float a1 = (hi ? p[3] : p[1]) + dpp_f<kDppRowRor8>(hi ? p[1] : p[3]);
+    float v = (b2 ? a1 : a0) + dpp_f<kDppHalfMirror>(b2 ? a0 : a1);
+    v += dpp_f<kDppQuad1032>(v);
+    v += dpp_f<kDppQuad2301>(v);
+    return v;
+  } else {
+    static_assert(QH == 8, "2, 4 or 8 query heads per KV head");
+    float A[4], B[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[i] = (hi ? p[i + 4] : p[i]) + dpp_f<kDppRowRor8>(hi ? p[i] : p[i + 4]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) B[i] = (b2 ? A[i + 2] : A[i]) + dpp_f<kDppHalfMirror>(b2 ? A[i] : A[i + 2]);
+    float v = (b1 ? B[1] : B[0]) + dpp_f<kDppQuad3210>(b1 ? B[0] : B[1]);
+    v += dpp_f<kDppQuad1032>(v);
+    return v;
+  }
 }
 
-template <int D, int C, bool WIDE>
-__global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const float* __restrict__ rope, int wpl) {
+// out[k] = v of the lane 16 k / QH places back in the row (row rotation), k < QH: the
+// value each head's lanes hold, spread to every lane
+template <int QH>
+__device__ __forceinline__ void row_spread(float v, float (&out)[QH]) {
+  out[0] = v;
+  if constexpr (QH == 2) {
+    out[1] = dpp_f<kDppRowRor0 + 8>(v);
+  } else if constexpr (QH == 4) {
+    out[1] = dpp_f<kDppRowRor0 + 4>(v);
+    out[2] = dpp_f<kDppRowRor0 + 8>(v);
+    out[3] = dpp_f<kDppRowRor0 + 12>(v);
+  } else {
+    out[1] = dpp_f<kDppRowRor0 + 2>(v);
+    out[2] = dpp_f<kDppRowRor0 + 4>(v);
+    out[3] = dpp_f<kDppRowRor0 + 6>(v);
+    out[4] = dpp_f<kDppRowRor0 + 8>(v);
+    out[5] = dpp_f<kDppRowRor0 + 10>(v);
+    out[6] = dpp_f<kDppRowRor0 + 12>(v);
+    out[7] = dpp_f<kDppRowRor0 + 14>(v);
+  }
+}
+
+template <int D, int C, int QH, bool WIDE>
+__global__ __launch_bounds__(group_waves<QH>() * 64) void attn_group_kernel(AttnArgs a, const float* __restrict__ rope,
+                                                                            int wpl) {
+  constexpr int kGW = group_waves<QH>();
+  constexpr int LPH = 16 / QH;    // lanes of a row per head after the row sum
   constexpr int NG = D / C;       // groups per head
   constexpr int HALF = D / 2;
   constexpr int NCH = D / 8;      // 16-byte chunks per codeword row in LDS
   static_assert(D == 128 && HALF == 64 && NCH * 16 == 256, "the grouped kernel is compiled for d = 128");
-  static_assert(kGroupHeads == 4 && kGroupQuad == 4, "four heads per KV head, four waves per range");
+  static_assert(kGroupQuad == 4 && (QH == 2 || QH == 4 || QH == 8), "2, 4 or 8 heads per KV head, four waves per range");
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* kl = (_Float16*)smem;                                   // K, V slices [256][D/8][8]
   float* phbuf = (float*)(smem + (size_t)2 * kCodes * D * 2);       // [kGW][2][kGPh]
@@ -122,15 +173,16 @@ __global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const 
 
   const int s = lane & 15, r = lane >> 4;
   const int toff = 4 * member + r;          // in-tile offset of this lane's tokens
-  const bool hi = (s & 8) != 0, b2 = (s & 4) != 0;
-  const int hsel = s >> 2;                  // the head whose score, maximum and sum the lane keeps
-  // heads whose weights the three row rotations bring (row_ror n moves lane i's value
-  // to lane i + n of the row): the output sums of head src[k] sit in o[k]
-  int src[4];
-  src[0] = hsel;
-  src[1] = __builtin_amdgcn_mov_dpp(hsel, kDppRowRor4, 0xF, 0xF, true);
-  src[2] = __builtin_amdgcn_mov_dpp(hsel, kDppRowRor8, 0xF, 0xF, true);
-  src[3] = __builtin_amdgcn_mov_dpp(hsel, kDppRowRor12, 0xF, 0xF, true);
+  const int hsel = s / LPH;                 // the head whose score, maximum and sum the lane keeps
+  // heads whose weights the row rotations bring: the output sums of head src[k] sit in
+  // o[k] (taken with the same moves, so nothing depends on the rotation's direction)
+  int src[QH];
+  {
+    float sf[QH];
+    row_spread<QH>(__int_as_float(hsel), sf);
+#pragma unroll
+    for (int k = 0; k < QH; ++k) src[k] = __float_as_int(sf[k]);
+  }
   // the groups of the lane's codes: low key channels 4s.., high key channels d/2 + 4s..,
   // value channels 8s..
   const int g_lo = (4 * s) / C, g_hi = (HALF + 4 * s) / C, g_v = (8 * s) / C;
@@ -163,15 +215,15 @@ __global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const 
       const int vt_lo = r0 / kTile;
       // F, G: each head's query, rotated to its position (log2 units), turned back by the
       // lane's in-tile offset, for the lane's four pairs
-      float F[4][4], Gc[4][4];
+      float F[QH][4], Gc[QH][4];
       {
         const f32x4 e1a = *(const f32x4*)(rope + (size_t)(a.rope_tiles + toff) * D + 8 * s);
         const f32x4 e1b = *(const f32x4*)(rope + (size_t)(a.rope_tiles + toff) * D + 8 * s + 4);
         const int pq = min(max(a.pos[b], 0), a.rope_tiles * kTile - 1);
         const float2 cs = phase(rope, a.rope_tiles, D, pq, lane);   // pair `lane` (64 pairs)
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-          const uint16_t* qv = a.q + ((size_t)b * a.Hq + h * 4 + hh) * D;
+        for (int hh = 0; hh < QH; ++hh) {
+          const uint16_t* qv = a.q + ((size_t)b * a.Hq + h * QH + hh) * D;
           const float x = bf2f(qv[lane]), y = bf2f(qv[lane + HALF]);
           ph[2 * lane] = (x * cs.x - y * cs.y) * a.scale_log2e;
           ph[2 * lane + 1] = (y * cs.x + x * cs.y) * a.scale_log2e;
@@ -188,17 +240,17 @@ __global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const 
       }
       float m = kNoMax, l = 0.f;
       float m_hi = kNoMax + kRescale;
-      float o[4][8];
+      float o[QH][8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < QH; ++k)
 #pragma unroll
         for (int c = 0; c < 8; ++c) o[k][c] = 0.f;
       // one token per row: the lane's rotated key pairs (x, y) give its four partial
       // scores; the row sum, the head's lazy maximum and the weights of the four heads
-      auto weights = [&](const float x[4], const float y[4], bool valid, float wr[4]) {
-        float ps[4];
+      auto weights = [&](const float x[4], const float y[4], bool valid, float (&wr)[QH]) {
+        float ps[QH];
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
+        for (int hh = 0; hh < QH; ++hh) {
           float acc = F[hh][0] * x[0];
           acc = fmaf(Gc[hh][0], y[0], acc);
 #pragma unroll
@@ -209,7 +261,7 @@ __global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const 
           ps[hh] = acc;
         }
         // (the row sum runs in every lane: the DPP moves read the other lanes of the row)
-        const float rs = row_scores4(ps, hi, b2);
+        const float rs = row_scores<QH>(ps, s);
         const float sc = valid ? rs : -__builtin_inff();
         if (__any(sc > m_hi)) {
           // the head's maximum over the wave's four rows (every lane of a quad holds the
@@ -221,18 +273,16 @@ __global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const 
           l *= f;
           m = mn;
           m_hi = mn + kRescale;
-          const float fr[4] = {f, dpp_f<kDppRowRor4>(f), dpp_f<kDppRowRor8>(f), dpp_f<kDppRowRor12>(f)};
+          float fr[QH];
+          row_spread<QH>(f, fr);
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
+          for (int k = 0; k < QH; ++k)
 #pragma unroll
             for (int c = 0; c < 8; ++c) o[k][c] *= fr[k];
         }
         const float w = __builtin_amdgcn_exp2f(sc - m);   // 0 for an invalid token
         l += w;
-        wr[0] = w;
-        wr[1] = dpp_f<kDppRowRor4>(w);
-        wr[2] = dpp_f<kDppRowRor8>(w);
-        wr[3] = dpp_f<kDppRowRor12>(w);
+        row_spread<QH>(w, wr);
       };
       const int P_lo = 2 * u_lo;
       const int P_hi = min(2 * min(u_hi, st.coded), qe >> 3);
@@ -289,11 +339,11 @@ __global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const 
           x[i] = fmaf(c0, (float)klo[i], -(s0 * (float)khi[i]));
           y[i] = fmaf(s0, (float)klo[i], c0 * (float)khi[i]);
         }
-        float wr[4];
+        float wr[QH];
         weights(x, y, valid, wr);
         const f16x8 v = lds_read16(__builtin_amdgcn_perm(in.vw, off_v, sel_v));
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < QH; ++k)
 #pragma unroll
           for (int c = 0; c < 8; ++c) o[k][c] = fmaf(wr[k], (float)v[c], o[k][c]);
       };
@@ -344,29 +394,29 @@ __global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const 
           x[i] = c0 * kx - s0 * ky;
           y[i] = s0 * kx + c0 * ky;
         }
-        float wr[4];
+        float wr[QH];
         weights(x, y, valid, wr);
         if (valid) {
           const u16x8 v = *(const u16x8*)(krow + (size_t)kPage * D + 8 * s);
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
+          for (int k = 0; k < QH; ++k)
 #pragma unroll
             for (int c = 0; c < 8; ++c) o[k][c] = fmaf(wr[k], bf2f(v[c]), o[k][c]);
         }
       }
       // head hh's sums are o[k] with src[k] == hh; then the sums over the four rows
-      float oh[4][8];
+      float oh[QH][8];
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh)
+      for (int hh = 0; hh < QH; ++hh)
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           float val = o[0][c];
 #pragma unroll
-          for (int k = 1; k < 4; ++k) val = src[k] == hh ? o[k][c] : val;
-          oh[hh][c] = src[0] == hh ? o[0][c] : val;
+          for (int k = 1; k < QH; ++k) val = src[k] == hh ? o[k][c] : val;
+          oh[hh][c] = val;
         }
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh)
+      for (int hh = 0; hh < QH; ++hh)
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           oh[hh][c] += __shfl_xor(oh[hh][c], 16);
@@ -374,14 +424,14 @@ __global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const 
         }
       l += __shfl_xor(l, 16);
       l += __shfl_xor(l, 32);
-      float* rec = a.part + ((size_t)h * a.n_rec + (size_t)(quad + b) * kGroupQuad + member) * (4 * (D + 2));
+      float* rec = a.part + ((size_t)h * a.n_rec + (size_t)(quad + b) * kGroupQuad + member) * (QH * (D + 2));
       if (r == 0) {
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh)
+        for (int hh = 0; hh < QH; ++hh)
 #pragma unroll
           for (int c = 0; c < 8; c += 2)
             *(float2*)(rec + hh * (D + 2) + 2 + 8 * s + c) = make_float2(oh[hh][c], oh[hh][c + 1]);
-        if ((s & 3) == 0) *(float2*)(rec + hsel * (D + 2)) = make_float2(m, l);
+        if (s % LPH == 0) *(float2*)(rec + hsel * (D + 2)) = make_float2(m, l);
       }
     }
     pos_t = __builtin_amdgcn_readfirstlane(tb + u_hi);
@@ -390,21 +440,22 @@ __global__ __launch_bounds__(kGW * 64) void attn_group_kernel(AttnArgs a, const 
   }
 }
 
-template <int D, int C, bool WIDE>
+template <int D, int C, int QH, bool WIDE>
 hipError_t launch_attn_group_t(const AttnArgs& a, hipStream_t s) {
-  constexpr size_t lds = group_lds_bytes<D>();
+  constexpr int kGW = group_waves<QH>();
+  constexpr size_t lds = group_lds_bytes<D, kGW>();
   static std::atomic<uint64_t> attr_set{0};
   hipError_t ea = once_per_device(attr_set, [&] {
-    return hipFuncSetAttribute((const void*)attn_group_kernel<D, C, WIDE>,
+    return hipFuncSetAttribute((const void*)attn_group_kernel<D, C, QH, WIDE>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   });
   if (ea != hipSuccess) return ea;
   const int wpl = a.n_waves / kGW;   // workgroups per KV head
   const int ranges = a.n_waves / kGroupQuad;
   if (wpl < 1 || a.n_waves % kGW || (ranges + 1) * kGroupQuad > merge_max_records() ||
-      a.n_rec != a.n_waves + kGroupQuad * a.B || !a.tile_start || a.Hq != kGroupHeads * a.H || a.d != D)
+      a.n_rec != a.n_waves + kGroupQuad * a.B || !a.tile_start || a.Hq != QH * a.H || a.d != D)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_group_kernel<D, C, WIDE>), dim3((unsigned)(wpl * a.H)), dim3(kGW * 64), lds, s, a,
+  hipLaunchKernelGGL((attn_group_kernel<D, C, QH, WIDE>), dim3((unsigned)(wpl * a.H)), dim3(kGW * 64), lds, s, a,
                      a.rope, wpl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -414,21 +465,33 @@ hipError_t launch_attn_group_t(const AttnArgs& a, hipStream_t s) {
   return launch_merge_records(m, (ranges + 1) * kGroupQuad, (ranges / (a.B > 0 ? a.B : 1) + 2) * kGroupQuad, s);
 }
 
+template <int QH>
+hipError_t launch_group_heads(const AttnArgs& a, int c, bool wide, hipStream_t s) {
+  if (c == 8) return wide ? launch_attn_group_t<128, 8, QH, true>(a, s) : launch_attn_group_t<128, 8, QH, false>(a, s);
+  if (c == 16) return wide ? launch_attn_group_t<128, 16, QH, true>(a, s) : launch_attn_group_t<128, 16, QH, false>(a, s);
+  return wide ? launch_attn_group_t<128, 32, QH, true>(a, s) : launch_attn_group_t<128, 32, QH, false>(a, s);
+}
+
 }  // namespace
 
-bool attn_group_supported(int d, int c) { return d == 128 && (c == 8 || c == 16 || c == 32); }
+bool attn_group_supported(int d, int c, int heads) {
+  return d == 128 && (c == 8 || c == 16 || c == 32) && (heads == 2 || heads == 4 || heads == 8);
+}
 
-int attn_group_waves_per_group() { return kGW; }
+int attn_group_waves_per_group(int heads) {
+  return heads == 8 ? group_waves<8>() : heads == 4 ? group_waves<4>() : group_waves<2>();
+}
 
 hipError_t launch_attn_group(const AttnArgs& a, hipStream_t s) {
   const int c = a.G / a.Tc;
-  if (a.d != 128 || !attn_group_supported(a.d, c)) return hipErrorInvalidValue;
+  const int heads = a.H > 0 ? a.Hq / a.H : 0;
+  if (a.H <= 0 || a.Hq % a.H || !attn_group_supported(a.d, c, heads)) return hipErrorInvalidValue;
   const uint64_t page_bytes = (uint64_t)(a.T / a.Tc) * a.H * 2 * kPage * (128 / c);
   const bool wide = (uint64_t)a.n_index_pages * page_bytes > 0xFFFFFFFFull || a.n_index_pages > (1 << 24) ||
                     page_bytes >= (1u << 24);
-  if (c == 8) return wide ? launch_attn_group_t<128, 8, true>(a, s) : launch_attn_group_t<128, 8, false>(a, s);
-  if (c == 16) return wide ? launch_attn_group_t<128, 16, true>(a, s) : launch_attn_group_t<128, 16, false>(a, s);
-  return wide ? launch_attn_group_t<128, 32, true>(a, s) : launch_attn_group_t<128, 32, false>(a, s);
+  if (heads == 2) return launch_group_heads<2>(a, c, wide, s);
+  if (heads == 4) return launch_group_heads<4>(a, c, wide, s);
+  return launch_group_heads<8>(a, c, wide, s);
 }
 
 }  // namespace lvq

@@ -61,7 +61,8 @@ EDGE = [  # config, B, lengths, H, Hq, d, T, Tc, G, n_sink, n_recent
     (35, 2, [515, 260], 1, 2, 128, 4, 2, 32, 0, 16),      # c = 16, no sink
     (36, 1, [600], 1, 1, 64, 4, 4, 32, 8, 8),             # d = 64, n_sink = 8, c = 8
     (37, 3, [0, 45, 0], 2, 2, 128, 4, 4, 32, 4, 16),      # empty batch slots: out 0, lse -inf
-    (38, 3, [45, 0, 20], 1, 8, 128, 4, 4, 32, 4, 16),     # the same on the multi-row route (GQA 8)
+    (38, 3, [45, 0, 20], 1, 16, 128, 4, 4, 32, 4, 16),    # the same on the multi-row route (GQA 16)
+    (72, 3, [45, 0, 20], 1, 8, 128, 4, 4, 32, 4, 16),     # the same on the grouped route (GQA 8)
 ]
 
 

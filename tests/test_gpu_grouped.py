@@ -1,7 +1,8 @@
-"""GPU parity of grouped-query decode (4 query heads per KV head, d = 128): lvq_decode_attn
-routes these shapes to the kernel that shares each key's dequantisation and rotation over
-the KV head's four query heads.  Same tolerance as the per-head decode tests: max-abs
-<= 2e-3 over every output element, max-rel <= 1e-2 where |oracle| >= 0.2, lse within 1e-4.
+"""GPU parity of grouped-query decode (2, 4 and 8 query heads per KV head, d = 128):
+lvq_decode_attn routes these shapes to the kernel that shares each key's dequantisation
+and rotation over the KV head's query heads.  Same tolerance as the per-head decode
+tests: max-abs <= 2e-3 over every output element, max-rel <= 1e-2 where |oracle| >= 0.2,
+lse within 1e-4.
 lvq_decode_scores keeps the per-head kernel on the same shapes, so the two kernels are
 also compared with each other."""
 import dataclasses
@@ -20,21 +21,27 @@ from test_gpu_attn import check
 pytestmark = pytest.mark.gpu
 
 
-GROUPED = [  # config, lengths, H, T, Tc, G, n_sink, n_recent
-    (60, [37, 300, 1000], 2, 4, 4, 32, 4, 16),      # c = 8, ragged lengths
-    (61, [515, 260], 1, 4, 2, 32, 0, 16),           # c = 16, no sink
-    (62, [1000, 33], 2, 1, 1, 32, 4, 64),           # prelude layer: Tc = 1, c = 32
-    (63, [1, 8, 19], 1, 4, 4, 32, 4, 64),           # shorter than sink + recent: all bf16
-    (64, [0, 45, 0], 2, 4, 4, 32, 4, 16),           # empty batch slots: out 0, lse -inf
-    (65, [300, 129], 2, 8, 4, 32, 8, 64),           # two loop blocks, n_sink = 8
+GROUPED = [  # config, lengths, H, query heads per KV head, T, Tc, G, n_sink, n_recent
+    (60, [37, 300, 1000], 2, 4, 4, 4, 32, 4, 16),      # c = 8, ragged lengths
+    (61, [515, 260], 1, 4, 4, 2, 32, 0, 16),           # c = 16, no sink
+    (62, [1000, 33], 2, 4, 1, 1, 32, 4, 64),           # prelude layer: Tc = 1, c = 32
+    (63, [1, 8, 19], 1, 4, 4, 4, 32, 4, 64),           # shorter than sink + recent: all bf16
+    (64, [0, 45, 0], 2, 4, 4, 4, 32, 4, 16),           # empty batch slots: out 0, lse -inf
+    (65, [300, 129], 2, 4, 8, 4, 32, 8, 64),           # two loop blocks, n_sink = 8
+    (69, [37, 300, 1000], 2, 2, 4, 4, 32, 4, 16),      # 2 heads per KV head, c = 8
+    (70, [515, 0, 260], 3, 2, 4, 2, 32, 0, 64),        # 2 heads per KV head, c = 16, an empty slot
+    (71, [1000, 8], 1, 2, 1, 1, 32, 8, 16),            # 2 heads per KV head, c = 32
+    (80, [37, 300, 1000], 1, 8, 4, 4, 32, 4, 16),      # 8 heads per KV head, c = 8
+    (81, [515, 0, 260], 2, 8, 4, 2, 32, 0, 64),        # 8 heads per KV head, c = 16, an empty slot
+    (82, [1000, 8], 1, 8, 1, 1, 32, 8, 16),            # 8 heads per KV head, c = 32
 ]
 
 
-@pytest.mark.parametrize("cfg,lengths,H,T,Tc,G,ns,nr", GROUPED)
-def test_grouped_decode_matches_oracle(cfg, lengths, H, T, Tc, G, ns, nr):
-    plog.case(f"grouped decode (4 query heads per KV head) cfg={cfg} L={lengths} H={H} Hq={4 * H} "
+@pytest.mark.parametrize("cfg,lengths,H,g,T,Tc,G,ns,nr", GROUPED)
+def test_grouped_decode_matches_oracle(cfg, lengths, H, g, T, Tc, G, ns, nr):
+    plog.case(f"grouped decode ({g} query heads per KV head) cfg={cfg} L={lengths} H={H} Hq={g * H} "
               f"T={T} Tc={Tc} G={G} n_sink={ns} n_recent={nr}; every step, every (b, head)")
-    cache = build_cache(cfg, len(lengths), lengths, H, 128, T, Tc, G, ns, nr, Hq=4 * H, books="random")
+    cache = build_cache(cfg, len(lengths), lengths, H, 128, T, Tc, G, ns, nr, Hq=g * H, books="random")
     dc = to_dev(cache)
     for t in range(T):
         out, lse = gpu_attn(dc, t)
@@ -91,14 +98,15 @@ def test_grouped_index_pool_beyond_4gib():
     np.testing.assert_array_equal(got_lse.cpu().numpy(), ref_lse.cpu().numpy())
 
 
-def test_grouped_decode_at_32k():
-    """The benchmark's grouped shape: B=8 sequences of 32768 tokens, 4 KV heads x 4 query
-    heads, d=128, T=4, Tc=4, G=32, 4 sink + 64 recent, shuffled pages, automatic split.
-    The oracle checks every query head of sequences 0, 3 and 7 at two loop steps; all 128
-    (b, head) outputs are compared with the per-head kernel."""
-    plog.case("grouped decode at 32K: B=8 L=32768 H=4 Hq=16 d=128 T=4 Tc=4 G=32; "
+@pytest.mark.parametrize("H,Hq", [(4, 16), (8, 16), (2, 16)])
+def test_grouped_decode_at_32k(H, Hq):
+    """The benchmark's grouped shapes: B=8 sequences of 32768 tokens, 16 query heads over 8,
+    4 or 2 KV heads, d=128, T=4, Tc=4, G=32, 4 sink + 64 recent, shuffled pages, automatic
+    split.  The oracle checks every query head of sequences 0, 3 and 7 at two loop steps;
+    all 128 (b, head) outputs are compared with the per-head kernel."""
+    plog.case(f"grouped decode at 32K: B=8 L=32768 H={H} Hq={Hq} d=128 T=4 Tc=4 G=32; "
               "oracle on sequences 0, 3, 7 (all heads), per-head kernel on all pairs")
-    cache = build_cache_light(68, 8, [32768] * 8, 4, 128, 4, 4, 32, 4, 64, Hq=16)
+    cache = build_cache_light(68, 8, [32768] * 8, H, 128, 4, 4, 32, 4, 64, Hq=Hq)
     dc = to_dev(cache)
     pairs = [(b, h) for b in (0, 3, 7) for h in range(16)]
     for t in (0, 3):

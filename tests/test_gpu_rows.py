@@ -200,11 +200,11 @@ def test_rows_rejects_bad_arguments():
 
 
 def test_decode_attn_routes_wide_groups_to_the_rows_kernel():
-    """lvq_decode_attn with 8 query heads per KV head (d = 128) runs on the multi-row kernel;
-    the result is the oracle's and the workspace query covers it."""
+    """lvq_decode_attn with 16 query heads per KV head (d = 128) runs on the multi-row
+    kernel; the result is the oracle's and the workspace query covers it."""
     from gpu_helpers import gpu_attn
-    plog.case("multi-row attention: decode attn, 8 query heads per KV head")
-    cache = build_cache(50, 2, [77, 640], 2, 128, 4, 2, 32, 4, 64, Hq=16, books="random")
+    plog.case("multi-row attention: decode attn, 16 query heads per KV head")
+    cache = build_cache(50, 2, [77, 640], 1, 128, 4, 2, 32, 4, 64, Hq=16, books="random")
     dc = to_dev(cache)
     out, lse = gpu_attn(dc, 3)
     ro, rl = cache.oracle_attn(3)
