@@ -646,8 +646,8 @@ def rows_bench(torch, lvq, inp, nq=512):
       head on fp32 matrix cores.  Context: the same attention in bf16 with torch matmuls on
       dense K/V (not the path).
     gqa: decode over 8 x 32768 tokens with 16 query heads over 4, 2 and 1 KV heads:
-      lvq_decode_attn (the grouped kernel at 4 heads per KV head, the multi-row kernel at 8
-      and 16) and the multi-row kernel against the per-head kernel on the same cache."""
+      lvq_decode_attn (the grouped kernel at 4 and 8 heads per KV head, the multi-row kernel
+      at 16) and the multi-row kernel against the per-head kernel on the same cache."""
     dev = torch.device("cuda:0")
     Ly = inp["layers"][0]
     gen = torch.Generator(device=dev)
@@ -704,8 +704,8 @@ def rows_bench(torch, lvq, inp, nq=512):
     qg = torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
     res["gqa_decode"] = {"workload": f"B={B}, L={L}, {Hq} query heads over Hk KV heads, d={D}, Tc={TC}, G={G}, "
                                      f"one (layer, step)"}
-    # lvq_decode_attn runs the grouped kernel at 4 query heads per KV head and the multi-row
-    # kernel at 8 and 16.  The per-head kernel is timed through lvq_decode_scores, which runs
+    # lvq_decode_attn runs the grouped kernel at 4 and 8 query heads per KV head and the
+    # multi-row kernel at 16.  The per-head kernel is timed through lvq_decode_scores, which runs
     # it on the same call and also writes every score (B x 16 x L float32, 16.8 MB); its cost
     # does not depend on the grouping, so the 4-KV-head run is the per-head baseline for
     # every group size
@@ -738,7 +738,7 @@ def rows_bench(torch, lvq, inp, nq=512):
             diff_ph = float((o1 - o3).abs().max())
         g = Hq // Hk
         res["gqa_decode"][f"g{g}"] = {
-            "route": "grouped kernel" if g == 4 else "multi-row kernel",
+            "route": "grouped kernel" if g <= 8 else "multi-row kernel",
             "rows_us": round(rs * 1e6, 1), "lvq_decode_attn_us": round(ds * 1e6, 1),
             "per_head_kernel_us": round(base_us * 1e6, 1),
             "speedup_vs_per_head": round(base_us / ds, 2),

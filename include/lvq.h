@@ -275,13 +275,13 @@ size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp);
  * results are merged per (b, hq) by log-sum-exp.  n_splits > 0 sets the number of
  * waves per query head (rounded up to whole workgroups of 12); 0 gives each head an
  * equal share of the 256 compute units.
- * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.  With exactly 4
+ * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.  With 2, 4 or 8
  * query heads per KV head at d = 128 the call runs on the grouped kernel, which
- * dequantises and rotates each key once for the four heads; the list is then per KV
- * head, its ranges go to quads of 4 waves, and n_splits counts waves per KV head
- * (whole workgroups of 16).  With 8 or more query heads per KV head at d = 128 it runs
- * on the multi-row kernel (see lvq_rows_attn), which shares each key's reconstruction
- * among those heads.  The workspace size accounts for either route.
+ * dequantises and rotates each key once for the KV head's query heads; the list is then
+ * per KV head, its ranges go to quads of 4 waves, and n_splits counts waves per KV head
+ * (whole workgroups of 16, of 8 at 8 heads).  With 16 or more query heads per KV head at
+ * d = 128 it runs on the multi-row kernel (see lvq_rows_attn), which shares each key's
+ * reconstruction among those heads.  The workspace size accounts for either route.
  */
 int lvq_decode_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
                     const uint16_t* bf16_pages, const int32_t* bf16_table,
