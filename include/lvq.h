@@ -239,7 +239,9 @@ typedef struct lvq_attn_shape {
 
 /* Workspace bytes of lvq_decode_attn / lvq_decode_scores for this shape: the
  * partial (max, sum, output) records of the Flash-Decoding split that the
- * log-sum-exp merge combines (the summary, section "전제와 한계"). */
+ * log-sum-exp merge combines (the summary, section "전제와 한계").  Returns 0 for a
+ * null or malformed shape (B, H, Hq, d, Tc, G or max_seq_len not positive, Hq not a
+ * multiple of H). */
 size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp);
 
 /*

@@ -720,7 +720,9 @@ int lvq_rows_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
 }
 
 size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp) {
-  if (!shp || shp->B <= 0 || shp->Hq <= 0 || shp->d <= 0 || shp->max_seq_len <= 0) return 0;
+  if (!shp || shp->B <= 0 || shp->H <= 0 || shp->Hq <= 0 || shp->Hq % shp->H || shp->d <= 0 ||
+      shp->max_seq_len <= 0 || shp->Tc <= 0 || shp->G <= 0)
+    return 0;
   return workspace_bytes(*shp);
 }
 

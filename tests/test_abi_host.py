@@ -143,6 +143,15 @@ def test_workspace_size_covers_every_split(L):
         assert nbytes == Hq * (W + B) * 130 * 4 + (B + 1) * 4, (B, Hq, msl, ns, nbytes)
 
 
+def test_workspace_query_refuses_malformed_shapes(L):
+    """The size query returns 0 (and does not divide by zero) for a shape the entry points
+    would refuse: H or Tc zero, Hq not a multiple of H."""
+    from sub_bit_loop_amd import _abi
+    for kw in (dict(H=0), dict(H=-1), dict(Hq=3), dict(Tc=0), dict(G=0), dict(B=0), dict(max_seq_len=0)):
+        assert _abi.lvq_decode_attn_workspace_bytes(shape(**kw)) == 0, kw
+    assert _abi.lvq_decode_attn_workspace_bytes(shape()) > 0
+
+
 def test_workspace_size_of_grouped_decode(L):
     """At 2, 4 and 8 query heads per KV head (d = 128) the workspace holds the larger of the
     per-head records (lvq_decode_scores keeps that kernel) and the grouped kernel's: records
