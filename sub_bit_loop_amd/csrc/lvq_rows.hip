@@ -14,17 +14,24 @@
 // head; the (KV head, row block) work list -- every sequence's 16-key tiles in order --
 // is cut into equal ranges, one per wave (token-balanced, as in the decode kernel), so
 // mixed sequence lengths keep every wave busy.  Each key is rebuilt and rotated once per
-// tile in float32 and shared by all 16 rows through v_mfma_f32_16x16x4f32:
+// tile in float32 and shared by all 16 rows through the matrix cores:
 //  * lane (key j, quarter k) holds key j's channel pairs [16k, 16k+16) with their
 //    partners + d/2, rebuilt by four 16-byte LDS gathers and rotated in registers (the
 //    rotation of a pair stays inside the lane); those 32 values are its B operands of
-//    the 32 score MFMAs, whose A operands are the rotated query rows in the same order;
+//    the score MFMAs, whose A operands are the rotated query rows in the same order;
 //  * the 16 x 16 scores land one row quarter per lane group; the online softmax keeps
 //    (max, sum) per row, with the same lazy maximum as the decode kernel;
 //  * probabilities go through a 1 KB LDS tile to the A-operand layout of the value
 //    MFMAs; lane (column c, key quarter) gathers chunk c (channels 8c .. 8c+7) of four
-//    keys, so output channel 8c + b of value block b sits in that lane: 32 MFMAs per tile.
-// Float32 MFMA keeps the products exact in float32, as in the decode kernel.
+//    keys, so output channel 8c + b of value block b sits in that lane.
+// Precision.  Coded tiles run on float16 MFMAs with float32 accumulation: the rotated
+// query and key values are split into float16 hi + lo parts and a score is the sum of
+// hi*hi, hi*lo and lo*hi (12 v_mfma_f32_16x16x32_f16 per tile); the probabilities are
+// split the same way against the float16 codewords, which are exact (16
+// v_mfma_f32_16x16x16_f16).  Products of float16 values are exact in float32, so a score
+// misses only the lo*lo terms and the rounding of the lo parts, about 2^-20 of each
+// product: float32-level results at a sixteenth of the float32 matrix-core time.  The
+// few bf16 tiles (sink, recent window, new keys) keep v_mfma_f32_16x16x4f32.
 #include "lvq_internal.h"
 
 namespace lvq {
@@ -32,6 +39,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRW = 8;          // waves per workgroup
@@ -50,6 +58,19 @@ constexpr size_t rows_lds_bytes() {
 }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// x = hi + lo + e with hi, lo float16 (hi the nearest float16 to x, lo the nearest to the
+// exact float32 remainder x - hi), so |e| <= 2^-11 |x - hi| <= 2^-22 |x| where no lo is
+// subnormal.  Products of float16 operands are exact in the MFMA's float32 accumulation:
+// a product of two split operands taken as hi*hi + hi*lo + lo*hi misses only lo*lo and the
+// e terms, about 2^-20 of |x y|.
+struct Split16 {
+  _Float16 hi, lo;
+};
+__device__ __forceinline__ Split16 split16(float x) {
+  const _Float16 hi = (_Float16)x;
+  return {hi, (_Float16)(x - (float)hi)};
+}
 
 // Chunk k of code x sits at slot k ^ (x mod 16) of the key slice (XOR swizzle): the 16
 // lanes that gather the same key chunk of random codes then spread over the LDS banks.
@@ -473,6 +494,19 @@ void rows_kernel(RowsArgs a, int wph) {
           in.e0 = *(const float2*)(a.rope + (size_t)a_tile * D + 2 * lane);
           return in;
         };
+        // A operands of the coded tiles' score MFMAs (v_mfma_f32_16x16x32_f16): the rotated
+        // query rows split into float16 hi + lo.  Block m holds, for lane (row j, quarter kq),
+        // k = 8 kq .. 8 kq + 7 <-> pairs 16 kq + 8 (m & 1) + i (m < 2) or their partners
+        // (m >= 2); the keys use the same order.
+        f16x8 qh[4], ql[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const Split16 v = split16(qf[(mb >> 1) * 16 + 8 * (mb & 1) + i]);
+            qh[mb][i] = v.hi;
+            ql[mb][i] = v.lo;
+          }
         auto coded_tile = [&](int P0, const CIn& in) {
           const int pbase = 8 * P0;
           *(float2*)(erow + 36 * (lane >> 4) + 2 * (lane & 15)) = in.e0;     // pair `lane`
@@ -485,7 +519,8 @@ void rows_kernel(RowsArgs a, int wph) {
             for (int u = 0; u < 4; ++u)
               xk[u] = gather_k(__builtin_amdgcn_ubfe(u < 2 ? in.kwl : in.kwh, shk[u], 8), chs[u]);
           }
-          f32x4 S = {0.f, 0.f, 0.f, 0.f};
+          // the lane's 32 rotated key values (float32), split into float16 hi + lo blocks
+          f16x8 kh[4], kl[4];
 #pragma unroll
           for (int s2 = 0; s2 < 8; ++s2) {
             const f32x4 e = *(const f32x4*)(erow + 36 * kq + 4 * s2);
@@ -495,19 +530,44 @@ void rows_kernel(RowsArgs a, int wph) {
               const float c0 = e[2 * u], s0 = e[2 * u + 1];
               const float c = c0 * e1c[s] - s0 * e1s[s], sn = s0 * e1c[s] + c0 * e1s[s];
               const float lo = (float)xk[s >> 3][s & 7], hi = (float)xk[2 + (s >> 3)][s & 7];
-              S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], lo * c - hi * sn, S, 0, 0, 0);
-              S = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[16 + s], lo * sn + hi * c, S, 0, 0, 0);
+              const Split16 x = split16(lo * c - hi * sn), y = split16(lo * sn + hi * c);
+              kh[s >> 3][s & 7] = x.hi;
+              kl[s >> 3][s & 7] = x.lo;
+              kh[2 + (s >> 3)][s & 7] = y.hi;
+              kl[2 + (s >> 3)][s & 7] = y.lo;
             }
           }
+          // scores: hi*hi on one accumulator, the two cross terms on another
+          f32x4 S = {0.f, 0.f, 0.f, 0.f}, Sx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            S = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[mb], kh[mb], S, 0, 0, 0);
+            Sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[mb], kl[mb], Sx, 0, 0, 0);
+            Sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[mb], kh[mb], Sx, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[r] += Sx[r];
           float pa[4];
           softmax_step(S, kok, -1, pa);
-          // invalid keys have P = 0 and finite codewords, so their values need no mask
+          // values (v_mfma_f32_16x16x16_f16): k = 4 kq + i <-> key 4 i + kq, so lane (row j,
+          // kq) holds P[j][4 i + kq] = pa[i] (split into hi + lo) and lane (column j, kq) the
+          // channel 8 j + c8 of the value chunks it gathered; the float16 codewords are exact.
+          // Invalid keys have P = 0 and finite codewords, so their values need no mask.
+          f16x8 xv[4];
 #pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) {
-            const f16x8 x = gather(vl, __builtin_amdgcn_ubfe(in.vw[s2], shv, 8), j);
+          for (int s2 = 0; s2 < 4; ++s2) xv[s2] = gather(vl, __builtin_amdgcn_ubfe(in.vw[s2], shv, 8), j);
+          f16x4 ph, pl;
 #pragma unroll
-            for (int c8 = 0; c8 < 8; ++c8)
-              O[c8] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s2], (float)x[c8], O[c8], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            const Split16 v = split16(pa[i]);
+            ph[i] = v.hi;
+            pl[i] = v.lo;
+          }
+#pragma unroll
+          for (int c8 = 0; c8 < 8; ++c8) {
+            const f16x4 vb = {xv[0][c8], xv[1][c8], xv[2][c8], xv[3][c8]};
+            O[c8] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb, O[c8], 0, 0, 0);
+            O[c8] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, O[c8], 0, 0, 0);
           }
         };
         // two tiles per iteration, each prefetched into the other register set
