@@ -40,6 +40,9 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRW = 8;          // waves per workgroup
@@ -70,6 +73,15 @@ struct Split16 {
 __device__ __forceinline__ Split16 split16(float x) {
   const _Float16 hi = (_Float16)x;
   return {hi, (_Float16)(x - (float)hi)};
+}
+// The same split of two values at once, as packed float16 words (one v_cvt_pk_f16_f32 for
+// each word; the remainders are exact in float32 and taken by v_fma_mix from the hi word).
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+  f32x2 r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r[0]) : "v"(hi), "v"(a));
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r[1]) : "v"(hi), "v"(b));
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, f16x2));
 }
 
 // Chunk k of code x sits at slot k ^ (x mod 16) of the key slice (XOR swizzle): the 16
@@ -519,23 +531,30 @@ void rows_kernel(RowsArgs a, int wph) {
             for (int u = 0; u < 4; ++u)
               xk[u] = gather_k(__builtin_amdgcn_ubfe(u < 2 ? in.kwl : in.kwh, shk[u], 8), chs[u]);
           }
-          // the lane's 32 rotated key values (float32), split into float16 hi + lo blocks
-          f16x8 kh[4], kl[4];
+          // the lane's 32 rotated key values (float32; the float16 key values enter the
+          // rotation through v_fma_mix), split pairwise into float16 hi + lo words
+          uint32_t khw[4][4], klw[4][4];   // [block][word]: elements 2 w, 2 w + 1 of the block
 #pragma unroll
           for (int s2 = 0; s2 < 8; ++s2) {
             const f32x4 e = *(const f32x4*)(erow + 36 * kq + 4 * s2);
+            float rx[2], ry[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               const int s = 2 * s2 + u;
               const float c0 = e[2 * u], s0 = e[2 * u + 1];
               const float c = c0 * e1c[s] - s0 * e1s[s], sn = s0 * e1c[s] + c0 * e1s[s];
               const float lo = (float)xk[s >> 3][s & 7], hi = (float)xk[2 + (s >> 3)][s & 7];
-              const Split16 x = split16(lo * c - hi * sn), y = split16(lo * sn + hi * c);
-              kh[s >> 3][s & 7] = x.hi;
-              kl[s >> 3][s & 7] = x.lo;
-              kh[2 + (s >> 3)][s & 7] = y.hi;
-              kl[2 + (s >> 3)][s & 7] = y.lo;
+              rx[u] = fmaf(lo, c, fmaf(hi, -sn, 0.f));
+              ry[u] = fmaf(lo, sn, fmaf(hi, c, 0.f));
             }
+            split_pair(rx[0], rx[1], khw[s2 >> 2][s2 & 3], klw[s2 >> 2][s2 & 3]);
+            split_pair(ry[0], ry[1], khw[2 + (s2 >> 2)][s2 & 3], klw[2 + (s2 >> 2)][s2 & 3]);
+          }
+          f16x8 kh[4], kl[4];
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            kh[mb] = __builtin_bit_cast(f16x8, u32x4{khw[mb][0], khw[mb][1], khw[mb][2], khw[mb][3]});
+            kl[mb] = __builtin_bit_cast(f16x8, u32x4{klw[mb][0], klw[mb][1], klw[mb][2], klw[mb][3]});
           }
           // scores: hi*hi on one accumulator, the two cross terms on another
           f32x4 S = {0.f, 0.f, 0.f, 0.f}, Sx = {0.f, 0.f, 0.f, 0.f};
