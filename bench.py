@@ -625,6 +625,7 @@ def manager_bench(torch, lvq, inp, n_tokens=64):
 
 
 FP32_MFMA_PEAK_TFLOPS = 157.3
+F16_MFMA_PEAK_TFLOPS = 2500.0   # dense float16 matrix peak
 
 
 def _event_time(torch, fn, reps):
@@ -642,12 +643,15 @@ def _event_time(torch, fn, reps):
 def rows_bench(torch, lvq, inp, nq=512):
     """Multi-row attention at the model shape.
     prefill: nq new tokens of sequence 0 over its 32768-token coded prefix (layer 0, loop
-      step 1, 16 heads), causal within the chunk; flops 4 d per (query, visible key) per
-      head on fp32 matrix cores.  Context: the same attention in bf16 with torch matmuls on
-      dense K/V (not the path).
+      step 1, 16 heads), causal within the chunk; algorithmic flops 4 d per (query, visible
+      key) per head at float32 precision, set against the fp32 matrix peak.  The coded
+      tiles execute them as float16 hi/lo products (10 d per pair: three score and two
+      value products), the bf16 tiles on fp32 matrix cores; those executed matrix flops are
+      reported beside it.  Context: the same attention in bf16 with torch matmuls on dense
+      K/V (not the path).
     gqa: decode over 8 x 32768 tokens with 16 query heads over 4, 2 and 1 KV heads:
-      lvq_decode_attn (the grouped kernel at 4 and 8 heads per KV head, the multi-row kernel
-      at 16) and the multi-row kernel against the per-head kernel on the same cache."""
+      lvq_decode_attn (the grouped kernel at 4 heads per KV head, the multi-row kernel at 8
+      and 16) and the multi-row kernel against the per-head kernel on the same cache."""
     dev = torch.device("cuda:0")
     Ly = inp["layers"][0]
     gen = torch.Generator(device=dev)
@@ -684,11 +688,24 @@ def rows_bench(torch, lvq, inp, nq=512):
 
     dsec = _event_time(torch, dense, 5)
     del Kd, KdT, Vd
+    # matrix flops as executed: each row block of 16 queries runs every 16-key tile of the
+    # coded prefix (10 d per pair on float16), the sink and recent tiles and the new-key
+    # tiles its rows can see (4 d per pair on fp32)
+    n_rb = nq // 16
+    qe = inp["q_end"]
+    coded_tiles = qe // 16
+    bf_tiles = (1 if N_SINK else 0) + (L - 1) // 16 + 1 - max(qe, N_SINK) // 16
+    new_tiles = sum(rb + 1 for rb in range(n_rb))
+    exec_f16 = H * n_rb * coded_tiles * 256 * 10 * D
+    exec_f32 = H * (n_rb * bf_tiles + new_tiles) * 256 * 4 * D
     res["prefill_chunk"] = {
         "workload": f"{nq} new tokens over a {L}-token coded prefix, 16 heads, d={D}, Tc={TC}, G={G}, one (layer, step)",
         "us": round(sec * 1e6, 1), "tokens_per_s": round(nq / sec, 1),
         "tflops": round(flops / sec / 1e12, 2), "fp32_mfma_peak": FP32_MFMA_PEAK_TFLOPS,
         "frac_fp32_mfma": round(flops / sec / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        "executed_f16_mfma_tflops": round(exec_f16 / sec / 1e12, 2), "f16_mfma_peak": F16_MFMA_PEAK_TFLOPS,
+        "frac_f16_mfma_executed": round(exec_f16 / sec / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+        "executed_f32_mfma_tflops": round(exec_f32 / sec / 1e12, 2),
         "dense_bf16_torch_us": round(dsec * 1e6, 1)}
     # ---- GQA decode: 16 query heads over 4, 2 or 1 KV heads
     c = G // TC
@@ -704,8 +721,8 @@ def rows_bench(torch, lvq, inp, nq=512):
     qg = torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
     res["gqa_decode"] = {"workload": f"B={B}, L={L}, {Hq} query heads over Hk KV heads, d={D}, Tc={TC}, G={G}, "
                                      f"one (layer, step)"}
-    # lvq_decode_attn runs the grouped kernel at 4 and 8 query heads per KV head and the
-    # multi-row kernel at 16.  The per-head kernel is timed through lvq_decode_scores, which runs
+    # lvq_decode_attn runs the grouped kernel at 4 query heads per KV head and the
+    # multi-row kernel at 8 and 16.  The per-head kernel is timed through lvq_decode_scores, which runs
     # it on the same call and also writes every score (B x 16 x L float32, 16.8 MB); its cost
     # does not depend on the grouping, so the 4-KV-head run is the per-head baseline for
     # every group size
@@ -738,7 +755,7 @@ def rows_bench(torch, lvq, inp, nq=512):
             diff_ph = float((o1 - o3).abs().max())
         g = Hq // Hk
         res["gqa_decode"][f"g{g}"] = {
-            "route": "grouped kernel" if g <= 8 else "multi-row kernel",
+            "route": "grouped kernel" if g <= 4 else "multi-row kernel",
             "rows_us": round(rs * 1e6, 1), "lvq_decode_attn_us": round(ds * 1e6, 1),
             "per_head_kernel_us": round(base_us * 1e6, 1),
             "speedup_vs_per_head": round(base_us / ds, 2),

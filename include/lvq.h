@@ -232,7 +232,8 @@ typedef struct lvq_attn_shape {
   int32_t n_bf16_pages;   /* rows of bf16_pages, >= 1 */
   int32_t max_seq_len;    /* upper bound of seq_len[b]; sizes the automatic split */
   int32_t rope_max_len;   /* max_len the rope table was built for; every pos and seq_len must be < it */
-  int32_t n_splits;       /* waves per query head (per KV head on the grouped route);
+  int32_t n_splits;       /* waves per query head (per KV head on the grouped route, per
+                             work list of lvq_rows_attn on the multi-row route);
                              0 = automatic (see lvq_decode_attn) */
   float scale;            /* softmax scale; 0 = 1/sqrt(d) */
 } lvq_attn_shape;
@@ -277,13 +278,14 @@ size_t lvq_decode_attn_workspace_bytes(const lvq_attn_shape* shp);
  * results are merged per (b, hq) by log-sum-exp.  n_splits > 0 sets the number of
  * waves per query head (rounded up to whole workgroups of 12); 0 gives each head an
  * equal share of the 256 compute units.
- * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.  With 2, 4 or 8
+ * Supported: d = 128 with c in {8, 16, 32}; d = 64 with c in {8, 16}.  With 2 or 4
  * query heads per KV head at d = 128 the call runs on the grouped kernel, which
  * dequantises and rotates each key once for the KV head's query heads; the list is then
  * per KV head, its ranges go to quads of 4 waves, and n_splits counts waves per KV head
- * (whole workgroups of 16, of 8 at 8 heads).  With 16 or more query heads per KV head at
- * d = 128 it runs on the multi-row kernel (see lvq_rows_attn), which shares each key's
- * reconstruction among those heads.  The workspace size accounts for either route.
+ * (whole workgroups of 16).  With 8 or more query heads per KV head at d = 128 it runs on
+ * the multi-row kernel (see lvq_rows_attn), which shares each key's reconstruction among
+ * those heads as the rows of its matrix-core products.  The workspace size accounts for
+ * every route.
  */
 int lvq_decode_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_pages,
                     const uint16_t* bf16_pages, const int32_t* bf16_table,
@@ -358,7 +360,8 @@ typedef struct lvq_rows_shape {
   int32_t n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages;
   int32_t max_prefix;     /* upper bound of prefix_len[b] */
   int32_t rope_max_len;   /* >= max_prefix + NQ; every pos[b] + NQ - 1 must be below it */
-  int32_t n_splits;       /* key chunks per row; 0 = automatic */
+  int32_t n_splits;       /* waves per work list (a KV head's block of 16 rows), rounded up
+                             to whole workgroups of 8; 0 = automatic */
   float scale;            /* softmax scale; 0 = 1/sqrt(d) */
 } lvq_rows_shape;
 

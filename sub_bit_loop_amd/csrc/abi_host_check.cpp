@@ -70,10 +70,10 @@ bool attn_supported(int d, int c) {
 }
 bool rows_supported(int d, int c) { return d == 128 && (c == 8 || c == 16 || c == 32); }
 bool attn_group_supported(int d, int c, int heads) {
-  return d == 128 && (c == 8 || c == 16 || c == 32) && (heads == 2 || heads == 4 || heads == 8);
+  return d == 128 && (c == 8 || c == 16 || c == 32) && (heads == 2 || heads == 4);
 }
 int attn_waves_per_group() { return 12; }
-int attn_group_waves_per_group(int heads) { return heads == 8 ? 8 : 16; }
+int attn_group_waves_per_group() { return 16; }
 int rows_waves_per_group() { return 8; }
 int merge_max_records() { return 4096; }
 int rope_tile() { return 16; }
@@ -96,8 +96,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t) {
 hipError_t launch_attn_group(const AttnArgs& a, hipStream_t) {
   ++g_launches;
   const int g = a.H > 0 ? a.Hq / a.H : 0;
-  const int w = attn_group_waves_per_group(g);
-  CHECK(a.H > 0 && a.Hq % a.H == 0 && (g == 2 || g == 4 || g == 8), "grouped: Hq %d over H %d", a.Hq, a.H);
+  const int w = attn_group_waves_per_group();
+  CHECK(a.H > 0 && a.Hq % a.H == 0 && (g == 2 || g == 4), "grouped: Hq %d over H %d", a.Hq, a.H);
   CHECK(a.n_waves > 0 && a.n_waves % w == 0, "grouped: n_waves %d not whole workgroups of %d", a.n_waves, w);
   CHECK(a.n_rec == a.n_waves + kGroupQuad * a.B, "grouped: n_rec %d != n_waves %d + 4 B", a.n_rec, a.n_waves);
   CHECK((a.n_waves / kGroupQuad + 1) * kGroupQuad <= merge_max_records(), "grouped: merge capacity");

@@ -195,16 +195,16 @@ size_t rows_workspace(const lvq_rows_shape& s) {
          (size_t)p.n_rb * (s.B + 1) * sizeof(int);
 }
 
-// Decode with 16 or more query heads per KV head runs on the multi-row kernel (one key
-// rebuild for all the heads, scores and values on the matrix cores); from 2 to 8 the
+// Decode with 8 or more query heads per KV head runs on the multi-row kernel (one key
+// rebuild for all the heads, scores and values on the matrix cores); at 2 and 4 the
 // grouped kernel below is the faster.
-constexpr int kRowsMinGroup = 16;
+constexpr int kRowsMinGroup = 8;
 
 bool decode_on_rows(const lvq_attn_shape& s) {
   return s.Hq / s.H >= kRowsMinGroup && lvq::rows_supported(s.d, s.G / s.Tc);
 }
 
-// Decode with 2, 4 or 8 query heads per KV head (d = 128) runs on the grouped kernel: the
+// Decode with 2 or 4 query heads per KV head (d = 128) runs on the grouped kernel: the
 // heads share each key's dequantisation and rotation.  lvq_decode_scores keeps the
 // per-head kernel (it writes per-head scores).
 int group_heads(const lvq_attn_shape& s) { return s.H > 0 && s.Hq % s.H == 0 ? s.Hq / s.H : 0; }
@@ -218,7 +218,7 @@ bool decode_on_group(const lvq_attn_shape& s) {
 // more quads than about 4 tiles each of the largest possible work list.  n_splits > 0
 // asks for that many waves per KV head (rounded up to whole workgroups).
 SplitPlan plan_group_splits(const lvq_attn_shape& s) {
-  const int w = lvq::attn_group_waves_per_group(group_heads(s));
+  const int w = lvq::attn_group_waves_per_group();
   const int quads_per_wg = w / lvq::kGroupQuad;
   const int max_wpl = (lvq::merge_max_records() / lvq::kGroupQuad - 1) / quads_per_wg;
   int wpl;

@@ -3,7 +3,7 @@
 // "전제와 한계" and "무엇과 다른가"; rit.work article, section "Когда LoopVQ меняет
 // план развёртывания").
 //
-// QH query heads per KV head (2, 4 or 8) share each key's dequantisation and tile
+// QH query heads per KV head (2 or 4) share each key's dequantisation and tile
 // rotation.  A quad of four waves covers the 16 positions of a tile: member m of the quad
 // takes in-tile offsets 4m..4m+3, one per 16-lane row r (offset o = 4m + r), so a lane's
 // offset never changes and its query coefficients F, G (QH heads x 4 channel pairs) are
@@ -17,16 +17,15 @@
 // weights for the value sum.  At QH = 4, about 7 lane operations per (token, head)
 // against 10.4 for the per-head kernel.  The work list of a KV head is the same as a
 // query head's; its ranges go to quads, and each wave of a quad writes its own partial
-// record (QH rows, one per head) per sequence its range meets.  Four waves per SIMD at
-// QH = 2 and 4 (16-wave workgroups); the 64 coefficient and 64 output registers of
-// QH = 8 leave two (8-wave workgroups).
+// record (QH rows, one per head) per sequence its range meets.  Four waves per SIMD
+// (16-wave workgroups).  From 8 query heads per KV head the multi-row kernel, whose float16
+// matrix-core products serve the heads as rows, is the faster one.
 #include "lvq_attn_common.h"
 
 namespace lvq {
 namespace {
-// waves per workgroup: four quads (four waves per SIMD), two at QH = 8 (two per SIMD)
-template <int QH>
-constexpr int group_waves() { return QH == 8 ? 8 : 16; }
+// waves per workgroup: four quads (four waves per SIMD)
+constexpr int kGroupWaves = 16;
 constexpr int kGPh = 128;   // floats per phase row: 64 pairs of (cos, sin)
 
 template <int D, int NW>
@@ -40,44 +39,35 @@ typedef const f16x4 __attribute__((address_space(3)))* lds_f16x4_ptr;
 __device__ __forceinline__ f16x4 lds_read8(uint32_t addr) { return *(lds_f16x4_ptr)(size_t)addr; }
 
 // DPP lane moves within 16-lane rows (every lane of the wave active): row rotations by
-// 2..14 lanes, the half-row mirror and quad permutes
+// 4, 8 and 12 lanes, the half-row mirror and quad permutes
 constexpr int kDppRowRor0 = 0x120;
 constexpr int kDppRowRor8 = kDppRowRor0 + 8;
-constexpr int kDppHalfMirror = 0x141, kDppQuad1032 = 0xB1, kDppQuad2301 = 0x4E, kDppQuad3210 = 0x1B;
+constexpr int kDppHalfMirror = 0x141, kDppQuad1032 = 0xB1, kDppQuad2301 = 0x4E;
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum of the QH per-lane partial scores p[] over a 16-lane row, by lanes trading halves
-// of their heads: s and s ^ 8 (row rotation by 8) first, then s and the half-row mirror
-// of s (bit 2 differs), then s and s ^ 3 (bit 1), and the rest of the row by quad
-// permutes.  Every lane ends with the whole row sum of head s / (16 / QH).
+// of their heads: s and s ^ 8 (row rotation by 8) first, then (QH = 4) s and the
+// half-row mirror of s (bit 2 differs), and the rest of the row by the half-row mirror
+// or quad permutes.  Every lane ends with the whole row sum of head s / (16 / QH).
 template <int QH>
 __device__ __forceinline__ float row_scores(const float (&p)[QH], int s) {
-  const bool hi = (s & 8) != 0, b2 = (s & 4) != 0, b1 = (s & 2) != 0;
+  const bool hi = (s & 8) != 0, b2 = (s & 4) != 0;
   if constexpr (QH == 2) {
     float v = (hi ? p[1] : p[0]) + dpp_f<kDppRowRor8>(hi ? p[0] : p[1]);
     v += dpp_f<kDppHalfMirror>(v);
     v += dpp_f<kDppQuad2301>(v);
     v += dpp_f<kDppQuad1032>(v);
     return v;
-  } else if constexpr (QH == 4) {
+  } else {
+    static_assert(QH == 4, "2 or 4 query heads per KV head");
     const float a0 = (hi ? p[2] : p[0]) + dpp_f<kDppRowRor8>(hi ? p[0] : p[2]);
     const float a1 = (hi ? p[3] : p[1]) + dpp_f<kDppRowRor8>(hi ? p[1] : p[3]);
     float v = (b2 ? a1 : a0) + dpp_f<kDppHalfMirror>(b2 ? a0 : a1);
     v += dpp_f<kDppQuad1032>(v);
     v += dpp_f<kDppQuad2301>(v);
-    return v;
-  } else {
-    static_assert(QH == 8, "2, 4 or 8 query heads per KV head");
-    float A[4], B[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) A[i] = (hi ? p[i + 4] : p[i]) + dpp_f<kDppRowRor8>(hi ? p[i] : p[i + 4]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) B[i] = (b2 ? A[i + 2] : A[i]) + dpp_f<kDppHalfMirror>(b2 ? A[i] : A[i + 2]);
-    float v = (b1 ? B[1] : B[0]) + dpp_f<kDppQuad3210>(b1 ? B[0] : B[1]);
-    v += dpp_f<kDppQuad1032>(v);
     return v;
   }
 }
@@ -89,31 +79,23 @@ __device__ __forceinline__ void row_spread(float v, float (&out)[QH]) {
   out[0] = v;
   if constexpr (QH == 2) {
     out[1] = dpp_f<kDppRowRor0 + 8>(v);
-  } else if constexpr (QH == 4) {
+  } else {
     out[1] = dpp_f<kDppRowRor0 + 4>(v);
     out[2] = dpp_f<kDppRowRor0 + 8>(v);
     out[3] = dpp_f<kDppRowRor0 + 12>(v);
-  } else {
-    out[1] = dpp_f<kDppRowRor0 + 2>(v);
-    out[2] = dpp_f<kDppRowRor0 + 4>(v);
-    out[3] = dpp_f<kDppRowRor0 + 6>(v);
-    out[4] = dpp_f<kDppRowRor0 + 8>(v);
-    out[5] = dpp_f<kDppRowRor0 + 10>(v);
-    out[6] = dpp_f<kDppRowRor0 + 12>(v);
-    out[7] = dpp_f<kDppRowRor0 + 14>(v);
   }
 }
 
 template <int D, int C, int QH, bool WIDE>
-__global__ __launch_bounds__(group_waves<QH>() * 64) void attn_group_kernel(AttnArgs a, const float* __restrict__ rope,
-                                                                            int wpl) {
-  constexpr int kGW = group_waves<QH>();
+__global__ __launch_bounds__(kGroupWaves * 64) void attn_group_kernel(AttnArgs a, const float* __restrict__ rope,
+                                                                      int wpl) {
+  constexpr int kGW = kGroupWaves;
   constexpr int LPH = 16 / QH;    // lanes of a row per head after the row sum
   constexpr int NG = D / C;       // groups per head
   constexpr int HALF = D / 2;
   constexpr int NCH = D / 8;      // 16-byte chunks per codeword row in LDS
   static_assert(D == 128 && HALF == 64 && NCH * 16 == 256, "the grouped kernel is compiled for d = 128");
-  static_assert(kGroupQuad == 4 && (QH == 2 || QH == 4 || QH == 8), "2, 4 or 8 heads per KV head, four waves per range");
+  static_assert(kGroupQuad == 4 && (QH == 2 || QH == 4), "2 or 4 heads per KV head, four waves per range");
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* kl = (_Float16*)smem;                                   // K, V slices [256][D/8][8]
   float* phbuf = (float*)(smem + (size_t)2 * kCodes * D * 2);       // [kGW][2][kGPh]
@@ -442,7 +424,7 @@ __global__ __launch_bounds__(group_waves<QH>() * 64) void attn_group_kernel(Attn
 
 template <int D, int C, int QH, bool WIDE>
 hipError_t launch_attn_group_t(const AttnArgs& a, hipStream_t s) {
-  constexpr int kGW = group_waves<QH>();
+  constexpr int kGW = kGroupWaves;
   constexpr size_t lds = group_lds_bytes<D, kGW>();
   static std::atomic<uint64_t> attr_set{0};
   hipError_t ea = once_per_device(attr_set, [&] {
@@ -475,12 +457,10 @@ hipError_t launch_group_heads(const AttnArgs& a, int c, bool wide, hipStream_t s
 }  // namespace
 
 bool attn_group_supported(int d, int c, int heads) {
-  return d == 128 && (c == 8 || c == 16 || c == 32) && (heads == 2 || heads == 4 || heads == 8);
+  return d == 128 && (c == 8 || c == 16 || c == 32) && (heads == 2 || heads == 4);
 }
 
-int attn_group_waves_per_group(int heads) {
-  return heads == 8 ? group_waves<8>() : heads == 4 ? group_waves<4>() : group_waves<2>();
-}
+int attn_group_waves_per_group() { return kGroupWaves; }
 
 hipError_t launch_attn_group(const AttnArgs& a, hipStream_t s) {
   const int c = a.G / a.Tc;
@@ -490,8 +470,7 @@ hipError_t launch_attn_group(const AttnArgs& a, hipStream_t s) {
   const bool wide = (uint64_t)a.n_index_pages * page_bytes > 0xFFFFFFFFull || a.n_index_pages > (1 << 24) ||
                     page_bytes >= (1u << 24);
   if (heads == 2) return launch_group_heads<2>(a, c, wide, s);
-  if (heads == 4) return launch_group_heads<4>(a, c, wide, s);
-  return launch_group_heads<8>(a, c, wide, s);
+  return launch_group_heads<4>(a, c, wide, s);
 }
 
 }  // namespace lvq

@@ -177,13 +177,13 @@ int attn_waves_per_group();   // waves per decode-attention workgroup
 int merge_max_records();      // candidate partial records per (b, query head) the merge accepts
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
-// Grouped-query decode: the 2, 4 or 8 query heads of a KV head share each key's
+// Grouped-query decode: the 2 or 4 query heads of a KV head share each key's
 // dequantisation and rotation; a range of a KV head's work list belongs to a quad of
 // kGroupQuad waves, each of which writes a record of Hq / H rows per sequence (n_rec =
 // n_waves + kGroupQuad * B per list).
 constexpr int kGroupQuad = 4;
 bool attn_group_supported(int d, int c, int heads);
-int attn_group_waves_per_group(int heads);   // waves per grouped-decode workgroup
+int attn_group_waves_per_group();   // waves per grouped-decode workgroup
 hipError_t launch_attn_group(const AttnArgs& a, hipStream_t s);
 
 }  // namespace lvq

@@ -153,16 +153,15 @@ def test_workspace_query_refuses_malformed_shapes(L):
 
 
 def test_workspace_size_of_grouped_decode(L):
-    """At 2, 4 and 8 query heads per KV head (d = 128) the workspace holds the larger of the
+    """At 2 and 4 query heads per KV head (d = 128) the workspace holds the larger of the
     per-head records (lvq_decode_scores keeps that kernel) and the grouped kernel's: records
-    [H][W + 4 B][g heads][d + 2] float32, W waves per KV head in whole workgroups of 16
-    (8 at g = 8),
+    [H][W + 4 B][g heads][d + 2] float32, W waves per KV head in whole workgroups of 16,
     automatically 256 / H workgroups per KV head capped at about 4 tiles per quad of the
     largest work list; then the tile table [B + 1] int32."""
     from sub_bit_loop_amd import _abi
     for B, H, g, msl, ns, Wg, Wph in ((8, 4, 4, 32768, 0, 1024, 192), (1, 4, 4, 65536, 0, 1024, 192),
                                       (2, 1, 4, 100, 0, 32, 12), (3, 2, 4, 4096, 1000, 1008, 1008),
-                                      (8, 8, 2, 32768, 0, 512, 192), (8, 2, 8, 32768, 0, 1024, 192)):
+                                      (8, 8, 2, 32768, 0, 512, 192)):
         Hq = g * H
         s = shape(B=B, H=H, Hq=Hq, max_seq_len=msl, rope_max_len=msl + 1, max_pages=(msl + 7) // 8,
                   n_splits=ns)
@@ -170,6 +169,25 @@ def test_workspace_size_of_grouped_decode(L):
         per_head = Hq * (Wph + B) * 130 * 4 + (B + 1) * 4
         nbytes = _abi.lvq_decode_attn_workspace_bytes(s)
         assert nbytes == max(grouped, per_head), (B, H, msl, ns, nbytes, grouped, per_head)
+
+
+def test_workspace_size_of_multi_row_decode(L):
+    """At 8 and 16 query heads per KV head (d = 128) lvq_decode_attn runs on the multi-row
+    kernel: the workspace holds the larger of the per-head records and the multi-row
+    kernel's, records [H][W + B][16 rows][d + 2] float32 and first units [B + 1] int32 (one
+    16-row block per KV head), W waves per KV head in whole workgroups of 8: automatically
+    256 / H workgroups capped at about 4 tiles per wave of the largest work list
+    (B * (max_seq_len / 16 + 4) tiles)."""
+    from sub_bit_loop_amd import _abi
+    for B, H, g, msl, ns, Wr, Wph in ((8, 2, 8, 32768, 0, 1024, 192), (8, 1, 16, 32768, 0, 2048, 192),
+                                      (2, 1, 8, 100, 0, 8, 12), (3, 2, 8, 4096, 100, 104, 108)):
+        Hq = g * H
+        s = shape(B=B, H=H, Hq=Hq, max_seq_len=msl, rope_max_len=msl + 1, max_pages=(msl + 7) // 8,
+                  n_splits=ns)
+        rows = H * (Wr + B) * 16 * 130 * 4 + (B + 1) * 4
+        per_head = Hq * (Wph + B) * 130 * 4 + (B + 1) * 4
+        nbytes = _abi.lvq_decode_attn_workspace_bytes(s)
+        assert nbytes == max(rows, per_head), (B, H, g, msl, ns, nbytes, rows, per_head)
 
 
 def test_builder_validation(L):

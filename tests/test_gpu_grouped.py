@@ -1,6 +1,7 @@
 """GPU parity of grouped-query decode (2, 4 and 8 query heads per KV head, d = 128):
-lvq_decode_attn routes these shapes to the kernel that shares each key's dequantisation
-and rotation over the KV head's query heads.  Same tolerance as the per-head decode
+lvq_decode_attn routes 2 and 4 heads per KV head to the kernel that shares each key's
+dequantisation and rotation over the KV head's query heads, and 8 to the multi-row
+kernel (the heads as the rows of its matrix-core products).  Same tolerance as the per-head decode
 tests: max-abs <= 2e-3 over every output element, max-rel <= 1e-2 where |oracle| >= 0.2,
 lse within 1e-4.
 lvq_decode_scores keeps the per-head kernel on the same shapes, so the two kernels are
@@ -31,9 +32,9 @@ GROUPED = [  # config, lengths, H, query heads per KV head, T, Tc, G, n_sink, n_
     (69, [37, 300, 1000], 2, 2, 4, 4, 32, 4, 16),      # 2 heads per KV head, c = 8
     (70, [515, 0, 260], 3, 2, 4, 2, 32, 0, 64),        # 2 heads per KV head, c = 16, an empty slot
     (71, [1000, 8], 1, 2, 1, 1, 32, 8, 16),            # 2 heads per KV head, c = 32
-    (80, [37, 300, 1000], 1, 8, 4, 4, 32, 4, 16),      # 8 heads per KV head, c = 8
-    (81, [515, 0, 260], 2, 8, 4, 2, 32, 0, 64),        # 8 heads per KV head, c = 16, an empty slot
-    (82, [1000, 8], 1, 8, 1, 1, 32, 8, 16),            # 8 heads per KV head, c = 32
+    (80, [37, 300, 1000], 1, 8, 4, 4, 32, 4, 16),      # 8 heads per KV head (multi-row route), c = 8
+    (81, [515, 0, 260], 2, 8, 4, 2, 32, 0, 64),        # 8 heads per KV head (multi-row route), c = 16
+    (82, [1000, 8], 1, 8, 1, 1, 32, 8, 16),            # 8 heads per KV head (multi-row route), c = 32
 ]
 
 
@@ -101,8 +102,8 @@ def test_grouped_index_pool_beyond_4gib():
 @pytest.mark.parametrize("H,Hq", [(4, 16), (8, 16), (2, 16)])
 def test_grouped_decode_at_32k(H, Hq):
     """The benchmark's grouped shapes: B=8 sequences of 32768 tokens, 16 query heads over 8,
-    4 or 2 KV heads, d=128, T=4, Tc=4, G=32, 4 sink + 64 recent, shuffled pages, automatic
-    split.  The oracle checks every query head of sequences 0, 3 and 7 at two loop steps;
+    4 or 2 KV heads (grouped, grouped and multi-row routes), d=128, T=4, Tc=4, G=32, 4 sink
+    + 64 recent, shuffled pages, automatic split.  The oracle checks every query head of sequences 0, 3 and 7 at two loop steps;
     all 128 (b, head) outputs are compared with the per-head kernel."""
     plog.case(f"grouped decode at 32K: B=8 L=32768 H={H} Hq={Hq} d=128 T=4 Tc=4 G=32; "
               "oracle on sequences 0, 3, 7 (all heads), per-head kernel on all pairs")
