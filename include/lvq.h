@@ -352,7 +352,12 @@ int lvq_decode_scores(const uint16_t* q, const int32_t* page_table, const uint8_
  *                 key at all (prefix_len 0 and no new keys) gets out = 0, lse = -inf.
  *   out:          float32 [B][NQ][Hq][d]; lse: float32 [B][NQ][Hq] or NULL.
  *   ws:           lvq_rows_attn_workspace_bytes(shp) bytes.
- * Scores and the value sum run on float32 matrix cores (products exact in float32).
+ * Scores and the value sum run on the matrix cores at float32 precision: on coded tiles
+ * the float32 operands are split into float16 hi + lo parts and three (scores) or two
+ * (values) float16 products are summed in float32, each missing about 2^-20 of its
+ * value; bf16 tiles use float32 matrix instructions.  The split needs the rotated
+ * query values times scale * log2(e) and the rotated key values inside the float16
+ * range (|x| < 65504), next to the codebook range every decode kernel needs.
  * Supported: d = 128, c in {8, 16, 32}.
  */
 typedef struct lvq_rows_shape {
