@@ -87,23 +87,45 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
 // Chunk k of code x sits at slot k ^ (x mod 16) of the key slice (XOR swizzle): the 16
 // lanes that gather the same key chunk of random codes then spread over the LDS banks.
 // The value slice keeps slot = k; its gathers already read distinct chunks per lane.
+// The two slices are loaded by every thread's 2 x 8 sixteen-byte pieces at once, all in
+// flight together (one after another, each load's round trip would add up: about 30 us
+// for a workgroup), then converted and stored.
 template <int C>
-__device__ __forceinline__ void stage_slice_rows(const RowsArgs& a, int beta, int kv, int h, int tau,
-                                                 _Float16* dst) {
-  constexpr int NG = kD / C;
-  constexpr int NCH = kD / 8;
-  const uint16_t* src = a.codebooks + ((((size_t)beta * 2 + kv) * a.H + h) * NG) * ((size_t)a.Tc * kCodes * C);
-  for (int e = threadIdx.x * 8; e < kCodes * kD; e += kRW * 64 * 8) {
-    const int x = e / kD, k = (e % kD) / 8;
-    const int g = (8 * k) / C, i = (8 * k) % C;
-    const u16x8 v = *(const u16x8*)(src + (((size_t)g * a.Tc + tau) * kCodes + x) * C + i);
-    f16x8 o;
+struct RowSlices {
+  static constexpr int NG = kD / C;
+  static constexpr int NCH = kD / 8;
+  static constexpr int PER = kCodes * kD / 8 / (kRW * 64);   // pieces per thread and slice
+  static_assert(PER * kRW * 64 * 8 == kCodes * kD, "whole pieces per thread");
+  u16x8 v[2][PER];
+  __device__ __forceinline__ void load(const RowsArgs& a, int beta, int h, int tau) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) o[q] = (_Float16)bf2f(v[q]);
-    const int slot = kv == 0 ? (k ^ (x & (NCH - 1))) : k;
-    *(f16x8*)(dst + ((size_t)x * NCH + slot) * 8) = o;
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* src = a.codebooks + ((((size_t)beta * 2 + kv) * a.H + h) * NG) * ((size_t)a.Tc * kCodes * C);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = (threadIdx.x + i * kRW * 64) * 8;
+        const int x = e / kD, k = (e % kD) / 8;
+        const int g = (8 * k) / C, j = (8 * k) % C;
+        v[kv][i] = *(const u16x8*)(src + (((size_t)g * a.Tc + tau) * kCodes + x) * C + j);
+      }
+    }
   }
-}
+  __device__ __forceinline__ void store(_Float16* kdst, _Float16* vdst) const {
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = (threadIdx.x + i * kRW * 64) * 8;
+        const int x = e / kD, k = (e % kD) / 8;
+        f16x8 o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = (_Float16)bf2f(v[kv][i][q]);
+        const int slot = kv == 0 ? (k ^ (x & (NCH - 1))) : k;
+        *(f16x8*)((kv == 0 ? kdst : vdst) + ((size_t)x * NCH + slot) * 8) = o;
+      }
+    }
+  }
+};
 
 // max over the 16 lanes of a lane group (xor offsets stay inside the group)
 __device__ __forceinline__ float group16_max(float v) {
@@ -134,20 +156,23 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // Token-balanced work split, as in the decode kernel.  The work list of one (KV head,
 // row block) is the units of sequences 0..B-1 in order: one per coded tile (two pages),
 // then kBfCostR per virtual tile (the bf16 sink and recent tiles, then the new-key tiles
-// the block's rows can see).  Here a tile's cost is set by its 64 matrix instructions
-// whatever its source, so every tile is one unit (measured: heavier virtual tiles only
-// slowed the 512-token prefill).  The W waves of a list take equal contiguous ranges
-// [wg*total/W, (wg+1)*total/W) and write one partial record per (row, sequence their
-// range meets), at record wg + b of the list.
-constexpr int kBfCostR = 1;
+// the block's rows can see).  A virtual tile reads its keys and values from HBM through
+// dependent loads and runs float32 matrix instructions, so it costs about four coded
+// tiles on the float16 path; counted as one, a sequence's five sink and recent tiles fall
+// to one wave, which then finishes last (GQA decode at 32K: 61.3 against 55.3 us at 16
+// heads per KV head; the 512-token prefill is the same either way).  The W waves of a
+// list take equal contiguous ranges [wg*total/W, (wg+1)*total/W) and write one partial
+// record per (row, sequence their range meets), at record wg + b of the list.
+constexpr int kBfCostR = 4;
 struct RowSeq {
   int coded;   // coded tiles (= their units)
   int n_vt;    // virtual tiles
   int total;   // units
 };
-__device__ __forceinline__ RowSeq row_seq(const RowsArgs& a, int b, int n_new) {
-  const int L = min(max(a.prefix_len[b], 0), a.max_prefix);
-  const int qe = max(min(a.q_end[b] & ~7, L), 0);
+// from sequence b's prefix_len and q_end entries
+__device__ __forceinline__ RowSeq row_seq_of(const RowsArgs& a, int prefix_len, int q_end, int n_new) {
+  const int L = min(max(prefix_len, 0), a.max_prefix);
+  const int qe = max(min(q_end & ~7, L), 0);
   const int ns = min(a.n_sink, L);
   const int r0 = max(qe, a.n_sink);
   const int vt_lo = r0 / kKeys;
@@ -155,6 +180,9 @@ __device__ __forceinline__ RowSeq row_seq(const RowsArgs& a, int b, int n_new) {
   const int coded = a.n_index_pages > 0 ? ((qe >> 3) + 1) >> 1 : 0;
   const int n_vt = (ns > 0 ? 1 : 0) + (vt_hi - vt_lo) + n_new;
   return {coded, n_vt, coded + kBfCostR * n_vt};
+}
+__device__ __forceinline__ RowSeq row_seq(const RowsArgs& a, int b, int n_new) {
+  return row_seq_of(a, a.prefix_len[b], a.q_end[b], n_new);
 }
 __device__ __forceinline__ int range_lo(int wg, int total, int W) { return (int)((long)wg * total / W); }
 
@@ -183,12 +211,20 @@ void rows_kernel(RowsArgs a, int wph) {
   const int i_max = min(a.NQ - 1, (rb * kRows + kRows - 1) / g);
   const int n_new = a.k_new ? i_max / kKeys + 1 : 0;
 
+  // The lengths of the first 64 sequences are loaded before the slices (vector loads
+  // return in order: loaded after them, the scan below would wait for every slice piece).
+  const int b_first = min(lane, a.B - 1);
+  const int pl_first = a.prefix_len[b_first], qe_first = a.q_end[b_first];
+  __builtin_amdgcn_sched_barrier(0);   // keep the two length loads ahead of the slice loads
+  RowSlices<C> slices;
+  slices.load(a, beta, h, tau);
+
   // the list's length and (one wave per row block) the sequences' first units
   int* tstart = a.tile_start + (size_t)rb * (a.B + 1);
   int total = 0;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int bb = b0 + lane;
-    const int n = bb < a.B ? row_seq(a, bb, n_new).total : 0;
+    const int n = bb < a.B ? (b0 == 0 ? row_seq_of(a, pl_first, qe_first, n_new) : row_seq(a, bb, n_new)).total : 0;
     if (h == 0 && wg == 0) {
       const int incl = total + wave_incl_scan(n);
       if (bb < a.B) tstart[bb] = incl - n;
@@ -200,8 +236,7 @@ void rows_kernel(RowsArgs a, int wph) {
   const int w_lo = __builtin_amdgcn_readfirstlane(range_lo(wg, total, W));
   const int w_hi = __builtin_amdgcn_readfirstlane(range_lo(wg + 1, total, W));
 
-  stage_slice_rows<C>(a, beta, 0, h, tau, kl);
-  stage_slice_rows<C>(a, beta, 1, h, tau, vl);
+  slices.store(kl, vl);
   __syncthreads();
   if (w_lo == w_hi) return;
 
@@ -211,7 +246,7 @@ void rows_kernel(RowsArgs a, int wph) {
     int base = 0;
     for (int b0 = 0; b0 < a.B; b0 += 64) {
       const int bb = b0 + lane;
-      const int n = bb < a.B ? row_seq(a, bb, n_new).total : 0;
+      const int n = bb < a.B ? (b0 == 0 ? row_seq_of(a, pl_first, qe_first, n_new) : row_seq(a, bb, n_new)).total : 0;
       const int incl = base + wave_incl_scan(n);
       const uint64_t hit = __ballot(bb < a.B && incl - n <= w_lo && w_lo < incl);
       if (hit) {
