@@ -683,8 +683,14 @@ hipError_t launch_merge_records(const AttnArgs& m, int cap, int per_item, hipStr
 hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
   if (a.n_waves + 1 > kMergeMax || !a.tile_start || a.d > kMergeThreads || kMergeThreads % a.d) return hipErrorInvalidValue;
   const int items = a.B * (a.merge_rows ? a.NQ : 1) * a.Hq;
-  hipLaunchKernelGGL((merge_kernel<kMergeThreads, 8>), dim3(items), dim3(kMergeThreads),
-                     (size_t)(a.n_waves + 1) * 12, s, a, a.n_waves + 1);
+  // records an item meets: its sequence's share of the list's waves, plus two
+  const int per_item = a.n_waves / (a.B > 0 ? a.B : 1) + 2;
+  if (per_item > 8 * (kMergeThreads / a.d))
+    hipLaunchKernelGGL((merge_kernel<2 * kMergeThreads, 32>), dim3(items), dim3(2 * kMergeThreads),
+                       (size_t)(a.n_waves + 1) * 12, s, a, a.n_waves + 1);
+  else
+    hipLaunchKernelGGL((merge_kernel<kMergeThreads, 8>), dim3(items), dim3(kMergeThreads),
+                       (size_t)(a.n_waves + 1) * 12, s, a, a.n_waves + 1);
   return hipGetLastError();
 }
 
