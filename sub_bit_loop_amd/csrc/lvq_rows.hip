@@ -294,14 +294,22 @@ void rows_kernel(RowsArgs a, int wph) {
         const uint16_t* qv = a.q + (((size_t)b * a.NQ + qi) * a.Hq + hq) * D;
         const float* e0 = a.rope + (size_t)(pq / kKeys) * D;
         const float* e1 = a.rope + (size_t)(a.rope_tiles + pq % kKeys) * D;
+        // the lane's 16 query pairs and partners and their phases in 16-byte loads
+        // (qi and hq stay in range for a padding row; its values are replaced by zeros)
+        const u16x8 xq[2] = {((const u16x8*)(qv + 16 * kq))[0], ((const u16x8*)(qv + 16 * kq))[1]};
+        const u16x8 yq[2] = {((const u16x8*)(qv + HALF + 16 * kq))[0], ((const u16x8*)(qv + HALF + 16 * kq))[1]};
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          const int pr = 16 * kq + s;
-          const float c0 = e0[2 * pr], s0 = e0[2 * pr + 1], c1 = e1[2 * pr], s1 = e1[2 * pr + 1];
-          const float c = c0 * c1 - s0 * s1, sn = s0 * c1 + c0 * s1;
-          const float x = row_ok ? bf2f(qv[pr]) : 0.f, y = row_ok ? bf2f(qv[pr + HALF]) : 0.f;
-          qf[s] = (x * c - y * sn) * a.scale_log2e;
-          qf[16 + s] = (y * c + x * sn) * a.scale_log2e;
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const f32x4 p0 = ((const f32x4*)(e0 + 32 * kq))[s2], p1 = ((const f32x4*)(e1 + 32 * kq))[s2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int s = 2 * s2 + u;
+            const float c0 = p0[2 * u], s0 = p0[2 * u + 1], c1 = p1[2 * u], s1 = p1[2 * u + 1];
+            const float c = c0 * c1 - s0 * s1, sn = s0 * c1 + c0 * s1;
+            const float x = row_ok ? bf2f(xq[s >> 3][s & 7]) : 0.f, y = row_ok ? bf2f(yq[s >> 3][s & 7]) : 0.f;
+            qf[s] = (x * c - y * sn) * a.scale_log2e;
+            qf[16 + s] = (y * c + x * sn) * a.scale_log2e;
+          }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -624,16 +632,22 @@ void rows_kernel(RowsArgs a, int wph) {
             O[c8] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, O[c8], 0, 0, 0);
           }
         };
-        // two tiles per iteration, each prefetched into the other register set
+        // three tiles per iteration in three register sets, each tile's inputs loaded two
+        // tiles ahead (a tile's float16 products take less time than an index load from
+        // HBM takes to return; fetches past the range read page 0 and are not used)
         if (P_lo < P_hi) {
           CIn in0 = fetch(P_lo);
-          for (int P0 = P_lo;; P0 += 4) {
-            const CIn in1 = fetch(P0 + 2);
+          CIn in1 = fetch(P_lo + 2);
+          for (int P0 = P_lo;; P0 += 6) {
+            const CIn in2 = fetch(P0 + 4);
             coded_tile(P0, in0);
             if (P0 + 2 >= P_hi) break;
-            in0 = fetch(P0 + 4);
+            in0 = fetch(P0 + 6);
             coded_tile(P0 + 2, in1);
             if (P0 + 4 >= P_hi) break;
+            in1 = fetch(P0 + 8);
+            coded_tile(P0 + 4, in2);
+            if (P0 + 6 >= P_hi) break;
           }
         }
       }
