@@ -114,6 +114,7 @@ __global__ __launch_bounds__(kGroupWaves * 64) void attn_group_kernel(AttnArgs a
   const int b_first = min(lane, a.B - 1);
   const int len_first = a.seq_len[b_first];
   const int qe_first = a.q_end[b_first];
+  __builtin_amdgcn_sched_barrier(0);   // keep the two length loads ahead of the slice loads
   SliceStage<D, C, kGW * 64> slices;
   slices.load(a, beta, h, tau);
   int total = 0, n_first = 0, incl_first = 0;
