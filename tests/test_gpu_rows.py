@@ -225,3 +225,61 @@ def test_prefill_chunk_with_an_empty_prefix_and_single_queries():
         dc = to_dev(cache, max_seq_len=max(lengths) + NQ)
         ck, cv, q = _chunk(cfg, len(lengths), 4, NQ, 2, 128, 2)
         compare(gpu_rows(dc, cache, q, 0, ck, cv), oracle_rows(cache, q, 0, ck, cv), f"cfg={cfg}")
+
+
+def test_split_products_keep_float32_precision_on_a_sharp_softmax():
+    """Queries scaled by 8 (exact in bf16) make every score 8 times larger and the softmax
+    sharp.  One float16 product per score (relative error 2^-11 per product) would move
+    lse by 1e-2 or more here; the multi-row kernel's hi/lo split products (about 2^-21)
+    keep it within the decode tolerance of the oracle, on lvq_decode_attn's multi-row
+    route (16 query heads per KV head).  The difference to the per-head kernel's float32
+    arithmetic on the same call is recorded."""
+    from gpu_helpers import gpu_attn
+    plog.case("multi-row attention: queries x8 (sharp softmax), 16 query heads per KV head, split products")
+    cache = build_cache(83, 2, [700, 230], 1, 128, 4, 4, 32, 4, 16, Hq=16, books="random")
+    bits = cache.q.view(np.uint16).astype(np.uint32) << 16
+    cache.q = ((bits.view(np.float32) * np.float32(8.0)).view(np.uint32) >> 16).astype(np.uint16)
+    dc = to_dev(cache)
+    for t in (0, 3):
+        out, lse = gpu_attn(dc, t)
+        ro, rl = cache.oracle_attn(t)
+        o = out.cpu().numpy()
+        ok, mabs, mrel = attn_close(o, ro)
+        lerr = float(np.abs(lse.cpu().numpy() - rl).max())
+        o2, l2, _ = gpu_attn(dc, t, scores=True)
+        dph = float(np.abs(o - o2.cpu().numpy()).max())
+        plog.line(f"t={t}: max-abs {mabs:.3e} max-rel {mrel:.3e} (|ref| >= 0.2), lse max-abs {lerr:.3e}; "
+                  f"multi-row vs per-head kernel max-abs {dph:.3e}")
+        assert ok, f"t={t}: output outside tolerance (max-abs {mabs:.3e})"
+        assert lerr <= 1e-4, f"t={t}: lse error {lerr:.3e}"
+
+
+def test_multirow_decode_over_many_ragged_sequences():
+    """70 sequences with lengths U[1, 400], one KV head with 16 query heads (the multi-row
+    route of lvq_decode_attn): automatic, one-workgroup and 4000-wave splits all match the
+    oracle and agree closely with each other; the same split twice gives identical bits.
+    Short sequences are mostly bf16 sink and recent tiles, which the split weighs as four
+    coded tiles each, so ranges end inside them; the 4000-wave split gives most waves an
+    empty range and sequences many records (the deep merge)."""
+    from gpu_helpers import gpu_attn
+    plog.case("multi-row decode, B=70 lengths U[1,400], H=1 Hq=16, splits 0/8/4000")
+    rl_ = np.random.default_rng(synth.seed_for(84, synth.STREAM_LENGTHS))
+    lengths = synth.uniform_lengths(rl_, 70, 1, 400)
+    cache = build_cache(84, 70, lengths, 1, 128, 4, 4, 32, 4, 16, Hq=16, books="random", index="random")
+    dc = to_dev(cache)
+    t = 1
+    ro, rl = cache.oracle_attn(t)
+    outs = []
+    for S in (0, 8, 4000):
+        out, lse = gpu_attn(dc, t, n_splits=S)
+        o = out.cpu().numpy()
+        ok, mabs, mrel = attn_close(o, ro)
+        lerr = float(np.abs(lse.cpu().numpy() - rl).max())
+        plog.line(f"splits={S}: max-abs {mabs:.3e} max-rel {mrel:.3e} (|ref| >= 0.2), lse max-abs {lerr:.3e}")
+        assert ok, f"splits={S}: output outside tolerance (max-abs {mabs:.3e})"
+        assert lerr <= 1e-4, f"splits={S}: lse error {lerr:.3e}"
+        outs.append(o)
+    for o in outs[1:]:
+        np.testing.assert_allclose(o, outs[0], rtol=2e-5, atol=2e-6)
+    again, _ = gpu_attn(dc, t, n_splits=4000)
+    np.testing.assert_array_equal(again.cpu().numpy(), outs[2])
