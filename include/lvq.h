@@ -236,6 +236,13 @@ typedef struct lvq_attn_shape {
                              work list of lvq_rows_attn on the multi-row route);
                              0 = automatic (see lvq_decode_attn) */
   float scale;            /* softmax scale; 0 = 1/sqrt(d) */
+  uint32_t* rejected;     /* NULL, or a device uint32 the kernels add one to for every page-id
+                             lookup outside its pool (page_table entries outside
+                             [0, n_index_pages) within a sequence's coded range, bf16_table
+                             entries outside [0, n_bf16_pages) for its sink and recent
+                             tokens); those tokens are left out whether or not it is given.
+                             An entry read by several heads or waves counts once for each.
+                             The caller clears it; calls that share it add up. */
 } lvq_attn_shape;
 
 /* Workspace bytes of lvq_decode_attn / lvq_decode_scores for this shape: the
@@ -368,6 +375,8 @@ typedef struct lvq_rows_shape {
   int32_t n_splits;       /* waves per work list (a KV head's block of 16 rows), rounded up
                              to whole workgroups of 8; 0 = automatic */
   float scale;            /* softmax scale; 0 = 1/sqrt(d) */
+  uint32_t* rejected;     /* NULL, or a device uint32 counting page-id lookups outside their
+                             pool, as in lvq_attn_shape */
 } lvq_rows_shape;
 
 size_t lvq_rows_attn_workspace_bytes(const lvq_rows_shape* shp);

@@ -32,14 +32,14 @@ class AttnShape(ctypes.Structure):
     """Mirror of lvq_attn_shape."""
     _fields_ = [(n, _i32) for n in ("B", "H", "Hq", "d", "T", "Tc", "G", "n_sink", "max_pages",
                                    "bf16_row", "n_index_pages", "n_bf16_pages", "max_seq_len",
-                                   "rope_max_len", "n_splits")] + [("scale", _f32)]
+                                   "rope_max_len", "n_splits")] + [("scale", _f32), ("rejected", _vp)]
 
 
 class RowsShape(ctypes.Structure):
     """Mirror of lvq_rows_shape."""
     _fields_ = [(n, _i32) for n in ("B", "NQ", "H", "Hq", "d", "T", "Tc", "G", "n_sink", "max_pages",
                                    "bf16_row", "n_index_pages", "n_bf16_pages", "max_prefix",
-                                   "rope_max_len", "n_splits")] + [("scale", _f32)]
+                                   "rope_max_len", "n_splits")] + [("scale", _f32), ("rejected", _vp)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -306,10 +306,22 @@ def lvq_rope_tables(max_len: int, d: int, base: float = 10000.0, device="cuda") 
     return tab
 
 
+def _counter_ptr(rejected):
+    """Device address of an optional int32/uint32 counter tensor (one element), or None."""
+    if rejected is None:
+        return None
+    _dev(rejected, "rejected", (torch.int32,), 1)
+    if rejected.numel() < 1:
+        raise ValueError("rejected must hold one element")
+    return rejected.data_ptr()
+
+
 def make_shape(B, H, Hq, d, T, Tc, G, n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages,
-               max_seq_len, rope_max_len, n_splits=0, scale=0.0) -> AttnShape:
+               max_seq_len, rope_max_len, n_splits=0, scale=0.0, rejected=None) -> AttnShape:
+    """rejected: None, or a one-element int32 device tensor that the kernels add one to for
+    every page-id lookup outside its pool (the caller zeroes it)."""
     return AttnShape(B, H, Hq, d, T, Tc, G, n_sink, max_pages, bf16_row, n_index_pages,
-                     n_bf16_pages, max_seq_len, rope_max_len, n_splits, scale)
+                     n_bf16_pages, max_seq_len, rope_max_len, n_splits, scale, _counter_ptr(rejected))
 
 
 def lvq_decode_attn_workspace_bytes(shp: AttnShape) -> int:
@@ -548,6 +560,6 @@ def lvq_rows_attn(q, page_table, index_pages, bf16_pages, bf16_table, codebooks,
 
 
 def make_rows_shape(B, NQ, H, Hq, d, T, Tc, G, n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages,
-                    max_prefix, rope_max_len, n_splits=0, scale=0.0) -> RowsShape:
+                    max_prefix, rope_max_len, n_splits=0, scale=0.0, rejected=None) -> RowsShape:
     return RowsShape(B, NQ, H, Hq, d, T, Tc, G, n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages,
-                     max_prefix, rope_max_len, n_splits, scale)
+                     max_prefix, rope_max_len, n_splits, scale, _counter_ptr(rejected))

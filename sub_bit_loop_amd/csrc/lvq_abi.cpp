@@ -250,6 +250,7 @@ lvq_rows_shape rows_shape_of(const lvq_attn_shape& s) {
   r.n_sink = s.n_sink; r.max_pages = s.max_pages; r.bf16_row = s.bf16_row;
   r.n_index_pages = s.n_index_pages; r.n_bf16_pages = s.n_bf16_pages;
   r.max_prefix = s.max_seq_len; r.rope_max_len = s.rope_max_len; r.n_splits = s.n_splits; r.scale = s.scale;
+  r.rejected = s.rejected;
   return r;
 }
 
@@ -301,6 +302,7 @@ int run_attn(const uint16_t* q, const int32_t* page_table, const uint8_t* index_
   a.out = out;
   a.lse = lse;
   a.scores = scores;
+  a.rejected = s.rejected;
   a.t = t;
   a.B = s.B;
   a.H = s.H;
@@ -678,6 +680,7 @@ int lvq_rows_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
   a.q_end = q_end;
   a.rope = rope_tab;
   a.part = (float*)ws;
+  a.rejected = s.rejected;
   a.t = t;
   a.B = s.B;
   a.NQ = s.NQ;

@@ -269,7 +269,9 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
 #pragma unroll
         for (int k = 0; k < kPtBatch / 64; ++k) {
           const int q = P + k * 64 + lane;
-          ptl[k * 64 + lane] = (q < P_hi && v[k] >= 0 && v[k] < a.n_index_pages) ? v[k] : -1;
+          const bool in_pool = v[k] >= 0 && v[k] < a.n_index_pages;
+          note_rejected(a.rejected, q < P_hi && !in_pool);
+          ptl[k * 64 + lane] = (q < P_hi && in_pool) ? v[k] : -1;
         }
       };
       // everything a lane loads for the tile starting at page P0
@@ -380,6 +382,7 @@ void attn_kernel(AttnArgs a, const float* __restrict__ rope, int wph) {
         if (p >= lo && p < hi) {
           const int slot = sink_tile ? 0 : 1 + (p >> 3) - (qe >> 3);
           const int pg = slot < a.bf16_row ? a.bf16_table[(size_t)b * a.bf16_row + slot] : -1;
+          note_rejected(a.rejected, !(pg >= 0 && pg < a.n_bf16_pages));
           if (pg >= 0 && pg < a.n_bf16_pages)
             krow = a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2) * kPage + (p & 7)) * D;
         }

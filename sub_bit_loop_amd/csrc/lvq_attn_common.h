@@ -22,6 +22,14 @@ constexpr int kPtBatch = 128;      // page ids staged in LDS per wave at a time
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Page ids read outside their pool ([0, n_index_pages) for coded pages, [0, n_bf16_pages)
+// for bf16 pages) are skipped: those tokens are left out.  When the caller passes a
+// counter, every such lookup also adds one to it (a lookup is one lane reading one table
+// entry, so an entry read by several heads or waves counts once for each).
+__device__ __forceinline__ void note_rejected(unsigned* counter, bool bad) {
+  if (counter && bad) atomicAdd(counter, 1u);
+}
+
 // 16-byte LDS read at a byte address.  The attention kernel declares no static LDS, so
 // its dynamic LDS starts at address 0 and the code-table offsets are LDS addresses.
 typedef const f16x8 __attribute__((address_space(3)))* lds_f16x8_ptr;

@@ -100,6 +100,7 @@ struct RowsArgs {
   const int32_t* q_end;       // [B]
   const float* rope;
   float* part;                // [H * n_rb][n_rec][16 rows][d + 2]
+  unsigned* rejected;         // optional counter of page-id lookups outside their pool, or null
   int t, B, NQ, H, Hq, d, T, Tc, G;
   int n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages, max_prefix, rope_tiles;
   int n_rb;                   // row blocks of 16 per KV head
@@ -157,6 +158,7 @@ struct AttnArgs {
   float* out;                 // [B][Hq][d]
   float* lse;                 // [B][Hq] or null
   float* scores;              // [B][Hq][max_seq_len] or null (probe)
+  unsigned* rejected;         // optional counter of page-id lookups outside their pool, or null
   int t, B, H, Hq, d, T, Tc, G;
   int n_sink, max_pages, bf16_row, n_index_pages, n_bf16_pages, max_seq_len, rope_tiles;
   int n_waves;                // waves per work list (token-balanced ranges)

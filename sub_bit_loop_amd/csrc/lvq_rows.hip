@@ -62,6 +62,14 @@ constexpr size_t rows_lds_bytes() {
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Page ids read outside their pool ([0, n_index_pages) for coded pages, [0, n_bf16_pages)
+// for bf16 pages) are skipped: those tokens are left out.  When the caller passes a
+// counter, every such lookup also adds one to it (a lookup is one lane reading one table
+// entry, so an entry read by several heads or waves counts once for each).
+__device__ __forceinline__ void note_rejected(unsigned* counter, bool bad) {
+  if (counter && bad) atomicAdd(counter, 1u);
+}
+
 // x = hi + lo + e with hi, lo float16 (hi the nearest float16 to x, lo the nearest to the
 // exact float32 remainder x - hi), so |e| <= 2^-11 |x - hi| <= 2^-22 |x| where no lo is
 // subnormal.  Products of float16 operands are exact in the MFMA's float32 accumulation:
@@ -476,6 +484,7 @@ void rows_kernel(RowsArgs a, int wph) {
             if (p < lo || p >= hi) return nullptr;
             const int slot = sink_tile ? 0 : 1 + (p >> 3) - (qe >> 3);
             const int pg = slot < a.bf16_row ? bt[slot] : -1;
+            note_rejected(a.rejected, pg < 0 || pg >= a.n_bf16_pages);
             if (pg < 0 || pg >= a.n_bf16_pages) return nullptr;
             return a.bf16_pages + (((((size_t)pg * a.T + a.t) * a.H + h) * 2) * kPage + (p & 7)) * D;
           };
@@ -509,7 +518,9 @@ void rows_kernel(RowsArgs a, int wph) {
 #pragma unroll
           for (int k = 0; k < kPtR / 64; ++k) {
             const int q = P + k * 64 + lane;
-            ptl[k * 64 + lane] = (q < P_hi && v[k] >= 0 && v[k] < a.n_index_pages) ? v[k] : -1;
+            const bool in_pool = v[k] >= 0 && v[k] < a.n_index_pages;
+            note_rejected(a.rejected, q < P_hi && !in_pool);
+            ptl[k * 64 + lane] = (q < P_hi && in_pool) ? v[k] : -1;
           }
           asm volatile("" ::: "memory");
         };

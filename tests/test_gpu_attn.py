@@ -291,3 +291,43 @@ def test_mixed_serving_batch_sampled():
             check(out, lse, ro, rl, f"T={T} t={t}", pairs=pairs)
         del dc
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("route,H,Hq", [("per-head", 2, 2), ("grouped", 2, 8), ("multi-row", 1, 16)])
+def test_out_of_pool_page_ids_are_skipped_and_counted(route, H, Hq):
+    """A coded page-table entry outside [0, n_index_pages) and a bf16-table entry outside
+    [0, n_bf16_pages) are skipped by every decode route (their tokens are left out); with a
+    counter in the shape each such lookup adds one to it.  On clean tables the counter stays
+    0, and giving it never changes the output bits."""
+    plog.case(f"out-of-pool page ids, {route} route (H={H}, Hq={Hq}): counted, skipped, output unchanged")
+    cache = build_cache(85, 2, [300, 520], H, 128, 4, 4, 32, 4, 16, Hq=Hq, books="random", index="random")
+    dc = to_dev(cache)
+    t = 1
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    clean, clean_lse = gpu_attn(dc, t)
+    got, got_lse = gpu_attn(dc, t, rejected=counter)
+    assert int(counter.item()) == 0
+    np.testing.assert_array_equal(got.cpu().numpy(), clean.cpu().numpy())
+    np.testing.assert_array_equal(got_lse.cpu().numpy(), clean_lse.cpu().numpy())
+    ro, rl = cache.oracle_attn(t)
+    check(got, got_lse, ro, rl, "clean tables")
+
+    # sequence 1: coded pages 3..5 point past the pool; sequence 0: its first recent page is missing
+    pt = dc.page_table.clone()
+    pt[1, 3:6] = dc.index_pages.shape[0] + 7
+    bt = dc.bf16_table.clone()
+    bt[0, 1] = -1
+    bad = dataclasses.replace(dc, page_table=pt, bf16_table=bt)
+    plain, plain_lse = gpu_attn(bad, t)
+    counter.zero_()
+    got, got_lse = gpu_attn(bad, t, rejected=counter)
+    n = int(counter.item())
+    plog.line(f"planted: 3 coded pages of sequence 1, 1 recent bf16 page of sequence 0 -> {n} rejected lookups")
+    assert n > 0
+    np.testing.assert_array_equal(got.cpu().numpy(), plain.cpu().numpy())
+    assert np.isfinite(got.cpu().numpy()).all()
+    # the skipped coded pages of sequence 1 leave sequence 0's output as it was
+    only1 = dataclasses.replace(dc, page_table=pt)
+    o1, _ = gpu_attn(only1, t)
+    np.testing.assert_array_equal(o1.cpu().numpy()[0], clean.cpu().numpy()[0])
+    assert not np.array_equal(o1.cpu().numpy()[1], clean.cpu().numpy()[1])
