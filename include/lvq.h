@@ -41,7 +41,9 @@
  *    LVQ_EDEVICE: a HIP launch error.
  *  - Device-side indices (page ids, page-table entries) are range-checked in
  *    the kernels: an out-of-range id is skipped (its tokens are treated as
- *    absent / its rows are not written) instead of being dereferenced.
+ *    absent / its rows are not written) instead of being dereferenced.  The
+ *    attention calls count such lookups in a caller's device counter when the
+ *    shape names one (lvq_attn_shape.rejected, lvq_rows_shape.rejected).
  *  - Codebook values must lie in the float16 range (|x| < 65504): the decode
  *    kernel stages the step-t slice in LDS as float16, which holds every such
  *    bfloat16 value exactly up to float16 subnormals.
