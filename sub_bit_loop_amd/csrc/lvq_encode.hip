@@ -418,11 +418,15 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
         b2 = key_min3(key_max(lo1, hi1), lo2, hi2);
       }
       const bool owner = own == b1;
-      // Float32 error bound for two expanded distances (33 or 17 rounded terms, each
-      // sum bounded by S = (|x| + max|C|)^2, plus the rounded |C|^2) and the six
-      // truncated key bits; the approximate square root only enters the bound.
-      const float S = xx + cmax2 + 2.f * __builtin_amdgcn_sqrtf(xx * cmax2);
-      const float tol = 80.f * 5.9604645e-8f * S + 3.0517578e-5f * fabsf(b1);
+      // Float32 error bound for the two distances and the six truncated key bits.  A
+      // distance is |C_k|^2, rounded once, plus G exact products summed in float32: at
+      // most G + 2 roundings of sums whose magnitudes stay below |C_k|^2 + 2 |x| |C_k|
+      // <= S = max|C|^2 + 2 |x| max|C|, so each is within (G + 2) u S (u = 2^-24); the
+      // tolerance takes 1.2 times that for two distances.  The approximate square
+      // root only enters the bound.
+      constexpr float kTolU = 2.4f * (G + 2);
+      const float S = cmax2 + 2.f * __builtin_amdgcn_sqrtf(xx * cmax2);
+      const float tol = kTolU * 5.9604645e-8f * S + 3.0517578e-5f * fabsf(b1);
       const bool need_exact = ok && !(b2 - b1 > tol);
       uint8_t* o = nullptr;   // this lane's destination byte (vector col)
       if constexpr (kDenseDst) {
