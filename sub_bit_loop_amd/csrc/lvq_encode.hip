@@ -33,7 +33,7 @@
 //    (block, head); the workgroups that read the other halves of the same
 //    128-byte cache rows run on the same XCD at the same time, and the waves of a
 //    workgroup meet at a barrier every two tiles, so a row line stays in L2 until
-//    its readers have taken it (the input is read from memory about 1.2-1.3 times).
+//    its readers have taken it (the input is read from memory about 1.1-1.3 times).
 #include "lvq_internal.h"
 
 #include <atomic>
