@@ -62,7 +62,10 @@ EDGE = [  # config, B, lengths, H, Hq, d, T, Tc, G, n_sink, n_recent
     (36, 1, [600], 1, 1, 64, 4, 4, 32, 8, 8),             # d = 64, n_sink = 8, c = 8
     (37, 3, [0, 45, 0], 2, 2, 128, 4, 4, 32, 4, 16),      # empty batch slots: out 0, lse -inf
     (38, 3, [45, 0, 20], 1, 16, 128, 4, 4, 32, 4, 16),    # the same on the multi-row route (GQA 16)
-    (72, 3, [45, 0, 20], 1, 8, 128, 4, 4, 32, 4, 16),     # the same on the grouped route (GQA 8)
+    (72, 3, [45, 0, 20], 1, 4, 128, 4, 4, 32, 4, 16),     # the same on the grouped route (GQA 4)
+    (73, 3, [45, 0, 20], 1, 8, 128, 4, 4, 32, 4, 16),     # the same on the multi-row route at GQA 8
+    (74, 2, [200, 333], 2, 2, 64, 4, 2, 32, 4, 16),       # d = 64 with c = 16
+    (75, 2, [129, 64], 2, 4, 128, 4, 4, 32, 4, 16),       # grouped route at GQA 2, ragged
 ]
 
 
