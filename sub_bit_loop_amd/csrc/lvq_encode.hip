@@ -422,11 +422,15 @@ void encode_kernel(EncodeArgs a0, int n_items, LayersArg<MODE> layers) {
       // distance is |C_k|^2, rounded once, plus G exact products summed in float32: at
       // most G + 2 roundings of sums whose magnitudes stay below |C_k|^2 + 2 |x| |C_k|
       // <= S = max|C|^2 + 2 |x| max|C|, so each is within (G + 2) u S (u = 2^-24); the
-      // tolerance takes 1.2 times that for two distances.  The approximate square
-      // root only enters the bound.
+      // tolerance takes 1.2 times that for two distances.  Products or sums below the
+      // float32 normal range may be flushed to zero, an absolute error under 2^-126
+      // per term: kTolAbs covers G + 2 of them per distance, so vectors of tiny
+      // magnitude always go to the float64 pass (as do those whose S overflows, where
+      // the tolerance is infinite).  The approximate square root only enters the bound.
       constexpr float kTolU = 2.4f * (G + 2);
+      constexpr float kTolAbs = 2.f * (G + 2) * 1.17549435e-38f;
       const float S = cmax2 + 2.f * __builtin_amdgcn_sqrtf(xx * cmax2);
-      const float tol = kTolU * 5.9604645e-8f * S + 3.0517578e-5f * fabsf(b1);
+      const float tol = kTolU * 5.9604645e-8f * S + (3.0517578e-5f * fabsf(b1) + kTolAbs);
       const bool need_exact = ok && !(b2 - b1 > tol);
       uint8_t* o = nullptr;   // this lane's destination byte (vector col)
       if constexpr (kDenseDst) {

@@ -135,6 +135,32 @@ def test_encode_zero_vectors_and_zero_codeword():
     np.testing.assert_array_equal(got, ref.idx)
 
 
+@pytest.mark.parametrize("e", [-70, -60, 60, 64])
+@pytest.mark.parametrize("Tc,G,d", [(2, 16, 64), (4, 32, 128)])
+def test_encode_extreme_magnitudes(e, Tc, G, d):
+    """Keys, values and codewords all scaled by 2^e (exact in bf16).  At 2^-70 the products
+    fall below the float32 normal range (they may be flushed), at 2^-60 some of them do,
+    at 2^60 some squared norms and at 2^64 all of them overflow float32.  The indices must
+    still be the float64 nearest codeword: the float32 decision is trusted only where its
+    error bound holds, and the float64 pass decides the rest."""
+    T, N, H = 4, 96, 1
+    plog.case(f"encode extreme magnitudes x 2^{e}: T={T} Tc={Tc} G={G} d={d} N={N} H={H}")
+    rng = np.random.default_rng(synth.seed_for(9, synth.STREAM_K))
+    sc = synth.channel_scales(rng, H, d)
+    kv = synth.gen_kv(rng, T, N, H, d, sc)
+    samp = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(synth.gen_kv(rng, T, 1024, H, d, sc)))
+    books = synth.codebooks_from_samples(samp, Tc, G, 91)                  # bf16 bits [nblk][H][ng][Tc][256][c]
+    scale = np.float32(2.0 ** e)
+    kv_s = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(kv)) * scale)
+    cb_s = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(np.stack([books, books], axis=1)) * scale)
+    assert np.isfinite(synth.bf16_bits_to_f32(kv_s)).all() and np.isfinite(synth.bf16_bits_to_f32(cb_s)).all()
+    got = gpu_encode(kv_s, cb_s, 0, T, Tc, G)
+    ref = orc.encode(kv_s, cb_s, 0, T, Tc, G)
+    n_exact = int((got == ref.idx).sum())
+    plog.line(f"{got.size} vectors, {n_exact} bit-exact")
+    np.testing.assert_array_equal(got, ref.idx)
+
+
 @pytest.mark.parametrize("Tc,G", [(4, 32), (2, 16)])
 def test_encode_full_size_slab(Tc, G):
     """Prefill-encode shape: T=4 steps x 32768 tokens x 16 heads x d=128, the whole tensor
