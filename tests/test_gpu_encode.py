@@ -57,6 +57,8 @@ CASES = [  # T, Tc, G, d, N, H
     (4, 4, 16, 64, 72, 1),      # c = 4
     (4, 1, 16, 64, 33, 1),      # c = 16, G = 16
     (2, 2, 32, 64, 17, 2),      # d = 64, c = 16
+    (4, 4, 32, 128, 1, 3),      # a single token, an odd head count
+    (4, 2, 16, 128, 65, 5),     # five heads (no power of two), one token past two tiles
 ]
 
 

@@ -55,6 +55,23 @@ def test_builder_matches_oracle(T, Tc, G, S, H, d, n_iter):
     _compare(out[:, 0], ref, [(b, h, g) for b in range(nblk) for h in range(H) for g in range(ng)])
 
 
+@pytest.mark.parametrize("e", [-70, 60])
+def test_builder_extreme_magnitudes(e):
+    """Samples scaled by 2^e (exact in bf16): at 2^-70 the encoder's float32 products fall
+    below the normal range, at 2^60 its squared norms reach float32 overflow; the
+    assignment must still be the float64 nearest center, so the books stay bit-exact."""
+    T, Tc, G, S, H, d, n_iter = 4, 2, 16, 400, 1, 64, 3
+    print(f"\ncase build extreme magnitudes x 2^{e}", flush=True)
+    bits, rng = _samples(63, T, S, H, d)
+    bits = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(bits) * np.float32(2.0 ** e))
+    assert np.isfinite(synth.bf16_bits_to_f32(bits)).all()
+    nblk, ng = T // Tc, d // (G // Tc)
+    draws = rng.random((nblk, H, ng, 256))
+    out = _gpu_build(bits, draws, 0, T, Tc, G, n_iter)
+    ref = orc.build_codebooks(bits, draws, Tc, G, n_iter)
+    _compare(out[:, 0], ref, [(b, h, g) for b in range(nblk) for h in range(H) for g in range(ng)])
+
+
 def test_builder_few_samples_and_v_half():
     """S < 256: the seeding runs out of distinct samples (every D^2 reaches 0 and the uniform
     fallback repeats samples); only the selected half (V) is written."""
