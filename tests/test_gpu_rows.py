@@ -156,6 +156,21 @@ def test_rows_split_count_does_not_change_the_result():
         compare(gpu_rows(dc, cache, q, 2, ck, cv, n_splits=n), ref, f"splits={n}")
 
 
+def test_long_chunk_over_short_prefixes_sampled():
+    """A chunk much longer than its prefixes: 700 new tokens over prefixes of 100 and 37
+    tokens (GQA x2, two row blocks per query position band), so most keys a row sees are
+    the chunk's own, causal over many tiles; sampled query positions at the tile and
+    row-block edges and the last one, every head."""
+    plog.case("multi-row attention: prefill chunk 700 over prefixes [100, 37]")
+    NQ = 700
+    cache = build_cache(49, 2, [100, 37], 1, 128, 4, 4, 32, 4, 16, Hq=2, books="random")
+    dc = to_dev(cache, max_seq_len=100 + NQ)
+    ck, cv, q = _chunk(49, 2, 4, NQ, 1, 128, 2)
+    got = gpu_rows(dc, cache, q, 3, ck, cv)
+    ref = oracle_rows(cache, q, 3, ck, cv, queries=(0, 1, 7, 8, 15, 16, 63, 64, 255, 256, 511, 512, 698, 699))
+    compare(got, ref, "t=3")
+
+
 def test_prefill_chunk_at_32k_sampled():
     """512 new tokens over a 32768-token coded prefix (Ouro-shaped head, 16 heads, MHA), the
     launch the bench times; the oracle checks eight query positions of four heads."""
