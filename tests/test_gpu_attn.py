@@ -336,3 +336,24 @@ def test_out_of_pool_page_ids_are_skipped_and_counted(route, H, Hq):
     o1, _ = gpu_attn(only1, t)
     np.testing.assert_array_equal(o1.cpu().numpy()[0], clean.cpu().numpy()[0])
     assert not np.array_equal(o1.cpu().numpy()[1], clean.cpu().numpy()[1])
+
+
+@pytest.mark.parametrize("route,H,Hq", [("per-head", 2, 2), ("grouped", 2, 8), ("multi-row", 1, 16)])
+def test_query_positions_other_than_the_length(route, H, Hq):
+    """The query is rotated at pos[b], which the decode call takes as its own input: here
+    one sequence at its length, one 500 positions beyond it and one at position 7, below
+    most of its keys (attention is limited by seq_len only).  Each route must rotate the
+    query at pos and each key at its own position."""
+    plog.case(f"attention query positions other than the length, {route} route (H={H}, Hq={Hq})")
+    lengths = [300, 261, 150]
+    cache = build_cache(78, 3, lengths, H, 128, 4, 4, 32, 4, 16, Hq=Hq, books="random", index="random")
+    cache.pos = np.asarray([300, 761, 7], dtype=np.int32)
+    dc = to_dev(cache)
+    for t in (0, 3):
+        out, lse = gpu_attn(dc, t)
+        ro, rl = cache.oracle_attn(t)
+        check(out, lse, ro, rl, f"t={t}")
+    # the same cache with pos = seq_len gives another result (the position is really used)
+    base = dataclasses.replace(cache, pos=cache.seq_len.copy())
+    ob, _ = gpu_attn(to_dev(base), 3)
+    assert np.abs(ob.cpu().numpy()[1:] - out.cpu().numpy()[1:]).max() > 1e-3
