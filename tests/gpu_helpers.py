@@ -47,15 +47,16 @@ def to_dev(cache, dev="cuda", max_seq_len: int | None = None, rope_base: float =
                     lvq.lvq_rope_tables(rml, cache.d, rope_base, device=dev), rml, msl)
 
 
-def shape_of(dc: DevCache, n_splits: int = 0, rejected=None) -> lvq.AttnShape:
+def shape_of(dc: DevCache, n_splits: int = 0, rejected=None, scale: float = 0.0) -> lvq.AttnShape:
     c = dc.host
     return lvq.make_shape(c.B, c.H, c.Hq, c.d, c.T, c.Tc, c.G, c.n_sink, dc.page_table.shape[1],
                           dc.bf16_table.shape[1], dc.index_pages.shape[0], dc.bf16_pages.shape[0],
-                          dc.max_seq_len, dc.rope_max_len, n_splits, rejected=rejected)
+                          dc.max_seq_len, dc.rope_max_len, n_splits, scale=scale, rejected=rejected)
 
 
-def gpu_attn(dc: DevCache, t: int, n_splits: int = 0, scores: bool = False, q=None, rejected=None):
-    shp = shape_of(dc, n_splits, rejected)
+def gpu_attn(dc: DevCache, t: int, n_splits: int = 0, scores: bool = False, q=None, rejected=None,
+             scale: float = 0.0):
+    shp = shape_of(dc, n_splits, rejected, scale)
     qq = dc.q[t] if q is None else q
     fn = lvq.lvq_decode_scores if scores else lvq.lvq_decode_attn
     res = fn(qq.contiguous(), dc.page_table, dc.index_pages, dc.bf16_pages, dc.bf16_table,

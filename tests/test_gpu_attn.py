@@ -357,3 +357,19 @@ def test_query_positions_other_than_the_length(route, H, Hq):
     base = dataclasses.replace(cache, pos=cache.seq_len.copy())
     ob, _ = gpu_attn(to_dev(base), 3)
     assert np.abs(ob.cpu().numpy()[1:] - out.cpu().numpy()[1:]).max() > 1e-3
+
+
+@pytest.mark.parametrize("route,H,Hq", [("per-head", 2, 2), ("grouped", 2, 8), ("multi-row", 1, 16)])
+def test_softmax_scale_and_rope_base(route, H, Hq):
+    """A softmax scale other than 1/sqrt(d) (0.2, a sharper softmax) and RoPE tables built
+    for base 500000 instead of 10000: both are inputs of the call, and each route must
+    apply them as the oracle does."""
+    plog.case(f"attention softmax scale 0.2 and RoPE base 500000, {route} route (H={H}, Hq={Hq})")
+    cache = build_cache(79, 2, [700, 333], H, 128, 4, 4, 32, 4, 16, Hq=Hq, books="random", index="random")
+    dc = to_dev(cache, rope_base=500000.0)
+    for t in (1, 2):
+        out, lse = gpu_attn(dc, t, scale=0.2)
+        ro, rl = orc.decode_attn(dataclasses.replace(cache.shape(500000.0), scale=0.2), cache.q[t],
+                                 cache.page_table, cache.index_pages, cache.bf16_pages, cache.bf16_table,
+                                 cache.codebooks, t, cache.pos, cache.seq_len, cache.q_end)
+        check(out, lse, ro, rl, f"t={t}")
