@@ -278,6 +278,45 @@ def test_encode_pages_and_reencode():
     np.testing.assert_array_equal(got, ref2)
 
 
+def test_page_ids_out_of_range_are_skipped():
+    """Chunk pages of lvq_encode_pages and source or destination pages of
+    lvq_reencode_pages that are negative or past their pool are skipped: nothing is
+    written for them, and every other page is coded as the oracle codes it."""
+    import sub_bit_loop_amd as lvq
+    T, Tc, G, d, H = 4, 4, 32, 128, 2
+    cache = build_cache(23, 1, [64], H, d, T, Tc, G, 4, 16, book_samples=1024)
+    c = G // Tc
+    nblk, ng = T // Tc, d // c
+    P = 12
+    toks = cache.k_tokens[0][:, :64]
+    pages = np.array([3, -1, 7, P, 0, 11, -5, P + 100], dtype=np.int32)
+    ip = torch.full((P, nblk, H, 2, 8, ng), 0xA5, dtype=torch.uint8, device="cuda")
+    lvq.lvq_encode_pages(dev(toks), dev(cache.codebooks), 1, T, Tc, G, dev(pages), ip)
+    torch.cuda.synchronize()
+    ref = np.full((P, nblk, H, 2, 8, ng), 0xA5, dtype=np.uint8)
+    r = orc.encode(toks, cache.codebooks, 1, T, Tc, G)
+    ok = (pages >= 0) & (pages < P)
+    for j in np.nonzero(ok)[0]:
+        ref[pages[j], :, :, 1] = r.idx[:, 8 * j:8 * j + 8].transpose(0, 2, 1, 3)
+    np.testing.assert_array_equal(ip.cpu().numpy(), ref)
+    # re-encode: the sink copy of tokens 0..7 into coded pages, with invalid entries mixed in
+    nbf = cache.bf16_pages.shape[0]
+    sp = int(cache.bf16_table[0, 0])
+    src = np.array([sp, -1, sp, nbf, sp], dtype=np.int32)
+    dst = np.array([2, 5, -1, 6, P], dtype=np.int32)
+    ip2 = torch.full((P, nblk, H, 2, 8, ng), 0x5A, dtype=torch.uint8, device="cuda")
+    lvq.lvq_reencode_pages(dev(cache.bf16_pages), dev(src), dev(dst), dev(cache.codebooks), T, Tc, G, ip2)
+    torch.cuda.synchronize()
+    got = ip2.cpu().numpy()
+    ref2 = np.full_like(got, 0x5A)
+    k0 = cache.k_tokens[0][:, :8]
+    v0 = cache.v_tokens[0][:, :8]
+    for kv, tk in ((0, k0), (1, v0)):
+        rr = orc.encode(tk, cache.codebooks, kv, T, Tc, G)
+        ref2[2, :, :, kv] = rr.idx[:, 0:8].transpose(0, 2, 1, 3)
+    np.testing.assert_array_equal(got, ref2)
+
+
 def test_reencode_layers_matches_per_layer_and_oracle():
     """lvq_reencode_pages_layers over 50 layers (two launches of at most 48) writes
     exactly what one lvq_reencode_pages call per layer writes, honours each layer's
