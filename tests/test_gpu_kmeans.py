@@ -118,6 +118,29 @@ def test_weighted_builder_matches_oracle(T, Tc, G, S, H, d, n_iter):
     _compare(out[:, 1], ref, [(b, h, g) for b in range(nblk) for h in range(H) for g in range(ng)])
 
 
+def test_weighted_builder_degenerate_weights():
+    """Books whose weights leave the seeding's corner rules in charge: all weights 0 (no
+    positive total: every draw takes floor(u S)), a single positive weight, three positive
+    weights (fewer than the 256 codes, so the D^2 terms run out), and one weight a million
+    times the others; the remaining books carry ordinary weights."""
+    T, Tc, G, S, H, d = 4, 2, 16, 300, 1, 64
+    print("\ncase weighted build, degenerate weights", flush=True)
+    bits, rng = _samples(67, T, S, H, d)
+    nblk, ng = T // Tc, d // (G // Tc)
+    draws = rng.random((nblk, H, ng, 256))
+    w = 10.0 ** rng.uniform(-1, 1, (nblk, S, H, ng))
+    w[0, :, 0, 0] = 0.0
+    w[0, :, 0, 1] = 0.0
+    w[0, 17, 0, 1] = 2.5
+    w[0, :, 0, 2] = 0.0
+    w[0, [5, 150, 299], 0, 2] = [1.0, 0.5, 3.0]
+    w[1, :, 0, 3] = 1.0
+    w[1, 42, 0, 3] = 1e6
+    out = _gpu_build(bits, draws, 0, T, Tc, G, 3, weights=w)
+    ref = orc.build_codebooks(bits, draws, Tc, G, 3, weights=w)
+    _compare(out[:, 0], ref, [(b, h, g) for b in range(nblk) for h in range(H) for g in range(ng)])
+
+
 def test_builder_at_the_lds_seeding_limit():
     """S = 8192, the largest count whose seeding keeps D^2 and running sums in LDS."""
     T, Tc, G, S, H, d = 4, 4, 32, 8192, 1, 64
