@@ -2,7 +2,8 @@
 lvq_decode_attn with a caller workspace, through the C ABI.  Same kernels, so the outputs
 must be bit-identical; one case is also checked against the oracle.  Several calls run in
 a row with different sizes (a smaller input after a larger one, then the larger again), on
-the per-head and on the multi-row route, so stale scratch contents can never leak."""
+the grouped (2 query heads per KV head), per-head (d = 64) and multi-row (8 query heads
+per KV head) routes, so stale scratch contents can never leak."""
 import numpy as np
 import pytest
 import torch
@@ -37,9 +38,10 @@ def _same(a, b):
 
 
 def test_noalloc_matches_the_workspace_entry_point():
-    print("\ncase lvq_decode_attn_noalloc: large, small, large again; per-head and multi-row routes", flush=True)
+    print("\ncase lvq_decode_attn_noalloc: large, small, large again; grouped, per-head and multi-row routes",
+          flush=True)
     big = to_dev(build_cache(61, 4, [3000, 2500, 1200, 900], 4, 128, 4, 4, 32, 4, 64, Hq=8,
-                             books="random", index="random"))
+                             books="random", index="random"))   # 2 query heads per KV head: grouped route
     small = build_cache(62, 2, [300, 101], 2, 64, 4, 2, 16, 4, 16, books="random", index="random")
     small_d = to_dev(small)
     wide = to_dev(build_cache(63, 2, [700, 1500], 1, 128, 4, 4, 32, 4, 64, Hq=8,
