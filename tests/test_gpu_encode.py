@@ -59,6 +59,7 @@ CASES = [  # T, Tc, G, d, N, H
     (2, 2, 32, 64, 17, 2),      # d = 64, c = 16
     (4, 4, 32, 128, 1, 3),      # a single token, an odd head count
     (4, 2, 16, 128, 65, 5),     # five heads (no power of two), one token past two tiles
+    (1, 1, 32, 64, 70, 3),      # d = 64, c = 32: two groups, so two-wave workgroups
 ]
 
 
