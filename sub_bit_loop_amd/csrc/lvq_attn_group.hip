@@ -14,8 +14,8 @@
 // FMAs per pair and head); a transposing reduction over the row (lanes trading halves of
 // their heads) leaves the score of head s / (16 / QH) in the 16 / QH lanes that keep that
 // head's running maximum and sum, and QH - 1 DPP row rotations give every lane the QH
-// weights for the value sum.  At QH = 4, about 7 lane operations per (token, head)
-// against 10.4 for the per-head kernel.  The work list of a KV head is the same as a
+// weights for the value sum.  At QH = 4, about 7.2 wave instructions per (token, head)
+// on the coded path against 9.6 for the per-head kernel.  The work list of a KV head is the same as a
 // query head's; its ranges go to quads, and each wave of a quad writes its own partial
 // record (QH rows, one per head) per sequence its range meets.  Four waves per SIMD
 // (16-wave workgroups).  From 8 query heads per KV head the multi-row kernel, whose float16
