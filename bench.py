@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=24)
-    ap.add_argument("--splits", type=int, default=0, help="coded splits per (b, head); 0 = automatic")
+    ap.add_argument("--splits", type=int, default=0, help="waves per query head of the decode call (the n_splits of its shape); 0 = automatic")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-encode", action="store_true", help="skip the encoder measurement")
     ap.add_argument("--headline-only", action="store_true",
