@@ -130,6 +130,52 @@ def _mass_over_max(scores, lse, lo, hi):
     # normalises by the largest score instead of the log-sum-exp
     return float(np.exp(scores[lo:hi] - np.max(scores)).sum())
 
+def _codewords_channel_major(cb_half):
+    # assembles the joint codeword channel-major (element i*Tc + tau) instead of step-major
+    nblk, H, ng, Tc, K, c = cb_half.shape
+    out = np.empty((nblk, H, ng, K, Tc * c), dtype=np.float64)
+    for tau in range(Tc):
+        out[..., tau::Tc] = cb_half[:, :, :, tau, :, :]
+    return out
+
+
+def _attend_lse_log2(qr, Kr, V, scale):
+    o, ls, s = orc_attend_orig(qr, Kr, V, scale)
+    return o, ls / np.log(2.0), s
+
+
+def _classes_sink_one_more(L, q_end, n_sink):
+    return orc_classes_orig(L, q_end, n_sink + 1 if L > n_sink else n_sink)
+
+
+def _decode_variant(head_map=None, q_at_length=False, rope_values=False):
+    def run(shp, q_bits, page_table, index_pages, bf16_pages, bf16_table, codebooks_bits, t, pos,
+            seq_len, q_end, return_scores=False, heads=None, pairs=None):
+        B, Hq, d = shp.B, shp.Hq, shp.d
+        grp = Hq // shp.H
+        cb = orc.bf16_to_f64(codebooks_bits)
+        q = orc.bf16_to_f64(q_bits)
+        out = np.full((B, Hq, d), np.nan)
+        lse = np.full((B, Hq), np.nan)
+        scores = {}
+        if pairs is None:
+            pairs = [(b, hq) for b in range(B) for hq in (range(Hq) if heads is None else heads)]
+        for b, hq in pairs:
+            L = int(seq_len[b])
+            h = head_map(hq, grp, shp.H) if head_map else hq // grp
+            K, V = orc_reconstruct_orig(shp, b, h, t, L, int(q_end[b]), page_table, index_pages,
+                                        bf16_pages, bf16_table, cb)
+            Kr = orc_rope_orig(K, np.arange(L), shp.rope_base)
+            if rope_values:
+                V = orc_rope_orig(V, np.arange(L), shp.rope_base)
+            qr = orc_rope_orig(q[b, hq], L if q_at_length else int(pos[b]), shp.rope_base)
+            o, ls, sc = orc_attend_orig(qr, Kr, V, shp.sm_scale)
+            out[b, hq], lse[b, hq] = o, ls
+            scores[(b, hq)] = sc
+        return (out, lse, scores) if return_scores else (out, lse)
+    return run
+
+
 MUTANTS = {
     "rope_sign": ("rope", _rope_sign_flipped),
     "rope_interleaved_pairs": ("rope", _rope_interleaved),
@@ -143,6 +189,12 @@ MUTANTS = {
     "wrong_step_slice": ("reconstruct_kv", _reconstruct_step_from_block_start),
     "mass_inclusive_end": ("needle_mass", _mass_inclusive_end),
     "mass_over_max": ("needle_mass", _mass_over_max),
+    "codewords_channel_major": ("joint_codewords", _codewords_channel_major),
+    "lse_in_log2": ("attend", _attend_lse_log2),
+    "sink_one_token_more": ("token_classes", _classes_sink_one_more),
+    "gqa_head_modulo": ("decode_attn", _decode_variant(head_map=lambda hq, grp, H: hq % H)),
+    "query_rotated_at_length": ("decode_attn", _decode_variant(q_at_length=True)),
+    "rope_on_values": ("decode_attn", _decode_variant(rope_values=True)),
 }
 
 

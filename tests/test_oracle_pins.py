@@ -194,11 +194,15 @@ def test_p2_tc1_is_per_step_coding():
 @pytest.mark.parametrize("L,Hq", [(37, 4), (1, 2), (64, 2)])
 def test_p4_all_bf16_is_textbook_attention(L, Hq):
     """q_end = 0: every token is bf16, so decode attention must equal RoPE (transformers'
-    rotate-half implementation) + scaled dot-product attention (torch).  Catches a RoPE sign
-    or pairing error, a wrong scale, a wrong GQA head map, a dropped sink or recent token."""
+    rotate-half implementation) + scaled dot-product attention (torch).  The queries sit at
+    positions other than the lengths (13 beyond the first sequence, 3 inside the second:
+    the position is an input of its own).  Catches a RoPE sign or pairing error, a wrong
+    scale, a wrong GQA head map, a query rotated at the wrong position, a dropped sink or
+    recent token."""
     H, d, T = 2, 64, 4
     cache = build_cache(12, 2, [L, L + 5], H, d, T, 2, 16, 4, 16, Hq=Hq, books="random",
                         q_end=[0, 0])
+    cache.pos = np.array([L + 13, 3])
     for t in (0, 3):
         out, lse = cache.oracle_attn(t)
         for b in range(2):
