@@ -176,6 +176,32 @@ def _decode_variant(head_map=None, q_at_length=False, rope_values=False):
     return run
 
 
+def _joint_block_offset(X, Tc, G):
+    # takes block beta's steps from beta + tau instead of beta * Tc + tau
+    T, N, H, d = X.shape
+    c = G // Tc
+    nblk, ng = T // Tc, d // c
+    out = np.empty((nblk, N, H, ng, G))
+    for beta in range(nblk):
+        for tau in range(Tc):
+            for g in range(ng):
+                out[beta, :, :, g, tau * c:(tau + 1) * c] = X[beta + tau][:, :, g * c:(g + 1) * c]
+    return out
+
+
+def _scatter_kv_swapped(idx, kv_sel, chunk_page, index_pages):
+    return orc_scatter_orig(idx, 1 - kv_sel, chunk_page, index_pages)
+
+
+def _scatter_slot_reversed(idx, kv_sel, chunk_page, index_pages):
+    nblk, N, H, ng = idx.shape
+    for n in range(N):
+        index_pages[int(chunk_page[n // 8]), :, :, kv_sel, 7 - n % 8, :] = idx[:, n, :, :]
+
+
+orc_scatter_orig = orc.scatter_index_pages
+
+
 MUTANTS = {
     "rope_sign": ("rope", _rope_sign_flipped),
     "rope_interleaved_pairs": ("rope", _rope_interleaved),
@@ -195,6 +221,9 @@ MUTANTS = {
     "gqa_head_modulo": ("decode_attn", _decode_variant(head_map=lambda hq, grp, H: hq % H)),
     "query_rotated_at_length": ("decode_attn", _decode_variant(q_at_length=True)),
     "rope_on_values": ("decode_attn", _decode_variant(rope_values=True)),
+    "joint_block_offset": ("joint_vectors", _joint_block_offset),
+    "scatter_kv_swapped": ("scatter_index_pages", _scatter_kv_swapped),
+    "scatter_slot_reversed": ("scatter_index_pages", _scatter_slot_reversed),
 }
 
 

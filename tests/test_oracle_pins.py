@@ -223,10 +223,12 @@ def test_p4_all_bf16_is_textbook_attention(L, Hq):
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("Tc,G", [(2, 16), (4, 32), (1, 32)])
 def test_p5_identity_codebook_end_to_end(Tc, G):
-    """Codeword k = joint vector of token k, so every distance to the right codeword is 0,
-    the indices are known, and the coded cache reproduces the bf16 tokens exactly: coded
-    attention must equal textbook attention on the raw tokens.  Catches any layout error in
-    gather, encode, page scatter, index-row read, step-slice read or value reconstruction."""
+    """Key codeword k = joint vector of key token k, value codeword qe - 1 - k = joint vector
+    of value token k (so the K and V index rows differ), every distance to the right
+    codeword is 0, the indices are known, and the coded cache reproduces the bf16 tokens
+    exactly: coded attention must equal textbook attention on the raw tokens.  Catches any
+    layout error in gather, encode, page scatter (K and V halves included), index-row read,
+    step-slice read or value reconstruction."""
     T, H, d, L, n_sink, n_recent = 4, 2, 64, 61, 4, 16
     cache = build_cache(13, 1, [L], H, d, T, Tc, G, n_sink, n_recent, books="random",
                         index="random", shuffle=True)
@@ -238,18 +240,19 @@ def test_p5_identity_codebook_end_to_end(Tc, G):
     cb = orc.bf16_to_f64(cache.codebooks).copy()
     rng = np.random.default_rng(5)
     cb[...] = 50.0 + rng.standard_normal(cb.shape)            # far-away filler codewords
+    order = {0: np.arange(qe), 1: np.arange(qe)[::-1]}        # codeword of token k
     for kv in (0, 1):
         for beta in range(nblk):
             for tau in range(Tc):
                 for g in range(ng):
-                    cb[beta, kv, :, g, tau, :qe, :] = X[kv][beta * Tc + tau, :qe, :, g * c:(g + 1) * c].transpose(1, 0, 2)
+                    cb[beta, kv, :, g, tau][:, order[kv], :] = X[kv][beta * Tc + tau, :qe, :, g * c:(g + 1) * c].transpose(1, 0, 2)
     cbb = synth.f32_to_bf16_bits(cb.astype(np.float32))
     assert np.array_equal(orc.bf16_to_f64(cbb)[..., :qe, :], cb[..., :qe, :])
     ip = np.zeros_like(cache.index_pages)
     for kv in (0, 1):
         toks = cache.k_tokens[0] if kv == 0 else cache.v_tokens[0]
         r = orc.encode(toks[:, :qe], cbb, kv, T, Tc, G)
-        expect = np.broadcast_to(np.arange(qe)[None, :, None, None], r.idx.shape)
+        expect = np.broadcast_to(order[kv][None, :, None, None], r.idx.shape)
         np.testing.assert_array_equal(r.idx, expect)
         assert np.all(r.d1 == 0)
         orc.scatter_index_pages(r.idx, kv, cache.page_table[0, :qe // 8], ip)
