@@ -72,6 +72,11 @@ def test_lloyd_matches_scikit_learn():
 
 
 def test_lloyd_update_is_member_mean_and_assignment_is_nearest():
+    # the assignment sees the centers rounded to bf16: 1 + 2^-9 rounds to 1, so the midpoint
+    # moves from 1.5 + 2^-10 to 1.5 and the sample 1.5 + 2^-11 goes to the second center
+    x = np.array([[1.5 + 2.0 ** -11]])
+    C1 = orc.lloyd(x, np.array([[1.0 + 2.0 ** -9], [2.0]]), 1)
+    np.testing.assert_array_equal(C1, [[1.0 + 2.0 ** -9], [1.5 + 2.0 ** -11]])
     rng = np.random.default_rng(6)
     X = orc.round_bf16(rng.standard_normal((600, 8)))
     C0 = X[rng.choice(600, 32, replace=False)]
@@ -114,7 +119,8 @@ def test_build_codebooks_layout_and_shape():
                 np.testing.assert_array_equal(books[beta, 0, g, tau], want[:, tau * 8:(tau + 1) * 8])
 
 
-@pytest.mark.parametrize("mutant", ["ge_not_gt", "highest_tie", "empty_to_zero", "ceil_first"])
+@pytest.mark.parametrize("mutant", ["ge_not_gt", "highest_tie", "empty_to_zero", "ceil_first",
+                                    "d2_last_center_only", "assign_unrounded"])
 def test_kmeans_mutants_are_caught(mutant, monkeypatch):
     """Plausible mistakes planted in the oracle (on the CPU) fail one of the pins above."""
     def seed_mut(X, draws, K=orc.NCODES):
@@ -133,14 +139,15 @@ def test_kmeans_mutants_are_caught(mutant, monkeypatch):
             else:
                 i = min(int(draws[k] * S), S - 1)
             picks[k] = i
-            D2 = np.minimum(D2, orc.sq_dist_sequential(X, X[i]))
+            D2i = orc.sq_dist_sequential(X, X[i])
+            D2 = D2i if mutant == "d2_last_center_only" else np.minimum(D2, D2i)
         return picks
 
     def lloyd_mut(X, centers, n_iter, bf16_assign=True):
         C = np.array(centers, dtype=np.float64)
         K, G = C.shape
         for _ in range(n_iter):
-            A = orc.round_bf16(C) if bf16_assign else C
+            A = orc.round_bf16(C) if bf16_assign and mutant != "assign_unrounded" else C
             D = ((X[:, None, :] - A[None]) ** 2).sum(-1)
             assign = (K - 1 - np.argmin(D[:, ::-1], axis=1)) if mutant == "highest_tie" else np.argmin(D, axis=1)
             new = C.copy()
@@ -157,7 +164,8 @@ def test_kmeans_mutants_are_caught(mutant, monkeypatch):
     monkeypatch.setattr(orc, "lloyd", lloyd_mut)
     failed = 0
     checks = [test_kmeanspp_hand_case, test_empty_cluster_keeps_its_center,
-              test_kmeanspp_picks_every_distinct_sample_once]
+              test_kmeanspp_picks_every_distinct_sample_once,
+              test_lloyd_update_is_member_mean_and_assignment_is_nearest]
     if mutant == "highest_tie":
         # duplicate centers tie exactly: the lowest index must win
         def tie_check():
