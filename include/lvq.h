@@ -92,7 +92,9 @@ const char* lvq_last_error(void);
  * these distances with a matrix product; the kernel uses the expansion
  * |x|^2 - 2 x.C + |C|^2 on bf16 MFMA with float32 accumulation and recomputes
  * in float64, by direct differences, every vector whose top two candidates
- * are too close for float32 to separate them).
+ * are too close for float32 to separate them; vectors whose products fall below
+ * the float32 normal range or whose norms overflow it always take that path, so
+ * the codes are the float64 ones at every finite bf16 input).
  *
  * Supported encoder shapes: G in {16, 32}; c = G/Tc in {8, 16, 32} for
  * G = 32 and {4, 8, 16} for G = 16; d in {64, 128}.
