@@ -129,12 +129,14 @@ def test_many_sequences_token_balanced_split():
         np.testing.assert_allclose(o, outs[0], rtol=2e-5, atol=2e-6)
 
 
-def test_index_pool_beyond_4gib():
-    """An index pool over 4 GiB takes the kernel's 64-bit page addressing.  The same pages
+@pytest.mark.parametrize("route,H,Hq", [("per-head", 2, 2), ("multi-row", 1, 16)])
+def test_index_pool_beyond_4gib(route, H, Hq):
+    """An index pool over 4 GiB takes the kernels' 64-bit page addressing.  The same pages
     moved to the top of such a pool give the same bits as the compact pool (page
     placement invariance), so the 32-bit and 64-bit address paths agree."""
-    plog.case("attention, index pool over 4 GiB (64-bit page addressing): bit-identical to the compact pool")
-    cache = build_cache(39, 1, [2000], 2, 128, 4, 4, 32, 4, 64, books="random", index="random")
+    plog.case(f"attention, index pool over 4 GiB (64-bit page addressing), {route} route: "
+              f"bit-identical to the compact pool")
+    cache = build_cache(39, 1, [2000], H, 128, 4, 4, 32, 4, 64, Hq=Hq, books="random", index="random")
     dc = to_dev(cache)
     ref, ref_lse = gpu_attn(dc, 1)
     pool = dc.index_pages
