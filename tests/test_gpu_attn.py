@@ -375,3 +375,20 @@ def test_softmax_scale_and_rope_base(route, H, Hq):
                                  cache.page_table, cache.index_pages, cache.bf16_pages, cache.bf16_table,
                                  cache.codebooks, t, cache.pos, cache.seq_len, cache.q_end)
         check(out, lse, ro, rl, f"t={t}")
+
+
+@pytest.mark.parametrize("route,H,Hq", [("per-head", 2, 2), ("grouped", 2, 8), ("multi-row", 1, 16)])
+def test_max_seq_len_far_above_the_lengths(route, H, Hq):
+    """max_seq_len sizes the automatic split; here it is 40000 for sequences of 37 and 100
+    tokens, so most waves get empty ranges and write no record (or records of weight 0)
+    that the merge must ignore.  The result must not depend on it."""
+    plog.case(f"attention with max_seq_len 40000 over lengths [37, 100], {route} route (H={H}, Hq={Hq})")
+    cache = build_cache(80, 2, [37, 100], H, 128, 4, 4, 32, 4, 16, Hq=Hq, books="random", index="random")
+    tight = to_dev(cache)
+    loose = to_dev(cache, max_seq_len=40000)
+    for t in (0, 3):
+        out, lse = gpu_attn(loose, t)
+        ro, rl = cache.oracle_attn(t)
+        check(out, lse, ro, rl, f"t={t}")
+        o2, l2 = gpu_attn(tight, t)
+        np.testing.assert_allclose(out.cpu().numpy(), o2.cpu().numpy(), rtol=2e-5, atol=2e-6)
