@@ -78,15 +78,10 @@ __device__ __forceinline__ float key_med3(float a, float b, float c) {
   return r;
 }
 
-// Exchange with lane ^ 16 (v_permlane16_swap) or lane ^ 32 (v_permlane32_swap), VALU
-// instructions with no LDS round trip.  Each lane gets its own value and its partner's
-// as (lo, hi), where lo is the value of the pair's lower lane on both lanes, so an
-// operation of (lo, hi) gives bit-identical results in the two lanes.
-__device__ __forceinline__ void pair16(float v, float& lo, float& hi) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  lo = __uint_as_float(r[0]);
-  hi = __uint_as_float(r[1]);
-}
+// Exchange with lane ^ 32 (v_permlane32_swap), a VALU instruction with no LDS round
+// trip.  Each lane gets its own value and its partner's as (lo, hi), where lo is the
+// value of the pair's lower lane on both lanes, so an operation of (lo, hi) gives
+// bit-identical results in the two lanes.
 __device__ __forceinline__ void pair32(float v, float& lo, float& hi) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   lo = __uint_as_float(r[0]);

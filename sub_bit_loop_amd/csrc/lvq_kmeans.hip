@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kKmThreads) void update_kernel(KmeansArgs a) {
         const int rank = __popcll(same & below);
         const int pos = cursor[c] + rank;
         list[pos] = (uint16_t)s;
-        if (rank == __popcll(same) - 1) cursor[c] = pos + 1;
+        if (rank == (int)__popcll(same) - 1) cursor[c] = pos + 1;
       }
     }
   }
