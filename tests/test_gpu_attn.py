@@ -244,7 +244,6 @@ def test_needle_64k():
     """Long-context retrieval shape: B=1, 65536 tokens, 16 heads, T=4, Tc=2, G=16, split-K
     over the coded tokens; every head at every loop step: output, lse, every score and the
     needle's attention mass against the oracle."""
-    import sub_bit_loop_amd as lvq  # noqa: F401
     plog.case("attention, 64K needle B=1 L=65536 H=16 d=128 T=4 Tc=2 G=16: all 16 heads, all 4 steps")
     cache = build_cache_light(3, 1, [65536], 16, 128, 4, 2, 16, 4, 64, books="kmeans",
                               book_samples=1024)

@@ -10,7 +10,6 @@ import torch
 
 from cachebuild import build_cache
 from gpu_helpers import attn_close, shape_of, to_dev
-from oracle import lvq_oracle as orc
 
 pytestmark = pytest.mark.gpu
 
