@@ -391,3 +391,20 @@ def test_max_seq_len_far_above_the_lengths(route, H, Hq):
         check(out, lse, ro, rl, f"t={t}")
         o2, l2 = gpu_attn(tight, t)
         np.testing.assert_allclose(out.cpu().numpy(), o2.cpu().numpy(), rtol=2e-5, atol=2e-6)
+
+
+@pytest.mark.parametrize("route,H,Hq", [("per-head", 2, 2), ("grouped", 2, 8), ("multi-row", 1, 16)])
+def test_three_hundred_short_sequences(route, H, Hq):
+    """B = 300 sequences of 1 to 200 tokens (empty slots included): the work-list scan runs
+    over five chunks of 64 sequences, and a wave's range meets many sequences, writing a
+    record for each; every (sequence, head) against the oracle."""
+    plog.case(f"attention over 300 short sequences, {route} route (H={H}, Hq={Hq})")
+    rng = np.random.default_rng(81)
+    lengths = rng.integers(1, 201, 300)
+    lengths[[7, 150, 299]] = 0
+    cache = build_cache(81, 300, lengths.tolist(), H, 128, 4, 4, 32, 4, 16, Hq=Hq, books="random",
+                        index="random")
+    dc = to_dev(cache)
+    out, lse = gpu_attn(dc, 2)
+    ro, rl = cache.oracle_attn(2)
+    check(out, lse, ro, rl, "t=2")
