@@ -68,6 +68,8 @@ EDGE = [  # config, B, lengths, H, Hq, d, T, Tc, G, n_sink, n_recent
     (75, 2, [129, 64], 2, 4, 128, 4, 4, 32, 4, 16),       # grouped route at GQA 2, ragged
     (76, 3, [72, 79, 80], 2, 2, 128, 4, 4, 32, 4, 64),    # q_end = 8, 8, 16: coded tokens 4..7 share page 0 with the sink
     (77, 2, [72, 80], 1, 16, 128, 4, 4, 32, 8, 64),       # n_sink = 8 = q_end: an empty coded range, multi-row route
+    (82, 2, [333, 90], 2, 6, 128, 4, 4, 32, 4, 16),       # 3 query heads per KV head: the per-head kernel's GQA map
+    (83, 2, [333, 90], 1, 12, 128, 4, 2, 32, 4, 16),      # 12 per KV head: multi-row route, 4 padding rows
 ]
 
 
