@@ -202,6 +202,25 @@ def _scatter_slot_reversed(idx, kv_sel, chunk_page, index_pages):
 orc_scatter_orig = orc.scatter_index_pages
 
 
+def _split_drops_chunk_end(qr, Kr, V, scale, bounds):
+    # each chunk of more than one key stops one key short of its bound
+    parts = []
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        parts += orc_split_orig(qr, Kr, V, scale, [lo, hi - 1 if hi - lo > 1 else hi])
+    return parts
+
+
+def _split_unnormalised_max(qr, Kr, V, scale, bounds):
+    # keeps each chunk's weights relative to the global maximum but reports the chunk maximum
+    parts = orc_split_orig(qr, Kr, V, scale, bounds)
+    s = (Kr @ qr) * scale
+    M = s.max()
+    return [(m, l * np.exp(m - M) if l > 0 else l, o * np.exp(m - M) if l > 0 else o) for m, l, o in parts]
+
+
+orc_split_orig = orc.split_partials
+
+
 MUTANTS = {
     "rope_sign": ("rope", _rope_sign_flipped),
     "rope_interleaved_pairs": ("rope", _rope_interleaved),
@@ -224,6 +243,8 @@ MUTANTS = {
     "joint_block_offset": ("joint_vectors", _joint_block_offset),
     "scatter_kv_swapped": ("scatter_index_pages", _scatter_kv_swapped),
     "scatter_slot_reversed": ("scatter_index_pages", _scatter_slot_reversed),
+    "split_drops_chunk_end": ("split_partials", _split_drops_chunk_end),
+    "split_mixed_maxima": ("split_partials", _split_unnormalised_max),
 }
 
 
